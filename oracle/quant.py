@@ -1,0 +1,104 @@
+"""Asymmetric min-max KV quantization (oracle; test infrastructure only).
+
+Source: TailorKV article ("TailorKV's hybrid compression architecture"),
+section 2.2, which prints a 1-bit quantizer: scale = (max - min) / (2**1 - 1),
+zero_point = min, q = clamp(round((x - zero_point) / scale), 0, 1), with scale
+and zero point returned as fp16.  The same section quantizes the key cache per
+channel and the value cache per token; its section 5.2 asks for group sizes that
+are multiples of 64.  The on-device KV article, section 3.1, gives INT4 keys
+asymmetric per channel with a zero point and INT4 values in groups of 32/64.
+
+Readings taken where the pages are silent or garbled (each listed in the design doc):
+  * b-bit generalization: the printed denominator 2**1 - 1 becomes 2**b - 1.
+  * The printed code takes one min/max over its whole input; we take it per
+    64-element group (the ``group_size`` argument it never uses).
+  * Arithmetic: fp32 for max - min, the division and the code; the stored
+    scale and zero point are fp16 (round to nearest even) and the code is
+    computed against those stored fp16 values, so dequantization sees exactly
+    what quantization assumed.  Rounding is half-to-even (``torch.round``).
+  * A zero scale (all-equal group) yields code 0; the zero point then holds the
+    value exactly.  -0.0 as a minimum is stored as +0.0.
+  * Values are asymmetric for V as well (the printed quantizer and the stored
+    zero point); the on-device article's "symmetric V" is not built.
+  * A group is quantized only once all 64 of its tokens exist; until then its
+    tokens stay fp16 (a "tail").  V follows K's group boundary.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+GROUP = 64
+
+
+def quantize_groups(x16: np.ndarray, bits: int):
+    """Quantize each length-64 group along the last axis.
+
+    x16: float16 array [..., 64].  Returns (codes uint8 [..., 64],
+    scale float16 [...], zero float16 [...]).
+    """
+    assert x16.dtype == np.float16 and x16.shape[-1] == GROUP
+    assert bits in (1, 4)
+    levels = F32(2 ** bits - 1)
+    x = x16.astype(F32)
+    mn = x.min(axis=-1)
+    mx = x.max(axis=-1)
+    s32 = (mx - mn) / levels                      # fp32, round to nearest even
+    s16 = s32.astype(np.float16)
+    z16 = (mn + F32(0.0)).astype(np.float16)      # exact: mn is an fp16 value
+    assert np.all(np.isfinite(s16)), "group range overflows the fp16 scale"
+    s = s16.astype(F32)[..., None]
+    z = z16.astype(F32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = (x - z) / s                           # fp32 sub, fp32 div
+    code = np.clip(np.rint(t), F32(0.0), levels)  # half to even
+    code = np.where(s == 0, F32(0.0), code)
+    return code.astype(np.uint8), s16, z16
+
+
+def dequantize(code: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
+    """code * scale + zero in fp64 (exact for fp16 scale/zero and codes < 16)."""
+    return code.astype(np.float64) * s16.astype(np.float64) + z16.astype(np.float64)
+
+
+def quantize_keys(k16: np.ndarray, bits: int):
+    """Per-channel K quantization over complete 64-token groups.
+
+    k16: float16 [N, D] for one (sequence, KV head).  Returns
+    (codes uint8 [nq, D], scale f16 [nq/64, D], zero f16 [nq/64, D]) where
+    nq = 64 * floor(N / 64); rows >= nq are the fp16 tail.
+    """
+    n, d = k16.shape
+    ng = n // GROUP
+    x = k16[: ng * GROUP].reshape(ng, GROUP, d).transpose(0, 2, 1)   # [ng, D, 64]
+    code, s, z = quantize_groups(np.ascontiguousarray(x), bits)
+    return code.transpose(0, 2, 1).reshape(ng * GROUP, d), s, z
+
+
+def quantize_values(v16: np.ndarray, bits: int):
+    """Per-token V quantization in 64-channel groups, over complete 64-token groups.
+
+    v16: float16 [N, D].  Returns (codes uint8 [nq, D], scale f16 [nq, D/64],
+    zero f16 [nq, D/64]).
+    """
+    n, d = v16.shape
+    nq = (n // GROUP) * GROUP
+    x = v16[:nq].reshape(nq, d // GROUP, GROUP)
+    code, s, z = quantize_groups(np.ascontiguousarray(x), bits)
+    return code.reshape(nq, d), s, z
+
+
+def dequant_keys(code, s, z) -> np.ndarray:
+    """fp64 K~ [nq, D] from per-channel group codes."""
+    nq, d = code.shape
+    rep_s = np.repeat(s, GROUP, axis=0)
+    rep_z = np.repeat(z, GROUP, axis=0)
+    return dequantize(code, rep_s, rep_z)
+
+
+def dequant_values(code, s, z) -> np.ndarray:
+    """fp64 V~ [nq, D] from per-token channel-group codes."""
+    nq, d = code.shape
+    rep_s = np.repeat(s, GROUP, axis=1)
+    rep_z = np.repeat(z, GROUP, axis=1)
+    return dequantize(code, rep_s, rep_z)
