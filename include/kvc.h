@@ -1,0 +1,245 @@
+/*
+ * kvc.h -- one decode step of attention over a jointly sparsified and quantized
+ * KV cache, on AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operations follow the problem statement of four pages:
+ *   [TKV]  TailorKV article (http://www.ijyty.com/news/1204784): 1-bit layers
+ *          with K quantized per channel and V per token (section 2.2, printed
+ *          quantizer), critical channels s_i = |q_i| max|K_i| and approximate
+ *          scores from them, Top-K token retrieval (section 2.3), the knobs
+ *          critical_channels = 8 and sparse_ratio = 0.03 (section 5.1), group
+ *          sizes that are multiples of 64 (section 5.2).
+ *   [MTG]  meeting-LLM KV article (https://www.ufo.work/2026/545.html):
+ *          query-aware scores and Top-K (section 2.2), hot fp16 / warm
+ *          quantized tiers (section 3.1), the FlashDecoding-Sparse decode step
+ *          with online softmax (section 8.1).
+ *   [SRV]  KV compression survey (https://bbs.huaweicloud.com/blogs/490932):
+ *          16-token PagedAttention blocks and block tables (section 1),
+ *          attention sinks plus a recent window (section 3.1), H2O cumulative
+ *          scores (section 3.2).
+ *   [DEV]  on-device KV article (https://www.ufo.work/2026/495.html): INT4 K
+ *          asymmetric per channel with zero point, V in groups of 64
+ *          (section 3.1); a fused dequantize -> QK^T -> softmax -> PV kernel
+ *          with scales and zero points held on chip (section 3.2).
+ *
+ * Conventions for every entry point
+ *   - All data pointers are device pointers owned by the caller.  The library
+ *     allocates nothing, frees nothing and keeps no state between calls; it is
+ *     reentrant.  Calls that share a workspace or outputs must not overlap.
+ *   - Every call validates its arguments on the host, enqueues kernels on
+ *     ``stream`` and returns without synchronizing.  On a validation error
+ *     nothing is enqueued and no output is touched.  Device faults surface at
+ *     the caller's next synchronization.
+ *   - fp16 data is passed as uint16_t bit patterns (IEEE binary16).
+ *   - head_dim is 128 and the quantization group is 64; other values return
+ *     KVC_ERR_UNSUPPORTED.
+ *   - Code and row pointers must be 16-byte aligned, metadata pointers 8-byte
+ *     aligned (KVC_ERR_INVALID otherwise).
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+#define KVC_HEAD_DIM 128
+#define KVC_GROUP 64
+#define KVC_MAX_GQA 8          /* query heads per KV head supported by attend */
+
+typedef int32_t kvc_status;
+enum {
+  KVC_OK = 0,
+  KVC_ERR_INVALID = 1,      /* null pointer, bad range, misalignment */
+  KVC_ERR_SHAPE = 2,        /* inconsistent sizes */
+  KVC_ERR_UNSUPPORTED = 3,  /* format / mode / size not built */
+  KVC_ERR_WORKSPACE = 4,    /* workspace missing or too small */
+  KVC_ERR_HIP = 5           /* a kernel launch failed (hipGetLastError) */
+};
+
+enum { KVC_FMT_FP16 = 0, KVC_FMT_INT4 = 1, KVC_FMT_INT1 = 2 };
+enum { KVC_SCORE_EXACT = 0, KVC_SCORE_CRITICAL = 1, KVC_SCORE_EXTERNAL = 2 };
+enum { KVC_ATTEND_DENSE = 0, KVC_ATTEND_DROP = 1, KVC_ATTEND_KEEP = 2 };
+enum { KVC_OP_SCORE_TOPK = 1, KVC_OP_ATTEND = 2 };
+
+/*
+ * kvc_cache -- description of one layer's KV cache (plain data, caller-owned
+ * device buffers).  B sequences, Hkv KV heads, D = 128 channels.
+ *
+ * Token addressing.  Let P = page_size if page_size > 0, else max_tokens.
+ * Token t of sequence b lives on logical page t / P at offset t % P; the
+ * physical page is block_table[b * max_pages + t / P] when paged, else b.
+ * Its "slot" for KV head g is  slot = (phys * Hkv + g) * P + t % P.
+ * (Paging follows [SRV] section 1: logical blocks mapped to physical blocks.)
+ *
+ * Quantized store (format INT4 or INT1; [TKV] 2.2, [DEV] 3.1).  K is quantized
+ * per channel over each complete 64-token group, V per token over each
+ * 64-channel half, both asymmetric min-max with fp16 scale s and zero z:
+ *     s = fp16((max - min) / (2^b - 1) + 0)   (fp32 subtract and divide)
+ *     z = fp16(min + 0)
+ *     code = s == 0 ? 0 : clamp(rint((x - z) / s), 0, 2^b - 1)   (fp32, half-even)
+ * and dequantized as code * s + z.  A group is quantized when its 64th token
+ * is appended; until then its tokens live in the fp16 tail.
+ *
+ *   k_codes, v_codes  Code tiles.  INT4: one 1024-byte tile per 16 slots,
+ *     tile index slot / 16.  INT1: one 1024-byte unit per 64 slots, unit index
+ *     slot / 64.  Within a tile/unit, byte offset 16*L + 4*d addresses dword d
+ *     of "lane" L (0..63, L = 16*hi + lo); bit positions below.
+ *     Nibble slot j (0..7) of an INT4 dword sits at bits 16*(j&1) + 4*(j>>1).
+ *       INT4 K, token n (0..15) of the tile, channel c:
+ *         L = 16*(c/32) + n, d = (c%32)/8, j = c%8.
+ *       INT4 V, token n, channel c:
+ *         L = 16*(n/4) + c%16, d = (c/16)/2, j = 4*((c/16)%2) + n%4.
+ *     Bit positions of an INT1 dword (32 codes): code k (0..31) -> word
+ *       w = k/2, half h = k%2, variant v = w/4, p = 6 + w%4; bit
+ *         v=0: p + 16h      v=1: p + 4 + 16h
+ *         v=2: p - 4 + 16h  v=3: h ? p + 8 : (p + 24) % 32
+ *       INT1 K, token n (0..63) of the unit, channel c:
+ *         L = 16*(c/32) + n%16, d = n/16, k = c%32.
+ *       INT1 V, token n, channel c (ct = c/16, i = n%4):
+ *         L = 16*((n%16)/4) + c%16, d = n/16,
+ *         k = 2*(4*((ct/4)*2 + i/2) + ct%4) + i%2.
+ *     (These orders let a shift and one mask-and-or per pair of codes produce
+ *     fp16 matrix-core operands.)
+ *   k_meta  fp16 [B][Hkv][max_tokens/64][2][128]: [..][0][c] scale, [..][1][c]
+ *     zero of channel c for that 64-token group (per sequence, not paged).
+ *   v_meta  fp16 [slot][4]: scale of channels 0-63, scale of 64-127, zero of
+ *     0-63, zero of 64-127.
+ *   k_tail, v_tail  fp16 [B][Hkv][64][128]: row r holds token 64*floor(n/64) + r
+ *     of the incomplete group (n = seq_lens[b]).
+ *
+ * fp16 rows (format FP16: the main store; INT4/INT1: an optional full copy of
+ * every appended token, required by KVC_ATTEND_KEEP; [MTG] 3.1 hot tier,
+ * [TKV] 3.1 key-token buffer):
+ *   k16, v16  fp16 [slot][128].
+ *   kT        optional fp16 [B][Hkv][128][max_tokens], channel-major K
+ *             (page_size must be 0); lets critical-channel scoring read 8
+ *             channels without touching whole rows ([TKV] 2.3).
+ *   k_absmax  float32 [B][Hkv][128]: max |K| per channel over all appended
+ *             tokens (fp16-exact values); zero-filled by the caller at creation.
+ *   seq_lens  int32 [B]: tokens cached per sequence; updated by
+ *             kvc_quantize_append.
+ */
+typedef struct kvc_cache {
+  int32_t abi_version;     /* KVC_ABI_VERSION */
+  int32_t format;          /* KVC_FMT_* */
+  int32_t batch;           /* B >= 1 */
+  int32_t num_kv_heads;    /* Hkv >= 1 */
+  int32_t head_dim;        /* 128 */
+  int32_t group_size;      /* 64 */
+  int32_t page_size;       /* 0 = contiguous; else multiple of 16 (64 for INT1) */
+  int32_t max_tokens;      /* per-sequence capacity, multiple of 64 (and of page_size) */
+  int32_t max_pages;       /* block_table row length (paged) */
+  int32_t num_pages;       /* physical pages in each pool (paged) */
+  const int32_t* block_table;
+  int32_t* seq_lens;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  uint16_t* k_meta;
+  uint16_t* v_meta;
+  uint16_t* k_tail;
+  uint16_t* v_tail;
+  uint16_t* k16;
+  uint16_t* v16;
+  uint16_t* kT;
+  float* k_absmax;
+} kvc_cache;
+
+/*
+ * kvc_quantize_append -- append n_new[b] tokens to every sequence b ([TKV] 2.2,
+ * [DEV] 3.1 and 3.2's online calibration from the appended values).
+ *   k_new, v_new  fp16 [B][n_new_max][Hkv][128]; rows >= n_new[b] are ignored.
+ *   n_new         device int32 [B], or NULL for n_new_max everywhere.
+ *   overflow      device int32 or NULL: set to 1 when some sequence would
+ *                 exceed max_tokens; that sequence is left unchanged.
+ * Writes every 64-token group the append completes (codes, k_meta, v_meta),
+ * the new tail rows, k16/v16/kT rows when those pointers are set, k_absmax,
+ * and finally seq_lens[b] += n_new[b].
+ */
+kvc_status kvc_quantize_append(const kvc_cache* cache, const uint16_t* k_new,
+                               const uint16_t* v_new, const int32_t* n_new,
+                               int32_t n_new_max, int32_t* overflow,
+                               hipStream_t stream);
+
+/*
+ * kvc_score_topk -- rank tokens and select the Top-K per (sequence, KV head)
+ * ([TKV] 2.3, [MTG] 2.2, [SRV] 3).
+ *   q           fp16 [B][Hq][128]; query head h belongs to KV head h / (Hq/Hkv).
+ *   score_mode  KVC_SCORE_EXACT: all 128 channels; KVC_SCORE_CRITICAL: the
+ *               n_crit channels with largest max_h|q_{h,c}| * k_absmax[c]
+ *               (ties to the lower channel); KVC_SCORE_EXTERNAL: r_t = ext[t].
+ *               Exact/critical score of token t: max over the group's heads of
+ *               the fp64 sum, channel by channel in ascending order from +0.0,
+ *               of q_{h,c} * k~_{t,c} (k~ = fp16 row or code*s + z), plus 0.0.
+ *   ext         float32 [B][Hkv][max_tokens] (EXTERNAL only).
+ *   candidates  tokens in [n_sink, n - n_window), n = seq_lens[b].
+ *   k_per_seq   device int32 [B] or NULL (then k_max); k_b = min(k, #candidates).
+ *   out_idx     int32 [B][Hkv][k_max]: the k_b best tokens under (score desc,
+ *               index asc), in ascending order, then -1.
+ *   out_scores  optional fp64 [B][Hkv][max_tokens]: r_t of every candidate.
+ *   out_channels optional int32 [B][Hkv][n_crit]: ascending critical channels.
+ *   workspace   kvc_workspace_bytes(KVC_OP_SCORE_TOPK, ...) bytes.
+ * Hq/Hkv must be 1..16; n_crit 1..128.
+ */
+kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num_q_heads,
+                          int32_t score_mode, int32_t n_crit, const float* ext,
+                          int32_t n_sink, int32_t n_window, const int32_t* k_per_seq,
+                          int32_t k_max, int32_t* out_idx, double* out_scores,
+                          int32_t* out_channels, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * kvc_attend_decode -- softmax(q K~^T * sm_scale) V~ for every query head over
+ * its attended tokens, dequantizing inside the kernel ([DEV] 3.2, [MTG] 8.1,
+ * [TKV] 2.1); query head h reads KV head h / G, G = Hq / Hkv (1..8).
+ *   mode  KVC_ATTEND_DENSE: every cached token.
+ *         KVC_ATTEND_DROP: sinks [0, n_sink), the valid entries of sel, and
+ *           the window [max(n - n_window, n_sink), n); other tokens dropped.
+ *         KVC_ATTEND_KEEP (INT4/INT1 with k16/v16): every token; those of the
+ *           DROP set read from the fp16 rows, the rest from codes or tail.
+ *   sel   int32 [B][Hkv][k_max], ascending, -1 padded (kvc_score_topk's
+ *         out_idx); entries outside [n_sink, n - n_window) are ignored.
+ *   out   float32 [B][Hq][128];  lse  float32 [B][Hq] (natural log; -inf and
+ *         out = 0 when nothing is attended).
+ *   logits optional float32, row (b, h) at logits + (b*Hq + h)*logits_stride:
+ *         DENSE/KEEP: position t = token t (t < n); DROP: position j with
+ *         j < n_sink -> token j, j - n_sink < k_max -> sel entry, then window
+ *         token max(n - n_window, n_sink) + (j - n_sink - k_max); positions
+ *         that attend nothing hold -inf.  Values are q.k~ * sm_scale.
+ *   workspace  kvc_workspace_bytes(KVC_OP_ATTEND, ...) bytes (split partials).
+ */
+kvc_status kvc_attend_decode(const kvc_cache* cache, const uint16_t* q, int32_t num_q_heads,
+                             float sm_scale, int32_t mode, const int32_t* sel, int32_t k_max,
+                             int32_t n_sink, int32_t n_window, float* out, float* lse,
+                             float* logits, int64_t logits_stride, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kvc_accum_scores -- H2O cumulative scores ([SRV] 3.2): for every attended
+ * position of a previous kvc_attend_decode with the same mode/sel/n_sink/
+ * n_window, acc[b][g][t] += sum over the G query heads of KV head g of
+ * exp(logit - lse).  acc is float32 [B][Hkv][max_tokens].
+ */
+kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const float* logits,
+                            int64_t logits_stride, const float* lse, int32_t mode,
+                            const int32_t* sel, int32_t k_max, int32_t n_sink, int32_t n_window,
+                            float* acc, hipStream_t stream);
+
+/* Workspace bytes for op (KVC_OP_*); 0 on invalid arguments. Host only. */
+size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t k_max);
+
+/* Static description of a status code. */
+const char* kvc_status_str(kvc_status status);
+
+/* KVC_ABI_VERSION of the built library. */
+int32_t kvc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVC_H_ */

@@ -17,7 +17,9 @@ Readings taken where the pages are silent or garbled (each listed in the design doc):
     computed against those stored fp16 values, so dequantization sees exactly
     what quantization assumed.  Rounding is half-to-even (``torch.round``).
   * A zero scale (all-equal group) yields code 0; the zero point then holds the
-    value exactly.  -0.0 as a minimum is stored as +0.0.
+    value exactly.  Zeros are stored as +0.0: a -0.0 minimum, and the scale of
+    a group of zeros of both signs (whose max - min could be -0.0 depending on
+    which zero the reductions return).
   * Values are asymmetric for V as well (the printed quantizer and the stored
     zero point); the on-device article's "symmetric V" is not built.
   * A group is quantized only once all 64 of its tokens exist; until then its
@@ -43,7 +45,7 @@ def quantize_groups(x16: np.ndarray, bits: int):
     x = x16.astype(F32)
     mn = x.min(axis=-1)
     mx = x.max(axis=-1)
-    s32 = (mx - mn) / levels                      # fp32, round to nearest even
+    s32 = (mx - mn) / levels + F32(0.0)           # fp32, round to nearest even; +0 not -0
     s16 = s32.astype(np.float16)
     z16 = (mn + F32(0.0)).astype(np.float16)      # exact: mn is an fp16 value
     assert np.all(np.isfinite(s16)), "group range overflows the fp16 scale"

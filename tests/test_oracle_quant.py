@@ -160,3 +160,12 @@ def test_dequant_keys_expands_group_parameters():
     z = np.full((1, 128), -2.0, np.float16)
     kq = Q.dequant_keys(code, s, z)
     assert np.array_equal(kq, (np.arange(64) % 16)[:, None] * 0.5 - 2.0 + np.zeros((1, 128)))
+
+
+def test_signed_zero_groups_store_positive_zeros():
+    x = np.zeros(64, np.float16)
+    x[::2] = -0.0
+    for bits in (4, 1):
+        code, s, z = Q.quantize_groups(x[None], bits)
+        assert s[0] == 0 and not np.signbit(s[0]) and not np.signbit(z[0])
+        assert np.all(code == 0)
