@@ -1,0 +1,113 @@
+// C ABI: host-side validation and dispatch.  Nothing here allocates, frees or
+// synchronizes; on a validation error nothing is enqueued.
+
+#include <math.h>
+
+#include "internal.h"
+
+using namespace kvc;
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+kvc_status check_cache(const kvc_cache* c) {
+  if (!c) return KVC_ERR_INVALID;
+  if (c->abi_version != KVC_ABI_VERSION) return KVC_ERR_INVALID;
+  if (c->format < KVC_FMT_FP16 || c->format > KVC_FMT_INT1) return KVC_ERR_UNSUPPORTED;
+  if (c->head_dim != KVC_HEAD_DIM || c->group_size != KVC_GROUP) return KVC_ERR_UNSUPPORTED;
+  if (c->batch < 1 || c->num_kv_heads < 1) return KVC_ERR_SHAPE;
+  if (c->max_tokens < KVC_GROUP || c->max_tokens % KVC_GROUP) return KVC_ERR_SHAPE;
+  if (!c->seq_lens) return KVC_ERR_INVALID;
+  if (c->page_size < 0) return KVC_ERR_SHAPE;
+  if (c->page_size > 0) {
+    const int unit = c->format == KVC_FMT_INT1 ? KVC_GROUP : 16;
+    if (c->page_size % unit || c->max_tokens % c->page_size) return KVC_ERR_SHAPE;
+    if ((int64_t)c->max_pages * c->page_size < c->max_tokens) return KVC_ERR_SHAPE;
+    if (!c->block_table || c->num_pages < 1) return KVC_ERR_INVALID;
+    if (c->kT) return KVC_ERR_UNSUPPORTED;   // channel-major copy needs a contiguous cache
+  }
+  if (c->format == KVC_FMT_FP16) {
+    if (!c->k16 || !c->v16) return KVC_ERR_INVALID;
+  } else {
+    if (!c->k_codes || !c->v_codes || !c->k_meta || !c->v_meta || !c->k_tail || !c->v_tail)
+      return KVC_ERR_INVALID;
+    if (!aligned(c->k_codes, 16) || !aligned(c->v_codes, 16) || !aligned(c->k_meta, 8) ||
+        !aligned(c->v_meta, 8) || !aligned(c->k_tail, 16) || !aligned(c->v_tail, 16))
+      return KVC_ERR_INVALID;
+  }
+  if ((c->k16 && !aligned(c->k16, 16)) || (c->v16 && !aligned(c->v16, 16)) ||
+      (c->kT && !aligned(c->kT, 16)) || (c->k_absmax && !aligned(c->k_absmax, 16)))
+    return KVC_ERR_INVALID;
+  if ((c->k16 == nullptr) != (c->v16 == nullptr)) return KVC_ERR_INVALID;
+  return KVC_OK;
+}
+
+inline kvc_status hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+const char* kvc_status_str(kvc_status s) {
+  switch (s) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_INVALID: return "invalid argument (null pointer, range or alignment)";
+    case KVC_ERR_SHAPE: return "inconsistent shapes";
+    case KVC_ERR_UNSUPPORTED: return "unsupported format, mode or size";
+    case KVC_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVC_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+kvc_status kvc_quantize_append(const kvc_cache* cache, const uint16_t* k_new,
+                               const uint16_t* v_new, const int32_t* n_new,
+                               int32_t n_new_max, int32_t* overflow, hipStream_t stream) {
+  kvc_status st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  if (n_new_max < 0 || n_new_max > cache->max_tokens) return KVC_ERR_SHAPE;
+  if (n_new_max == 0) return KVC_OK;
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return KVC_ERR_INVALID;
+  if (n_new && !aligned(n_new, 4)) return KVC_ERR_INVALID;
+  return hip_status(launch_append(*cache, k_new, v_new, n_new, n_new_max, overflow, stream));
+}
+
+kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num_q_heads,
+                          int32_t score_mode, int32_t n_crit, const float* ext,
+                          int32_t n_sink, int32_t n_window, const int32_t* k_per_seq,
+                          int32_t k_max, int32_t* out_idx, double* out_scores,
+                          int32_t* out_channels, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  kvc_status st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  return KVC_ERR_UNSUPPORTED;
+}
+
+kvc_status kvc_attend_decode(const kvc_cache* cache, const uint16_t* q, int32_t num_q_heads,
+                             float sm_scale, int32_t mode, const int32_t* sel, int32_t k_max,
+                             int32_t n_sink, int32_t n_window, float* out, float* lse,
+                             float* logits, int64_t logits_stride, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  kvc_status st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  return KVC_ERR_UNSUPPORTED;
+}
+
+kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const float* logits,
+                            int64_t logits_stride, const float* lse, int32_t mode,
+                            const int32_t* sel, int32_t k_max, int32_t n_sink, int32_t n_window,
+                            float* acc, hipStream_t stream) {
+  kvc_status st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  return KVC_ERR_UNSUPPORTED;
+}
+
+size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t k_max) {
+  if (check_cache(cache) != KVC_OK) return 0;
+  return 0;
+}
+
+}  // extern "C"

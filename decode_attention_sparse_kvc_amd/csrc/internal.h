@@ -1,0 +1,63 @@
+// Internal helpers shared by the kvc kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+constexpr int D = KVC_HEAD_DIM;    // channels per head
+constexpr int GS = KVC_GROUP;      // quantization group (tokens for K, channels for V)
+constexpr int TILE = 16;           // tokens per INT4 code tile / matrix-core tile
+constexpr int UNIT_BYTES = 1024;   // bytes per INT4 tile (16 tokens) or INT1 unit (64 tokens)
+
+// Tokens per page: the page size, or the whole capacity when contiguous.
+__host__ __device__ inline int page_tokens(const kvc_cache& c) {
+  return c.page_size > 0 ? c.page_size : c.max_tokens;
+}
+
+// Slot of token t of (sequence b, KV head g): (phys * Hkv + g) * P + t % P.
+// Returns -1 when the block table names a page outside the pools, so callers
+// skip the token instead of touching memory they do not own.
+__device__ inline int64_t slot_of(const kvc_cache& c, int b, int g, int t) {
+  const int P = page_tokens(c);
+  const int page = t / P;
+  const int off = t - page * P;
+  int64_t phys = b;
+  if (c.page_size > 0) {
+    if (page >= c.max_pages) return -1;
+    phys = c.block_table[(int64_t)b * c.max_pages + page];
+    if (phys < 0 || phys >= c.num_pages) return -1;
+  }
+  return (phys * c.num_kv_heads + g) * (int64_t)P + off;
+}
+
+// Bit position of nibble slot j (0..7) in an INT4 code dword.
+__host__ __device__ constexpr int nib_pos(int j) { return 16 * (j & 1) + 4 * (j >> 1); }
+
+// Bit position of code k (0..31) in an INT1 code dword.
+__host__ __device__ constexpr int bit_pos(int k) {
+  const int w = k >> 1, h = k & 1, v = w >> 2, p = 6 + (w & 3);
+  return v == 0 ? p + 16 * h
+       : v == 1 ? p + 4 + 16 * h
+       : v == 2 ? p - 4 + 16 * h
+       : (h ? p + 8 : (p + 24) & 31);
+}
+
+// INT1 V: code index k inside lane dword for (channel tile ct, token i of the quad).
+__host__ __device__ constexpr int v1_code(int ct, int i) {
+  return 2 * (4 * ((ct >> 2) * 2 + (i >> 1)) + (ct & 3)) + (i & 1);
+}
+
+__device__ inline float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+__device__ inline uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
+
+// ---- launchers (host side, defined next to their kernels) ----
+hipError_t launch_append(const kvc_cache& c, const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* n_new, int32_t n_new_max, int32_t* overflow,
+                         hipStream_t s);
+
+}  // namespace kvc

@@ -1,0 +1,274 @@
+// Append + quantize (TailorKV article section 2.2; on-device KV article section 3.1).
+//
+// One workgroup per (64-token group touched by the append, KV head, sequence).
+// It stages the group's fp16 K/V rows in LDS (old tail rows + new rows), writes
+// the fp16 copies (k16/v16 rows, channel-major kT), folds |K| into k_absmax
+// and, when the append completes the group, quantizes it:
+//   K: per channel over the 64 tokens;  V: per token over each 64-channel half;
+//   s = fp16((max - min) / (2^b - 1) + 0), z = fp16(min + 0),
+//   code = s == 0 ? 0 : clamp(rint((x - z) / s), 0, 2^b - 1) in fp32.
+// The packed code tiles follow the lane/dword layout of include/kvc.h.
+// A second, per-sequence kernel then rewrites the fp16 tail and seq_lens.
+
+#include "internal.h"
+
+namespace kvc {
+namespace {
+
+constexpr int NT = 256;   // threads per workgroup
+
+template <int BITS>
+struct GroupQuant {
+  // Scale and zero for a group with fp32 extremes mn, mx (fp16 values).
+  __device__ static inline void params(float mn, float mx, float& s, float& z,
+                                       uint16_t& s16, uint16_t& z16) {
+    constexpr float levels = float((1 << BITS) - 1);
+    const float s32 = __fadd_rn(__fdiv_rn(__fsub_rn(mx, mn), levels), 0.0f);
+    s16 = f2h(s32);
+    z16 = f2h(__fadd_rn(mn, 0.0f));
+    s = h2f(s16);
+    z = h2f(z16);
+  }
+  __device__ static inline uint32_t code(float x, float s, float z) {
+    if (s == 0.0f) return 0u;
+    constexpr float top = float((1 << BITS) - 1);
+    float t = rintf(__fdiv_rn(__fsub_rn(x, z), s));
+    t = fminf(fmaxf(t, 0.0f), top);
+    return (uint32_t)t;
+  }
+};
+
+template <int FMT>
+__global__ __launch_bounds__(NT) void append_groups_kernel(
+    kvc_cache c, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ n_new, int n_new_max) {
+  constexpr int BITS = FMT == KVC_FMT_INT4 ? 4 : 1;
+  __shared__ __align__(16) uint16_t sK[GS][D];
+  __shared__ __align__(16) uint16_t sV[GS][D];
+  __shared__ uint8_t sKc[GS][D];
+  __shared__ uint8_t sVc[GS][D];
+  __shared__ float sRed[4][D];
+
+  const int b = blockIdx.z, g = blockIdx.y, tid = threadIdx.x;
+  const int Hkv = c.num_kv_heads;
+  const int L = c.seq_lens[b];
+  const int n = n_new ? n_new[b] : n_new_max;
+  if (n <= 0 || n > n_new_max || L < 0 || L + n > c.max_tokens) return;
+  const int g0 = (L / GS + (int)blockIdx.x) * GS;
+  if (g0 >= L + n) return;
+  const int hi = min(g0 + GS, L + n);   // tokens [g0, hi) exist after the append
+  const int lo = max(g0, L);            // tokens [lo, hi) are new
+
+  // Old rows [g0, L) are read back from the tail only when this append completes
+  // the group of a quantized cache (nothing else needs them; an fp16 cache has no tail).
+  const bool complete = FMT != KVC_FMT_FP16 && hi == g0 + GS;
+  const int r0 = complete ? 0 : lo - g0;
+
+  // ---- stage rows [g0 + r0, hi) in LDS: 16 threads per row, 8 halves each
+  for (int e = tid; e < (hi - g0 - r0) * 16; e += NT) {
+    const int r = r0 + (e >> 4), ch = (e & 15) * 8;
+    const int t = g0 + r;
+    const uint4* srcK;
+    const uint4* srcV;
+    if (t < L) {  // old row, still in the tail
+      const int64_t off = (((int64_t)b * Hkv + g) * GS + r) * D + ch;
+      srcK = reinterpret_cast<const uint4*>(c.k_tail + off);
+      srcV = reinterpret_cast<const uint4*>(c.v_tail + off);
+    } else {
+      const int64_t off = (((int64_t)b * n_new_max + (t - L)) * Hkv + g) * D + ch;
+      srcK = reinterpret_cast<const uint4*>(k_new + off);
+      srcV = reinterpret_cast<const uint4*>(v_new + off);
+    }
+    *reinterpret_cast<uint4*>(&sK[r][ch]) = *srcK;
+    *reinterpret_cast<uint4*>(&sV[r][ch]) = *srcV;
+  }
+  __syncthreads();
+
+  // ---- fp16 row copies of the new tokens
+  if (c.k16) {
+    for (int e = tid; e < (hi - lo) * 16; e += NT) {
+      const int r = lo - g0 + (e >> 4), ch = (e & 15) * 8;
+      const int64_t slot = slot_of(c, b, g, g0 + r);
+      if (slot < 0) continue;
+      *reinterpret_cast<uint4*>(c.k16 + slot * D + ch) = *reinterpret_cast<const uint4*>(&sK[r][ch]);
+      *reinterpret_cast<uint4*>(c.v16 + slot * D + ch) = *reinterpret_cast<const uint4*>(&sV[r][ch]);
+    }
+  }
+  if (c.kT) {  // channel-major: consecutive lanes write consecutive tokens of one channel
+    for (int e = tid; e < (hi - lo) * D; e += NT) {
+      const int ch = e / (hi - lo), r = lo - g0 + e % (hi - lo);
+      c.kT[(((int64_t)b * Hkv + g) * D + ch) * c.max_tokens + g0 + r] = sK[r][ch];
+    }
+  }
+  if (c.k_absmax && tid < D) {
+    float m = 0.0f;
+    for (int r = lo - g0; r < hi - g0; ++r) m = fmaxf(m, fabsf(h2f(sK[r][tid])));
+    atomicMax(reinterpret_cast<unsigned int*>(c.k_absmax) + ((int64_t)b * Hkv + g) * D + tid,
+              __float_as_uint(m));
+  }
+
+  if constexpr (FMT == KVC_FMT_FP16) {
+    return;
+  } else {
+    if (!complete) return;  // group not complete yet: it stays in the tail
+
+    // ---- K: per channel over 64 tokens.  Thread (channel ck, half hk) scans 32 tokens.
+    const int ck = tid & (D - 1), hk = tid >> 7;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int r = 32 * hk; r < 32 * hk + 32; ++r) {
+      const float x = h2f(sK[r][ck]);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+    sRed[2 * hk][ck] = mn;
+    sRed[2 * hk + 1][ck] = mx;
+    __syncthreads();
+    mn = fminf(sRed[0][ck], sRed[2][ck]);
+    mx = fmaxf(sRed[1][ck], sRed[3][ck]);
+    float ks, kz;
+    uint16_t ks16, kz16;
+    GroupQuant<BITS>::params(mn, mx, ks, kz, ks16, kz16);
+    const int G = g0 / GS;
+    if (hk == 0) {
+      uint16_t* meta = c.k_meta + ((((int64_t)b * Hkv + g) * (c.max_tokens / GS) + G) * 2) * D;
+      meta[ck] = ks16;
+      meta[D + ck] = kz16;
+    }
+    for (int r = 32 * hk; r < 32 * hk + 32; ++r)
+      sKc[r][ck] = (uint8_t)GroupQuant<BITS>::code(h2f(sK[r][ck]), ks, kz);
+
+    // ---- V: per token over each 64-channel half.  Thread (token nv, quarter qv).
+    const int nv = tid >> 2, qv = tid & 3, jv = qv >> 1, c0 = 32 * qv;
+    float vmn = INFINITY, vmx = -INFINITY;
+    for (int i = 0; i < 32; ++i) {
+      const float x = h2f(sV[nv][c0 + i]);
+      vmn = fminf(vmn, x);
+      vmx = fmaxf(vmx, x);
+    }
+    vmn = fminf(vmn, __shfl_xor(vmn, 1));
+    vmx = fmaxf(vmx, __shfl_xor(vmx, 1));
+    float vs, vz;
+    uint16_t vs16, vz16;
+    GroupQuant<BITS>::params(vmn, vmx, vs, vz, vs16, vz16);
+    if ((qv & 1) == 0) {
+      const int64_t slot = slot_of(c, b, g, g0 + nv);
+      if (slot >= 0) {
+        c.v_meta[slot * 4 + jv] = vs16;
+        c.v_meta[slot * 4 + 2 + jv] = vz16;
+      }
+    }
+    for (int i = 0; i < 32; ++i)
+      sVc[nv][c0 + i] = (uint8_t)GroupQuant<BITS>::code(h2f(sV[nv][c0 + i]), vs, vz);
+    __syncthreads();
+
+    // ---- pack codes into the lane/dword tile layout
+    const int W = tid, lane = W >> 2, d = W & 3;
+    if constexpr (BITS == 4) {
+      for (int tile = 0; tile < GS / TILE; ++tile) {
+        const int64_t slot = slot_of(c, b, g, g0 + TILE * tile);
+        if (slot < 0) continue;
+        // K: lane = 16*(c/32) + n, dword d = (c%32)/8, nibble j = c%8
+        {
+          const int n = lane & 15, chunk = lane >> 4, tok = TILE * tile + n;
+          const int cb = 32 * chunk + 8 * d;
+          uint32_t u = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) u |= (uint32_t)sKc[tok][cb + j] << nib_pos(j);
+          reinterpret_cast<uint32_t*>(c.k_codes + (slot / TILE) * UNIT_BYTES)[W] = u;
+        }
+        // V: lane = 16*(n/4) + c%16, dword d = (c/16)/2, nibble j = 4*((c/16)%2) + n%4
+        {
+          const int kb = lane >> 4, m = lane & 15;
+          uint32_t u = 0;
+#pragma unroll
+          for (int par = 0; par < 2; ++par)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              u |= (uint32_t)sVc[TILE * tile + 4 * kb + i][16 * (2 * d + par) + m] << nib_pos(4 * par + i);
+          reinterpret_cast<uint32_t*>(c.v_codes + (slot / TILE) * UNIT_BYTES)[W] = u;
+        }
+      }
+    } else {
+      const int64_t slot = slot_of(c, b, g, g0);
+      if (slot >= 0) {
+        // K: lane = 16*(c/32) + n%16, dword d = n/16, code k = c%32
+        {
+          const int tok = 16 * d + (lane & 15), cb = 32 * (lane >> 4);
+          uint32_t u = 0;
+#pragma unroll
+          for (int k = 0; k < 32; ++k) u |= (uint32_t)sKc[tok][cb + k] << bit_pos(k);
+          reinterpret_cast<uint32_t*>(c.k_codes + (slot / GS) * UNIT_BYTES)[W] = u;
+        }
+        // V: lane = 16*((n%16)/4) + c%16, dword d = n/16, code k = v1_code(c/16, n%4)
+        {
+          const int kb = lane >> 4, m = lane & 15;
+          uint32_t u = 0;
+#pragma unroll
+          for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              u |= (uint32_t)sVc[16 * d + 4 * kb + i][16 * ct + m] << bit_pos(v1_code(ct, i));
+          reinterpret_cast<uint32_t*>(c.v_codes + (slot / GS) * UNIT_BYTES)[W] = u;
+        }
+      }
+    }
+  }
+}
+
+// Per sequence: move the rows of the (new) incomplete group into the tail and
+// publish the new length.  Runs after append_groups_kernel on the same stream,
+// so every old tail row it overwrites has already been consumed.
+__global__ __launch_bounds__(NT) void append_finish_kernel(
+    kvc_cache c, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ n_new, int n_new_max, int32_t* overflow) {
+  const int b = blockIdx.x, tid = threadIdx.x, Hkv = c.num_kv_heads;
+  const int L = c.seq_lens[b];
+  const int n = n_new ? n_new[b] : n_new_max;
+  if (n <= 0) return;
+  if (n > n_new_max || L < 0 || L + n > c.max_tokens) {
+    if (tid == 0 && overflow) *overflow = 1;
+    return;
+  }
+  const bool quantized = c.format != KVC_FMT_FP16;
+  if (quantized) {
+    const int nq_old = L & ~(GS - 1), nq_new = (L + n) & ~(GS - 1);
+    const int t0 = nq_new > nq_old ? nq_new : L;  // first token to place in the tail
+    const int rows = L + n - t0;
+    for (int e = tid; e < rows * Hkv * 16; e += NT) {
+      const int ch = (e & 15) * 8, rg = e >> 4, g = rg % Hkv, r = rg / Hkv;
+      const int t = t0 + r;
+      const int64_t src = (((int64_t)b * n_new_max + (t - L)) * Hkv + g) * D + ch;
+      const int64_t dst = (((int64_t)b * Hkv + g) * GS + (t - nq_new)) * D + ch;
+      *reinterpret_cast<uint4*>(c.k_tail + dst) = *reinterpret_cast<const uint4*>(k_new + src);
+      *reinterpret_cast<uint4*>(c.v_tail + dst) = *reinterpret_cast<const uint4*>(v_new + src);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) c.seq_lens[b] = L + n;
+}
+
+}  // namespace
+
+hipError_t launch_append(const kvc_cache& c, const uint16_t* k_new, const uint16_t* v_new,
+                         const int32_t* n_new, int32_t n_new_max, int32_t* overflow,
+                         hipStream_t s) {
+  if (n_new_max <= 0) return hipSuccess;
+  const dim3 grid((n_new_max + GS - 1) / GS + 1, c.num_kv_heads, c.batch);
+  switch (c.format) {
+    case KVC_FMT_INT4:
+      append_groups_kernel<KVC_FMT_INT4><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max);
+      break;
+    case KVC_FMT_INT1:
+      append_groups_kernel<KVC_FMT_INT1><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max);
+      break;
+    default:
+      append_groups_kernel<KVC_FMT_FP16><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max);
+      break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  append_finish_kernel<<<c.batch, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max, overflow);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,92 @@
+"""C-ABI library: loads, exports every declared symbol, rejects bad arguments on the host.
+
+CPU only: every call below fails validation before any HIP call, so no GPU is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_sparse_kvc_amd import kvc
+from kvc_layout import check_bit_tables
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvc.lib()
+    names = declared_functions()
+    assert {"kvc_quantize_append", "kvc_score_topk", "kvc_attend_decode", "kvc_accum_scores",
+            "kvc_workspace_bytes", "kvc_status_str", "kvc_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert kvc.kvc_abi_version() == kvc.ABI_VERSION
+
+
+def test_status_strings():
+    for s in range(6):
+        assert kvc.kvc_status_str(s) and "unknown" not in kvc.kvc_status_str(s)
+    assert "unknown" in kvc.kvc_status_str(99)
+
+
+def test_struct_field_count_matches_header():
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct kvc_cache {"):text.index("} kvc_cache;")]
+    fields = [l for l in body.splitlines()[1:] if ";" in l]
+    assert len(fields) == len(kvc.kvc_cache._fields_)
+    for line, (name, _) in zip(fields, kvc.kvc_cache._fields_):
+        assert re.search(r"\b%s\s*;" % name, line), (line, name)
+
+
+def _desc(**kw):
+    d = kvc.kvc_cache()
+    base = dict(abi_version=1, format=1, batch=1, num_kv_heads=1, head_dim=128, group_size=64,
+                page_size=0, max_tokens=64, max_pages=0, num_pages=0,
+                seq_lens=0x1000, k_codes=0x2000, v_codes=0x3000, k_meta=0x4000, v_meta=0x5000,
+                k_tail=0x6000, v_tail=0x7000, k_absmax=0x8000)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+BAD = [
+    (dict(abi_version=2), 1), (dict(format=7), 3), (dict(head_dim=64), 3), (dict(group_size=32), 3),
+    (dict(batch=0), 2), (dict(max_tokens=100), 2), (dict(seq_lens=None), 1),
+    (dict(k_codes=None), 1), (dict(k_meta=0x4004), 1), (dict(k_codes=0x2008), 1),
+    (dict(page_size=8, max_tokens=64, max_pages=8, num_pages=8, block_table=0x9000), 2),
+    (dict(format=2, page_size=16, max_tokens=64, max_pages=4, num_pages=4, block_table=0x9000), 2),
+    (dict(page_size=16, max_tokens=64, max_pages=2, num_pages=4, block_table=0x9000), 2),
+    (dict(page_size=16, max_tokens=64, max_pages=4, num_pages=4), 1),
+    (dict(format=0), 1),   # fp16 cache without k16/v16
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD)
+def test_quantize_append_rejects_bad_descriptors(kw, status):
+    d = _desc(**kw)
+    st = kvc.lib().kvc_quantize_append(ctypes.byref(d), 0x10000, 0x20000, None, 1, None, None)
+    assert st == status
+
+
+def test_quantize_append_argument_checks():
+    d = _desc()
+    L = kvc.lib()
+    assert L.kvc_quantize_append(None, 0x10000, 0x20000, None, 1, None, None) == 1
+    assert L.kvc_quantize_append(ctypes.byref(d), None, 0x20000, None, 1, None, None) == 1
+    assert L.kvc_quantize_append(ctypes.byref(d), 0x10008, 0x20000, None, 1, None, None) == 1
+    assert L.kvc_quantize_append(ctypes.byref(d), 0x10000, 0x20000, None, 65, None, None) == 2
+    assert L.kvc_quantize_append(ctypes.byref(d), 0x10000, 0x20000, None, -1, None, None) == 2
+    assert L.kvc_quantize_append(ctypes.byref(d), 0x10000, 0x20000, None, 0, None, None) == 0
+
+
+def test_packing_tables_are_permutations():
+    check_bit_tables()

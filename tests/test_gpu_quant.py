@@ -1,0 +1,126 @@
+"""GPU parity of kvc_quantize_append against the oracle: codes, scales, zeros,
+tails, fp16 copies and max|K| bit-exact, over ragged multi-step appends,
+contiguous and paged caches, and the full-size 128K / 32K prefill."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from decode_attention_sparse_kvc_amd import KvcCache
+from gpu_util import dev, host
+from kvc_layout import slots, unpack_codes
+from oracle import step as ST
+
+pytestmark = pytest.mark.gpu
+
+
+def _u16(a):
+    return np.ascontiguousarray(a).view(np.uint16)
+
+
+def check_cache_state(cache: KvcCache, rows_k, rows_v, lens, table=None):
+    """Compare every buffer of ``cache`` with the oracle's cache for rows[:len]."""
+    fmt = cache.fmt
+    seq = host(cache.seq_lens)
+    assert seq.tolist() == list(lens), (seq, lens)
+    absmax = host(cache.k_absmax)
+    if fmt != "fp16":
+        kc, vc = host(cache.k_codes), host(cache.v_codes)
+        km, vm = host(cache.k_meta), host(cache.v_meta)
+        kt, vt = host(cache.k_tail), host(cache.v_tail)
+    k16 = host(cache.k16) if cache.k16 is not None else None
+    v16 = host(cache.v16) if cache.v16 is not None else None
+    kT = host(cache.kT) if cache.kT is not None else None
+    for b in range(cache.batch):
+        n = int(lens[b])
+        for g in range(cache.hkv):
+            hc = ST.build_head_cache(rows_k[b][:n, g], rows_v[b][:n, g], fmt)
+            where = f"b={b} g={g} n={n}"
+            assert np.array_equal(_u16(absmax[b, g].astype(np.float16)), _u16(hc.kabs)), where
+            sl = slots(b, g, np.arange(n), cache.hkv, cache.max_tokens, cache.page_size, table)
+            if k16 is not None:
+                assert np.array_equal(_u16(k16[sl]), _u16(hc.k16)), where
+                assert np.array_equal(_u16(v16[sl]), _u16(hc.v16)), where
+            if kT is not None:
+                assert np.array_equal(_u16(kT[b, g, :, :n].T), _u16(hc.k16)), where
+            if fmt == "fp16":
+                continue
+            nq = hc.nq
+            sq = sl[:nq]
+            assert np.array_equal(unpack_codes(kc, fmt, "k", sq), hc.k_code), "K codes " + where
+            assert np.array_equal(unpack_codes(vc, fmt, "v", sq), hc.v_code), "V codes " + where
+            assert np.array_equal(_u16(km[b, g, : nq // 64, 0]), _u16(hc.k_scale)), where
+            assert np.array_equal(_u16(km[b, g, : nq // 64, 1]), _u16(hc.k_zero)), where
+            assert np.array_equal(_u16(vm[sq, 0:2]), _u16(hc.v_scale)), where
+            assert np.array_equal(_u16(vm[sq, 2:4]), _u16(hc.v_zero)), where
+            assert np.array_equal(_u16(kt[b, g, : n - nq]), _u16(hc.k16[nq:])), "tail " + where
+            assert np.array_equal(_u16(vt[b, g, : n - nq]), _u16(hc.v16[nq:])), "tail " + where
+
+
+def _rows(rng, B, n, hkv, outliers=True):
+    k = rng.standard_normal((B, n, hkv, 128), dtype=np.float32)
+    if outliers:
+        k[..., [3, 77]] *= 8
+    v = rng.standard_normal((B, n, hkv, 128), dtype=np.float32)
+    k[0, :64, 0, 5] = 0.0            # an all-equal channel group (zero scale)
+    v[0, 7, 0, :64] = -1.25          # an all-equal value group
+    return k.astype(np.float16), v.astype(np.float16)
+
+
+STEPS = [[100, 64, 3], [1, 1, 1], [63, 0, 130], [70, 5, 61], [1, 64, 0]]
+
+
+@pytest.mark.parametrize("fmt,page", [("int4", 0), ("int1", 0), ("int4", 16), ("int1", 64),
+                                      ("fp16", 0), ("fp16", 16)])
+def test_incremental_ragged_appends(fmt, page):
+    rng = np.random.default_rng(7)
+    B, hkv, cap = 3, 2, 384
+    total = np.sum(STEPS, axis=0)
+    k, v = _rows(rng, B, int(total.max()), hkv)
+    table = None
+    kw = {}
+    if page:
+        per = cap // page
+        table = rng.permutation(B * per).astype(np.int32).reshape(B, per)
+        kw = dict(page_size=page, block_table=torch.from_numpy(table), num_pages=B * per)
+    cache = KvcCache(fmt, B, hkv, cap, fp16_rows=(fmt != "fp16" and page == 16) or fmt == "fp16",
+                     kT=(fmt == "fp16" and page == 0), **kw)
+    lens = np.zeros(B, np.int64)
+    for step in STEPS:
+        nmax = max(step)
+        kn = np.zeros((B, nmax, hkv, 128), np.float16)
+        vn = np.zeros_like(kn)
+        for b in range(B):
+            kn[b, :step[b]] = k[b, lens[b]:lens[b] + step[b]]
+            vn[b, :step[b]] = v[b, lens[b]:lens[b] + step[b]]
+        cache.append(dev(kn), dev(vn), dev(np.array(step, np.int32)))
+        lens += step
+        torch.cuda.synchronize()
+        check_cache_state(cache, k, v, lens, table)
+
+
+def test_overflow_leaves_sequence_unchanged():
+    rng = np.random.default_rng(8)
+    k, v = _rows(rng, 2, 128, 1)
+    cache = KvcCache("int4", 2, 1, 128)
+    cache.append(dev(k[:, :100]), dev(v[:, :100]))
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kn = np.concatenate([k[:, 100:128], k[:, :10]], axis=1)
+    vn = np.concatenate([v[:, 100:128], v[:, :10]], axis=1)
+    n_new = dev(np.array([38, 28], np.int32))     # sequence 0 would reach 138 > 128
+    cache.append(dev(kn), dev(vn), n_new, overflow=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 1
+    rows_k = [k[0], np.concatenate([k[1, :100], kn[1, :28]])]
+    rows_v = [v[0], np.concatenate([v[1, :100], vn[1, :28]])]
+    check_cache_state(cache, rows_k, rows_v, [100, 128])
+
+
+@pytest.mark.parametrize("make", [lambda: W.int1_dense(131072), lambda: W.int4_dense(32768)],
+                         ids=["int1_128k", "int4_32k"])
+def test_full_size_prefill(make):
+    w = make()
+    cache = KvcCache(w.fmt, w.batch, w.hkv, w.max_tokens)
+    cache.append(dev(w.k), dev(w.v))
+    torch.cuda.synchronize()
+    check_cache_state(cache, w.k, w.v, w.seq_lens)
