@@ -1,6 +1,7 @@
 // C ABI: host-side validation and dispatch.  Nothing here allocates, frees or
 // synchronizes; on a validation error nothing is enqueued.
 
+#include <limits.h>
 #include <math.h>
 
 #include "internal.h"
@@ -44,6 +45,24 @@ kvc_status check_cache(const kvc_cache* c) {
 }
 
 inline kvc_status hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
+
+// Shared by kvc_attend_decode, kvc_accum_scores and the workspace query.
+kvc_status check_attend_args(const kvc_cache* c, int32_t hq, int32_t mode, const int32_t* sel,
+                             int32_t k_max, int32_t n_sink, int32_t n_window,
+                             bool sizing_only = false) {
+  if (hq < 1 || hq % c->num_kv_heads) return KVC_ERR_SHAPE;
+  const int G = hq / c->num_kv_heads;
+  if (G > KVC_MAX_GQA) return KVC_ERR_UNSUPPORTED;
+  if (mode < KVC_ATTEND_DENSE || mode > KVC_ATTEND_KEEP) return KVC_ERR_INVALID;
+  if (mode != KVC_ATTEND_DENSE) {
+    if (k_max < 0 || n_sink < 0 || n_window < 0) return KVC_ERR_INVALID;
+    if ((int64_t)n_sink + k_max + n_window + KVC_GROUP > (int64_t)INT32_MAX / 2) return KVC_ERR_SHAPE;
+    if (k_max > 0 && !sel && !sizing_only) return KVC_ERR_INVALID;
+    if (sel && !aligned(sel, 4)) return KVC_ERR_INVALID;
+  }
+  if (mode == KVC_ATTEND_KEEP && (c->format == KVC_FMT_FP16 || !c->k16)) return KVC_ERR_UNSUPPORTED;
+  return KVC_OK;
+}
 
 }  // namespace
 
@@ -93,7 +112,19 @@ kvc_status kvc_attend_decode(const kvc_cache* cache, const uint16_t* q, int32_t 
                              size_t workspace_bytes, hipStream_t stream) {
   kvc_status st = check_cache(cache);
   if (st != KVC_OK) return st;
-  return KVC_ERR_UNSUPPORTED;
+  st = check_attend_args(cache, num_q_heads, mode, sel, k_max, n_sink, n_window);
+  if (st != KVC_OK) return st;
+  if (!q || !aligned(q, 16) || !out || !lse) return KVC_ERR_INVALID;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return KVC_ERR_INVALID;
+  if (logits) {
+    const int64_t need = mode == KVC_ATTEND_DROP ? (int64_t)n_sink + k_max + n_window
+                                                 : (int64_t)cache->max_tokens;
+    if (logits_stride < need) return KVC_ERR_SHAPE;
+  }
+  const size_t ws = attend_workspace_bytes(*cache, num_q_heads, mode, k_max, n_sink, n_window);
+  if (!workspace || workspace_bytes < ws || !aligned(workspace, 16)) return KVC_ERR_WORKSPACE;
+  return hip_status(launch_attend(*cache, q, num_q_heads, sm_scale, mode, sel, k_max, n_sink,
+                                  n_window, out, lse, logits, logits_stride, workspace, stream));
 }
 
 kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const float* logits,
@@ -105,8 +136,14 @@ kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const f
   return KVC_ERR_UNSUPPORTED;
 }
 
-size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t k_max) {
+size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t mode,
+                           int32_t k_max, int32_t n_sink, int32_t n_window) {
   if (check_cache(cache) != KVC_OK) return 0;
+  if (op == KVC_OP_ATTEND) {
+    if (check_attend_args(cache, num_q_heads, mode, nullptr, k_max, n_sink, n_window, true) != KVC_OK)
+      return 0;
+    return attend_workspace_bytes(*cache, num_q_heads, mode, k_max, n_sink, n_window);
+  }
   return 0;
 }
 

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <algorithm>
 
 #include "../../include/kvc.h"
 
@@ -58,6 +61,13 @@ __device__ inline uint16_t f2h(float f) { return __half_as_ushort(__float2half_r
 // ---- launchers (host side, defined next to their kernels) ----
 hipError_t launch_append(const kvc_cache& c, const uint16_t* k_new, const uint16_t* v_new,
                          const int32_t* n_new, int32_t n_new_max, int32_t* overflow,
+                         hipStream_t s);
+
+size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, int n_sink,
+                              int n_window);
+hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm_scale, int mode,
+                         const int32_t* sel, int k_max, int n_sink, int n_window, float* out,
+                         float* lse, float* logits, int64_t logits_stride, void* ws,
                          hipStream_t s);
 
 }  // namespace kvc

@@ -76,7 +76,7 @@ def _load():
     lib.kvc_accum_scores.argtypes = [P, c_int32, c_void_p, c_int64, c_void_p, c_int32, c_void_p,
                                      c_int32, c_int32, c_int32, c_void_p, c_void_p]
     lib.kvc_workspace_bytes.restype = c_size_t
-    lib.kvc_workspace_bytes.argtypes = [c_int32, P, c_int32, c_int32]
+    lib.kvc_workspace_bytes.argtypes = [c_int32, P, c_int32, c_int32, c_int32, c_int32, c_int32]
     if lib.kvc_abi_version() != ABI_VERSION:
         raise ImportError(f"{LIB_PATH}: ABI version {lib.kvc_abi_version()} != {ABI_VERSION}")
     _lib = lib
@@ -149,5 +149,7 @@ def kvc_accum_scores(cache, num_q_heads: int, logits, logits_stride: int, lse, m
         k_max, n_sink, n_window, _ptr(acc), _stream(stream)))
 
 
-def kvc_workspace_bytes(op: int, cache, num_q_heads: int, k_max: int) -> int:
-    return int(lib().kvc_workspace_bytes(op, ctypes.byref(cache), num_q_heads, k_max))
+def kvc_workspace_bytes(op: int, cache, num_q_heads: int, mode: int = 0, k_max: int = 0,
+                        n_sink: int = 0, n_window: int = 0) -> int:
+    return int(lib().kvc_workspace_bytes(op, ctypes.byref(cache), num_q_heads, mode, k_max,
+                                         n_sink, n_window))

@@ -230,8 +230,11 @@ kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const f
                             const int32_t* sel, int32_t k_max, int32_t n_sink, int32_t n_window,
                             float* acc, hipStream_t stream);
 
-/* Workspace bytes for op (KVC_OP_*); 0 on invalid arguments. Host only. */
-size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t k_max);
+/* Workspace bytes for op (KVC_OP_*) called with these arguments (mode is the
+ * attend mode; it is ignored for KVC_OP_SCORE_TOPK); 0 on invalid arguments.
+ * Host only. */
+size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t mode,
+                           int32_t k_max, int32_t n_sink, int32_t n_window);
 
 /* Static description of a status code. */
 const char* kvc_status_str(kvc_status status);
