@@ -42,7 +42,8 @@ constexpr int NW = 4;          // waves per workgroup
 constexpr int NT = 64 * NW;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
-constexpr int PART = 2 + D;    // floats per split partial: m (log2 units), l, o[128]
+constexpr int PART = 4 + D;    // floats per split partial: m (log2 units), l, pad, o[128]
+constexpr int PO = 4;          // offset of o inside a partial (16-byte aligned)
 
 struct AttendArgs {
   kvc_cache c;
@@ -74,14 +75,24 @@ __device__ inline float max_kb(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   return fmaxf(x, __shfl_xor(x, 32));
 }
-__device__ inline void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+// LDS accesses of one wave execute in issue order, so exchanging data through
+// LDS inside a wave only needs the compiler to keep program order.
+__device__ inline void wave_sync_lds() { asm volatile("" ::: "memory"); }
+
+// exp2 on the transcendental unit (inputs here are <= 0; results below 2^-126
+// flush to zero, which the softmax sums cannot see).
+__device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A loop-invariant constant held in a VGPR, so the mask-and-or decodes below
+// assemble to single three-operand VALU ops (gfx9 VOP3 takes no literals).
+__device__ inline uint32_t vconst(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 // INT4 dword (nibble slots j at bits 16*(j&1) + 4*(j>>1)) -> 8 fp16 values 16 + code_j.
-__device__ inline h8 dec4(uint32_t u) {
-  const uint32_t M = 0x03C003C0u, B = 0x4C004C00u;
+// M = 0x03C003C0 and B = 0x4C004C00 (fp16 16.0 in both halves) come in VGPRs.
+__device__ inline h8 dec4(uint32_t u, uint32_t M, uint32_t B) {
   uint4 w;
   w.x = ((u << 6) & M) | B;
   w.y = ((u << 2) & M) | B;
@@ -92,11 +103,26 @@ __device__ inline h8 dec4(uint32_t u) {
 
 // INT1 dword -> word (variant v, position r): bit pair (6 + r, 22 + r) of the
 // v-th shifted copy, with fp16 base 2^(4 - r) so each value is base + bit.
-__device__ inline uint32_t dec1_word(uint32_t u, int v, int r) {
+// mask[r] = 0x00400040 << r and base[r] = 0x4C004C00 - 0x04000400 * r in VGPRs.
+__device__ inline uint32_t dec1_word(uint32_t u, int v, int r, const uint32_t* mask,
+                                     const uint32_t* base) {
   const uint32_t s = v == 0 ? u : v == 1 ? (u >> 4) : v == 2 ? (u << 4) : __builtin_amdgcn_alignbit(u, u, 24);
-  const uint32_t mask = 0x00400040u << r;
-  const uint32_t base = 0x4C004C00u - 0x04000400u * (uint32_t)r;
-  return (s & mask) | base;
+  return (s & mask[r]) | base[r];
+}
+
+struct DecConst {
+  uint32_t M4, B4, m1[4], b1[4];
+};
+__device__ inline DecConst make_dec() {
+  DecConst d;
+  d.M4 = vconst(0x03C003C0u);
+  d.B4 = vconst(0x4C004C00u);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    d.m1[r] = vconst(0x00400040u << r);
+    d.b1[r] = vconst(0x4C004C00u - 0x04000400u * (uint32_t)r);
+  }
+  return d;
 }
 
 __device__ inline f4 mfma32(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
@@ -120,24 +146,241 @@ __device__ inline int window_start(int n, int n_sink, int n_window) {
 }
 
 // ---------------------------------------------------------------- quantized role
+// Raw loads of one 64-token group: code tiles and the two metadata words.
 template <int FMT>
+struct GroupData {
+  uint4 k[FMT == KVC_FMT_INT4 ? 4 : 1];
+  uint4 v[FMT == KVC_FMT_INT4 ? 4 : 1];
+  uint2 km, vm;
+};
+
+// Per-wave running state of the quantized role.
+struct QState {
+  float m, l, sp0, sp1, sz0, sz1;
+  f4 acc[8];
+  int ptr;
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, int gi, int lane,
+                                           GroupData<FMT>& d) {
+  const kvc_cache& c = a.c;
+  const int t0 = gi * GS;
+  if constexpr (FMT == KVC_FMT_INT4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t s = slot_of(c, b, g, t0 + TILE * j);
+      const int64_t off = (s < 0 ? 0 : (s / TILE)) * UNIT_BYTES + lane * 16;
+      d.k[j] = *reinterpret_cast<const uint4*>(c.k_codes + off);
+      d.v[j] = *reinterpret_cast<const uint4*>(c.v_codes + off);
+    }
+  } else {
+    const int64_t s = slot_of(c, b, g, t0);
+    const int64_t off = (s < 0 ? 0 : (s / GS)) * UNIT_BYTES + lane * 16;
+    d.k[0] = *reinterpret_cast<const uint4*>(c.k_codes + off);
+    d.v[0] = *reinterpret_cast<const uint4*>(c.v_codes + off);
+  }
+  const uint16_t* km = c.k_meta +
+      ((((int64_t)b * c.num_kv_heads + g) * (c.max_tokens / GS) + gi) * 2) * D;
+  d.km = *reinterpret_cast<const uint2*>(km + 4 * lane);
+  const int64_t vs = slot_of(c, b, g, t0 + lane);
+  d.vm = vs < 0 ? uint2{0u, 0u} : *reinterpret_cast<const uint2*>(c.v_meta + vs * 4);
+}
+
+template <int FMT, bool DENSE, bool LOGITS>
+__device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, int gi, int lane,
+                                           int w, int n, const GroupData<FMT>& d, QState& st,
+                                           const h2* qv, const DecConst& dc, uint16_t* sKm,
+                                           uint16_t* sVm, uint32_t* sMask, int* sPos) {
+  const int G = a.G;
+  const int col = lane & 15, kb = lane >> 4, head = col & 7;
+  const bool hv = head < G;
+  const bool hi_lane = hv && col < 8;
+  const uint32_t lo_sel = (hv && !hi_lane) ? 0xFFFFFFFFu : 0u;  // lo lanes subtract hi
+  const uint32_t hv_sel = hv ? 0xFFFFFFFFu : 0u;
+  const int t0 = gi * GS;
+
+  // ---- which tokens of this group are attended from the codes
+  uint64_t att = ~0ull;
+  if constexpr (!DENSE) {
+    const int32_t* sel = a.sel ? a.sel + ((int64_t)b * a.c.num_kv_heads + g) * a.k_max : nullptr;
+    const int w0 = window_start(n, a.n_sink, a.n_window);
+    const int tl = t0 + lane;
+    const bool in = tl < a.n_sink || tl >= w0;
+    uint32_t* mw = sMask + 2 * w;
+    if (lane < 2) mw[lane] = 0u;
+    wave_sync_lds();
+    int e = INT_MAX;
+    if (sel && st.ptr + lane < a.k_max) e = sel_key(sel[st.ptr + lane]);
+    const bool ing = e < t0 + GS;                 // entries before ptr are < t0
+    const int cnt = __popcll(__ballot(ing));
+    if (ing && e >= a.n_sink && e < n - a.n_window) {
+      atomicOr(&mw[(e - t0) >> 5], 1u << ((e - t0) & 31));
+      sPos[GS * w + (e - t0)] = a.n_sink + st.ptr + lane;
+    }
+    st.ptr += cnt;
+    wave_sync_lds();
+    const uint64_t selm = (uint64_t)mw[0] | ((uint64_t)mw[1] << 32);
+    const uint64_t inset = __ballot(in) | selm;
+    att = a.mode == KVC_ATTEND_DROP ? inset : ~inset;
+    if (a.mode == KVC_ATTEND_DROP && a.logits && in)   // logits positions of sinks / window
+      sPos[GS * w + lane] = tl < a.n_sink ? tl : a.n_sink + a.k_max + (tl - w0);
+    wave_sync_lds();
+    if (att == 0) return;
+  }
+
+  // ---- stage the group's K scales/zeros and V token metadata in LDS
+  *reinterpret_cast<uint2*>(sKm + 256 * w + 4 * lane) = d.km;
+  *reinterpret_cast<uint2*>(sVm + 256 * w + 4 * lane) = d.vm;
+  wave_sync_lds();
+
+  // ---- q' = q * s as fp16 hi (columns < 8) / lo (columns >= 8); bias
+  h8 qp[4];
+  float qz = 0.f, qb = 0.f;
+  {
+    const uint16_t* ks = sKm + 256 * w;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const uint4 s4 = *reinterpret_cast<const uint4*>(ks + 32 * kb + 8 * kc);
+      const uint4 z4 = *reinterpret_cast<const uint4*>(ks + D + 32 * kb + 8 * kc);
+      const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+      const uint32_t zw[4] = {z4.x, z4.y, z4.z, z4.w};
+      uint32_t out[4];
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) {
+        const h2 qq = qv[4 * kc + pr];
+        const h2 ss = bc<h2>(sw[pr]);
+        const h2 hi = qq * ss;
+        const h2 sub = bc<h2>(bc<uint32_t>(hi) & lo_sel);
+        const h2 r = __builtin_elementwise_fma(qq, ss, -sub);
+        const uint32_t rw = bc<uint32_t>(r) & hv_sel;
+        out[pr] = rw;
+        qz = __builtin_amdgcn_fdot2(qq, bc<h2>(zw[pr]), qz, false);
+        h2 base;
+        if constexpr (FMT == KVC_FMT_INT4) {
+          base = h2{(_Float16)16.f, (_Float16)16.f};
+        } else {
+          const _Float16 bv = (_Float16)(float)(16 >> pr);   // slots 2pr, 2pr+1
+          base = h2{bv, bv};
+        }
+        qb = __builtin_amdgcn_fdot2(bc<h2>(rw), base, qb, false);
+      }
+      qp[kc] = bc<h8>(uint4{out[0], out[1], out[2], out[3]});
+    }
+  }
+  const float bias = sum_kb((hi_lane ? qz : 0.f) - qb);
+
+  // ---- S^T = codes x q'^T per 16-token tile; hi + lo; scale to log2 units
+  float x[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f4 s = f4{bias, bias, bias, bias};
+    if constexpr (FMT == KVC_FMT_INT4) {
+      s = mfma32(dec4(d.k[j].x, dc.M4, dc.B4), qp[0], s);
+      s = mfma32(dec4(d.k[j].y, dc.M4, dc.B4), qp[1], s);
+      s = mfma32(dec4(d.k[j].z, dc.M4, dc.B4), qp[2], s);
+      s = mfma32(dec4(d.k[j].w, dc.M4, dc.B4), qp[3], s);
+    } else {
+      const uint32_t u = j == 0 ? d.k[0].x : j == 1 ? d.k[0].y : j == 2 ? d.k[0].z : d.k[0].w;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        const uint4 wv = uint4{dec1_word(u, kc, 0, dc.m1, dc.b1), dec1_word(u, kc, 1, dc.m1, dc.b1),
+                               dec1_word(u, kc, 2, dc.m1, dc.b1), dec1_word(u, kc, 3, dc.m1, dc.b1)};
+        s = mfma32(bc<h8>(wv), qp[kc], s);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = s[i] + ror8(s[i]);
+      const int bit = TILE * j + 4 * kb + i;
+      const bool on = DENSE || ((att >> bit) & 1ull);
+      x[j][i] = on ? v * a.sm2 : -INFINITY;
+      if (LOGITS && hi_lane && on) {
+        const int pos = a.mode == KVC_ATTEND_DROP ? sPos[GS * w + bit] : t0 + bit;
+        a.logits[((int64_t)b * a.hq + g * G + head) * a.logits_stride + pos] = v * a.sm;
+      }
+    }
+  }
+
+  // ---- online softmax (log2 units)
+  float gmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gmax = fmaxf(gmax, x[j][i]);
+  gmax = max_kb(gmax);
+  const float m_new = fmaxf(st.m, gmax);
+  const float ms = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = ex2(st.m - ms);
+  st.m = m_new;
+  st.l *= alpha;
+  st.sp0 *= alpha; st.sp1 *= alpha; st.sz0 *= alpha; st.sz1 *= alpha;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= alpha;
+
+  // ---- O^T += V^T P'^T per tile
+  const uint16_t* vmeta = sVm + 256 * w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = ex2(x[j][i] - ms);
+      st.l += p[i];
+    }
+    const uint4 m01 = *reinterpret_cast<const uint4*>(vmeta + 4 * (TILE * j + 4 * kb));
+    const uint4 m23 = *reinterpret_cast<const uint4*>(vmeta + 4 * (TILE * j + 4 * kb + 2));
+    const uint32_t mwd[8] = {m01.x, m01.y, m01.z, m01.w, m23.x, m23.y, m23.z, m23.w};
+    h4 A0, A1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const h2 s01 = bc<h2>(mwd[2 * i]);       // (s0, s1) of token i
+      const h2 z01 = bc<h2>(mwd[2 * i + 1]);   // (z0, z1)
+      const _Float16 P0 = (_Float16)(p[i] * (float)s01.x);
+      const _Float16 P1 = (_Float16)(p[i] * (float)s01.y);
+      A0[i] = P0;
+      A1[i] = P1;
+      st.sp0 += (float)P0;
+      st.sp1 += (float)P1;
+      st.sz0 = fmaf(p[i], (float)z01.x, st.sz0);
+      st.sz1 = fmaf(p[i], (float)z01.y, st.sz1);
+    }
+    if constexpr (FMT == KVC_FMT_INT4) {
+      const uint32_t dw[4] = {d.v[j].x, d.v[j].y, d.v[j].z, d.v[j].w};
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd) {
+        const h8 v8 = dec4(dw[dd], dc.M4, dc.B4);
+        const h4 va = h4{v8[0], v8[1], v8[2], v8[3]};   // channel tile 2dd, tokens 0..3
+        const h4 vb = h4{v8[4], v8[5], v8[6], v8[7]};   // channel tile 2dd + 1
+        st.acc[2 * dd] = mfma16(va, dd < 2 ? A0 : A1, st.acc[2 * dd]);
+        st.acc[2 * dd + 1] = mfma16(vb, dd < 2 ? A0 : A1, st.acc[2 * dd + 1]);
+      }
+    } else {
+      const uint32_t u = j == 0 ? d.v[0].x : j == 1 ? d.v[0].y : j == 2 ? d.v[0].z : d.v[0].w;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const uint32_t w0v = dec1_word(u, 2 * (ct >> 2), ct & 3, dc.m1, dc.b1);
+        const uint32_t w1v = dec1_word(u, 2 * (ct >> 2) + 1, ct & 3, dc.m1, dc.b1);
+        const h4 va = bc<h4>(uint2{w0v, w1v});
+        st.acc[ct] = mfma16(va, ct < 4 ? A0 : A1, st.acc[ct]);
+      }
+    }
+  }
+}
+
+template <int FMT, bool DENSE, bool LOGITS>
 __device__ void quant_role(const AttendArgs& a, int b, int g, int split, int lane, int w,
                            float* sO, float* sML, uint16_t* sKm, uint16_t* sVm,
                            uint32_t* sMask, int* sPos) {
   const kvc_cache& c = a.c;
-  const int n = c.seq_lens[b];
-  const int ngroups = max(n, 0) >> 6;
+  const int n = max(c.seq_lens[b], 0);
+  const int ngroups = n >> 6;
   const int G = a.G;
   const int col = lane & 15, kb = lane >> 4, head = col & 7;
-  const bool hv = head < G;              // this lane's column carries a head (hi or lo half)
+  const bool hv = head < G;
   const bool hi_lane = hv && col < 8;
   const int ga = (split * NW + w) * a.gpw;
   const int gb = min(ga + a.gpw, ngroups);
-  const int Hkv = c.num_kv_heads;
-  const int max_groups = c.max_tokens / GS;
-  const int dense = a.mode == KVC_ATTEND_DENSE;
-  const int w0 = window_start(n, a.n_sink, a.n_window);
-  const int32_t* sel = a.sel ? a.sel + ((int64_t)b * Hkv + g) * a.k_max : nullptr;
 
   // q of this lane's head, channels [32kb, 32kb + 32), as fp16 pairs
   h2 qv[16];
@@ -156,212 +399,33 @@ __device__ void quant_role(const AttendArgs& a, int b, int g, int split, int lan
       qv[4 * k + 3] = bc<h2>(raw[k].w);
     }
   }
-  const uint32_t lo_sel = (hv && !hi_lane) ? 0xFFFFFFFFu : 0u;  // lo lanes subtract hi
-  const uint32_t hv_sel = hv ? 0xFFFFFFFFu : 0u;
 
-  float m = -INFINITY, l = 0.f;
-  float sp0 = 0.f, sp1 = 0.f, sz0 = 0.f, sz1 = 0.f;
-  f4 acc[8];
+  QState st;
+  st.m = -INFINITY;
+  st.l = st.sp0 = st.sp1 = st.sz0 = st.sz1 = 0.f;
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < 8; ++ct) st.acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
+  st.ptr = 0;
+  if (!DENSE && a.sel && ga < gb)
+    st.ptr = lower_bound_sel(a.sel + ((int64_t)b * c.num_kv_heads + g) * a.k_max, a.k_max, ga * GS);
 
-  int ptr = 0;
-  if (!dense && sel && ga < gb) ptr = lower_bound_sel(sel, a.k_max, ga * GS);
+  const DecConst dc = make_dec();
 
-  for (int gi = ga; gi < gb; ++gi) {
-    const int t0 = gi * GS;
-    // ---- which tokens of this group are attended from the codes
-    uint64_t att = ~0ull;
-    if (!dense) {
-      const int tl = t0 + lane;
-      bool in = tl < a.n_sink || tl >= w0;
-      uint32_t* mw = sMask + 2 * w;
-      if (lane < 2) mw[lane] = 0u;
-      wave_sync_lds();
-      int e = INT_MAX;
-      if (sel && ptr + lane < a.k_max) e = sel_key(sel[ptr + lane]);
-      const bool ing = e < t0 + GS;                 // entries before ptr are < t0
-      const int cnt = __popcll(__ballot(ing));
-      if (ing && e >= a.n_sink && e < n - a.n_window) {
-        atomicOr(&mw[(e - t0) >> 5], 1u << ((e - t0) & 31));
-        sPos[GS * w + (e - t0)] = a.n_sink + ptr + lane;
-      }
-      ptr += cnt;
-      wave_sync_lds();
-      const uint64_t selm = (uint64_t)mw[0] | ((uint64_t)mw[1] << 32);
-      const uint64_t inset = __ballot(in) | selm;
-      att = a.mode == KVC_ATTEND_DROP ? inset : ~inset;
-      if (a.mode == KVC_ATTEND_DROP && a.logits) {   // logits positions of sinks / window
-        int pos = tl < a.n_sink ? tl : a.n_sink + a.k_max + (tl - w0);
-        if (in) sPos[GS * w + lane] = pos;
-      }
-      wave_sync_lds();
-      if (att == 0) continue;
-    }
-
-    // ---- loads: code tiles, K group meta, V token meta
-    uint4 kq[4], vq[4];
-    if constexpr (FMT == KVC_FMT_INT4) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t s = slot_of(c, b, g, t0 + TILE * j);
-        const int64_t off = (s < 0 ? 0 : (s / TILE)) * UNIT_BYTES + lane * 16;
-        kq[j] = *reinterpret_cast<const uint4*>(c.k_codes + off);
-        vq[j] = *reinterpret_cast<const uint4*>(c.v_codes + off);
-      }
-    } else {
-      const int64_t s = slot_of(c, b, g, t0);
-      const int64_t off = (s < 0 ? 0 : (s / GS)) * UNIT_BYTES + lane * 16;
-      kq[0] = *reinterpret_cast<const uint4*>(c.k_codes + off);
-      vq[0] = *reinterpret_cast<const uint4*>(c.v_codes + off);
-    }
-    {
-      const uint16_t* km = c.k_meta + ((((int64_t)b * Hkv + g) * max_groups + gi) * 2) * D;
-      const uint2 kmw = *reinterpret_cast<const uint2*>(km + 4 * lane);
-      const int64_t vs = slot_of(c, b, g, t0 + lane);
-      const uint2 vmw = vs < 0 ? uint2{0u, 0u} : *reinterpret_cast<const uint2*>(c.v_meta + vs * 4);
-      *reinterpret_cast<uint2*>(sKm + 256 * w + 4 * lane) = kmw;
-      *reinterpret_cast<uint2*>(sVm + 256 * w + 4 * lane) = vmw;
-    }
-    wave_sync_lds();
-
-    // ---- q' = q * s as fp16 hi (columns < 8) / lo (columns >= 8); bias
-    h8 qp[4];
-    float qz = 0.f, qb = 0.f;
-    {
-      const uint16_t* ks = sKm + 256 * w;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        const uint4 s4 = *reinterpret_cast<const uint4*>(ks + 32 * kb + 8 * kc);
-        const uint4 z4 = *reinterpret_cast<const uint4*>(ks + D + 32 * kb + 8 * kc);
-        const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
-        const uint32_t zw[4] = {z4.x, z4.y, z4.z, z4.w};
-        uint32_t out[4];
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          const h2 qq = qv[4 * kc + pr];
-          const h2 ss = bc<h2>(sw[pr]);
-          const h2 hi = qq * ss;
-          const h2 sub = bc<h2>(bc<uint32_t>(hi) & lo_sel);
-          const h2 r = __builtin_elementwise_fma(qq, ss, -sub);
-          const uint32_t rw = bc<uint32_t>(r) & hv_sel;
-          out[pr] = rw;
-          qz = __builtin_amdgcn_fdot2(qq, bc<h2>(zw[pr]), qz, false);
-          h2 base;
-          if constexpr (FMT == KVC_FMT_INT4) {
-            base = h2{(_Float16)16.f, (_Float16)16.f};
-          } else {
-            const _Float16 bv = (_Float16)(float)(16 >> pr);   // slots 2pr, 2pr+1
-            base = h2{bv, bv};
-          }
-          qb = __builtin_amdgcn_fdot2(bc<h2>(rw), base, qb, false);
-        }
-        qp[kc] = bc<h8>(uint4{out[0], out[1], out[2], out[3]});
-      }
-    }
-    const float bias = sum_kb((hi_lane ? qz : 0.f) - qb);
-
-    // ---- S^T = codes x q'^T per 16-token tile; hi + lo; scale to log2 units
-    float x[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f4 s = f4{bias, bias, bias, bias};
-      if constexpr (FMT == KVC_FMT_INT4) {
-        s = mfma32(dec4(kq[j].x), qp[0], s);
-        s = mfma32(dec4(kq[j].y), qp[1], s);
-        s = mfma32(dec4(kq[j].z), qp[2], s);
-        s = mfma32(dec4(kq[j].w), qp[3], s);
-      } else {
-        const uint32_t u = j == 0 ? kq[0].x : j == 1 ? kq[0].y : j == 2 ? kq[0].z : kq[0].w;
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const uint4 wv = uint4{dec1_word(u, kc, 0), dec1_word(u, kc, 1), dec1_word(u, kc, 2),
-                                 dec1_word(u, kc, 3)};
-          s = mfma32(bc<h8>(wv), qp[kc], s);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = s[i] + ror8(s[i]);
-        const int bit = TILE * j + 4 * kb + i;
-        const bool on = (att >> bit) & 1ull;
-        x[j][i] = on ? v * a.sm2 : -INFINITY;
-        if (a.logits && hi_lane && on) {
-          const int pos = a.mode == KVC_ATTEND_DROP ? sPos[GS * w + bit] : t0 + bit;
-          a.logits[((int64_t)b * a.hq + g * G + head) * a.logits_stride + pos] = v * a.sm;
-        }
-      }
-    }
-
-    // ---- online softmax (log2 units)
-    float gmax = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) gmax = fmaxf(gmax, x[j][i]);
-    gmax = max_kb(gmax);
-    const float m_new = fmaxf(m, gmax);
-    const float ms = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m - ms);
-    m = m_new;
-    l *= alpha;
-    sp0 *= alpha; sp1 *= alpha; sz0 *= alpha; sz1 *= alpha;
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) acc[ct] *= alpha;
-
-    // ---- O^T += V^T P'^T per tile
-    const uint16_t* vmeta = sVm + 256 * w;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = exp2f(x[j][i] - ms);
-        l += p[i];
-      }
-      const uint4 m01 = *reinterpret_cast<const uint4*>(vmeta + 4 * (TILE * j + 4 * kb));
-      const uint4 m23 = *reinterpret_cast<const uint4*>(vmeta + 4 * (TILE * j + 4 * kb + 2));
-      const uint32_t mw[8] = {m01.x, m01.y, m01.z, m01.w, m23.x, m23.y, m23.z, m23.w};
-      h4 A0, A1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const h2 s01 = bc<h2>(mw[2 * i]);       // (s0, s1) of token i
-        const h2 z01 = bc<h2>(mw[2 * i + 1]);   // (z0, z1)
-        const _Float16 P0 = (_Float16)(p[i] * (float)s01.x);
-        const _Float16 P1 = (_Float16)(p[i] * (float)s01.y);
-        A0[i] = P0;
-        A1[i] = P1;
-        sp0 += (float)P0;
-        sp1 += (float)P1;
-        sz0 = fmaf(p[i], (float)z01.x, sz0);
-        sz1 = fmaf(p[i], (float)z01.y, sz1);
-      }
-      if constexpr (FMT == KVC_FMT_INT4) {
-        const uint32_t dw[4] = {vq[j].x, vq[j].y, vq[j].z, vq[j].w};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const h8 v8 = dec4(dw[d]);
-          const h4 va = h4{v8[0], v8[1], v8[2], v8[3]};   // channel tile 2d, tokens 0..3
-          const h4 vb = h4{v8[4], v8[5], v8[6], v8[7]};   // channel tile 2d + 1
-          acc[2 * d] = mfma16(va, d < 2 ? A0 : A1, acc[2 * d]);
-          acc[2 * d + 1] = mfma16(vb, d < 2 ? A0 : A1, acc[2 * d + 1]);
-        }
-      } else {
-        const uint32_t u = j == 0 ? vq[0].x : j == 1 ? vq[0].y : j == 2 ? vq[0].z : vq[0].w;
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-          const uint32_t w0v = dec1_word(u, 2 * (ct >> 2), ct & 3);
-          const uint32_t w1v = dec1_word(u, 2 * (ct >> 2) + 1, ct & 3);
-          const h4 va = bc<h4>(uint2{w0v, w1v});
-          acc[ct] = mfma16(va, ct < 4 ? A0 : A1, acc[ct]);
-        }
-      }
-    }
+  // two-deep software pipeline: group gi + 1 is in flight while gi computes
+  GroupData<FMT> da, db;
+  if (ga < gb) load_group<FMT>(a, b, g, ga, lane, da);
+  for (int gi = ga; gi < gb; gi += 2) {
+    if (gi + 1 < gb) load_group<FMT>(a, b, g, gi + 1, lane, db);
+    group_body<FMT, DENSE, LOGITS>(a, b, g, gi, lane, w, n, da, st, qv, dc, sKm, sVm, sMask, sPos);
+    if (gi + 1 >= gb) break;
+    if (gi + 2 < gb) load_group<FMT>(a, b, g, gi + 2, lane, da);
+    group_body<FMT, DENSE, LOGITS>(a, b, g, gi + 1, lane, w, n, db, st, qv, dc, sKm, sVm, sMask, sPos);
   }
 
   // ---- finish: sums over the four token quads, base and zero-point corrections
-  l = sum_kb(l);
-  sp0 = sum_kb(sp0); sp1 = sum_kb(sp1); sz0 = sum_kb(sz0); sz1 = sum_kb(sz1);
+  const float l = sum_kb(st.l);
+  const float sp0 = sum_kb(st.sp0), sp1 = sum_kb(st.sp1);
+  const float sz0 = sum_kb(st.sz0), sz1 = sum_kb(st.sz1);
   if (hi_lane) {
     float* o = sO + (w * 8 + head) * D;
 #pragma unroll
@@ -369,10 +433,10 @@ __device__ void quant_role(const AttendArgs& a, int b, int g, int split, int lan
       const float base = FMT == KVC_FMT_INT4 ? 16.f : (float)(16 >> (ct & 3));
       const float corr = ct < 4 ? sz0 - base * sp0 : sz1 - base * sp1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[16 * ct + 4 * kb + i] = acc[ct][i] + corr;
+      for (int i = 0; i < 4; ++i) o[16 * ct + 4 * kb + i] = st.acc[ct][i] + corr;
     }
     if (kb == 0) {
-      sML[(w * 8 + head) * 2] = m;
+      sML[(w * 8 + head) * 2] = st.m;
       sML[(w * 8 + head) * 2 + 1] = l;
     }
   }
@@ -520,12 +584,12 @@ __device__ void rows_role(const AttendArgs& a, int b, int g, int rsplit, int lan
     gmax = max_kb(gmax);
     const float m_new = fmaxf(m, gmax);
     const float ms = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m - ms);
+    const float alpha = ex2(m - ms);
     m = m_new;
     l *= alpha;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float pi = exp2f(x[i] - ms);
+      const float pi = ex2(x[i] - ms);
       l += pi;
       if (hv) P[(4 * kb + i) * 8 + col] = pi;
     }
@@ -574,8 +638,8 @@ __device__ void rows_role(const AttendArgs& a, int b, int g, int rsplit, int lan
   }
 }
 
-template <int FMT>
-__global__ __launch_bounds__(NT) void attend_kernel(AttendArgs a) {
+template <int FMT, bool DENSE, bool LOGITS>
+__global__ __launch_bounds__(NT, 2) void attend_kernel(AttendArgs a) {
   __shared__ float sO[NW * 8 * D];
   __shared__ float sML[NW * 8 * 2];
   __shared__ __align__(16) uint16_t sKm[NW * 256];
@@ -596,7 +660,7 @@ __global__ __launch_bounds__(NT) void attend_kernel(AttendArgs a) {
 
   if constexpr (FMT != KVC_FMT_FP16) {
     if (split < a.s_q)
-      quant_role<FMT>(a, b, g, split, lane, w, sO, sML, sKm, sVm, sMask, sPos);
+      quant_role<FMT, DENSE, LOGITS>(a, b, g, split, lane, w, sO, sML, sKm, sVm, sMask, sPos);
     else
       rows_role<FMT>(a, b, g, split - a.s_q, lane, w, sO, sML, sP, sTok, sOff, sAl);
   } else {
@@ -616,34 +680,65 @@ __global__ __launch_bounds__(NT) void attend_kernel(AttendArgs a) {
     for (int ww = 0; ww < NW; ++ww) {
       const float mw = sML[(ww * 8 + h) * 2];
       const float sc = mw == -INFINITY ? 0.f : exp2f(mw - ms);
-      if (k == 0) v = 0.f;
-      else if (k == 1) v += sc * sML[(ww * 8 + h) * 2 + 1];
-      else v += sc * sO[(ww * 8 + h) * D + (k - 2)];
+      if (k == 1) v += sc * sML[(ww * 8 + h) * 2 + 1];
+      else if (k >= 2) v += sc * sO[(ww * 8 + h) * D + (k - 2)];
     }
     if (k == 0) v = mx;
     float* part = a.part + (((int64_t)b * a.hq + g * G + h) * a.s_total + split) * PART;
-    part[k] = v;
+    part[k < 2 ? k : PO + (k - 2)] = v;
   }
 }
 
 // ---------------------------------------------------------------- split merge
-__global__ __launch_bounds__(D) void merge_kernel(const float* __restrict__ part, int s_total,
-                                                  float* __restrict__ out, float* __restrict__ lse) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+// One workgroup per (sequence, query head): log-sum-exp combination of the
+// split partials.  Thread t adds channel quad t % 32 over splits t / 32, +8, ...
+constexpr int MT = 256;
+constexpr int MAX_SPLITS = 2048;
+
+__global__ __launch_bounds__(MT) void merge_kernel(const float* __restrict__ part, int s_total,
+                                                   float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ float sw[MAX_SPLITS];
+  __shared__ float red[MT / 64];
+  __shared__ f4 racc[MT];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float* pp = part + (int64_t)bh * s_total * PART;
   float mx = -INFINITY;
-  for (int s = 0; s < s_total; ++s) mx = fmaxf(mx, pp[s * PART]);
+  for (int s = tid; s < s_total; s += MT) mx = fmaxf(mx, pp[s * PART]);
+  for (int o = 32; o; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[wv] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float ms = mx == -INFINITY ? 0.f : mx;
-  float L = 0.f, O = 0.f;
-  for (int s = 0; s < s_total; ++s) {
+  __syncthreads();
+  float L = 0.f;
+  for (int s = tid; s < s_total; s += MT) {
     const float m = pp[s * PART];
-    if (m == -INFINITY) continue;
-    const float sc = exp2f(m - ms);
+    const float sc = m == -INFINITY ? 0.f : exp2f(m - ms);
+    sw[s] = sc;
     L = fmaf(sc, pp[s * PART + 1], L);
-    O = fmaf(sc, pp[s * PART + 2 + c], O);
   }
-  out[(int64_t)bh * D + c] = L > 0.f ? O / L : 0.f;
-  if (c == 0) lse[bh] = L > 0.f ? (mx + log2f(L)) * LN2 : -INFINITY;
+  for (int o = 32; o; o >>= 1) L += __shfl_xor(L, o);
+  __syncthreads();
+  if (lane == 0) red[wv] = L;
+  __syncthreads();
+  L = red[0] + red[1] + red[2] + red[3];
+  const int cq = tid & 31, sl = tid >> 5;
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = sl; s < s_total; s += MT / 32) {
+    const f4 o = *reinterpret_cast<const f4*>(pp + s * PART + PO + 4 * cq);
+    acc += sw[s] * o;
+  }
+  racc[tid] = acc;
+  __syncthreads();
+  if (tid < 32) {
+    f4 t = racc[tid];
+#pragma unroll
+    for (int k = 1; k < MT / 32; ++k) t += racc[tid + 32 * k];
+    const f4 r = L > 0.f ? t / L : f4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f4*>(out + (int64_t)bh * D + 4 * tid) = r;
+    if (tid == 0) lse[bh] = L > 0.f ? (mx + log2f(L)) * LN2 : -INFINITY;
+  }
 }
 
 struct Plan {
@@ -659,7 +754,9 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   Plan p{0, 0, 1, TILE};
   const int pairs = c.batch * c.num_kv_heads;
   const bool quant = c.format != KVC_FMT_FP16;
-  const int target = env_int("KVC_ATTEND_TARGET_WG", 1024);   // workgroups per launch
+  // workgroups resident at once: 256 CUs x 2 four-wave workgroups (the quantized
+  // role runs two waves per SIMD); one full round keeps every CU streaming
+  const int target = env_int("KVC_ATTEND_TARGET_WG", 512);
   if (quant) {
     const int groups = c.max_tokens / GS;
     const int64_t waves = (int64_t)target * NW;
@@ -670,10 +767,14 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   if (mode == KVC_ATTEND_DENSE) np = quant ? GS : c.max_tokens;
   else np = (int64_t)n_sink + k_max + n_window + (mode == KVC_ATTEND_KEEP ? GS : 0);
   const int64_t tiles = std::max<int64_t>(1, (np + TILE - 1) / TILE);
-  const int64_t rwaves = (int64_t)(quant ? std::max(1, target / 4) : target) * NW;
+  const int64_t rwaves = (int64_t)(quant ? std::max(1, target / 4) : 2 * target) * NW;
   const int64_t tpw = std::max<int64_t>(1, (tiles * pairs + rwaves - 1) / rwaves);
   p.ppw = (int)(tpw * TILE);
   p.s_r = (int)((tiles + NW * tpw - 1) / (NW * tpw));
+  while (p.s_q + p.s_r > MAX_SPLITS) {   // keep the merge's per-split weights in LDS
+    if (p.s_q >= p.s_r) { p.gpw *= 2; p.s_q = (c.max_tokens / GS + NW * p.gpw - 1) / (NW * p.gpw); }
+    else { p.ppw *= 2; p.s_r = (int)((tiles * TILE + (int64_t)NW * p.ppw - 1) / ((int64_t)NW * p.ppw)); }
+  }
   return p;
 }
 
@@ -710,14 +811,23 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   a.gpw = p.gpw;
   a.ppw = p.ppw;
   const dim3 grid(a.s_total, c.num_kv_heads, c.batch);
+  const bool dense = mode == KVC_ATTEND_DENSE, lg = logits != nullptr;
+#define KVC_LAUNCH(F, DN, LG) attend_kernel<F, DN, LG><<<grid, NT, 0, s>>>(a)
+#define KVC_LAUNCH_F(F)                                   \
+  do {                                                    \
+    if (dense) { if (lg) KVC_LAUNCH(F, true, true); else KVC_LAUNCH(F, true, false); } \
+    else { if (lg) KVC_LAUNCH(F, false, true); else KVC_LAUNCH(F, false, false); }     \
+  } while (0)
   switch (c.format) {
-    case KVC_FMT_INT4: attend_kernel<KVC_FMT_INT4><<<grid, NT, 0, s>>>(a); break;
-    case KVC_FMT_INT1: attend_kernel<KVC_FMT_INT1><<<grid, NT, 0, s>>>(a); break;
-    default: attend_kernel<KVC_FMT_FP16><<<grid, NT, 0, s>>>(a); break;
+    case KVC_FMT_INT4: KVC_LAUNCH_F(KVC_FMT_INT4); break;
+    case KVC_FMT_INT1: KVC_LAUNCH_F(KVC_FMT_INT1); break;
+    default: KVC_LAUNCH_F(KVC_FMT_FP16); break;
   }
+#undef KVC_LAUNCH_F
+#undef KVC_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  merge_kernel<<<c.batch * hq, D, 0, s>>>(a.part, a.s_total, out, lse);
+  merge_kernel<<<c.batch * hq, MT, 0, s>>>(a.part, a.s_total, out, lse);
   return hipGetLastError();
 }
 
