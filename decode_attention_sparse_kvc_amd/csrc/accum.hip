@@ -1,0 +1,63 @@
+// H2O cumulative attention scores (StreamingLLM / H2O survey, section 3.2):
+// after a decode step, every attended token of (sequence b, KV head g) gains
+// the attention probabilities exp(logit - lse) of all query heads that read
+// that KV head.  Positions follow kvc_attend_decode's logits layout, so one
+// thread per position adds one token; every token appears at most once.
+
+#include <math.h>
+
+#include "internal.h"
+
+namespace kvc {
+namespace {
+
+constexpr int AT = 256;
+
+__global__ __launch_bounds__(AT) void accum_kernel(kvc_cache c, int hq, const float* __restrict__ logits,
+                                                   int64_t stride, const float* __restrict__ lse,
+                                                   int mode, const int32_t* __restrict__ sel, int k_max,
+                                                   int n_sink, int n_window, float* __restrict__ acc) {
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int p = blockIdx.x * AT + threadIdx.x;
+  const int G = hq / c.num_kv_heads;
+  const int n = max(c.seq_lens[b], 0);
+  int t;
+  bool ok;
+  if (mode == KVC_ATTEND_DROP) {
+    const int w0 = max(n - n_window, min(n_sink, n));
+    if (p < n_sink) {
+      t = p;
+      ok = p < n;
+    } else if (p < n_sink + k_max) {
+      t = sel[((int64_t)b * c.num_kv_heads + g) * k_max + (p - n_sink)];
+      ok = t >= n_sink && t < n - n_window;
+    } else {
+      t = w0 + (p - n_sink - k_max);
+      ok = p < n_sink + k_max + n_window && t < n;
+    }
+  } else {
+    t = p;
+    ok = p < n;
+  }
+  if (!ok) return;
+  float s = 0.f;
+  for (int h = 0; h < G; ++h) {
+    const int64_t row = (int64_t)b * hq + g * G + h;
+    s += expf(logits[row * stride + p] - lse[row]);
+  }
+  acc[((int64_t)b * c.num_kv_heads + g) * c.max_tokens + t] += s;
+}
+
+}  // namespace
+
+hipError_t launch_accum(const kvc_cache& c, int hq, const float* logits, int64_t stride,
+                        const float* lse, int mode, const int32_t* sel, int k_max, int n_sink,
+                        int n_window, float* acc, hipStream_t s) {
+  const int64_t np = mode == KVC_ATTEND_DROP ? (int64_t)n_sink + k_max + n_window : c.max_tokens;
+  if (np <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((np + AT - 1) / AT), c.num_kv_heads, c.batch);
+  accum_kernel<<<grid, AT, 0, s>>>(c, hq, logits, stride, lse, mode, sel, k_max, n_sink, n_window, acc);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

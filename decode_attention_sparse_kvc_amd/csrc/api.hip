@@ -102,7 +102,31 @@ kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num
                           hipStream_t stream) {
   kvc_status st = check_cache(cache);
   if (st != KVC_OK) return st;
-  return KVC_ERR_UNSUPPORTED;
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads) return KVC_ERR_SHAPE;
+  if (num_q_heads / cache->num_kv_heads > 16) return KVC_ERR_UNSUPPORTED;
+  if (score_mode < KVC_SCORE_EXACT || score_mode > KVC_SCORE_EXTERNAL) return KVC_ERR_INVALID;
+  if (n_sink < 0 || n_window < 0 || k_max < 0) return KVC_ERR_INVALID;
+  if (!out_idx || !aligned(out_idx, 4)) return KVC_ERR_INVALID;
+  if (k_per_seq && !aligned(k_per_seq, 4)) return KVC_ERR_INVALID;
+  if (out_scores && !aligned(out_scores, 8)) return KVC_ERR_INVALID;
+  if (score_mode == KVC_SCORE_EXTERNAL) {
+    if (!ext || !aligned(ext, 4)) return KVC_ERR_INVALID;
+  } else {
+    if (!q || !aligned(q, 2)) return KVC_ERR_INVALID;
+  }
+  if (score_mode == KVC_SCORE_CRITICAL) {
+    if (n_crit < 1 || n_crit > KVC_HEAD_DIM) return KVC_ERR_INVALID;
+    if (!cache->k_absmax) return KVC_ERR_INVALID;
+    if (out_channels && !aligned(out_channels, 4)) return KVC_ERR_INVALID;
+  } else {
+    out_channels = nullptr;
+  }
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < topk_workspace_bytes(*cache))
+    return KVC_ERR_WORKSPACE;
+  if (k_max == 0) return KVC_OK;
+  return hip_status(launch_score_topk(*cache, q, num_q_heads, score_mode, n_crit, ext, n_sink,
+                                      n_window, k_per_seq, k_max, out_idx, out_scores,
+                                      out_channels, workspace, stream));
 }
 
 kvc_status kvc_attend_decode(const kvc_cache* cache, const uint16_t* q, int32_t num_q_heads,
@@ -133,7 +157,15 @@ kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const f
                             float* acc, hipStream_t stream) {
   kvc_status st = check_cache(cache);
   if (st != KVC_OK) return st;
-  return KVC_ERR_UNSUPPORTED;
+  st = check_attend_args(cache, num_q_heads, mode, sel, k_max, n_sink, n_window);
+  if (st != KVC_OK && !(st == KVC_ERR_UNSUPPORTED && mode == KVC_ATTEND_KEEP)) return st;
+  if (!logits || !lse || !acc || !aligned(logits, 4) || !aligned(lse, 4) || !aligned(acc, 4))
+    return KVC_ERR_INVALID;
+  const int64_t need = mode == KVC_ATTEND_DROP ? (int64_t)n_sink + k_max + n_window
+                                               : (int64_t)cache->max_tokens;
+  if (logits_stride < need) return KVC_ERR_SHAPE;
+  return hip_status(launch_accum(*cache, num_q_heads, logits, logits_stride, lse, mode, sel, k_max,
+                                 n_sink, n_window, acc, stream));
 }
 
 size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t mode,
@@ -144,6 +176,7 @@ size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_hea
       return 0;
     return attend_workspace_bytes(*cache, num_q_heads, mode, k_max, n_sink, n_window);
   }
+  if (op == KVC_OP_SCORE_TOPK) return topk_workspace_bytes(*cache);
   return 0;
 }
 

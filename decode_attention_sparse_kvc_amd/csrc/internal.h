@@ -70,4 +70,13 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
                          float* lse, float* logits, int64_t logits_stride, void* ws,
                          hipStream_t s);
 
+size_t topk_workspace_bytes(const kvc_cache& c);
+hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int mode, int n_crit,
+                             const float* ext, int n_sink, int n_window, const int32_t* k_per_seq,
+                             int k_max, int32_t* out_idx, double* out_scores,
+                             int32_t* out_channels, void* ws, hipStream_t s);
+hipError_t launch_accum(const kvc_cache& c, int hq, const float* logits, int64_t stride,
+                        const float* lse, int mode, const int32_t* sel, int k_max, int n_sink,
+                        int n_window, float* acc, hipStream_t s);
+
 }  // namespace kvc

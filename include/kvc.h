@@ -178,7 +178,8 @@ kvc_status kvc_quantize_append(const kvc_cache* cache, const uint16_t* k_new,
  *               of q_{h,c} * k~_{t,c} (k~ = fp16 row or code*s + z), plus 0.0.
  *   ext         float32 [B][Hkv][max_tokens] (EXTERNAL only).
  *   candidates  tokens in [n_sink, n - n_window), n = seq_lens[b].
- *   k_per_seq   device int32 [B] or NULL (then k_max); k_b = min(k, #candidates).
+ *   k_per_seq   device int32 [B] or NULL (then k_max);
+ *               k_b = min(max(k_per_seq[b], 0), k_max, #candidates).
  *   out_idx     int32 [B][Hkv][k_max]: the k_b best tokens under (score desc,
  *               index asc), in ascending order, then -1.
  *   out_scores  optional fp64 [B][Hkv][max_tokens]: r_t of every candidate.

@@ -67,7 +67,7 @@ def topk_indices(r: np.ndarray, lo: int, hi: int, k: int, k_max: int) -> np.ndar
     lo = max(lo, 0)
     hi = min(hi, r.shape[0])
     cand = np.arange(lo, hi) if hi > lo else np.zeros(0, np.int64)
-    take = min(max(k, 0), cand.size)
+    take = min(max(k, 0), cand.size, k_max)    # the output holds k_max entries
     # lexsort: last key is primary; -r descending, then t ascending
     order = np.lexsort((cand, -r[cand])) if cand.size else cand
     chosen = np.sort(cand[order[:take]])

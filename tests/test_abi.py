@@ -90,3 +90,41 @@ def test_quantize_append_argument_checks():
 
 def test_packing_tables_are_permutations():
     check_bit_tables()
+
+
+def test_score_topk_and_accum_argument_checks():
+    d = _desc(format=0, k16=0x10000, v16=0x20000, k_codes=None, v_codes=None, k_meta=None,
+              v_meta=None, k_tail=None, v_tail=None)
+    L = kvc.lib()
+    ok = dict(q=0x30000, hq=8, mode=1, n_crit=8, ext=None, sink=0, win=0, kps=None, kmax=4,
+              idx=0x40000, sc=None, ch=None, ws=0x50000, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.kvc_score_topk(ctypes.byref(d), a["q"], a["hq"], a["mode"], a["n_crit"], a["ext"],
+                                a["sink"], a["win"], a["kps"], a["kmax"], a["idx"], a["sc"],
+                                a["ch"], a["ws"], a["wsb"], None)
+    assert call(hq=0) == 2
+    assert call(hq=17) == 3              # more than 16 query heads per KV head
+    assert call(mode=5) == 1
+    assert call(n_crit=0) == 1 and call(n_crit=129) == 1
+    assert call(kmax=-1) == 1 and call(sink=-1) == 1
+    assert call(idx=None) == 1
+    assert call(wsb=16) == 4 and call(ws=None) == 4
+    assert call(mode=2) == 1             # external scores need ext
+    assert call(kmax=0) == 0             # nothing to select: no launch
+    d.k_absmax = None
+    assert call() == 1                   # critical channels need max|K|
+    assert L.kvc_accum_scores(ctypes.byref(d), 1, 0x60000, 7, 0x70000, 1, 0x80000, 4, 2, 2, 0x90000, None) == 2
+    assert L.kvc_accum_scores(ctypes.byref(d), 1, None, 100, 0x70000, 0, None, 0, 0, 0, 0x90000, None) == 1
+
+
+def test_workspace_sizes():
+    d = _desc(max_tokens=4096)
+    L = kvc.lib()
+    a1 = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 4, 0, 0, 0, 0)
+    a2 = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 4, 1, 128, 4, 64)
+    t = kvc.kvc_workspace_bytes(kvc.OP_SCORE_TOPK, d, 4)
+    assert a1 > 0 and a2 > 0 and t >= 4096 * 8
+    assert kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 4, 7, 0, 0, 0) == 0      # bad mode
+    assert kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 36, 0, 0, 0, 0) == 0     # G = 36 > 8

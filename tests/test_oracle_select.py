@@ -126,3 +126,9 @@ def test_attended_tokens_hand_example():
     assert S.attended_tokens("drop", 4, 2, 3, []).tolist() == [0, 1, 2, 3]
     assert S.attended_tokens("dense", 5, 2, 3, [1]).tolist() == [0, 1, 2, 3, 4]
     assert S.keep_set(10, 2, 3, [4]).tolist() == [1, 1, 0, 0, 1, 0, 0, 1, 1, 1]
+
+
+def test_topk_output_capacity_caps_k():
+    r = np.arange(50, dtype=np.float64)
+    got = S.topk_indices(r, 0, 50, 40, 8)
+    assert got.tolist() == list(range(42, 50))
