@@ -66,15 +66,30 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "copies": 20}))
 
 
-def attend_bytes(fmt: str, lens, hkv: int, hq: int, batch: int) -> int:
-    """Algorithmic bytes of one kvc_attend_decode over every cached token (dense)."""
+def attend_bytes(w, lens, k_sel) -> int:
+    """Algorithmic bytes of one kvc_attend_decode: every byte of the attended
+    K/V (codes + metadata, or fp16 rows), q, out, lse and logits written."""
+    fmt, hkv, hq, B = w.fmt, w.hkv, w.hq, w.batch
     total = 0
-    for n in lens:
-        nq = (int(n) // 64) * 64
-        per_head = nq * CODE_BYTES[fmt] + (int(n) - nq) * 512 if fmt != "fp16" else int(n) * 512
+    for b, n in enumerate(lens):
+        n = int(n)
+        nq = (n // 64) * 64
+        if w.mode == "dense":
+            per_head = nq * CODE_BYTES[fmt] + (n - nq) * 512 if fmt != "fp16" else n * 512
+        elif w.mode == "drop":
+            w0 = max(n - w.n_window, min(w.n_sink, n))
+            attended = min(w.n_sink, n) + int(k_sel[b]) + (n - w0)
+            per_head = attended * (512 if fmt == "fp16" else CODE_BYTES[fmt])
+        else:   # keep: fp16 keep set, codes for the rest (tail rows fp16)
+            w0 = max(n - w.n_window, min(w.n_sink, n))
+            keep = min(w.n_sink, n) + int(k_sel[b]) + (n - w0)
+            rest = n - keep
+            per_head = keep * 512 + rest * CODE_BYTES[fmt]
         total += hkv * per_head
-    total += batch * hq * 128 * 2           # q
-    total += batch * hq * (128 + 1) * 4     # out + lse
+        if w.accumulate:                          # logits written
+            total += hq * (n if w.mode != "drop" else w.n_sink + int(w.top_k.max()) + w.n_window) * 4
+    total += B * hq * 128 * 2           # q
+    total += B * hq * (128 + 1) * 4     # out + lse
     return total
 
 
@@ -142,14 +157,17 @@ def main():
     from decode_attention_sparse_kvc_amd import KvcCache, kvc
 
     w = W.FULL[args.workload]()
-    if w.mode != "dense":
-        raise SystemExit(f"bench.py: workload {args.workload} needs kvc_score_topk (not built yet)")
     dev = torch.device("cuda")
-    table = torch.from_numpy(w.block_table) if w.block_table is not None else None
-    extra = args.warmup + args.steps + 64
+    extra = args.warmup + args.steps + 64      # room for the tokens the steps append
     cap = ((int(w.seq_lens.max()) + extra + 63) // 64) * 64
+    table, num_pages = None, 0
+    if w.page_size:   # shuffled pages covering the grown capacity of every sequence
+        per = cap // w.page_size
+        num_pages = w.batch * per
+        perm = np.random.default_rng(w.seed).permutation(num_pages).astype(np.int32)
+        table = torch.from_numpy(perm.reshape(w.batch, per))
     base = KvcCache(w.fmt, w.batch, w.hkv, cap, page_size=w.page_size, block_table=table,
-                    num_pages=w.num_pages, fp16_rows=w.fp16_shadow, kT=w.kT)
+                    num_pages=num_pages, fp16_rows=w.fp16_shadow, kT=w.kT)
     base.append(torch.from_numpy(w.k).to(dev), torch.from_numpy(w.v).to(dev),
                 torch.from_numpy(w.seq_lens).to(dev))
     torch.cuda.synchronize()
@@ -161,50 +179,84 @@ def main():
     k_new = torch.from_numpy(w.k_new).to(dev)
     v_new = torch.from_numpy(w.v_new).to(dev)
     mode = kvc.MODE[w.mode]
+    sparse = w.score is not None
+    k_max = int(w.top_k.max()) if sparse else 0
     out = torch.empty(w.batch, w.hq, 128, device=dev)
     lse = torch.empty(w.batch, w.hq, device=dev)
-    nbytes = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, base.desc, w.hq, mode, 0, 0, 0)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    nbytes = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, base.desc, w.hq, mode, k_max, w.n_sink, w.n_window)
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    if sparse:
+        tk_bytes = kvc.kvc_workspace_bytes(kvc.OP_SCORE_TOPK, base.desc, w.hq)
+        tk_ws = torch.empty(tk_bytes, dtype=torch.uint8, device=dev)
+        sel = torch.full((w.batch, w.hkv, k_max), -1, dtype=torch.int32, device=dev)
+        k_per_seq = torch.from_numpy(w.top_k.astype(np.int32)).to(dev)
+    accs = None
+    if w.accumulate:
+        acc0 = np.zeros((w.batch, w.hkv, cap), np.float32)
+        acc0[:, :, : w.acc.shape[2]] = w.acc[:, :, :cap]
+        accs = [torch.from_numpy(acc0).to(dev) for _ in reps]
+        stride = w.n_sink + k_max + w.n_window if w.mode == "drop" else cap
+        logits = torch.empty(w.batch, w.hq, stride, device=dev)
     stream = torch.cuda.current_stream()
+    names = ["append"] + (["score_topk"] if sparse else []) + ["attend"] + (["accum"] if accs else [])
 
     def step(i, ev=None):
         r = i % nrep
         c = reps[r]
+        rec = (lambda k: ev[k].record(stream)) if ev is not None else (lambda k: None)
+        rec(0)
         kvc.kvc_quantize_append(c.desc, k_new, v_new, None, 1, None, stream)
         lens[r] += 1
-        if ev is not None:
-            ev[0].record(stream)
-        kvc.kvc_attend_decode(c.desc, q, w.hq, w.sm_scale, mode, None, 0, 0, 0, out, lse,
-                              None, 0, ws, nbytes, stream)
-        if ev is not None:
-            ev[1].record(stream)
+        rec(1)
+        e = 1
+        if sparse:
+            ext = accs[r] if w.score == "external" else None
+            kvc.kvc_score_topk(c.desc, q, w.hq, kvc.SCORE[w.score], w.n_crit, ext, w.n_sink,
+                               w.n_window, k_per_seq, k_max, sel, None, None, tk_ws, tk_bytes, stream)
+            e += 1
+            rec(e)
+        kvc.kvc_attend_decode(c.desc, q, w.hq, w.sm_scale, mode, sel if sparse else None, k_max,
+                              w.n_sink, w.n_window, out, lse, logits if accs else None,
+                              stride if accs else 0, ws, nbytes, stream)
+        e += 1
+        rec(e)
+        if accs:
+            kvc.kvc_accum_scores(c.desc, w.hq, logits, stride, lse, mode, sel if sparse else None,
+                                 k_max, w.n_sink, w.n_window, accs[r], stream)
+            e += 1
+            rec(e)
         return r
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    nev = len(names) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     ctx_tokens = 0
     att_bytes = 0
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for s in range(args.steps):
-        r = step(args.warmup + s, events[s])
+    for s_ in range(args.steps):
+        r = step(args.warmup + s_, events[s_])
         ctx_tokens += int(lens[r].sum())
-        att_bytes += attend_bytes(w.fmt, lens[r], w.hkv, w.hq, w.batch)
+        att_bytes += attend_bytes(w, lens[r], w.top_k if sparse else None)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    attend_ms = sum(a.elapsed_time(b) for a, b in events)
+    per_op_us = {nm: sum(ev[k].elapsed_time(ev[k + 1]) for ev in events) / args.steps * 1e3
+                 for k, nm in enumerate(names)}
     ms_per_step = total_ms / args.steps
-    attend_us = attend_ms / args.steps * 1e3
+    attend_us = per_op_us["attend"]
     achieved = att_bytes / args.steps / (attend_us * 1e-6) / 1e9
     digest = src_digest()
     traffic = read_traffic("attend_kernel", args.workload, digest)
+    step_desc = " + ".join({"append": "kvc_quantize_append(1 token)",
+                            "score_topk": f"kvc_score_topk({w.score})",
+                            "attend": f"kvc_attend_decode({w.mode})",
+                            "accum": "kvc_accum_scores"}[nm] for nm in names)
 
     result = {
         "metric": "decode attention context-tokens/s per layer at 128K; achieved HBM GB/s vs peak",
@@ -224,12 +276,14 @@ def main():
             "format": w.fmt,
             "batch": w.batch,
             "context": int(w.seq_lens.max()),
+            "context_total": int(w.seq_lens.sum()),
             "q_heads": w.hq,
             "kv_heads": w.hkv,
             "head_dim": 128,
-            "step": "kvc_quantize_append(1 token) + kvc_attend_decode(dense)",
+            "step": step_desc,
             "cache_replicas": nrep,
             "replica_bytes": base.nbytes(),
+            "per_op_us": per_op_us,
         },
         "roofline": {
             "bound": "hbm",
