@@ -19,12 +19,14 @@
 // (hi = fp16(q s), lo = fma(q, s, -hi)); hi sits in matrix columns [0, G) and
 // lo in columns [8, 8 + G) of the 16-wide B operand, so one 16x16x32 MFMA per
 // 32 channels yields both and a row rotation adds them.  Codes enter the MFMA
-// as fp16 "base + code" values built by one mask-and-or per code pair (base 16
-// for INT4; 16/8/4/2 by bit position for INT1); the bases come back out through
-// sum_c q'_c base_c.  For P.V the output is computed transposed, O^T = V^T P'^T,
-// so a lane's accumulator column is its own query head and the online rescale
-// needs no cross-lane traffic; P' = p * s_v per token and V half, and
-// sum_t p z_v and sum_t P' base are kept beside it.
+// as fp16 "base + code" values built by one mask-and-or per code pair (bases
+// 256/16 by nibble position for INT4, 16/8/4/2 by bit position for INT1).  Two more MFMAs per 32 channels give each tile its starting value
+// sum_c q_c z_c - sum_c q'_c base_c.  For P.V the output is computed
+// transposed, O^T = V^T P'^T, so a lane's accumulator column is its own query
+// head; P' = p * s_v per token and V half.  sum_t p z_v is kept on the vector
+// unit and sum_t P'_t base_t on the matrix cores beside the output.  When a KV
+// head serves at most 4 query heads, the softmax of the four tiles of a group
+// runs packed into all 64 lanes (tile j in lanes 4j..4j+3 of each row).
 
 #include <math.h>
 
@@ -56,6 +58,8 @@ struct AttendArgs {
   float* logits;
   int64_t logits_stride;
   float* part;                // [B][Hq][s_total][PART]
+  uint32_t* sbits;            // drop/keep: [B][Hkv][max_tokens/32] valid sel entries as bits
+  int32_t* spre;              // drop/keep: [B][Hkv][max_tokens/32] sel index of the word's first token
   int s_q, s_total;
   int gpw;                    // quantized role: 64-token groups per wave
   int ppw;                    // rows role: positions per wave (multiple of 16)
@@ -90,17 +94,6 @@ __device__ inline uint32_t vconst(uint32_t x) {
   return x;
 }
 
-// INT4 dword (nibble slots j at bits 16*(j&1) + 4*(j>>1)) -> 8 fp16 values 16 + code_j.
-// M = 0x03C003C0 and B = 0x4C004C00 (fp16 16.0 in both halves) come in VGPRs.
-__device__ inline h8 dec4(uint32_t u, uint32_t M, uint32_t B) {
-  uint4 w;
-  w.x = ((u << 6) & M) | B;
-  w.y = ((u << 2) & M) | B;
-  w.z = ((u >> 2) & M) | B;
-  w.w = ((u >> 6) & M) | B;
-  return bc<h8>(w);
-}
-
 // INT1 dword -> word (variant v, position r): bit pair (6 + r, 22 + r) of the
 // v-th shifted copy, with fp16 base 2^(4 - r) so each value is base + bit.
 // mask[r] = 0x00400040 << r and base[r] = 0x4C004C00 - 0x04000400 * r in VGPRs.
@@ -108,21 +101,6 @@ __device__ inline uint32_t dec1_word(uint32_t u, int v, int r, const uint32_t* m
                                      const uint32_t* base) {
   const uint32_t s = v == 0 ? u : v == 1 ? (u >> 4) : v == 2 ? (u << 4) : __builtin_amdgcn_alignbit(u, u, 24);
   return (s & mask[r]) | base[r];
-}
-
-struct DecConst {
-  uint32_t M4, B4, m1[4], b1[4];
-};
-__device__ inline DecConst make_dec() {
-  DecConst d;
-  d.M4 = vconst(0x03C003C0u);
-  d.B4 = vconst(0x4C004C00u);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    d.m1[r] = vconst(0x00400040u << r);
-    d.b1[r] = vconst(0x4C004C00u - 0x04000400u * (uint32_t)r);
-  }
-  return d;
 }
 
 __device__ inline f4 mfma32(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
@@ -146,20 +124,62 @@ __device__ inline int window_start(int n, int n_sink, int n_window) {
 }
 
 // ---------------------------------------------------------------- quantized role
-// Raw loads of one 64-token group: code tiles and the two metadata words.
+// Raw loads of one 64-token group: code tiles, metadata words, selection bits.
 template <int FMT>
 struct GroupData {
   uint4 k[FMT == KVC_FMT_INT4 ? 4 : 1];
   uint4 v[FMT == KVC_FMT_INT4 ? 4 : 1];
   uint2 km, vm;
+  uint2 bits;   // drop/keep: selected tokens of the group (two 32-token words)
 };
 
-// Per-wave running state of the quantized role.
+// Per-wave running state of the quantized role.  m is the running maximum of
+// the raw score q.k~ for the lane's head; the rest is relative to exp2(m * sm2).
 struct QState {
-  float m, l, sp0, sp1, sz0, sz1;
-  f4 acc[8];
-  int ptr;
+  float m, l, sz0, sz1;
+  f4 acc[8];        // O^T, channel tiles 0..7 (lane column = head)
+  f4 corr0, corr1;  // sum_t P'_t * base_t per V half, replicated over rows
 };
+
+// Code decoders.  Each pair of codes becomes an fp16 pair "base + code" with
+// one mask-and-or; the bases (per slot) are removed later by the matrix cores.
+//  INT4 dword (nibble slot j at bit 16*(j&1) + 4*(j>>1)): slots 0,1 and 4,5
+//   move to mantissa bits 2-5 (base 256), slots 2,3 and 6,7 to bits 6-9
+//   (base 16), from two shifted copies of the dword.  For keys the 8 slots are
+//   8 channels; for values slots 0-3 are tokens 0-3 of channel tile 2d and
+//   slots 4-7 the same tokens of tile 2d + 1.
+//  INT1: see dec1_word.
+struct Dec {
+  uint32_t mlo, mhi, blo, bhi;
+  uint32_t m1[4], b1[4];
+};
+__device__ inline Dec make_decoder() {
+  Dec d;
+  d.mlo = vconst(0x003C003Cu);
+  d.mhi = vconst(0x03C003C0u);
+  d.blo = vconst(0x5C005C00u);   // fp16 256.0
+  d.bhi = vconst(0x4C004C00u);   // fp16 16.0
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    d.m1[r] = vconst(0x00400040u << r);
+    d.b1[r] = vconst(0x4C004C00u - 0x04000400u * (uint32_t)r);
+  }
+  return d;
+}
+__device__ inline uint4 dec4(uint32_t u, const Dec& dc) {
+  const uint32_t a = u << 2, b = u >> 6;
+  return uint4{(a & dc.mlo) | dc.blo, (a & dc.mhi) | dc.bhi, (b & dc.mlo) | dc.blo,
+               (b & dc.mhi) | dc.bhi};
+}
+__device__ inline h8 dec4k(uint32_t u, const Dec& dc) { return bc<h8>(dec4(u, dc)); }
+__device__ inline void dec4v(uint32_t u, const Dec& dc, h4& va, h4& vb) {
+  const uint4 w = dec4(u, dc);
+  va = bc<h4>(uint2{w.x, w.y});
+  vb = bc<h4>(uint2{w.z, w.w});
+}
+__device__ inline uint32_t dec1w(uint32_t u, int v, int r, const Dec& dc) {
+  return dec1_word(u, v, r, dc.m1, dc.b1);
+}
 
 template <int FMT>
 __device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, int gi, int lane,
@@ -167,12 +187,23 @@ __device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, in
   const kvc_cache& c = a.c;
   const int t0 = gi * GS;
   if constexpr (FMT == KVC_FMT_INT4) {
+    if (c.page_size == 0 || c.page_size >= GS) {   // the group's four tiles are adjacent
+      const int64_t s = slot_of(c, b, g, t0);
+      const uint8_t* kp = c.k_codes + (s < 0 ? 0 : (s / TILE)) * UNIT_BYTES + lane * 16;
+      const uint8_t* vp = c.v_codes + (s < 0 ? 0 : (s / TILE)) * UNIT_BYTES + lane * 16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t s = slot_of(c, b, g, t0 + TILE * j);
-      const int64_t off = (s < 0 ? 0 : (s / TILE)) * UNIT_BYTES + lane * 16;
-      d.k[j] = *reinterpret_cast<const uint4*>(c.k_codes + off);
-      d.v[j] = *reinterpret_cast<const uint4*>(c.v_codes + off);
+      for (int j = 0; j < 4; ++j) {
+        d.k[j] = *reinterpret_cast<const uint4*>(kp + j * UNIT_BYTES);
+        d.v[j] = *reinterpret_cast<const uint4*>(vp + j * UNIT_BYTES);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t s = slot_of(c, b, g, t0 + TILE * j);
+        const int64_t off = (s < 0 ? 0 : (s / TILE)) * UNIT_BYTES + lane * 16;
+        d.k[j] = *reinterpret_cast<const uint4*>(c.k_codes + off);
+        d.v[j] = *reinterpret_cast<const uint4*>(c.v_codes + off);
+      }
     }
   } else {
     const int64_t s = slot_of(c, b, g, t0);
@@ -185,66 +216,82 @@ __device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, in
   d.km = *reinterpret_cast<const uint2*>(km + 4 * lane);
   const int64_t vs = slot_of(c, b, g, t0 + lane);
   d.vm = vs < 0 ? uint2{0u, 0u} : *reinterpret_cast<const uint2*>(c.v_meta + vs * 4);
+  if (a.sbits) {
+    const int words = c.max_tokens / 32;
+    d.bits = *reinterpret_cast<const uint2*>(a.sbits + ((int64_t)b * c.num_kv_heads + g) * words + 2 * gi);
+  }
 }
 
-template <int FMT, bool DENSE, bool LOGITS>
+// Value from lane (l - 4k) of the same 16-lane row into lanes of bank k only.
+template <int K>
+__device__ inline float put_bank(float old, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x),
+                                                    0x110 + 4 * K, 0xF, 1 << K, false));
+}
+// Word of lane (l + 4k) of the same row (0 past the row's end).
+template <int K>
+__device__ inline uint32_t take_bank(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x100 + 4 * K, 0xF, 0xF, true);
+}
+__device__ inline float ror4(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+}
+
+template <int FMT, bool DENSE, bool LOGITS, bool PACK>
 __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, int gi, int lane,
                                            int w, int n, const GroupData<FMT>& d, QState& st,
-                                           const h2* qv, const DecConst& dc, uint16_t* sKm,
-                                           uint16_t* sVm, uint32_t* sMask, int* sPos) {
+                                           const h2* qv, const Dec& dc, uint16_t* sKm,
+                                           uint16_t* sVm) {
   const int G = a.G;
   const int col = lane & 15, kb = lane >> 4, head = col & 7;
   const bool hv = head < G;
   const bool hi_lane = hv && col < 8;
   const uint32_t lo_sel = (hv && !hi_lane) ? 0xFFFFFFFFu : 0u;  // lo lanes subtract hi
-  const uint32_t hv_sel = hv ? 0xFFFFFFFFu : 0u;
   const int t0 = gi * GS;
 
   // ---- which tokens of this group are attended from the codes
   uint64_t att = ~0ull;
+  const int w0 = window_start(n, a.n_sink, a.n_window);
+  const uint64_t selm = DENSE ? 0ull : ((uint64_t)d.bits.x | ((uint64_t)d.bits.y << 32));
   if constexpr (!DENSE) {
-    const int32_t* sel = a.sel ? a.sel + ((int64_t)b * a.c.num_kv_heads + g) * a.k_max : nullptr;
-    const int w0 = window_start(n, a.n_sink, a.n_window);
     const int tl = t0 + lane;
-    const bool in = tl < a.n_sink || tl >= w0;
-    uint32_t* mw = sMask + 2 * w;
-    if (lane < 2) mw[lane] = 0u;
-    wave_sync_lds();
-    int e = INT_MAX;
-    if (sel && st.ptr + lane < a.k_max) e = sel_key(sel[st.ptr + lane]);
-    const bool ing = e < t0 + GS;                 // entries before ptr are < t0
-    const int cnt = __popcll(__ballot(ing));
-    if (ing && e >= a.n_sink && e < n - a.n_window) {
-      atomicOr(&mw[(e - t0) >> 5], 1u << ((e - t0) & 31));
-      sPos[GS * w + (e - t0)] = a.n_sink + st.ptr + lane;
-    }
-    st.ptr += cnt;
-    wave_sync_lds();
-    const uint64_t selm = (uint64_t)mw[0] | ((uint64_t)mw[1] << 32);
-    const uint64_t inset = __ballot(in) | selm;
+    const uint64_t inset = __ballot(tl < a.n_sink || tl >= w0) | selm;
     att = a.mode == KVC_ATTEND_DROP ? inset : ~inset;
-    if (a.mode == KVC_ATTEND_DROP && a.logits && in)   // logits positions of sinks / window
-      sPos[GS * w + lane] = tl < a.n_sink ? tl : a.n_sink + a.k_max + (tl - w0);
-    wave_sync_lds();
     if (att == 0) return;
   }
 
-  // ---- stage the group's K scales/zeros and V token metadata in LDS
-  *reinterpret_cast<uint2*>(sKm + 256 * w + 4 * lane) = d.km;
-  *reinterpret_cast<uint2*>(sVm + 256 * w + 4 * lane) = d.vm;
+  // ---- stage K scales and zeros / 2 (zeros are added back doubled, see bias) and V metadata
+  {
+    uint2 km = d.km;
+    if (lane >= 32) {   // halves 128..255 are the zeros
+      const h2 half = h2{(_Float16)0.5f, (_Float16)0.5f};
+      km.x = bc<uint32_t>(bc<h2>(km.x) * half);
+      km.y = bc<uint32_t>(bc<h2>(km.y) * half);
+    }
+    *reinterpret_cast<uint2*>(sKm + 256 * w + 4 * lane) = km;
+    *reinterpret_cast<uint2*>(sVm + 256 * w + 4 * lane) = d.vm;
+  }
   wave_sync_lds();
 
-  // ---- q' = q * s as fp16 hi (columns < 8) / lo (columns >= 8); bias
+  // ---- q' = q * s as fp16 hi (columns < 8) / lo (columns >= 8); per-group bias on the MFMA:
+  //      columns get sum_c (z/2) q (hi and lo alike, so they add to sum z q) minus sum_c base_c q'
   h8 qp[4];
-  float qz = 0.f, qb = 0.f;
+  f4 bias = f4{0.f, 0.f, 0.f, 0.f};
   {
     const uint16_t* ks = sKm + 256 * w;
+    h8 nbase;
+    if constexpr (FMT == KVC_FMT_INT4) {
+      const _Float16 x = (_Float16)-256.f, y = (_Float16)-16.f;
+      nbase = h8{x, x, y, y, x, x, y, y};
+    } else {
+      nbase = h8{(_Float16)-16.f, (_Float16)-16.f, (_Float16)-8.f, (_Float16)-8.f,
+                 (_Float16)-4.f, (_Float16)-4.f, (_Float16)-2.f, (_Float16)-2.f};
+    }
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const uint4 s4 = *reinterpret_cast<const uint4*>(ks + 32 * kb + 8 * kc);
       const uint4 z4 = *reinterpret_cast<const uint4*>(ks + D + 32 * kb + 8 * kc);
       const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
-      const uint32_t zw[4] = {z4.x, z4.y, z4.z, z4.w};
       uint32_t out[4];
 #pragma unroll
       for (int pr = 0; pr < 4; ++pr) {
@@ -252,126 +299,210 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
         const h2 ss = bc<h2>(sw[pr]);
         const h2 hi = qq * ss;
         const h2 sub = bc<h2>(bc<uint32_t>(hi) & lo_sel);
-        const h2 r = __builtin_elementwise_fma(qq, ss, -sub);
-        const uint32_t rw = bc<uint32_t>(r) & hv_sel;
-        out[pr] = rw;
-        qz = __builtin_amdgcn_fdot2(qq, bc<h2>(zw[pr]), qz, false);
-        h2 base;
-        if constexpr (FMT == KVC_FMT_INT4) {
-          base = h2{(_Float16)16.f, (_Float16)16.f};
-        } else {
-          const _Float16 bv = (_Float16)(float)(16 >> pr);   // slots 2pr, 2pr+1
-          base = h2{bv, bv};
-        }
-        qb = __builtin_amdgcn_fdot2(bc<h2>(rw), base, qb, false);
+        out[pr] = bc<uint32_t>(__builtin_elementwise_fma(qq, ss, -sub));
       }
       qp[kc] = bc<h8>(uint4{out[0], out[1], out[2], out[3]});
+      const h8 qk = bc<h8>(uint4{bc<uint32_t>(qv[4 * kc]), bc<uint32_t>(qv[4 * kc + 1]),
+                                 bc<uint32_t>(qv[4 * kc + 2]), bc<uint32_t>(qv[4 * kc + 3])});
+      bias = mfma32(bc<h8>(z4), qk, bias);
+      bias = mfma32(nbase, qp[kc], bias);
     }
   }
-  const float bias = sum_kb((hi_lane ? qz : 0.f) - qb);
 
-  // ---- S^T = codes x q'^T per 16-token tile; hi + lo; scale to log2 units
+  // ---- S^T = codes x q'^T per 16-token tile; hi + lo columns added (raw units)
   float x[4][4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    f4 s = f4{bias, bias, bias, bias};
+    f4 s = bias;
     if constexpr (FMT == KVC_FMT_INT4) {
-      s = mfma32(dec4(d.k[j].x, dc.M4, dc.B4), qp[0], s);
-      s = mfma32(dec4(d.k[j].y, dc.M4, dc.B4), qp[1], s);
-      s = mfma32(dec4(d.k[j].z, dc.M4, dc.B4), qp[2], s);
-      s = mfma32(dec4(d.k[j].w, dc.M4, dc.B4), qp[3], s);
+      s = mfma32(dec4k(d.k[j].x, dc), qp[0], s);
+      s = mfma32(dec4k(d.k[j].y, dc), qp[1], s);
+      s = mfma32(dec4k(d.k[j].z, dc), qp[2], s);
+      s = mfma32(dec4k(d.k[j].w, dc), qp[3], s);
     } else {
       const uint32_t u = j == 0 ? d.k[0].x : j == 1 ? d.k[0].y : j == 2 ? d.k[0].z : d.k[0].w;
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        const uint4 wv = uint4{dec1_word(u, kc, 0, dc.m1, dc.b1), dec1_word(u, kc, 1, dc.m1, dc.b1),
-                               dec1_word(u, kc, 2, dc.m1, dc.b1), dec1_word(u, kc, 3, dc.m1, dc.b1)};
+        const uint4 wv = uint4{dec1w(u, kc, 0, dc), dec1w(u, kc, 1, dc), dec1w(u, kc, 2, dc),
+                               dec1w(u, kc, 3, dc)};
         s = mfma32(bc<h8>(wv), qp[kc], s);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float v = s[i] + ror8(s[i]);
-      const int bit = TILE * j + 4 * kb + i;
-      const bool on = DENSE || ((att >> bit) & 1ull);
-      x[j][i] = on ? v * a.sm2 : -INFINITY;
-      if (LOGITS && hi_lane && on) {
-        const int pos = a.mode == KVC_ATTEND_DROP ? sPos[GS * w + bit] : t0 + bit;
-        a.logits[((int64_t)b * a.hq + g * G + head) * a.logits_stride + pos] = v * a.sm;
-      }
-    }
+    for (int i = 0; i < 4; ++i) x[j][i] = s[i] + ror8(s[i]);
   }
 
-  // ---- online softmax (log2 units)
-  float gmax = -INFINITY;
+  // ---- logits (natural units) of the attended tokens
+  if constexpr (LOGITS) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gmax = fmaxf(gmax, x[j][i]);
-  gmax = max_kb(gmax);
-  const float m_new = fmaxf(st.m, gmax);
-  const float ms = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = ex2(st.m - ms);
-  st.m = m_new;
-  st.l *= alpha;
-  st.sp0 *= alpha; st.sp1 *= alpha; st.sz0 *= alpha; st.sz1 *= alpha;
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= alpha;
+      for (int i = 0; i < 4; ++i) {
+        const int bit = TILE * j + 4 * kb + i;
+        const bool on = DENSE || ((att >> bit) & 1ull);
+        if (hi_lane && on) {
+          int pos = t0 + bit;
+          if (a.mode == KVC_ATTEND_DROP) {
+            const int t = t0 + bit;
+            if (t < a.n_sink) {
+              pos = t;
+            } else if (t >= w0) {
+              pos = a.n_sink + a.k_max + (t - w0);
+            } else {
+              const uint32_t word = (bit >> 5) ? d.bits.y : d.bits.x;
+              const int32_t base = a.spre[((int64_t)b * a.c.num_kv_heads + g) * (a.c.max_tokens / 32) + (t >> 5)];
+              pos = a.n_sink + base + __popc(word & ((1u << (t & 31)) - 1u));
+            }
+          }
+          a.logits[((int64_t)b * a.hq + g * G + head) * a.logits_stride + pos] = x[j][i] * a.sm;
+        }
+      }
+  }
 
-  // ---- O^T += V^T P'^T per tile
   const uint16_t* vmeta = sVm + 256 * w;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float p[4];
+  h4 B0[4], B1[4];   // P' of each tile as the B operand of P.V (lane column = head)
+  if constexpr (PACK) {
+    // ---- pack the four tiles into all 64 lanes: lane (4j + h, kb) takes head h of tile j
+    float y[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = ex2(x[j][i] - ms);
-      st.l += p[i];
+      float v = x[0][i];
+      v = put_bank<1>(v, x[1][i]);
+      v = put_bank<2>(v, x[2][i]);
+      v = put_bank<3>(v, x[3][i]);
+      y[i] = v;
     }
-    const uint4 m01 = *reinterpret_cast<const uint4*>(vmeta + 4 * (TILE * j + 4 * kb));
-    const uint4 m23 = *reinterpret_cast<const uint4*>(vmeta + 4 * (TILE * j + 4 * kb + 2));
+    const int jj = col >> 2;
+    if constexpr (!DENSE) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!((att >> (TILE * jj + 4 * kb + i)) & 1ull)) y[i] = -INFINITY;
+    }
+    float gmax = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
+    gmax = fmaxf(gmax, ror4(gmax));
+    gmax = fmaxf(gmax, ror8(gmax));
+    gmax = max_kb(gmax);
+    const float m_new = fmaxf(st.m, gmax);
+    if (__any(m_new > st.m)) {   // rescale only when some head's maximum grows
+      const float alpha = st.m == -INFINITY ? 0.f : ex2((st.m - m_new) * a.sm2);
+      st.m = m_new;
+      st.l *= alpha;
+      st.sz0 *= alpha;
+      st.sz1 *= alpha;
+      st.corr0 *= alpha;
+      st.corr1 *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= alpha;
+    }
+    const float msc = st.m == -INFINITY ? 0.f : st.m * a.sm2;
+    const uint4 m01 = *reinterpret_cast<const uint4*>(vmeta + 4 * (TILE * jj + 4 * kb));
+    const uint4 m23 = *reinterpret_cast<const uint4*>(vmeta + 4 * (TILE * jj + 4 * kb + 2));
     const uint32_t mwd[8] = {m01.x, m01.y, m01.z, m01.w, m23.x, m23.y, m23.z, m23.w};
     h4 A0, A1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const h2 s01 = bc<h2>(mwd[2 * i]);       // (s0, s1) of token i
-      const h2 z01 = bc<h2>(mwd[2 * i + 1]);   // (z0, z1)
-      const _Float16 P0 = (_Float16)(p[i] * (float)s01.x);
-      const _Float16 P1 = (_Float16)(p[i] * (float)s01.y);
-      A0[i] = P0;
-      A1[i] = P1;
-      st.sp0 += (float)P0;
-      st.sp1 += (float)P1;
-      st.sz0 = fmaf(p[i], (float)z01.x, st.sz0);
-      st.sz1 = fmaf(p[i], (float)z01.y, st.sz1);
+      const float p = ex2(fmaf(y[i], a.sm2, -msc));
+      st.l += p;
+      const h2 s01 = bc<h2>(mwd[2 * i]);
+      const h2 z01 = bc<h2>(mwd[2 * i + 1]);
+      A0[i] = (_Float16)(p * (float)s01.x);
+      A1[i] = (_Float16)(p * (float)s01.y);
+      st.sz0 = fmaf(p, (float)z01.x, st.sz0);
+      st.sz1 = fmaf(p, (float)z01.y, st.sz1);
     }
+    // ---- unpack: tile j's P' back to lanes (h, kb)
+    const uint2 a0 = bc<uint2>(A0), a1 = bc<uint2>(A1);
+    B0[0] = A0;
+    B1[0] = A1;
+    B0[1] = bc<h4>(uint2{take_bank<1>(a0.x), take_bank<1>(a0.y)});
+    B1[1] = bc<h4>(uint2{take_bank<1>(a1.x), take_bank<1>(a1.y)});
+    B0[2] = bc<h4>(uint2{take_bank<2>(a0.x), take_bank<2>(a0.y)});
+    B1[2] = bc<h4>(uint2{take_bank<2>(a1.x), take_bank<2>(a1.y)});
+    B0[3] = bc<h4>(uint2{take_bank<3>(a0.x), take_bank<3>(a0.y)});
+    B1[3] = bc<h4>(uint2{take_bank<3>(a1.x), take_bank<3>(a1.y)});
+  } else {
+    if constexpr (!DENSE) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((att >> (TILE * j + 4 * kb + i)) & 1ull)) x[j][i] = -INFINITY;
+    }
+    float gmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gmax = fmaxf(gmax, x[j][i]);
+    gmax = max_kb(gmax);
+    const float m_new = fmaxf(st.m, gmax);
+    if (__any(m_new > st.m)) {
+      const float alpha = st.m == -INFINITY ? 0.f : ex2((st.m - m_new) * a.sm2);
+      st.m = m_new;
+      st.l *= alpha;
+      st.sz0 *= alpha;
+      st.sz1 *= alpha;
+      st.corr0 *= alpha;
+      st.corr1 *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= alpha;
+    }
+    const float msc = st.m == -INFINITY ? 0.f : st.m * a.sm2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 m01 = *reinterpret_cast<const uint4*>(vmeta + 4 * (TILE * j + 4 * kb));
+      const uint4 m23 = *reinterpret_cast<const uint4*>(vmeta + 4 * (TILE * j + 4 * kb + 2));
+      const uint32_t mwd[8] = {m01.x, m01.y, m01.z, m01.w, m23.x, m23.y, m23.z, m23.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = ex2(fmaf(x[j][i], a.sm2, -msc));
+        st.l += p;
+        const h2 s01 = bc<h2>(mwd[2 * i]);
+        const h2 z01 = bc<h2>(mwd[2 * i + 1]);
+        B0[j][i] = (_Float16)(p * (float)s01.x);
+        B1[j][i] = (_Float16)(p * (float)s01.y);
+        st.sz0 = fmaf(p, (float)z01.x, st.sz0);
+        st.sz1 = fmaf(p, (float)z01.y, st.sz1);
+      }
+    }
+  }
+
+  // ---- O^T += V^T P'^T per tile; bases of the V codes accumulate beside it
+  h4 vbase;
+  if constexpr (FMT == KVC_FMT_INT4) {
+    const _Float16 x1 = (_Float16)256.f, x2 = (_Float16)16.f;
+    vbase = h4{x1, x1, x2, x2};
+  } else {
+    const _Float16 one = (_Float16)1.f;
+    vbase = h4{one, one, one, one};
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    st.corr0 = mfma16(vbase, B0[j], st.corr0);
+    st.corr1 = mfma16(vbase, B1[j], st.corr1);
     if constexpr (FMT == KVC_FMT_INT4) {
       const uint32_t dw[4] = {d.v[j].x, d.v[j].y, d.v[j].z, d.v[j].w};
 #pragma unroll
       for (int dd = 0; dd < 4; ++dd) {
-        const h8 v8 = dec4(dw[dd], dc.M4, dc.B4);
-        const h4 va = h4{v8[0], v8[1], v8[2], v8[3]};   // channel tile 2dd, tokens 0..3
-        const h4 vb = h4{v8[4], v8[5], v8[6], v8[7]};   // channel tile 2dd + 1
-        st.acc[2 * dd] = mfma16(va, dd < 2 ? A0 : A1, st.acc[2 * dd]);
-        st.acc[2 * dd + 1] = mfma16(vb, dd < 2 ? A0 : A1, st.acc[2 * dd + 1]);
+        h4 va, vb;
+        dec4v(dw[dd], dc, va, vb);
+        st.acc[2 * dd] = mfma16(va, dd < 2 ? B0[j] : B1[j], st.acc[2 * dd]);
+        st.acc[2 * dd + 1] = mfma16(vb, dd < 2 ? B0[j] : B1[j], st.acc[2 * dd + 1]);
       }
     } else {
       const uint32_t u = j == 0 ? d.v[0].x : j == 1 ? d.v[0].y : j == 2 ? d.v[0].z : d.v[0].w;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
-        const uint32_t w0v = dec1_word(u, 2 * (ct >> 2), ct & 3, dc.m1, dc.b1);
-        const uint32_t w1v = dec1_word(u, 2 * (ct >> 2) + 1, ct & 3, dc.m1, dc.b1);
-        const h4 va = bc<h4>(uint2{w0v, w1v});
-        st.acc[ct] = mfma16(va, ct < 4 ? A0 : A1, st.acc[ct]);
+        const uint32_t w0v = dec1w(u, 2 * (ct >> 2), ct & 3, dc);
+        const uint32_t w1v = dec1w(u, 2 * (ct >> 2) + 1, ct & 3, dc);
+        st.acc[ct] = mfma16(bc<h4>(uint2{w0v, w1v}), ct < 4 ? B0[j] : B1[j], st.acc[ct]);
       }
     }
   }
 }
 
-template <int FMT, bool DENSE, bool LOGITS>
+template <int FMT, bool DENSE, bool LOGITS, bool PACK>
 __device__ void quant_role(const AttendArgs& a, int b, int g, int split, int lane, int w,
-                           float* sO, float* sML, uint16_t* sKm, uint16_t* sVm,
-                           uint32_t* sMask, int* sPos) {
+                           float* sO, float* sML, uint16_t* sKm, uint16_t* sVm) {
   const kvc_cache& c = a.c;
   const int n = max(c.seq_lens[b], 0);
   const int ngroups = n >> 6;
@@ -382,7 +513,7 @@ __device__ void quant_role(const AttendArgs& a, int b, int g, int split, int lan
   const int ga = (split * NW + w) * a.gpw;
   const int gb = min(ga + a.gpw, ngroups);
 
-  // q of this lane's head, channels [32kb, 32kb + 32), as fp16 pairs
+  // q of this lane's head, channels [32kb, 32kb + 32), as fp16 pairs (zero off-head)
   h2 qv[16];
   {
     uint4 raw[4] = {};
@@ -402,41 +533,48 @@ __device__ void quant_role(const AttendArgs& a, int b, int g, int split, int lan
 
   QState st;
   st.m = -INFINITY;
-  st.l = st.sp0 = st.sp1 = st.sz0 = st.sz1 = 0.f;
+  st.l = st.sz0 = st.sz1 = 0.f;
+  st.corr0 = st.corr1 = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) st.acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
-  st.ptr = 0;
-  if (!DENSE && a.sel && ga < gb)
-    st.ptr = lower_bound_sel(a.sel + ((int64_t)b * c.num_kv_heads + g) * a.k_max, a.k_max, ga * GS);
-
-  const DecConst dc = make_dec();
+  const Dec dc = make_decoder();
 
   // two-deep software pipeline: group gi + 1 is in flight while gi computes
   GroupData<FMT> da, db;
   if (ga < gb) load_group<FMT>(a, b, g, ga, lane, da);
   for (int gi = ga; gi < gb; gi += 2) {
     if (gi + 1 < gb) load_group<FMT>(a, b, g, gi + 1, lane, db);
-    group_body<FMT, DENSE, LOGITS>(a, b, g, gi, lane, w, n, da, st, qv, dc, sKm, sVm, sMask, sPos);
+    group_body<FMT, DENSE, LOGITS, PACK>(a, b, g, gi, lane, w, n, da, st, qv, dc, sKm, sVm);
     if (gi + 1 >= gb) break;
     if (gi + 2 < gb) load_group<FMT>(a, b, g, gi + 2, lane, da);
-    group_body<FMT, DENSE, LOGITS>(a, b, g, gi + 1, lane, w, n, db, st, qv, dc, sKm, sVm, sMask, sPos);
+    group_body<FMT, DENSE, LOGITS, PACK>(a, b, g, gi + 1, lane, w, n, db, st, qv, dc, sKm, sVm);
   }
 
-  // ---- finish: sums over the four token quads, base and zero-point corrections
-  const float l = sum_kb(st.l);
-  const float sp0 = sum_kb(st.sp0), sp1 = sum_kb(st.sp1);
-  const float sz0 = sum_kb(st.sz0), sz1 = sum_kb(st.sz1);
+  // ---- finish: sums over the lanes of each head, bases and zero points
+  float l = st.l, sz0 = st.sz0, sz1 = st.sz1;
+  if constexpr (PACK) {   // lanes h, h+4, h+8, h+12 of each row hold head h
+    l += ror4(l);
+    l += ror8(l);
+    sz0 += ror4(sz0);
+    sz0 += ror8(sz0);
+    sz1 += ror4(sz1);
+    sz1 += ror8(sz1);
+  }
+  l = sum_kb(l);
+  sz0 = sum_kb(sz0);
+  sz1 = sum_kb(sz1);
   if (hi_lane) {
     float* o = sO + (w * 8 + head) * D;
+    const float c0 = st.corr0[0], c1 = st.corr1[0];
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      const float base = FMT == KVC_FMT_INT4 ? 16.f : (float)(16 >> (ct & 3));
-      const float corr = ct < 4 ? sz0 - base * sp0 : sz1 - base * sp1;
+      const float scale = FMT == KVC_FMT_INT4 ? 1.f : (float)(16 >> (ct & 3));
+      const float corr = ct < 4 ? sz0 - scale * c0 : sz1 - scale * c1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[16 * ct + 4 * kb + i] = st.acc[ct][i] + corr;
     }
     if (kb == 0) {
-      sML[(w * 8 + head) * 2] = st.m;
+      sML[(w * 8 + head) * 2] = st.m == -INFINITY ? -INFINITY : st.m * a.sm2;
       sML[(w * 8 + head) * 2 + 1] = l;
     }
   }
@@ -487,9 +625,8 @@ __device__ inline RowRef resolve(const AttendArgs& a, int b, int g, int n, int n
       r.tail = true;
       r.ok = r.t < n && r.t >= a.n_sink && r.t < w0;
       if (r.ok) {
-        const int32_t* sel = a.sel + ((int64_t)b * Hkv + g) * a.k_max;
-        const int i = lower_bound_sel(sel, a.k_max, r.t);
-        if (i < a.k_max && sel[i] == r.t && r.t < n - a.n_window) r.ok = false;
+        const uint32_t word = a.sbits[((int64_t)b * Hkv + g) * (c.max_tokens / 32) + (r.t >> 5)];
+        if ((word >> (r.t & 31)) & 1u) r.ok = false;
       }
     }
   }
@@ -605,11 +742,19 @@ __device__ void rows_role(const AttendArgs& a, int b, int g, int rsplit, int lan
         o[h][1] *= ah;
       }
     }
+    // all 16 rows' loads in flight before any use; empty rows read a valid
+    // address and are zeroed afterwards (their p is 0 as well)
+    const uint16_t* vsafe = c.v16 ? c.v16 : c.v_tail;
+    uint32_t vraw[TILE];
+#pragma unroll
     for (int i = 0; i < TILE; ++i) {
       const int tv = tok[i];
-      if (tv == -1) continue;
-      const uint16_t* vrow = (tv <= -2 ? c.v_tail : c.v16) + roff[i];
-      const h2 v = *reinterpret_cast<const h2*>(vrow + 2 * lane);
+      const uint16_t* vrow = tv == -1 ? vsafe : (tv <= -2 ? c.v_tail : c.v16) + roff[i];
+      vraw[i] = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
+    }
+#pragma unroll
+    for (int i = 0; i < TILE; ++i) {
+      const h2 v = bc<h2>(tok[i] == -1 ? 0u : vraw[i]);
       const float v0 = (float)v.x, v1 = (float)v.y;
 #pragma unroll
       for (int h = 0; h < 8; ++h) {
@@ -638,14 +783,12 @@ __device__ void rows_role(const AttendArgs& a, int b, int g, int rsplit, int lan
   }
 }
 
-template <int FMT, bool DENSE, bool LOGITS>
+template <int FMT, bool DENSE, bool LOGITS, bool PACK>
 __global__ __launch_bounds__(NT, 2) void attend_kernel(AttendArgs a) {
   __shared__ float sO[NW * 8 * D];
   __shared__ float sML[NW * 8 * 2];
   __shared__ __align__(16) uint16_t sKm[NW * 256];
   __shared__ __align__(16) uint16_t sVm[NW * 256];
-  __shared__ uint32_t sMask[NW * 2];
-  __shared__ int sPos[NW * GS];
   __shared__ float sP[NW * 16 * 8];
   __shared__ int sTok[NW * 16];
   __shared__ int64_t sOff[NW * 16];
@@ -660,7 +803,7 @@ __global__ __launch_bounds__(NT, 2) void attend_kernel(AttendArgs a) {
 
   if constexpr (FMT != KVC_FMT_FP16) {
     if (split < a.s_q)
-      quant_role<FMT, DENSE, LOGITS>(a, b, g, split, lane, w, sO, sML, sKm, sVm, sMask, sPos);
+      quant_role<FMT, DENSE, LOGITS, PACK>(a, b, g, split, lane, w, sO, sML, sKm, sVm);
     else
       rows_role<FMT>(a, b, g, split - a.s_q, lane, w, sO, sML, sP, sTok, sOff, sAl);
   } else {
@@ -687,6 +830,29 @@ __global__ __launch_bounds__(NT, 2) void attend_kernel(AttendArgs a) {
     float* part = a.part + (((int64_t)b * a.hq + g * G + h) * a.s_total + split) * PART;
     part[k < 2 ? k : PO + (k - 2)] = v;
   }
+}
+
+// ---------------------------------------------------------------- selection plan
+// One thread per 32-token word of (sequence, KV head): which valid sel entries
+// fall in the word (bits) and the sel index of the first entry at or after the
+// word's first token (prefix).  Every word is written, so no clearing is needed.
+__global__ __launch_bounds__(256) void sel_plan_kernel(AttendArgs a) {
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int wd = blockIdx.x * 256 + threadIdx.x;
+  const int words = a.c.max_tokens / 32;
+  if (wd >= words) return;
+  const int64_t pi = (int64_t)b * a.c.num_kv_heads + g;
+  const int n = max(a.c.seq_lens[b], 0);
+  const int32_t* sel = a.k_max > 0 ? a.sel + pi * a.k_max : nullptr;
+  const int lo = lower_bound_sel(sel, a.k_max, 32 * wd);
+  const int hi = lower_bound_sel(sel, a.k_max, 32 * wd + 32);
+  uint32_t bits = 0u;
+  for (int i = lo; i < hi; ++i) {
+    const int e = sel[i];
+    if (e >= a.n_sink && e < n - a.n_window) bits |= 1u << (e & 31);
+  }
+  a.sbits[pi * words + wd] = bits;
+  a.spre[pi * words + wd] = lo;
 }
 
 // ---------------------------------------------------------------- split merge
@@ -767,7 +933,9 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   if (mode == KVC_ATTEND_DENSE) np = quant ? GS : c.max_tokens;
   else np = (int64_t)n_sink + k_max + n_window + (mode == KVC_ATTEND_KEEP ? GS : 0);
   const int64_t tiles = std::max<int64_t>(1, (np + TILE - 1) / TILE);
-  const int64_t rwaves = (int64_t)(quant ? std::max(1, target / 4) : 2 * target) * NW;
+  // a dense quantized cache leaves only its tail (< 64 tokens) to this role
+  const int64_t rwaves = (quant && mode == KVC_ATTEND_DENSE) ? (int64_t)pairs * NW
+                                                             : (int64_t)4 * target * NW;
   const int64_t tpw = std::max<int64_t>(1, (tiles * pairs + rwaves - 1) / rwaves);
   p.ppw = (int)(tpw * TILE);
   p.s_r = (int)((tiles + NW * tpw - 1) / (NW * tpw));
@@ -783,7 +951,10 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
 size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, int n_sink,
                               int n_window) {
   const Plan p = plan_attend(c, mode, k_max, n_sink, n_window);
-  return (size_t)c.batch * hq * (p.s_q + p.s_r) * PART * sizeof(float);
+  size_t bytes = (size_t)c.batch * hq * (p.s_q + p.s_r) * PART * sizeof(float);
+  if (mode != KVC_ATTEND_DENSE && c.format != KVC_FMT_FP16)   // selection bitmap + prefix
+    bytes += 2 * (size_t)c.batch * c.num_kv_heads * (c.max_tokens / 32) * sizeof(uint32_t);
+  return bytes;
 }
 
 hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm_scale, int mode,
@@ -806,23 +977,39 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   a.logits = logits;
   a.logits_stride = logits_stride;
   a.part = static_cast<float*>(ws);
+  a.sbits = nullptr;
+  a.spre = nullptr;
+  const size_t part_bytes = (size_t)c.batch * hq * (p.s_q + p.s_r) * PART * sizeof(float);
+  const size_t sel_words = (size_t)c.batch * c.num_kv_heads * (c.max_tokens / 32);
+  if (mode != KVC_ATTEND_DENSE && c.format != KVC_FMT_FP16) {
+    a.sbits = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + part_bytes);
+    a.spre = reinterpret_cast<int32_t*>(a.sbits + sel_words);
+  }
   a.s_q = p.s_q;
   a.s_total = p.s_q + p.s_r;
   a.gpw = p.gpw;
   a.ppw = p.ppw;
   const dim3 grid(a.s_total, c.num_kv_heads, c.batch);
+  if (mode != KVC_ATTEND_DENSE && c.format != KVC_FMT_FP16) {   // k_max == 0: all-zero bits
+    const int words = c.max_tokens / 32;
+    sel_plan_kernel<<<dim3((words + 255) / 256, c.num_kv_heads, c.batch), 256, 0, s>>>(a);
+  }
   const bool dense = mode == KVC_ATTEND_DENSE, lg = logits != nullptr;
-#define KVC_LAUNCH(F, DN, LG) attend_kernel<F, DN, LG><<<grid, NT, 0, s>>>(a)
-#define KVC_LAUNCH_F(F)                                   \
-  do {                                                    \
-    if (dense) { if (lg) KVC_LAUNCH(F, true, true); else KVC_LAUNCH(F, true, false); } \
-    else { if (lg) KVC_LAUNCH(F, false, true); else KVC_LAUNCH(F, false, false); }     \
+  const bool pk = a.G <= 4 && c.format != KVC_FMT_FP16;   // packed softmax (quantized role only)
+#define KVC_LAUNCH(F, DN, LG, PK) attend_kernel<F, DN, LG, PK><<<grid, NT, 0, s>>>(a)
+#define KVC_LAUNCH_P(F, DN, LG) \
+  do { if (pk) KVC_LAUNCH(F, DN, LG, true); else KVC_LAUNCH(F, DN, LG, false); } while (0)
+#define KVC_LAUNCH_F(F)                                                                      \
+  do {                                                                                       \
+    if (dense) { if (lg) KVC_LAUNCH_P(F, true, true); else KVC_LAUNCH_P(F, true, false); }   \
+    else { if (lg) KVC_LAUNCH_P(F, false, true); else KVC_LAUNCH_P(F, false, false); }       \
   } while (0)
   switch (c.format) {
     case KVC_FMT_INT4: KVC_LAUNCH_F(KVC_FMT_INT4); break;
     case KVC_FMT_INT1: KVC_LAUNCH_F(KVC_FMT_INT1); break;
     default: KVC_LAUNCH_F(KVC_FMT_FP16); break;
   }
+#undef KVC_LAUNCH_P
 #undef KVC_LAUNCH_F
 #undef KVC_LAUNCH
   hipError_t e = hipGetLastError();
