@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--replica-bytes", type=float, default=1.5 * 2**30,
                     help="total bytes of rotated cache replicas (defeats the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every call from Python instead of replaying HIP graphs")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
@@ -158,7 +160,7 @@ def main():
 
     w = W.FULL[args.workload]()
     dev = torch.device("cuda")
-    extra = args.warmup + args.steps + 64      # room for the tokens the steps append
+    extra = args.warmup + 2 * args.steps + 64      # room for the tokens the steps append
     cap = ((int(w.seq_lens.max()) + extra + 63) // 64) * 64
     table, num_pages = None, 0
     if w.page_size:   # shuffled pages covering the grown capacity of every sequence
@@ -197,42 +199,50 @@ def main():
         accs = [torch.from_numpy(acc0).to(dev) for _ in reps]
         stride = w.n_sink + k_max + w.n_window if w.mode == "drop" else cap
         logits = torch.empty(w.batch, w.hq, stride, device=dev)
-    stream = torch.cuda.current_stream()
     names = ["append"] + (["score_topk"] if sparse else []) + ["attend"] + (["accum"] if accs else [])
 
-    def step(i, ev=None):
-        r = i % nrep
-        c = reps[r]
-        rec = (lambda k: ev[k].record(stream)) if ev is not None else (lambda k: None)
-        rec(0)
-        kvc.kvc_quantize_append(c.desc, k_new, v_new, None, 1, None, stream)
-        lens[r] += 1
-        rec(1)
-        e = 1
-        if sparse:
-            ext = accs[r] if w.score == "external" else None
-            kvc.kvc_score_topk(c.desc, q, w.hq, kvc.SCORE[w.score], w.n_crit, ext, w.n_sink,
-                               w.n_window, k_per_seq, k_max, sel, None, None, tk_ws, tk_bytes, stream)
-            e += 1
-            rec(e)
-        kvc.kvc_attend_decode(c.desc, q, w.hq, w.sm_scale, mode, sel if sparse else None, k_max,
-                              w.n_sink, w.n_window, out, lse, logits if accs else None,
-                              stride if accs else 0, ws, nbytes, stream)
-        e += 1
-        rec(e)
-        if accs:
-            kvc.kvc_accum_scores(c.desc, w.hq, logits, stride, lse, mode, sel if sparse else None,
-                                 k_max, w.n_sink, w.n_window, accs[r], stream)
-            e += 1
-            rec(e)
-        return r
+    def op_append(r, st):
+        kvc.kvc_quantize_append(reps[r].desc, k_new, v_new, None, 1, None, st)
 
+    def op_score_topk(r, st):
+        ext = accs[r] if w.score == "external" else None
+        kvc.kvc_score_topk(reps[r].desc, q, w.hq, kvc.SCORE[w.score], w.n_crit, ext, w.n_sink,
+                           w.n_window, k_per_seq, k_max, sel, None, None, tk_ws, tk_bytes, st)
+
+    def op_attend(r, st):
+        kvc.kvc_attend_decode(reps[r].desc, q, w.hq, w.sm_scale, mode, sel if sparse else None,
+                              k_max, w.n_sink, w.n_window, out, lse, logits if accs else None,
+                              stride if accs else 0, ws, nbytes, st)
+
+    def op_accum(r, st):
+        kvc.kvc_accum_scores(reps[r].desc, w.hq, logits, stride, lse, mode, sel if sparse else None,
+                             k_max, w.n_sink, w.n_window, accs[r], st)
+
+    ops = {"append": op_append, "score_topk": op_score_topk, "attend": op_attend, "accum": op_accum}
+
+    def step(r, st):
+        for nm in names:
+            ops[nm](r, st)
+
+    stream = torch.cuda.current_stream()
     for i in range(args.warmup):
-        step(i)
+        step(i % nrep, stream)
+        lens[i % nrep] += 1
     torch.cuda.synchronize()
 
-    nev = len(names) + 1
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    def capture(fn):
+        """A HIP graph of fn(stream); nothing runs until it is replayed."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(torch.cuda.current_stream())
+        return g
+
+    graph = not args.no_graph
+    if graph:   # one graph per replica holding one whole step
+        step_graphs = [capture(lambda st, r=r: step(r, st)) for r in range(nrep)]
+        torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps, the replicas in rotation
     ctx_tokens = 0
     att_bytes = 0
     t_start = torch.cuda.Event(enable_timing=True)
@@ -240,17 +250,46 @@ def main():
     torch.cuda.synchronize()
     t_start.record(stream)
     for s_ in range(args.steps):
-        r = step(args.warmup + s_, events[s_])
+        r = (args.warmup + s_) % nrep
+        if graph:
+            step_graphs[r].replay()
+        else:
+            step(r, stream)
+        lens[r] += 1
         ctx_tokens += int(lens[r].sum())
         att_bytes += attend_bytes(w, lens[r], w.top_k if sparse else None)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    per_op_us = {nm: sum(ev[k].elapsed_time(ev[k + 1]) for ev in events) / args.steps * 1e3
-                 for k, nm in enumerate(names)}
     ms_per_step = total_ms / args.steps
+
+    # ---- per-op durations: each op alone, one graph call per replica, replayed
+    # until `steps` calls have run, bracketed by events on the launch stream
+    per_op_us = {}
+    for nm in names:
+        if graph:
+            g = capture(lambda st: [ops[nm](r, st) for r in range(nrep)])
+            torch.cuda.synchronize()
+        reps_needed = -(-args.steps // nrep)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps_needed):
+            if graph:
+                g.replay()
+            else:
+                for r in range(nrep):
+                    ops[nm](r, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_op_us[nm] = e0.elapsed_time(e1) / (reps_needed * nrep) * 1e3
+        if nm == "append":
+            for r in range(nrep):
+                lens[r] += reps_needed
     attend_us = per_op_us["attend"]
-    achieved = att_bytes / args.steps / (attend_us * 1e-6) / 1e9
+    attend_calls_bytes = sum(attend_bytes(w, lens[r], w.top_k if sparse else None)
+                             for r in range(nrep)) / nrep
+    achieved = attend_calls_bytes / (attend_us * 1e-6) / 1e9
     digest = src_digest()
     traffic = read_traffic("attend_kernel", args.workload, digest)
     step_desc = " + ".join({"append": "kvc_quantize_append(1 token)",
@@ -287,13 +326,13 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "kvc_attend_decode (attend_kernel + split merge)",
+            "kernel": "kvc_attend_decode call (attend_kernel + merge_kernel)",
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": att_bytes / args.steps,
+            "algorithmic_bytes_per_launch": attend_calls_bytes,
             "launch_us": attend_us,
             "src_digest": digest,
         },

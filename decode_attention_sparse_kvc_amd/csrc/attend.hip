@@ -63,6 +63,7 @@ struct AttendArgs {
   int s_q, s_total;
   int gpw;                    // quantized role: 64-token groups per wave
   int ppw;                    // rows role: positions per wave (multiple of 16)
+  PageDiv pd;                 // token -> page division of the cache
 };
 
 template <typename T, typename F>
@@ -71,13 +72,20 @@ __device__ inline T bc(const F& f) { return __builtin_bit_cast(T, f); }
 __device__ inline float ror8(float x) {   // value of lane (l +- 8) within its row of 16
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
-__device__ inline float sum_kb(float x) {  // sum over lanes l, l^16, l^32, l^48
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+// Sums / maxima over lanes l, l^16, l^32, l^48 with the gfx950 row-swap moves
+// (no LDS round trip): each swap of a value with itself yields the value and
+// its partner lane's value.
+__device__ inline float sum_kb(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 __device__ inline float max_kb(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 // LDS accesses of one wave execute in issue order, so exchanging data through
 // LDS inside a wave only needs the compiler to keep program order.
@@ -186,35 +194,41 @@ __device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, in
                                            GroupData<FMT>& d) {
   const kvc_cache& c = a.c;
   const int t0 = gi * GS;
-  if constexpr (FMT == KVC_FMT_INT4) {
-    if (c.page_size == 0 || c.page_size >= GS) {   // the group's four tiles are adjacent
-      const int64_t s = slot_of(c, b, g, t0);
-      const uint8_t* kp = c.k_codes + (s < 0 ? 0 : (s / TILE)) * UNIT_BYTES + lane * 16;
-      const uint8_t* vp = c.v_codes + (s < 0 ? 0 : (s / TILE)) * UNIT_BYTES + lane * 16;
+  int64_t vs;   // slot of this lane's token (V metadata)
+  if (FMT == KVC_FMT_INT1 || c.page_size % GS == 0) {   // the group is 64 adjacent slots
+    const int64_t s = slot_fast(c, a.pd, b, g, t0);
+    const int64_t u = s < 0 ? 0 : (s >> 4);
+    const uint8_t* kp = c.k_codes + u * UNIT_BYTES + lane * 16;
+    const uint8_t* vp = c.v_codes + u * UNIT_BYTES + lane * 16;
+    if constexpr (FMT == KVC_FMT_INT4) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         d.k[j] = *reinterpret_cast<const uint4*>(kp + j * UNIT_BYTES);
         d.v[j] = *reinterpret_cast<const uint4*>(vp + j * UNIT_BYTES);
       }
-    } else {
+    } else {   // one 1024-byte unit per 64 tokens: unit index s / 64
+      const int64_t off = (s < 0 ? 0 : (s >> 6)) * UNIT_BYTES + lane * 16;
+      d.k[0] = *reinterpret_cast<const uint4*>(c.k_codes + off);
+      d.v[0] = *reinterpret_cast<const uint4*>(c.v_codes + off);
+    }
+    vs = s < 0 ? -1 : s + lane;
+  } else {   // INT4 with pages of 16 * odd tokens: one page lookup per 16-token tile
+    int64_t sj[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t s = slot_of(c, b, g, t0 + TILE * j);
-        const int64_t off = (s < 0 ? 0 : (s / TILE)) * UNIT_BYTES + lane * 16;
+    for (int j = 0; j < 4; ++j) {
+      sj[j] = slot_fast(c, a.pd, b, g, t0 + TILE * j);
+      const int64_t off = (sj[j] < 0 ? 0 : (sj[j] >> 4)) * UNIT_BYTES + lane * 16;
+      if constexpr (FMT == KVC_FMT_INT4) {
         d.k[j] = *reinterpret_cast<const uint4*>(c.k_codes + off);
         d.v[j] = *reinterpret_cast<const uint4*>(c.v_codes + off);
       }
     }
-  } else {
-    const int64_t s = slot_of(c, b, g, t0);
-    const int64_t off = (s < 0 ? 0 : (s / GS)) * UNIT_BYTES + lane * 16;
-    d.k[0] = *reinterpret_cast<const uint4*>(c.k_codes + off);
-    d.v[0] = *reinterpret_cast<const uint4*>(c.v_codes + off);
+    const int64_t st = lane < 16 ? sj[0] : lane < 32 ? sj[1] : lane < 48 ? sj[2] : sj[3];
+    vs = st < 0 ? -1 : st + (lane & 15);
   }
   const uint16_t* km = c.k_meta +
       ((((int64_t)b * c.num_kv_heads + g) * (c.max_tokens / GS) + gi) * 2) * D;
   d.km = *reinterpret_cast<const uint2*>(km + 4 * lane);
-  const int64_t vs = slot_of(c, b, g, t0 + lane);
   d.vm = vs < 0 ? uint2{0u, 0u} : *reinterpret_cast<const uint2*>(c.v_meta + vs * 4);
   if (a.sbits) {
     const int words = c.max_tokens / 32;
@@ -634,7 +648,7 @@ __device__ inline RowRef resolve(const AttendArgs& a, int b, int g, int n, int n
   if (r.tail) {
     r.off = (((int64_t)b * Hkv + g) * GS + (r.t - nq)) * D;
   } else {
-    const int64_t s = slot_of(c, b, g, r.t);
+    const int64_t s = slot_fast(c, a.pd, b, g, r.t);
     if (s < 0) { r.ok = false; return r; }
     r.off = s * D;
   }
@@ -795,7 +809,8 @@ __global__ __launch_bounds__(NT, 2) void attend_kernel(AttendArgs a) {
   __shared__ float sAl[NW * 8];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform per wave
   const int G = a.G;
   for (int e = tid; e < NW * 8 * 2; e += NT) sML[e] = (e & 1) ? 0.f : -INFINITY;
   for (int e = tid; e < NW * 8 * D; e += NT) sO[e] = 0.f;
@@ -858,54 +873,54 @@ __global__ __launch_bounds__(256) void sel_plan_kernel(AttendArgs a) {
 // ---------------------------------------------------------------- split merge
 // One workgroup per (sequence, query head): log-sum-exp combination of the
 // split partials.  Thread t adds channel quad t % 32 over splits t / 32, +8, ...
+// Log-sum-exp merge of the split partials, one workgroup per (sequence, query
+// head).  Thread (quad cq, replica r) folds splits r, r + 8, ... into a running
+// (max, sum, o[4 cq .. 4 cq + 3]) with online rescaling, so its loads do not
+// wait on one another; the 8 replicas are then combined through LDS.
 constexpr int MT = 256;
-constexpr int MAX_SPLITS = 2048;
-
 __global__ __launch_bounds__(MT) void merge_kernel(const float* __restrict__ part, int s_total,
                                                    float* __restrict__ out, float* __restrict__ lse) {
-  __shared__ float sw[MAX_SPLITS];
-  __shared__ float red[MT / 64];
-  __shared__ f4 racc[MT];
-  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ f4 sacc[MT];
+  __shared__ float sml[2 * MT];
+  const int bh = blockIdx.x, tid = threadIdx.x, cq = tid & 31, r = tid >> 5;
   const float* pp = part + (int64_t)bh * s_total * PART;
-  float mx = -INFINITY;
-  for (int s = tid; s < s_total; s += MT) mx = fmaxf(mx, pp[s * PART]);
-  for (int o = 32; o; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if (lane == 0) red[wv] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float ms = mx == -INFINITY ? 0.f : mx;
-  __syncthreads();
-  float L = 0.f;
-  for (int s = tid; s < s_total; s += MT) {
-    const float m = pp[s * PART];
-    const float sc = m == -INFINITY ? 0.f : exp2f(m - ms);
-    sw[s] = sc;
-    L = fmaf(sc, pp[s * PART + 1], L);
-  }
-  for (int o = 32; o; o >>= 1) L += __shfl_xor(L, o);
-  __syncthreads();
-  if (lane == 0) red[wv] = L;
-  __syncthreads();
-  L = red[0] + red[1] + red[2] + red[3];
-  const int cq = tid & 31, sl = tid >> 5;
+  float mr = -INFINITY, lr = 0.f;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = sl; s < s_total; s += MT / 32) {
-    const f4 o = *reinterpret_cast<const f4*>(pp + s * PART + PO + 4 * cq);
-    acc += sw[s] * o;
+#pragma unroll 8
+  for (int sp = r; sp < s_total; sp += MT / 32) {
+    const float m = pp[(int64_t)sp * PART];
+    const float l = pp[(int64_t)sp * PART + 1];
+    const f4 o = *reinterpret_cast<const f4*>(pp + (int64_t)sp * PART + PO + 4 * cq);
+    const float mn = fmaxf(mr, m);
+    const float sc = mr == -INFINITY ? 0.f : exp2f(mr - mn);
+    const float wt = m == -INFINITY ? 0.f : exp2f(m - mn);
+    acc = acc * sc + o * wt;
+    lr = fmaf(lr, sc, l * wt);
+    mr = mn;
   }
-  racc[tid] = acc;
+  sacc[tid] = acc;
+  sml[2 * tid] = mr;
+  sml[2 * tid + 1] = lr;
   __syncthreads();
-  if (tid < 32) {
-    f4 t = racc[tid];
+  if (r == 0) {
 #pragma unroll
-    for (int k = 1; k < MT / 32; ++k) t += racc[tid + 32 * k];
-    const f4 r = L > 0.f ? t / L : f4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f4*>(out + (int64_t)bh * D + 4 * tid) = r;
-    if (tid == 0) lse[bh] = L > 0.f ? (mx + log2f(L)) * LN2 : -INFINITY;
+    for (int k = 1; k < MT / 32; ++k) {
+      const int t = tid + 32 * k;
+      const float m = sml[2 * t], l = sml[2 * t + 1];
+      const float mn = fmaxf(mr, m);
+      const float sc = mr == -INFINITY ? 0.f : exp2f(mr - mn);
+      const float wt = m == -INFINITY ? 0.f : exp2f(m - mn);
+      acc = acc * sc + sacc[t] * wt;
+      lr = fmaf(lr, sc, l * wt);
+      mr = mn;
+    }
+    const f4 res = lr > 0.f ? acc / lr : f4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f4*>(out + (int64_t)bh * D + 4 * cq) = res;
+    if (cq == 0) lse[bh] = lr > 0.f ? (mr + log2f(lr)) * LN2 : -INFINITY;
   }
 }
+
+constexpr int MAX_SPLITS = 2048;
 
 struct Plan {
   int s_q, s_r, gpw, ppw;
@@ -939,7 +954,7 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   const int64_t tpw = std::max<int64_t>(1, (tiles * pairs + rwaves - 1) / rwaves);
   p.ppw = (int)(tpw * TILE);
   p.s_r = (int)((tiles + NW * tpw - 1) / (NW * tpw));
-  while (p.s_q + p.s_r > MAX_SPLITS) {   // keep the merge's per-split weights in LDS
+  while (p.s_q + p.s_r > MAX_SPLITS) {   // bound the merge's work per query head
     if (p.s_q >= p.s_r) { p.gpw *= 2; p.s_q = (c.max_tokens / GS + NW * p.gpw - 1) / (NW * p.gpw); }
     else { p.ppw *= 2; p.s_r = (int)((tiles * TILE + (int64_t)NW * p.ppw - 1) / ((int64_t)NW * p.ppw)); }
   }
@@ -977,6 +992,7 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   a.logits = logits;
   a.logits_stride = logits_stride;
   a.part = static_cast<float*>(ws);
+  a.pd = make_page_div(c);
   a.sbits = nullptr;
   a.spre = nullptr;
   const size_t part_bytes = (size_t)c.batch * hq * (p.s_q + p.s_r) * PART * sizeof(float);

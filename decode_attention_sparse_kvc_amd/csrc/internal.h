@@ -38,6 +38,37 @@ __device__ inline int64_t slot_of(const kvc_cache& c, int b, int g, int t) {
   return (phys * c.num_kv_heads + g) * (int64_t)P + off;
 }
 
+// Division by the page length without a divide instruction: for 0 <= t < 2^31
+// and P >= 1, t / P == (t * M) >> (32 + l) with l = ceil(log2 P) and
+// M = ceil(2^(32 + l) / P) (the rounding error of M stays below one step).
+struct PageDiv {
+  uint64_t M;
+  int sh;   // 32 + l
+  int P;
+};
+inline PageDiv make_page_div(const kvc_cache& c) {
+  PageDiv d;
+  d.P = page_tokens(c);
+  int l = 0;
+  while ((1ll << l) < d.P) ++l;
+  d.sh = 32 + l;
+  d.M = (uint64_t)((((unsigned __int128)1 << d.sh) + (unsigned)d.P - 1) / (unsigned)d.P);
+  return d;
+}
+__device__ inline int page_of(const PageDiv& d, int t) {
+  return (int)(((uint64_t)(uint32_t)t * d.M) >> d.sh);
+}
+// slot_of with the division replaced by a PageDiv of the same cache.
+__device__ inline int64_t slot_fast(const kvc_cache& c, const PageDiv& d, int b, int g, int t) {
+  if (c.page_size == 0) return ((int64_t)b * c.num_kv_heads + g) * (int64_t)c.max_tokens + t;
+  const int page = page_of(d, t);
+  const int off = t - page * d.P;
+  if (page >= c.max_pages) return -1;
+  const int64_t phys = c.block_table[(int64_t)b * c.max_pages + page];
+  if (phys < 0 || phys >= c.num_pages) return -1;
+  return (phys * c.num_kv_heads + g) * (int64_t)d.P + off;
+}
+
 // Bit position of nibble slot j (0..7) in an INT4 code dword.
 __host__ __device__ constexpr int nib_pos(int j) { return 16 * (j & 1) + 4 * (j >> 1); }
 

@@ -212,7 +212,9 @@ kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num
  *         j < n_sink -> token j, j - n_sink < k_max -> sel entry, then window
  *         token max(n - n_window, n_sink) + (j - n_sink - k_max); positions
  *         that attend nothing hold -inf.  Values are q.k~ * sm_scale.
- *   workspace  kvc_workspace_bytes(KVC_OP_ATTEND, ...) bytes (split partials).
+ *   workspace  kvc_workspace_bytes(KVC_OP_ATTEND, ...) bytes: split partials
+ *         (and, for DROP/KEEP on INT4/INT1, the selection bitmap); contents
+ *         on entry are ignored.
  */
 kvc_status kvc_attend_decode(const kvc_cache* cache, const uint16_t* q, int32_t num_q_heads,
                              float sm_scale, int32_t mode, const int32_t* sel, int32_t k_max,

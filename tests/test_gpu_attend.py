@@ -31,7 +31,7 @@ def run_attend(cache, w, sel=None, k_max=0, logits=True):
     stride = w.n_sink + k_max + w.n_window if w.mode == "drop" else cache.max_tokens
     lg = torch.full((B, hq, stride), float("nan"), device="cuda") if logits else None
     nbytes = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, cache.desc, hq, mode, k_max, w.n_sink, w.n_window)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     sel_t = dev(sel) if sel is not None else None
     kvc.kvc_attend_decode(cache.desc, dev(w.q), hq, w.sm_scale, mode, sel_t, k_max, w.n_sink,
                           w.n_window, out, lse, lg, stride, ws, nbytes)
@@ -95,6 +95,56 @@ def test_dense(fmt, n):
     res, cache = oracle_and_cache(w)
     out, lse, lg, stride = run_attend(cache, w)
     check_against_oracle(w, res, out, lse, lg)
+
+
+def paged(w, page, seed=0, room=1):
+    """Move w onto a paged cache: capacity (longest sequence + room) rounded up to
+    lcm(page, 64), pages shuffled."""
+    unit = int(np.lcm(page, 64))
+    cap = -(-(int(w.seq_lens.max()) + room) // unit) * unit
+    per = cap // page
+    perm = np.random.default_rng(seed).permutation(w.batch * per).astype(np.int32)
+    w.page_size, w.block_table = page, perm.reshape(w.batch, per)
+    w.num_pages, w.max_tokens = w.batch * per, cap
+    return w
+
+
+@pytest.mark.parametrize("fmt,page", [("int4", 16), ("int4", 48), ("int4", 64), ("int4", 192),
+                                      ("int1", 64), ("int1", 192), ("fp16", 48)])
+def test_dense_paged(fmt, page):
+    """Page lengths that split a 64-token group (16, 48) take one page lookup per tile."""
+    w = W.int1_dense(1500) if fmt == "int1" else W.int4_dense(1500)
+    w.fmt = fmt
+    paged(w, page)
+    res, cache = oracle_and_cache(w)
+    out, lse, lg, _ = run_attend(cache, w)
+    check_against_oracle(w, res, out, lse, lg)
+
+
+def test_workspace_reuse(monkeypatch):
+    """One workspace (holding stale partials of earlier calls) serves call after call, also
+    when the split count changes between calls; repeated calls agree bit for bit."""
+    w = W.int4_dense(3000)
+    res, cache = oracle_and_cache(w)
+    mode = kvc.MODE[w.mode]
+    sizes = {}
+    for t in ["512", "3", "64"]:
+        monkeypatch.setenv("KVC_ATTEND_TARGET_WG", t)
+        sizes[t] = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, cache.desc, w.hq, mode, 0, 0, 0)
+    ws = torch.full((max(sizes.values()),), 255, dtype=torch.uint8, device="cuda")   # NaN bytes
+    outs = []
+    for t in ["512", "3", "512", "64", "3"]:
+        monkeypatch.setenv("KVC_ATTEND_TARGET_WG", t)
+        out = torch.full((w.batch, w.hq, 128), float("nan"), device="cuda")
+        lse = torch.full((w.batch, w.hq), float("nan"), device="cuda")
+        kvc.kvc_attend_decode(cache.desc, dev(w.q), w.hq, w.sm_scale, mode, None, 0, 0, 0,
+                              out, lse, None, 0, ws, ws.numel())
+        torch.cuda.synchronize()
+        check_against_oracle(w, res, host(out), host(lse), None)
+        outs.append((t, host(out), host(lse)))
+    for t, o, l in outs:
+        same = [o2 for t2, o2, _ in outs if t2 == t]
+        assert all(np.array_equal(o, o2) for o2 in same), f"target {t}: repeated calls differ"
 
 
 @pytest.mark.parametrize("n", [0, 1, 5, 63, 64, 65])

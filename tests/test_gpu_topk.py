@@ -183,7 +183,7 @@ def accum_case(w, append=False):
     lse = torch.empty(B, hq, device="cuda")
     lg = torch.full((B, hq, stride), float("nan"), device="cuda")
     nb = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, cache.desc, hq, mode, km, w.n_sink, w.n_window)
-    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device="cuda")
     kvc.kvc_attend_decode(cache.desc, dev(w.q), hq, w.sm_scale, mode, dev(sel) if sel is not None else None,
                           km, w.n_sink, w.n_window, out, lse, lg, stride, ws, nb)
     acc = run_accum(cache, w, lg, stride, lse, sel, km)
