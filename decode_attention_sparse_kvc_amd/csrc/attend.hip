@@ -61,13 +61,19 @@ struct AttendArgs {
   uint32_t* sbits;            // drop/keep: [B][Hkv][max_tokens/32] valid sel entries as bits
   int32_t* spre;              // drop/keep: [B][Hkv][max_tokens/32] sel index of the word's first token
   int s_q, s_total;
-  int gpw;                    // quantized role: 64-token groups per wave
   int ppw;                    // rows role: positions per wave (multiple of 16)
   PageDiv pd;                 // token -> page division of the cache
 };
 
 template <typename T, typename F>
 __device__ inline T bc(const F& f) { return __builtin_bit_cast(T, f); }
+
+// Code tiles are read once per call: nontemporal loads keep them from
+// displacing reused lines in the caches.
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+__device__ inline uint4 load_stream(const uint8_t* p) {
+  return bc<uint4>(__builtin_nontemporal_load(reinterpret_cast<const u4v*>(p)));
+}
 
 __device__ inline float ror8(float x) {   // value of lane (l +- 8) within its row of 16
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
@@ -112,7 +118,7 @@ __device__ inline uint32_t dec1_word(uint32_t u, int v, int r, const uint32_t* m
 }
 
 __device__ inline f4 mfma32(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
-__device__ inline f4 mfma16(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
+__device__ inline h8 cat(h4 a, h4 b) { return h8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}; }
 
 __device__ inline int sel_key(int e) { return e < 0 ? INT_MAX : e; }
 
@@ -189,50 +195,64 @@ __device__ inline uint32_t dec1w(uint32_t u, int v, int r, const Dec& dc) {
   return dec1_word(u, v, r, dc.m1, dc.b1);
 }
 
-template <int FMT>
+// Read-only tables that every lane indexes alike are read through the scalar
+// cache (constant address space), keeping them off the vector-memory counter
+// that orders the code-tile prefetches.
+template <typename T>
+__device__ inline const __attribute__((address_space(4))) T* scalar_ptr(const T* p) {
+  return (const __attribute__((address_space(4))) T*)p;
+}
+
+// Slot of token t (the same t in every lane); -1 for a page outside the pool.
+__device__ inline int64_t slot_uniform(const kvc_cache& c, const PageDiv& d, int b, int g, int t) {
+  if (c.page_size == 0) return ((int64_t)b * c.num_kv_heads + g) * (int64_t)c.max_tokens + t;
+  const int page = page_of(d, t);
+  const int off = t - page * d.P;
+  const int pg = min(page, c.max_pages - 1);
+  const int64_t phys = scalar_ptr(c.block_table)[(int64_t)b * c.max_pages + pg];
+  const bool ok = page < c.max_pages && phys >= 0 && phys < c.num_pages;
+  return ok ? (phys * c.num_kv_heads + g) * (int64_t)d.P + off : -1;
+}
+
+// Loads of group gi: a fixed set of vector loads with no branch between them,
+// so the wait before a group's first use leaves the next group's loads in
+// flight.  A tile whose page is outside the pool reads tile 0 of the pool.
+template <int FMT, bool DENSE>
 __device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, int gi, int lane,
                                            GroupData<FMT>& d) {
   const kvc_cache& c = a.c;
   const int t0 = gi * GS;
-  int64_t vs;   // slot of this lane's token (V metadata)
-  if (FMT == KVC_FMT_INT1 || c.page_size % GS == 0) {   // the group is 64 adjacent slots
-    const int64_t s = slot_fast(c, a.pd, b, g, t0);
-    const int64_t u = s < 0 ? 0 : (s >> 4);
-    const uint8_t* kp = c.k_codes + u * UNIT_BYTES + lane * 16;
-    const uint8_t* vp = c.v_codes + u * UNIT_BYTES + lane * 16;
-    if constexpr (FMT == KVC_FMT_INT4) {
+  int64_t st[4];   // slot of the first token of each 16-token tile
+  if (FMT == KVC_FMT_INT1 || c.page_size % GS == 0) {
+    const int64_t s0 = slot_uniform(c, a.pd, b, g, t0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        d.k[j] = *reinterpret_cast<const uint4*>(kp + j * UNIT_BYTES);
-        d.v[j] = *reinterpret_cast<const uint4*>(vp + j * UNIT_BYTES);
-      }
-    } else {   // one 1024-byte unit per 64 tokens: unit index s / 64
-      const int64_t off = (s < 0 ? 0 : (s >> 6)) * UNIT_BYTES + lane * 16;
-      d.k[0] = *reinterpret_cast<const uint4*>(c.k_codes + off);
-      d.v[0] = *reinterpret_cast<const uint4*>(c.v_codes + off);
-    }
-    vs = s < 0 ? -1 : s + lane;
-  } else {   // INT4 with pages of 16 * odd tokens: one page lookup per 16-token tile
-    int64_t sj[4];
+    for (int j = 0; j < 4; ++j) st[j] = s0 < 0 ? -1 : s0 + TILE * j;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st[j] = slot_uniform(c, a.pd, b, g, t0 + TILE * j);
+  }
+  if constexpr (FMT == KVC_FMT_INT4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      sj[j] = slot_fast(c, a.pd, b, g, t0 + TILE * j);
-      const int64_t off = (sj[j] < 0 ? 0 : (sj[j] >> 4)) * UNIT_BYTES + lane * 16;
-      if constexpr (FMT == KVC_FMT_INT4) {
-        d.k[j] = *reinterpret_cast<const uint4*>(c.k_codes + off);
-        d.v[j] = *reinterpret_cast<const uint4*>(c.v_codes + off);
-      }
+      const int64_t off = (st[j] < 0 ? 0 : (st[j] >> 4)) * UNIT_BYTES;
+      d.k[j] = load_stream(c.k_codes + off + lane * 16);
+      d.v[j] = load_stream(c.v_codes + off + lane * 16);
     }
-    const int64_t st = lane < 16 ? sj[0] : lane < 32 ? sj[1] : lane < 48 ? sj[2] : sj[3];
-    vs = st < 0 ? -1 : st + (lane & 15);
+  } else {   // one 1024-byte unit per 64 slots
+    const int64_t off = (st[0] < 0 ? 0 : (st[0] >> 6)) * UNIT_BYTES;
+    d.k[0] = load_stream(c.k_codes + off + lane * 16);
+    d.v[0] = load_stream(c.v_codes + off + lane * 16);
   }
+  const int64_t sl = lane < 16 ? st[0] : lane < 32 ? st[1] : lane < 48 ? st[2] : st[3];
+  const int64_t vs = sl < 0 ? 0 : sl + (lane & 15);
   const uint16_t* km = c.k_meta +
       ((((int64_t)b * c.num_kv_heads + g) * (c.max_tokens / GS) + gi) * 2) * D;
   d.km = *reinterpret_cast<const uint2*>(km + 4 * lane);
-  d.vm = vs < 0 ? uint2{0u, 0u} : *reinterpret_cast<const uint2*>(c.v_meta + vs * 4);
-  if (a.sbits) {
+  d.vm = *reinterpret_cast<const uint2*>(c.v_meta + vs * 4);
+  if constexpr (!DENSE) {
     const int words = c.max_tokens / 32;
-    d.bits = *reinterpret_cast<const uint2*>(a.sbits + ((int64_t)b * c.num_kv_heads + g) * words + 2 * gi);
+    const auto* sb = scalar_ptr(a.sbits + ((int64_t)b * c.num_kv_heads + g) * words + 2 * gi);
+    d.bits = uint2{sb[0], sb[1]};
   }
 }
 
@@ -348,6 +368,12 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
 
   // ---- logits (natural units) of the attended tokens
   if constexpr (LOGITS) {
+    int32_t pre0 = 0, pre1 = 0;   // sel index of the group's two 32-token words (drop mode)
+    if (!DENSE && a.mode == KVC_ATTEND_DROP) {
+      const auto* sp = scalar_ptr(a.spre + ((int64_t)b * a.c.num_kv_heads + g) * (a.c.max_tokens / 32) + 2 * gi);
+      pre0 = sp[0];
+      pre1 = sp[1];
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -364,7 +390,7 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
               pos = a.n_sink + a.k_max + (t - w0);
             } else {
               const uint32_t word = (bit >> 5) ? d.bits.y : d.bits.x;
-              const int32_t base = a.spre[((int64_t)b * a.c.num_kv_heads + g) * (a.c.max_tokens / 32) + (t >> 5)];
+              const int32_t base = (bit >> 5) ? pre1 : pre0;
               pos = a.n_sink + base + __popc(word & ((1u << (t & 31)) - 1u));
             }
           }
@@ -480,35 +506,43 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
     }
   }
 
-  // ---- O^T += V^T P'^T per tile; bases of the V codes accumulate beside it
-  h4 vbase;
+  // ---- O^T += V^T P'^T, two tiles (32 tokens) per MFMA: k slots 0-3 are
+  // tile 2jp's tokens of the lane's quad, k slots 4-7 tile 2jp + 1's; the bases
+  // of the V codes accumulate beside it
+  h8 vbase;
   if constexpr (FMT == KVC_FMT_INT4) {
     const _Float16 x1 = (_Float16)256.f, x2 = (_Float16)16.f;
-    vbase = h4{x1, x1, x2, x2};
+    vbase = h8{x1, x1, x2, x2, x1, x1, x2, x2};
   } else {
     const _Float16 one = (_Float16)1.f;
-    vbase = h4{one, one, one, one};
+    vbase = h8{one, one, one, one, one, one, one, one};
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    st.corr0 = mfma16(vbase, B0[j], st.corr0);
-    st.corr1 = mfma16(vbase, B1[j], st.corr1);
+  for (int jp = 0; jp < 2; ++jp) {
+    const int j0 = 2 * jp, j1 = 2 * jp + 1;
+    const h8 P0 = cat(B0[j0], B0[j1]), P1 = cat(B1[j0], B1[j1]);
+    st.corr0 = mfma32(vbase, P0, st.corr0);
+    st.corr1 = mfma32(vbase, P1, st.corr1);
     if constexpr (FMT == KVC_FMT_INT4) {
-      const uint32_t dw[4] = {d.v[j].x, d.v[j].y, d.v[j].z, d.v[j].w};
+      const uint32_t da_[4] = {d.v[j0].x, d.v[j0].y, d.v[j0].z, d.v[j0].w};
+      const uint32_t db_[4] = {d.v[j1].x, d.v[j1].y, d.v[j1].z, d.v[j1].w};
 #pragma unroll
       for (int dd = 0; dd < 4; ++dd) {
-        h4 va, vb;
-        dec4v(dw[dd], dc, va, vb);
-        st.acc[2 * dd] = mfma16(va, dd < 2 ? B0[j] : B1[j], st.acc[2 * dd]);
-        st.acc[2 * dd + 1] = mfma16(vb, dd < 2 ? B0[j] : B1[j], st.acc[2 * dd + 1]);
+        h4 va0, vb0, va1, vb1;
+        dec4v(da_[dd], dc, va0, vb0);
+        dec4v(db_[dd], dc, va1, vb1);
+        st.acc[2 * dd] = mfma32(cat(va0, va1), dd < 2 ? P0 : P1, st.acc[2 * dd]);
+        st.acc[2 * dd + 1] = mfma32(cat(vb0, vb1), dd < 2 ? P0 : P1, st.acc[2 * dd + 1]);
       }
     } else {
-      const uint32_t u = j == 0 ? d.v[0].x : j == 1 ? d.v[0].y : j == 2 ? d.v[0].z : d.v[0].w;
+      const uint32_t u0 = jp == 0 ? d.v[0].x : d.v[0].z;
+      const uint32_t u1 = jp == 0 ? d.v[0].y : d.v[0].w;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
-        const uint32_t w0v = dec1w(u, 2 * (ct >> 2), ct & 3, dc);
-        const uint32_t w1v = dec1w(u, 2 * (ct >> 2) + 1, ct & 3, dc);
-        st.acc[ct] = mfma16(bc<h4>(uint2{w0v, w1v}), ct < 4 ? B0[j] : B1[j], st.acc[ct]);
+        const int v = 2 * (ct >> 2), r = ct & 3;
+        const uint4 wv = uint4{dec1w(u0, v, r, dc), dec1w(u0, v + 1, r, dc), dec1w(u1, v, r, dc),
+                               dec1w(u1, v + 1, r, dc)};
+        st.acc[ct] = mfma32(bc<h8>(wv), ct < 4 ? P0 : P1, st.acc[ct]);
       }
     }
   }
@@ -524,8 +558,10 @@ __device__ void quant_role(const AttendArgs& a, int b, int g, int split, int lan
   const int col = lane & 15, kb = lane >> 4, head = col & 7;
   const bool hv = head < G;
   const bool hi_lane = hv && col < 8;
-  const int ga = (split * NW + w) * a.gpw;
-  const int gb = min(ga + a.gpw, ngroups);
+  // the waves of (b, g) take groups round-robin, so at any moment they read
+  // one window of adjacent groups (long runs for the DRAM pages)
+  const int W = a.s_q * NW;
+  const int ga = split * NW + w;
 
   // q of this lane's head, channels [32kb, 32kb + 32), as fp16 pairs (zero off-head)
   h2 qv[16];
@@ -536,6 +572,10 @@ __device__ void quant_role(const AttendArgs& a, int b, int g, int split, int lan
 #pragma unroll
       for (int k = 0; k < 4; ++k) raw[k] = qp[k];
     }
+    // q is in registers before the group loop (so no wait inside the loop,
+    // where the next group's loads are in flight, is spent on it)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) asm volatile("" :: "v"(raw[k].x), "v"(raw[k].y), "v"(raw[k].z), "v"(raw[k].w));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       qv[4 * k + 0] = bc<h2>(raw[k].x);
@@ -554,14 +594,24 @@ __device__ void quant_role(const AttendArgs& a, int b, int g, int split, int lan
   const Dec dc = make_decoder();
 
   // two-deep software pipeline: group gi + 1 is in flight while gi computes
-  GroupData<FMT> da, db;
-  if (ga < gb) load_group<FMT>(a, b, g, ga, lane, da);
-  for (int gi = ga; gi < gb; gi += 2) {
-    if (gi + 1 < gb) load_group<FMT>(a, b, g, gi + 1, lane, db);
-    group_body<FMT, DENSE, LOGITS, PACK>(a, b, g, gi, lane, w, n, da, st, qv, dc, sKm, sVm);
-    if (gi + 1 >= gb) break;
-    if (gi + 2 < gb) load_group<FMT>(a, b, g, gi + 2, lane, da);
-    group_body<FMT, DENSE, LOGITS, PACK>(a, b, g, gi + 1, lane, w, n, db, st, qv, dc, sKm, sVm);
+  // (the loads are unconditional -- past the last group they repeat it -- so
+  // the compiler can count them exactly)
+  // two-deep software pipeline: the wave's next group is in flight while the
+  // current one computes (past the wave's last group the load repeats it, so
+  // every load is unconditional and the compiler can count them)
+  const int nmine = ga < ngroups ? (ngroups - 1 - ga) / W + 1 : 0;
+  auto gid = [&](int k) { return ga + min(k, nmine - 1) * W; };
+  if (nmine > 0) {
+    GroupData<FMT> d0, d1;
+    load_group<FMT, DENSE>(a, b, g, gid(0), lane, d0);
+    for (int k = 0;; k += 2) {
+      load_group<FMT, DENSE>(a, b, g, gid(k + 1), lane, d1);
+      group_body<FMT, DENSE, LOGITS, PACK>(a, b, g, gid(k), lane, w, n, d0, st, qv, dc, sKm, sVm);
+      if (k + 1 >= nmine) break;
+      load_group<FMT, DENSE>(a, b, g, gid(k + 2), lane, d0);
+      group_body<FMT, DENSE, LOGITS, PACK>(a, b, g, gid(k + 1), lane, w, n, d1, st, qv, dc, sKm, sVm);
+      if (k + 2 >= nmine) break;
+    }
   }
 
   // ---- finish: sums over the lanes of each head, bases and zero points
@@ -935,9 +985,9 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   Plan p{0, 0, 1, TILE};
   const int pairs = c.batch * c.num_kv_heads;
   const bool quant = c.format != KVC_FMT_FP16;
-  // workgroups resident at once: 256 CUs x 2 four-wave workgroups (the quantized
-  // role runs two waves per SIMD); one full round keeps every CU streaming
-  const int target = env_int("KVC_ATTEND_TARGET_WG", 512);
+  // one four-wave workgroup per CU: measured on the 128K layers, fewer
+  // concurrent streams keep the DRAM pages open longer and beat two per CU
+  const int target = env_int("KVC_ATTEND_TARGET_WG", 256);
   if (quant) {
     const int groups = c.max_tokens / GS;
     const int64_t waves = (int64_t)target * NW;
@@ -1003,7 +1053,6 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   }
   a.s_q = p.s_q;
   a.s_total = p.s_q + p.s_r;
-  a.gpw = p.gpw;
   a.ppw = p.ppw;
   const dim3 grid(a.s_total, c.num_kv_heads, c.batch);
   if (mode != KVC_ATTEND_DENSE && c.format != KVC_FMT_FP16) {   // k_max == 0: all-zero bits
