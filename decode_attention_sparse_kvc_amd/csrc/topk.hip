@@ -13,8 +13,8 @@
 //           an order-preserving 64-bit key (0 = not a candidate); histogram of
 //           the key's top byte.
 //   radix   passes 1..7: histogram of the next byte among keys that share the
-//           bytes chosen so far (each workgroup re-derives those bytes from the
-//           earlier histograms).
+//           bytes chosen so far; each pass derives the byte of the previous
+//           pass from its histogram and the stored state of the pass before.
 //   mark    bitmaps of keys above the k-th largest key T and equal to T.
 //   emit    one workgroup per (sequence, KV head): the first k - #above keys
 //           equal to T by index, then every selected index in ascending order.
@@ -30,6 +30,8 @@ constexpr int ST = 256;        // threads of the scoring / radix workgroups
 constexpr int TPB = 1024;      // tokens per radix / mark workgroup
 constexpr int ET = 1024;       // threads of the emit workgroup
 constexpr int PASSES = 8;
+constexpr int HREP = 8;        // copies of each histogram (spread the global atomics)
+constexpr int HSTRIDE = PASSES * HREP * 256;   // histogram words per (sequence, KV head)
 
 struct TopkArgs {
   kvc_cache c;
@@ -44,10 +46,13 @@ struct TopkArgs {
   int32_t* out_channels;
   // workspace
   uint64_t* keys;      // [B][Hkv][max_tokens]
-  uint32_t* hist;      // [B][Hkv][PASSES][256]
+  uint32_t* hist;      // [B][Hkv][PASSES][HREP][256]
   uint32_t* above;     // [B][Hkv][max_tokens / 32]
   uint32_t* equal;     // [B][Hkv][max_tokens / 32]
   int32_t* channels;   // [B][Hkv][128]
+  uint64_t* prefix;    // [B][Hkv] key prefix of the bytes chosen so far (radix state)
+  int32_t* krem;       // [B][Hkv] keys still to take from the current bucket
+  int32_t* done;       // [B][Hkv] 0, or 8p once pass p found its bucket taken whole
 };
 
 __device__ inline uint64_t order_key(double d) {
@@ -71,17 +76,21 @@ __device__ inline void cand_range(const TopkArgs& a, int b, int& lo, int& hi, in
 }
 
 // ------------------------------------------------------------------ prep
+constexpr int GMAX_PREP = 16;
 __global__ __launch_bounds__(D) void prep_kernel(TopkArgs a) {
   const int g = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
   const int64_t pi = pair_index(a, b, g);
-  uint32_t* h = a.hist + pi * PASSES * 256;
-  for (int e = c; e < PASSES * 256; e += D) h[e] = 0u;
+  uint4* h = reinterpret_cast<uint4*>(a.hist + pi * HSTRIDE);
+  for (int e = c; e < HSTRIDE / 4; e += D) h[e] = uint4{0u, 0u, 0u, 0u};
+  if (c == 0) a.done[pi] = 0;
   __shared__ double s[D];
   __shared__ int chosen[D];
   if (a.mode == KVC_SCORE_CRITICAL) {
     double qm = 0.0;
-    for (int hh = 0; hh < a.G; ++hh)
-      qm = fmax(qm, fabs((double)h2f(a.q[((int64_t)b * a.hq + g * a.G + hh) * D + c])));
+    const uint16_t* qg = a.q + ((int64_t)b * a.hq + g * a.G) * D + c;
+#pragma unroll
+    for (int hh = 0; hh < GMAX_PREP; ++hh)   // the group's loads issued together
+      if (hh < a.G) qm = fmax(qm, fabs((double)h2f(qg[hh * D])));
     const double kabs = (double)a.c.k_absmax[pi * D + c];
     s[c] = __dmul_rn(qm, kabs);
     __syncthreads();
@@ -99,50 +108,81 @@ __global__ __launch_bounds__(D) void prep_kernel(TopkArgs a) {
 }
 
 // ------------------------------------------------------------------ score
-// k value of token t, channel ch as an exact double: fp16 row, tail row, or
-// code * scale + zero (fp64 multiply then add, both exact).
-__device__ inline double key_value(const TopkArgs& a, int b, int g, int t, int ch, int nq,
-                                   int64_t slot) {
-  const kvc_cache& c = a.c;
-  const int fmt = c.format;
-  if (fmt == KVC_FMT_FP16) {
-    if (c.kT && c.page_size == 0)
-      return (double)h2f(c.kT[((int64_t)(b * c.num_kv_heads + g) * D + ch) * c.max_tokens + t]);
-    return (double)h2f(c.k16[slot * D + ch]);
+constexpr int GMAX = 16;       // query heads per KV head supported by scoring
+constexpr int CB_CRIT = 8;     // channels whose loads are issued together (critical channels)
+constexpr int CB_EXACT = 32;   // (every channel)
+
+// Scores of one token on the channel list: per query head, +0.0 then one
+// channel at a time in ascending order.  The loads of CB channels are issued
+// together, then their q values are read from LDS, then the adds run.  GT is
+// the query group size when it is known at compile time (0: up to GMAX).
+template <int GT, int CB, typename Load, typename Aux, typename Value>
+__device__ inline double token_score(int G, int nch, const int* sch, const double* sq, Load load,
+                                     Aux aux, Value value) {
+  constexpr int GN = GT > 0 ? GT : GMAX;
+  double acc[GN];
+#pragma unroll
+  for (int hh = 0; hh < GN; ++hh) acc[hh] = 0.0;
+  for (int k0 = 0; k0 < nch; k0 += CB) {
+    int ch[CB];
+    uint32_t raw[CB], mx[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) ch[u] = sch[min(k0 + u, nch - 1)];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) raw[u] = load(ch[u]);   // global loads, all in flight
+#pragma unroll
+    for (int u = 0; u < CB; ++u) mx[u] = aux(ch[u]);     // LDS reads, all in flight
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const bool on = k0 + u < nch;
+      const double v = value(ch[u], raw[u], mx[u]);
+      const int kq = min(k0 + u, nch - 1);
+#pragma unroll
+      for (int hh = 0; hh < GN; ++hh) {
+        if (GT > 0 || hh < G) {
+          const double nx = __dadd_rn(acc[hh], __dmul_rn(sq[hh * D + kq], v));
+          acc[hh] = on ? nx : acc[hh];
+        }
+      }
+    }
   }
-  if (t >= nq)
-    return (double)h2f(c.k_tail[(((int64_t)b * c.num_kv_heads + g) * GS + (t - nq)) * D + ch]);
-  uint32_t code;
-  if (fmt == KVC_FMT_INT4) {
-    const int n = (int)(slot % TILE);
-    const int lane = 16 * (ch / 32) + n, d = (ch % 32) / 8, j = ch % 8;
-    const uint32_t u = reinterpret_cast<const uint32_t*>(c.k_codes + (slot / TILE) * UNIT_BYTES)[lane * 4 + d];
-    code = (u >> nib_pos(j)) & 15u;
-  } else {
-    const int n = (int)(slot % GS);
-    const int lane = 16 * (ch / 32) + n % 16, d = n / 16;
-    const uint32_t u = reinterpret_cast<const uint32_t*>(c.k_codes + (slot / GS) * UNIT_BYTES)[lane * 4 + d];
-    code = (u >> bit_pos(ch % 32)) & 1u;
-  }
-  const uint16_t* meta = c.k_meta +
-      ((((int64_t)b * c.num_kv_heads + g) * (c.max_tokens / GS) + t / GS) * 2) * D;
-  return __dadd_rn(__dmul_rn((double)code, (double)h2f(meta[ch])), (double)h2f(meta[D + ch]));
+  double r = acc[0];
+#pragma unroll
+  for (int hh = 1; hh < GN; ++hh)
+    if (GT > 0 || hh < G) r = fmax(r, acc[hh]);
+  return r;
 }
 
-constexpr int GMAX = 16;       // query heads per KV head supported by scoring
-
+// One thread per token: the score on the channel list (max over the query
+// group), an order-preserving key, and the histogram of the key's top byte.
+template <int FMT, bool KT, int GT, bool EXACT>
 __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
+  constexpr int CB = EXACT ? CB_EXACT : CB_CRIT;
   const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int t = blockIdx.x * ST + tid;
   const int64_t pi = pair_index(a, b, g);
   __shared__ double sq[GMAX * D];   // q as fp64, [head][channel slot]
   __shared__ int sch[D];
   __shared__ uint32_t sh[256];
+  __shared__ uint32_t smeta[FMT == KVC_FMT_FP16 ? 1 : (ST / GS) * D];   // (scale | zero << 16) per channel
   const int G = a.G;
+  const kvc_cache& c = a.c;
   const int nch = a.mode == KVC_SCORE_CRITICAL ? a.n_crit : (a.mode == KVC_SCORE_EXACT ? D : 0);
   for (int e = tid; e < nch; e += ST)
     sch[e] = a.mode == KVC_SCORE_CRITICAL ? a.channels[pi * D + e] : e;
   sh[tid] = 0u;
+  if (FMT != KVC_FMT_FP16 && nch > 0) {   // K metadata of the block's groups, channel pairs a thread
+    const int groups = c.max_tokens / GS;
+    const int gq = blockIdx.x * (ST / GS) + tid / 64, j = tid % 64;
+    uint32_t s2 = 0u, z2 = 0u;
+    if (gq < groups) {
+      const uint32_t* km = reinterpret_cast<const uint32_t*>(c.k_meta + (pi * groups + gq) * 2 * D);
+      s2 = km[j];
+      z2 = km[D / 2 + j];
+    }
+    smeta[(tid / 64) * D + 2 * j] = (s2 & 0xFFFFu) | (z2 << 16);
+    smeta[(tid / 64) * D + 2 * j + 1] = (s2 >> 16) | (z2 & 0xFFFF0000u);
+  }
   __syncthreads();
   for (int e = tid; e < G * nch; e += ST) {
     const int hh = e / nch, k = e % nch;
@@ -152,151 +192,220 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
 
   int lo, hi, kk;
   cand_range(a, b, lo, hi, kk);
-  const int n = max(a.c.seq_lens[b], 0);
-  const bool in = t < a.c.max_tokens;
+  const int n = max(c.seq_lens[b], 0);
+  const bool in = t < c.max_tokens;
   uint64_t key = 0;
   if (in && t >= lo && t < hi) {
     double r;
     if (a.mode == KVC_SCORE_EXTERNAL) {
-      r = (double)a.ext[pi * a.c.max_tokens + t];
+      r = (double)a.ext[pi * c.max_tokens + t];
     } else {
-      const int nq = a.c.format == KVC_FMT_FP16 ? n : (n & ~(GS - 1));
-      const int64_t slot = slot_of(a.c, b, g, t);
+      const int nq = FMT == KVC_FMT_FP16 ? n : (n & ~(GS - 1));
+      const int64_t slot = slot_of(c, b, g, t);
       r = -INFINITY;
       if (slot >= 0) {
-        // per head: +0.0, then one channel at a time in ascending order
-        double acc[GMAX];
-#pragma unroll
-        for (int hh = 0; hh < GMAX; ++hh) acc[hh] = 0.0;
-        for (int k = 0; k < nch; ++k) {
-          const double kv = key_value(a, b, g, t, sch[k], nq, slot);
-#pragma unroll
-          for (int hh = 0; hh < GMAX; ++hh)
-            if (hh < G) acc[hh] = __dadd_rn(acc[hh], __dmul_rn(sq[hh * D + k], kv));
+        const int64_t bg = (int64_t)b * c.num_kv_heads + g;
+        if (FMT == KVC_FMT_FP16) {
+          auto load = [&](int ch) -> uint32_t {
+            if (KT) return c.kT[(bg * D + ch) * c.max_tokens + t];
+            return c.k16[slot * D + ch];
+          };
+          auto aux = [&](int) -> uint32_t { return 0u; };
+          auto value = [&](int, uint32_t raw, uint32_t) { return (double)h2f((uint16_t)raw); };
+          r = token_score<GT, CB>(G, nch, sch, sq, load, aux, value);
+        } else if (t >= nq) {   // fp16 tail row of a quantized cache
+          const uint16_t* row = c.k_tail + (bg * GS + (t - nq)) * D;
+          auto load = [&](int ch) -> uint32_t { return row[ch]; };
+          auto aux = [&](int) -> uint32_t { return 0u; };
+          auto value = [&](int, uint32_t raw, uint32_t) { return (double)h2f((uint16_t)raw); };
+          r = token_score<GT, CB>(G, nch, sch, sq, load, aux, value);
+        } else {
+          const uint32_t* meta = smeta + (tid / GS) * D;
+          const int n16 = FMT == KVC_FMT_INT4 ? (int)(slot % TILE) : (int)(slot % GS) % 16;
+          const uint32_t* unit = reinterpret_cast<const uint32_t*>(
+              c.k_codes + (FMT == KVC_FMT_INT4 ? slot / TILE : slot / GS) * UNIT_BYTES);
+          const int dsel = FMT == KVC_FMT_INT4 ? 0 : (int)(slot % GS) / 16;
+          auto load = [&](int ch) -> uint32_t {
+            const int lane = 16 * (ch / 32) + n16;
+            return unit[lane * 4 + (FMT == KVC_FMT_INT4 ? (ch % 32) / 8 : dsel)];
+          };
+          auto aux = [&](int ch) -> uint32_t { return meta[ch]; };
+          auto value = [&](int ch, uint32_t raw, uint32_t m) {
+            const uint32_t code = FMT == KVC_FMT_INT4 ? (raw >> nib_pos(ch % 8)) & 15u
+                                                      : (raw >> bit_pos(ch % 32)) & 1u;
+            return __dadd_rn(__dmul_rn((double)code, (double)h2f((uint16_t)(m & 0xFFFFu))),
+                             (double)h2f((uint16_t)(m >> 16)));
+          };
+          r = token_score<GT, CB>(G, nch, sch, sq, load, aux, value);
         }
-#pragma unroll
-        for (int hh = 0; hh < GMAX; ++hh)
-          if (hh < G) r = fmax(r, acc[hh]);
       }
     }
     r = __dadd_rn(r, 0.0);
     key = order_key(r);
-    if (a.out_scores) a.out_scores[pi * a.c.max_tokens + t] = r;
+    if (a.out_scores) a.out_scores[pi * c.max_tokens + t] = r;
   }
-  if (in) a.keys[pi * a.c.max_tokens + t] = key;
+  if (in) a.keys[pi * c.max_tokens + t] = key;
   if (key) atomicAdd(&sh[key >> 56], 1u);
   __syncthreads();
-  if (sh[tid]) atomicAdd(&a.hist[pi * PASSES * 256 + tid], sh[tid]);
+  if (sh[tid]) atomicAdd(&a.hist[pi * HSTRIDE + (blockIdx.x % HREP) * 256 + tid], sh[tid]);
 }
 
 // ------------------------------------------------------------------ radix passes
-// From the histograms of passes [0, p): the byte chosen at each pass, the key
-// prefix, and how many keys of the current bucket still have to be taken.
-// Executed redundantly by every workgroup (256 threads); returns via LDS.
-__device__ void derive_prefix(const uint32_t* hist, int p, int k, uint64_t* s_prefix, int* s_krem,
-                              uint32_t* s_scan) {
-  const int tid = threadIdx.x;
-  uint64_t prefix = 0;
-  int krem = k;
-  for (int pp = 0; pp < p; ++pp) {
-    // suffix sums: number of keys in the bucket with byte >= d
-    s_scan[tid] = hist[pp * 256 + tid];
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-      const uint32_t v = tid + o < 256 ? s_scan[tid + o] : 0u;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
-    }
-    // chosen byte d: suffix(d) >= krem > suffix(d + 1)
-    const uint32_t ge = s_scan[tid];
-    const uint32_t gt = tid < 255 ? s_scan[tid + 1] : 0u;
-    if (ge >= (uint32_t)krem && gt < (uint32_t)krem) {
-      s_prefix[0] = (prefix << 8) | (uint64_t)tid;
-      s_krem[0] = krem - (int)gt;
-    }
-    __syncthreads();
-    prefix = s_prefix[0];
-    krem = s_krem[0];
-    __syncthreads();
+// One selection step (256 threads; hist_pp holds HREP copies of the pass's
+// histogram; s_krem[1] receives the chosen bucket's size): given the prefix of the bytes chosen so far
+// and the number of keys still to take, pick the byte d of pass pp whose
+// bucket holds the krem-th largest key (suffix count of buckets >= d reaches
+// krem, of buckets > d does not).  Results through LDS.
+__device__ void select_byte(const uint32_t* hist_pp, uint64_t prefix, int krem, uint64_t* s_prefix,
+                            int* s_krem, uint32_t* s_scan) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // suffix sum over bins: inclusive scan of the reversed histogram (copies summed)
+  uint32_t x = 0;
+#pragma unroll
+  for (int r = 0; r < HREP; ++r) x += hist_pp[r * 256 + 255 - tid];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  if (tid == 0) {
-    s_prefix[0] = prefix;
-    s_krem[0] = krem;
+  if (lane == 63) s_scan[256 + wv] = x;
+  __syncthreads();
+  for (int k = 0; k < wv; ++k) x += s_scan[256 + k];
+  s_scan[255 - tid] = x;   // s_scan[d] = keys in buckets >= d
+  __syncthreads();
+  const uint32_t ge = s_scan[tid];
+  const uint32_t gt = tid < 255 ? s_scan[tid + 1] : 0u;
+  if (ge >= (uint32_t)krem && gt < (uint32_t)krem) {
+    s_prefix[0] = (prefix << 8) | (uint64_t)tid;
+    s_krem[0] = krem - (int)gt;
+    s_krem[1] = (int)(ge - gt);   // keys in the chosen bucket
   }
   __syncthreads();
+}
+
+// State after pass p - 1 (prefix of p bytes) for (pair pi): pass 0's comes from
+// k alone; later ones from the state stored by the previous pass kernel.
+__device__ void state_after(const TopkArgs& a, int64_t pi, int p, int k, uint64_t* s_prefix,
+                            int* s_krem, uint32_t* s_scan) {
+  const uint32_t* hist = a.hist + pi * HSTRIDE;
+  const uint64_t prefix = p == 1 ? 0ull : a.prefix[pi];
+  const int krem = p == 1 ? k : a.krem[pi];
+  select_byte(hist + (p - 1) * HREP * 256, prefix, krem, s_prefix, s_krem, s_scan);
 }
 
 __global__ __launch_bounds__(ST) void radix_kernel(TopkArgs a, int p) {
   const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int64_t pi = pair_index(a, b, g);
   __shared__ uint64_t s_prefix[1];
-  __shared__ int s_krem[1];
-  __shared__ uint32_t s_scan[256];
+  __shared__ int s_krem[2];
+  __shared__ uint32_t s_scan[256 + 4];
   __shared__ uint32_t sh[256];
   int lo, hi, k;
   cand_range(a, b, lo, hi, k);
-  if (k <= 0) return;
-  uint32_t* hist = a.hist + pi * PASSES * 256;
-  derive_prefix(hist, p, k, s_prefix, s_krem, s_scan);
-  const uint64_t prefix = s_prefix[0];
-  sh[tid] = 0u;
-  __syncthreads();
-  const int shift = 64 - 8 * p;   // bits above the current byte
+  if (k <= 0 || a.done[pi]) return;
+  // this workgroup's keys, loaded while the state is derived
+  constexpr int KPT = TPB / ST;
   const int t0 = blockIdx.x * TPB;
   const uint64_t* keys = a.keys + pi * a.c.max_tokens;
-  for (int t = t0 + tid; t < min(t0 + TPB, a.c.max_tokens); t += ST) {
-    const uint64_t key = keys[t];
-    if (key && (key >> shift) == prefix) atomicAdd(&sh[(key >> (shift - 8)) & 255u], 1u);
+  uint64_t kv[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int t = t0 + tid + i * ST;
+    kv[i] = t < a.c.max_tokens ? keys[t] : 0ull;
   }
+  sh[tid] = 0u;
+  state_after(a, pi, p, k, s_prefix, s_krem, s_scan);
+  const uint64_t prefix = s_prefix[0];
+  const bool whole = s_krem[1] == s_krem[0];   // every key of the bucket is taken: done
+  if (blockIdx.x == 0 && tid == 0) {   // every workgroup derived the same state
+    a.prefix[pi] = prefix;
+    a.krem[pi] = s_krem[0];
+    if (whole) a.done[pi] = 8 * p;
+  }
+  if (whole) return;
+  const int shift = 64 - 8 * p;   // bits above the current byte
+#pragma unroll
+  for (int i = 0; i < KPT; ++i)
+    if (kv[i] && (kv[i] >> shift) == prefix) atomicAdd(&sh[(kv[i] >> (shift - 8)) & 255u], 1u);
   __syncthreads();
-  if (sh[tid]) atomicAdd(&hist[p * 256 + tid], sh[tid]);
+  if (sh[tid]) atomicAdd(&a.hist[pi * HSTRIDE + (p * HREP + blockIdx.x % HREP) * 256 + tid], sh[tid]);
 }
 
 // ------------------------------------------------------------------ mark
+// One thread per key; a wave's ballots are two 32-token words of each bitmap.
 __global__ __launch_bounds__(ST) void mark_kernel(TopkArgs a) {
-  const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, lane = tid & 63;
   const int64_t pi = pair_index(a, b, g);
   __shared__ uint64_t s_prefix[1];
-  __shared__ int s_krem[1];
-  __shared__ uint32_t s_scan[256];
+  __shared__ int s_krem[2];
+  __shared__ uint32_t s_scan[256 + 4];
   int lo, hi, k;
   cand_range(a, b, lo, hi, k);
+  // keys of this workgroup, loaded while the threshold is derived
+  constexpr int KPT = TPB / ST;
+  const uint64_t* keys = a.keys + pi * a.c.max_tokens;
+  uint64_t kv[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int t = blockIdx.x * TPB + tid + i * ST;
+    kv[i] = t < a.c.max_tokens ? keys[t] : 0ull;
+  }
+  // selected: key above the k-th largest key T, or equal to it (first ones by
+  // index, in emit); when a pass found its bucket taken whole, every key whose
+  // top `bits` bits reach the stored prefix
   uint64_t T = ~0ull;     // nothing is above the all-ones key and nothing equals it
+  int bits = 0;
+  uint64_t P = 0;
   if (k > 0) {
-    derive_prefix(a.hist + pi * PASSES * 256, PASSES, k, s_prefix, s_krem, s_scan);
-    T = s_prefix[0];
+    bits = a.done[pi];
+    if (bits) {
+      P = a.prefix[pi];
+    } else {
+      state_after(a, pi, PASSES, k, s_prefix, s_krem, s_scan);
+      T = s_prefix[0];
+    }
   }
   const int words = a.c.max_tokens / 32;
-  const uint64_t* keys = a.keys + pi * a.c.max_tokens;
-  const int w0 = blockIdx.x * (TPB / 32);
-  for (int wd = w0 + tid; wd < min(w0 + TPB / 32, words); wd += ST) {
-    uint32_t ab = 0u, eq = 0u;
-    for (int i = 0; i < 32; ++i) {
-      const uint64_t key = keys[wd * 32 + i];
-      ab |= (uint32_t)(key != 0 && key > T && k > 0) << i;
-      eq |= (uint32_t)(key != 0 && key == T && k > 0) << i;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int t = blockIdx.x * TPB + tid + i * ST;
+    if (t >= a.c.max_tokens) break;   // whole waves (max_tokens and TPB are multiples of 64)
+    const uint64_t key = kv[i];
+    const bool ab_t = bits ? (key >> (64 - bits)) >= P : key > T;
+    const uint64_t ab = __ballot(key != 0 && ab_t && k > 0);
+    const uint64_t eq = __ballot(key != 0 && !bits && key == T && k > 0);
+    const int wd = (t - lane) / 32;   // first of the wave's two words
+    if (lane == 0) {
+      a.above[pi * words + wd] = (uint32_t)ab;
+      a.equal[pi * words + wd] = (uint32_t)eq;
+    } else if (lane == 32) {
+      a.above[pi * words + wd + 1] = (uint32_t)(ab >> 32);
+      a.equal[pi * words + wd + 1] = (uint32_t)(eq >> 32);
     }
-    a.above[pi * words + wd] = ab;
-    a.equal[pi * words + wd] = eq;
   }
 }
 
 // ------------------------------------------------------------------ emit
+// Exclusive prefix sum over the ET threads (wave scans, then the wave totals).
 __device__ inline int block_exclusive_scan(int v, int* s, int& total) {
-  const int tid = threadIdx.x;
-  s[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < ET; o <<= 1) {
-    const int x = tid >= o ? s[tid - o] : 0;
-    __syncthreads();
-    s[tid] += x;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  total = s[ET - 1];
-  const int excl = s[tid] - v;
+  if (lane == 63) s[wv] = x;
   __syncthreads();
-  return excl;
+  int before = 0;
+  total = 0;
+  for (int k = 0; k < ET / 64; ++k) {
+    const int t = s[k];
+    before += k < wv ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return before + x - v;
 }
 
 __global__ __launch_bounds__(ET) void emit_kernel(TopkArgs a) {
@@ -364,9 +473,10 @@ size_t topk_workspace_bytes(const kvc_cache& c) {
   const size_t pairs = (size_t)c.batch * c.num_kv_heads;
   const size_t words = c.max_tokens / 32;
   size_t bytes = pairs * c.max_tokens * sizeof(uint64_t);
-  bytes += pairs * PASSES * 256 * sizeof(uint32_t);
+  bytes += pairs * HSTRIDE * sizeof(uint32_t);
   bytes += 2 * pairs * words * sizeof(uint32_t);
   bytes += pairs * D * sizeof(int32_t);
+  bytes += pairs * (sizeof(uint64_t) + 2 * sizeof(int32_t));
   return bytes;
 }
 
@@ -395,16 +505,44 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   a.keys = reinterpret_cast<uint64_t*>(p);
   p += pairs * c.max_tokens * sizeof(uint64_t);
   a.hist = reinterpret_cast<uint32_t*>(p);
-  p += pairs * PASSES * 256 * sizeof(uint32_t);
+  p += pairs * HSTRIDE * sizeof(uint32_t);
   a.above = reinterpret_cast<uint32_t*>(p);
   p += pairs * words * sizeof(uint32_t);
   a.equal = reinterpret_cast<uint32_t*>(p);
   p += pairs * words * sizeof(uint32_t);
   a.channels = reinterpret_cast<int32_t*>(p);
+  p += pairs * D * sizeof(int32_t);
+  a.prefix = reinterpret_cast<uint64_t*>(p);
+  p += pairs * sizeof(uint64_t);
+  a.krem = reinterpret_cast<int32_t*>(p);
+  p += pairs * sizeof(int32_t);
+  a.done = reinterpret_cast<int32_t*>(p);
 
   const int Hkv = c.num_kv_heads, B = c.batch;
   prep_kernel<<<dim3(Hkv, B), D, 0, s>>>(a);
-  score_kernel<<<dim3((c.max_tokens + ST - 1) / ST, Hkv, B), ST, 0, s>>>(a);
+  const dim3 sgrid((c.max_tokens + ST - 1) / ST, Hkv, B);
+  const bool exact = mode == KVC_SCORE_EXACT;
+#define KVC_SCORE_E(F, KT, GG)                                                \
+  do {                                                                        \
+    if (exact) score_kernel<F, KT, GG, true><<<sgrid, ST, 0, s>>>(a);         \
+    else score_kernel<F, KT, GG, false><<<sgrid, ST, 0, s>>>(a);              \
+  } while (0)
+#define KVC_SCORE_G(F, KT)                                                    \
+  do {                                                                        \
+    switch (a.G) {                                                            \
+      case 1: KVC_SCORE_E(F, KT, 1); break;                                   \
+      case 2: KVC_SCORE_E(F, KT, 2); break;                                   \
+      case 4: KVC_SCORE_E(F, KT, 4); break;                                   \
+      case 8: KVC_SCORE_E(F, KT, 8); break;                                   \
+      default: KVC_SCORE_E(F, KT, 0); break;                                  \
+    }                                                                         \
+  } while (0)
+  if (c.format == KVC_FMT_INT4) KVC_SCORE_G(KVC_FMT_INT4, false);
+  else if (c.format == KVC_FMT_INT1) KVC_SCORE_G(KVC_FMT_INT1, false);
+  else if (c.kT && c.page_size == 0) KVC_SCORE_G(KVC_FMT_FP16, true);
+  else KVC_SCORE_G(KVC_FMT_FP16, false);
+#undef KVC_SCORE_G
+#undef KVC_SCORE_E
   const dim3 rgrid((c.max_tokens + TPB - 1) / TPB, Hkv, B);
   for (int pass = 1; pass < PASSES; ++pass) radix_kernel<<<rgrid, ST, 0, s>>>(a, pass);
   mark_kernel<<<rgrid, ST, 0, s>>>(a);
