@@ -549,7 +549,7 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
 }
 
 template <int FMT, bool DENSE, bool LOGITS, bool PACK>
-__device__ void quant_role(const AttendArgs& a, int b, int g, int split, int lane, int w,
+__device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, int split, int lane, int w,
                            float* sO, float* sML, uint16_t* sKm, uint16_t* sVm) {
   const kvc_cache& c = a.c;
   const int n = max(c.seq_lens[b], 0);
@@ -706,7 +706,7 @@ __device__ inline RowRef resolve(const AttendArgs& a, int b, int g, int n, int n
 }
 
 template <int FMT>
-__device__ void rows_role(const AttendArgs& a, int b, int g, int rsplit, int lane, int w,
+__device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int rsplit, int lane, int w,
                           float* sO, float* sML, float* sP, int* sTok, int64_t* sOff,
                           float* sAl) {
   const kvc_cache& c = a.c;
