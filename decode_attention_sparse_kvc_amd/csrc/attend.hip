@@ -68,11 +68,22 @@ struct AttendArgs {
 template <typename T, typename F>
 __device__ inline T bc(const F& f) { return __builtin_bit_cast(T, f); }
 
-// Code tiles are read once per call: nontemporal loads keep them from
-// displacing reused lines in the caches.
-typedef unsigned u4v __attribute__((ext_vector_type(4)));
-__device__ inline uint4 load_stream(const uint8_t* p) {
-  return bc<uint4>(__builtin_nontemporal_load(reinterpret_cast<const u4v*>(p)));
+// Buffer resource over bytes [p, p + n) (raw 32-bit buffer, gfx9 data-format
+// word): a vector load through it that falls outside the range reads zero and
+// never reaches memory.  Group loads use one resource per contiguous run, so
+// all address arithmetic stays scalar and a lane's offset is a loop-invariant
+// register.
+typedef __amdgpu_buffer_rsrc_t Buf;
+__device__ inline Buf make_buf(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)n, 0x00020000);
+}
+// Code tiles are read once per call: nontemporal loads (cache policy bit 1)
+// keep them from displacing reused lines in the caches.
+__device__ inline uint4 buf_load16_stream(Buf r, uint32_t off) {
+  return bc<uint4>(__builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
+__device__ inline uint2 buf_load8(Buf r, uint32_t off) {
+  return bc<uint2>(__builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
 }
 
 __device__ inline float ror8(float x) {   // value of lane (l +- 8) within its row of 16
@@ -139,11 +150,14 @@ __device__ inline int window_start(int n, int n_sink, int n_window) {
 
 // ---------------------------------------------------------------- quantized role
 // Raw loads of one 64-token group: code tiles, metadata words, selection bits.
-template <int FMT>
+// TILED: the group's four 16-token tiles are addressed one by one (pages of
+// 16 or 32 tokens); otherwise the group is one contiguous run of slots.
+template <int FMT, bool TILED>
 struct GroupData {
   uint4 k[FMT == KVC_FMT_INT4 ? 4 : 1];
   uint4 v[FMT == KVC_FMT_INT4 ? 4 : 1];
-  uint2 km, vm;
+  uint2 km;
+  uint2 vm[TILED ? 4 : 1];   // TILED: tile j's words in lanes 16j..16j+15, zero elsewhere
   uint2 bits;   // drop/keep: selected tokens of the group (two 32-token words)
 };
 
@@ -216,39 +230,50 @@ __device__ inline int64_t slot_uniform(const kvc_cache& c, const PageDiv& d, int
 
 // Loads of group gi: a fixed set of vector loads with no branch between them,
 // so the wait before a group's first use leaves the next group's loads in
-// flight.  A tile whose page is outside the pool reads tile 0 of the pool.
-template <int FMT, bool DENSE>
-__device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, int gi, int lane,
-                                           GroupData<FMT>& d) {
+// flight.  live == false (a group past the wave's last) and a page outside the
+// pool give empty ranges: the loads read zero without touching memory.
+template <int FMT, bool DENSE, bool TILED>
+__device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, int gi, bool live,
+                                           int lane, GroupData<FMT, TILED>& d) {
   const kvc_cache& c = a.c;
   const int t0 = gi * GS;
-  int64_t st[4];   // slot of the first token of each 16-token tile
-  if (FMT == KVC_FMT_INT1 || c.page_size % GS == 0) {
+  const uint32_t l16 = 16u * lane, l8 = 8u * lane;
+  if constexpr (!TILED) {   // 64 consecutive slots: one range per array
     const int64_t s0 = slot_uniform(c, a.pd, b, g, t0);
+    const bool ok = live && s0 >= 0;
+    const int64_t sl = ok ? s0 : 0;
+    const int64_t unit = FMT == KVC_FMT_INT4 ? (sl >> 4) : (sl >> 6);
+    constexpr uint32_t run = FMT == KVC_FMT_INT4 ? 4 * UNIT_BYTES : UNIT_BYTES;
+    const Buf rk = make_buf(c.k_codes + unit * UNIT_BYTES, ok ? run : 0u);
+    const Buf rv = make_buf(c.v_codes + unit * UNIT_BYTES, ok ? run : 0u);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st[j] = s0 < 0 ? -1 : s0 + TILE * j;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) st[j] = slot_uniform(c, a.pd, b, g, t0 + TILE * j);
-  }
-  if constexpr (FMT == KVC_FMT_INT4) {
+    for (int j = 0; j < (FMT == KVC_FMT_INT4 ? 4 : 1); ++j) {
+      d.k[j] = buf_load16_stream(rk, l16 + j * UNIT_BYTES);
+      d.v[j] = buf_load16_stream(rv, l16 + j * UNIT_BYTES);
+    }
+    d.vm[0] = buf_load8(make_buf(c.v_meta + sl * 4, ok ? GS * 8u : 0u), l8);
+  } else {                  // INT4 tiles on pages of 16 or 32 tokens
+    int64_t st[4];
+    bool ok[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t off = (st[j] < 0 ? 0 : (st[j] >> 4)) * UNIT_BYTES;
-      d.k[j] = load_stream(c.k_codes + off + lane * 16);
-      d.v[j] = load_stream(c.v_codes + off + lane * 16);
+      st[j] = slot_uniform(c, a.pd, b, g, t0 + TILE * j);
+      ok[j] = live && st[j] >= 0;
+      if (!ok[j]) st[j] = 0;
     }
-  } else {   // one 1024-byte unit per 64 slots
-    const int64_t off = (st[0] < 0 ? 0 : (st[0] >> 6)) * UNIT_BYTES;
-    d.k[0] = load_stream(c.k_codes + off + lane * 16);
-    d.v[0] = load_stream(c.v_codes + off + lane * 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      d.k[j] = buf_load16_stream(make_buf(c.k_codes + (st[j] >> 4) * UNIT_BYTES, ok[j] ? UNIT_BYTES : 0u), l16);
+      d.v[j] = buf_load16_stream(make_buf(c.v_codes + (st[j] >> 4) * UNIT_BYTES, ok[j] ? UNIT_BYTES : 0u), l16);
+    }
+    // lanes of other tiles fall outside tile j's 128-byte range (and read zero)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      d.vm[j] = buf_load8(make_buf(c.v_meta + st[j] * 4, ok[j] ? TILE * 8u : 0u), l8 - 128u * j);
   }
-  const int64_t sl = lane < 16 ? st[0] : lane < 32 ? st[1] : lane < 48 ? st[2] : st[3];
-  const int64_t vs = sl < 0 ? 0 : sl + (lane & 15);
   const uint16_t* km = c.k_meta +
       ((((int64_t)b * c.num_kv_heads + g) * (c.max_tokens / GS) + gi) * 2) * D;
-  d.km = *reinterpret_cast<const uint2*>(km + 4 * lane);
-  d.vm = *reinterpret_cast<const uint2*>(c.v_meta + vs * 4);
+  d.km = buf_load8(make_buf(km, live ? 2 * D * 2u : 0u), l8);
   if constexpr (!DENSE) {
     const int words = c.max_tokens / 32;
     const auto* sb = scalar_ptr(a.sbits + ((int64_t)b * c.num_kv_heads + g) * words + 2 * gi);
@@ -271,9 +296,9 @@ __device__ inline float ror4(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
 }
 
-template <int FMT, bool DENSE, bool LOGITS, bool PACK>
+template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED>
 __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, int gi, int lane,
-                                           int w, int n, const GroupData<FMT>& d, QState& st,
+                                           int w, int n, const GroupData<FMT, TILED>& d, QState& st,
                                            const h2* qv, const Dec& dc, uint16_t* sKm,
                                            uint16_t* sVm) {
   const int G = a.G;
@@ -303,7 +328,12 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
       km.y = bc<uint32_t>(bc<h2>(km.y) * half);
     }
     *reinterpret_cast<uint2*>(sKm + 256 * w + 4 * lane) = km;
-    *reinterpret_cast<uint2*>(sVm + 256 * w + 4 * lane) = d.vm;
+    uint2 vm = d.vm[0];
+    if constexpr (TILED) {
+#pragma unroll
+      for (int j = 1; j < 4; ++j) vm = uint2{vm.x | d.vm[j].x, vm.y | d.vm[j].y};
+    }
+    *reinterpret_cast<uint2*>(sVm + 256 * w + 4 * lane) = vm;
   }
   wave_sync_lds();
 
@@ -548,7 +578,7 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
   }
 }
 
-template <int FMT, bool DENSE, bool LOGITS, bool PACK>
+template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED>
 __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, int split, int lane, int w,
                            float* sO, float* sML, uint16_t* sKm, uint16_t* sVm) {
   const kvc_cache& c = a.c;
@@ -562,27 +592,37 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
   // one window of adjacent groups (long runs for the DRAM pages)
   const int W = a.s_q * NW;
   const int ga = split * NW + w;
+  const int nmine = ga < ngroups ? (ngroups - 1 - ga) / W + 1 : 0;
+  // k-th group of this wave; past the last one the loads of the last repeat
+  // with empty ranges (no memory traffic), so every load is unconditional and
+  // the compiler's wait before a group counts exactly (a wave with no group
+  // names group 0, whose selection words are in range)
+  auto gid = [&](int k) { return nmine > 0 ? ga + min(k, nmine - 1) * W : 0; };
 
-  // q of this lane's head, channels [32kb, 32kb + 32), as fp16 pairs (zero off-head)
+  // q of this lane's head, channels [32kb, 32kb + 32), as fp16 pairs (zero
+  // off-head); the first two groups' loads go out before q is waited for
+  uint4 raw[4] = {};
+  if (hv) {
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + head) * D + 32 * kb);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) raw[k] = qp[k];
+  }
+  GroupData<FMT, TILED> d0, d1;
+  load_group<FMT, DENSE, TILED>(a, b, g, gid(0), nmine > 0, lane, d0);
+  load_group<FMT, DENSE, TILED>(a, b, g, gid(1), nmine > 1, lane, d1);
+  // q is in registers before the group loop (so no wait inside the loop, where
+  // the next group's loads are in flight, is spent on it); the memory clobber
+  // keeps the group loads above issued first
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    asm volatile("" :: "v"(raw[k].x), "v"(raw[k].y), "v"(raw[k].z), "v"(raw[k].w) : "memory");
   h2 qv[16];
-  {
-    uint4 raw[4] = {};
-    if (hv) {
-      const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + head) * D + 32 * kb);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) raw[k] = qp[k];
-    }
-    // q is in registers before the group loop (so no wait inside the loop,
-    // where the next group's loads are in flight, is spent on it)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) asm volatile("" :: "v"(raw[k].x), "v"(raw[k].y), "v"(raw[k].z), "v"(raw[k].w));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      qv[4 * k + 0] = bc<h2>(raw[k].x);
-      qv[4 * k + 1] = bc<h2>(raw[k].y);
-      qv[4 * k + 2] = bc<h2>(raw[k].z);
-      qv[4 * k + 3] = bc<h2>(raw[k].w);
-    }
+  for (int k = 0; k < 4; ++k) {
+    qv[4 * k + 0] = bc<h2>(raw[k].x);
+    qv[4 * k + 1] = bc<h2>(raw[k].y);
+    qv[4 * k + 2] = bc<h2>(raw[k].z);
+    qv[4 * k + 3] = bc<h2>(raw[k].w);
   }
 
   QState st;
@@ -593,26 +633,19 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
   for (int ct = 0; ct < 8; ++ct) st.acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
   const Dec dc = make_decoder();
 
-  // two-deep software pipeline: group gi + 1 is in flight while gi computes
-  // (the loads are unconditional -- past the last group they repeat it -- so
-  // the compiler can count them exactly)
-  // two-deep software pipeline: the wave's next group is in flight while the
-  // current one computes (past the wave's last group the load repeats it, so
-  // every load is unconditional and the compiler can count them)
-  const int nmine = ga < ngroups ? (ngroups - 1 - ga) / W + 1 : 0;
-  auto gid = [&](int k) { return ga + min(k, nmine - 1) * W; };
-  if (nmine > 0) {
-    GroupData<FMT> d0, d1;
-    load_group<FMT, DENSE>(a, b, g, gid(0), lane, d0);
-    for (int k = 0;; k += 2) {
-      load_group<FMT, DENSE>(a, b, g, gid(k + 1), lane, d1);
-      group_body<FMT, DENSE, LOGITS, PACK>(a, b, g, gid(k), lane, w, n, d0, st, qv, dc, sKm, sVm);
-      if (k + 1 >= nmine) break;
-      load_group<FMT, DENSE>(a, b, g, gid(k + 2), lane, d0);
-      group_body<FMT, DENSE, LOGITS, PACK>(a, b, g, gid(k + 1), lane, w, n, d1, st, qv, dc, sKm, sVm);
-      if (k + 2 >= nmine) break;
-    }
+  // two-deep software pipeline: while group k computes, group k + 1 is in
+  // flight.  Pairs of groups per trip and no exit inside a trip: the loop
+  // header then sees the same loads pending from both of its predecessors,
+  // and its wait leaves the newer group's loads in flight.
+  int k = 0;
+  for (; k + 2 <= nmine; k += 2) {
+    group_body<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, gid(k), lane, w, n, d0, st, qv, dc, sKm, sVm);
+    load_group<FMT, DENSE, TILED>(a, b, g, gid(k + 2), k + 2 < nmine, lane, d0);
+    group_body<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, gid(k + 1), lane, w, n, d1, st, qv, dc, sKm, sVm);
+    load_group<FMT, DENSE, TILED>(a, b, g, gid(k + 3), k + 3 < nmine, lane, d1);
   }
+  if (k < nmine)
+    group_body<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, gid(k), lane, w, n, d0, st, qv, dc, sKm, sVm);
 
   // ---- finish: sums over the lanes of each head, bases and zero points
   float l = st.l, sz0 = st.sz0, sz1 = st.sz1;
@@ -847,7 +880,7 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
   }
 }
 
-template <int FMT, bool DENSE, bool LOGITS, bool PACK>
+template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED>
 __global__ __launch_bounds__(NT, 2) void attend_kernel(AttendArgs a) {
   __shared__ float sO[NW * 8 * D];
   __shared__ float sML[NW * 8 * 2];
@@ -868,7 +901,7 @@ __global__ __launch_bounds__(NT, 2) void attend_kernel(AttendArgs a) {
 
   if constexpr (FMT != KVC_FMT_FP16) {
     if (split < a.s_q)
-      quant_role<FMT, DENSE, LOGITS, PACK>(a, b, g, split, lane, w, sO, sML, sKm, sVm);
+      quant_role<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, split, lane, w, sO, sML, sKm, sVm);
     else
       rows_role<FMT>(a, b, g, split - a.s_q, lane, w, sO, sML, sP, sTok, sOff, sAl);
   } else {
@@ -1011,6 +1044,37 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   return p;
 }
 
+// Kernel instance for (format, mode, logits, packing, tile addressing); fp16
+// caches have no quantized role, and only INT4 has 16-token tiles.
+template <int F, bool DN, bool LG>
+void launch_inst(dim3 grid, hipStream_t s, const AttendArgs& a, bool pk, bool tiled) {
+  if constexpr (F == KVC_FMT_FP16) {
+    attend_kernel<F, DN, LG, false, false><<<grid, NT, 0, s>>>(a);
+  } else if constexpr (F == KVC_FMT_INT4) {
+    if (tiled) {
+      if (pk) attend_kernel<F, DN, LG, true, true><<<grid, NT, 0, s>>>(a);
+      else attend_kernel<F, DN, LG, false, true><<<grid, NT, 0, s>>>(a);
+    } else {
+      if (pk) attend_kernel<F, DN, LG, true, false><<<grid, NT, 0, s>>>(a);
+      else attend_kernel<F, DN, LG, false, false><<<grid, NT, 0, s>>>(a);
+    }
+  } else {
+    if (pk) attend_kernel<F, DN, LG, true, false><<<grid, NT, 0, s>>>(a);
+    else attend_kernel<F, DN, LG, false, false><<<grid, NT, 0, s>>>(a);
+  }
+}
+template <int F>
+void launch_fmt(dim3 grid, hipStream_t s, const AttendArgs& a, bool dense, bool lg, bool pk,
+                bool tiled) {
+  if (dense) {
+    if (lg) launch_inst<F, true, true>(grid, s, a, pk, tiled);
+    else launch_inst<F, true, false>(grid, s, a, pk, tiled);
+  } else {
+    if (lg) launch_inst<F, false, true>(grid, s, a, pk, tiled);
+    else launch_inst<F, false, false>(grid, s, a, pk, tiled);
+  }
+}
+
 }  // namespace
 
 size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, int n_sink,
@@ -1060,23 +1124,13 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
     sel_plan_kernel<<<dim3((words + 255) / 256, c.num_kv_heads, c.batch), 256, 0, s>>>(a);
   }
   const bool dense = mode == KVC_ATTEND_DENSE, lg = logits != nullptr;
-  const bool pk = a.G <= 4 && c.format != KVC_FMT_FP16;   // packed softmax (quantized role only)
-#define KVC_LAUNCH(F, DN, LG, PK) attend_kernel<F, DN, LG, PK><<<grid, NT, 0, s>>>(a)
-#define KVC_LAUNCH_P(F, DN, LG) \
-  do { if (pk) KVC_LAUNCH(F, DN, LG, true); else KVC_LAUNCH(F, DN, LG, false); } while (0)
-#define KVC_LAUNCH_F(F)                                                                      \
-  do {                                                                                       \
-    if (dense) { if (lg) KVC_LAUNCH_P(F, true, true); else KVC_LAUNCH_P(F, true, false); }   \
-    else { if (lg) KVC_LAUNCH_P(F, false, true); else KVC_LAUNCH_P(F, false, false); }       \
-  } while (0)
+  const bool pk = a.G <= 4;   // packed softmax (quantized role only)
+  const bool tiled = c.page_size % GS != 0;   // INT4 on pages of 16 or 32 tokens
   switch (c.format) {
-    case KVC_FMT_INT4: KVC_LAUNCH_F(KVC_FMT_INT4); break;
-    case KVC_FMT_INT1: KVC_LAUNCH_F(KVC_FMT_INT1); break;
-    default: KVC_LAUNCH_F(KVC_FMT_FP16); break;
+    case KVC_FMT_INT4: launch_fmt<KVC_FMT_INT4>(grid, s, a, dense, lg, pk, tiled); break;
+    case KVC_FMT_INT1: launch_fmt<KVC_FMT_INT1>(grid, s, a, dense, lg, pk, false); break;
+    default: launch_fmt<KVC_FMT_FP16>(grid, s, a, dense, lg, false, false); break;
   }
-#undef KVC_LAUNCH_P
-#undef KVC_LAUNCH_F
-#undef KVC_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   merge_kernel<<<c.batch * hq, MT, 0, s>>>(a.part, a.s_total, out, lse);
