@@ -895,9 +895,7 @@ __global__ __launch_bounds__(NT, 2) void attend_kernel(AttendArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform per wave
   const int G = a.G;
-  for (int e = tid; e < NW * 8 * 2; e += NT) sML[e] = (e & 1) ? 0.f : -INFINITY;
-  for (int e = tid; e < NW * 8 * D; e += NT) sO[e] = 0.f;
-  __syncthreads();
+  // (every wave of either role writes its sO / sML slots of heads < G)
 
   if constexpr (FMT != KVC_FMT_FP16) {
     if (split < a.s_q)
@@ -909,24 +907,36 @@ __global__ __launch_bounds__(NT, 2) void attend_kernel(AttendArgs a) {
   }
   __syncthreads();
 
-  // ---- merge the four waves and write this split's partial per query head
-  for (int e = tid; e < G * (D + 2); e += NT) {
-    const int h = e / (D + 2), k = e % (D + 2);
+  // ---- combine the waves and write this split's partial per query head:
+  // thread h < G finds the head's maximum and each wave's weight, then thread
+  // (h, channel quad) sums the weighted outputs
+  float* sWt = sAl;   // NW * 8 weights (the rows role is done with sAl)
+  float* part = a.part + ((int64_t)b * a.hq + g * G) * a.s_total * PART + (int64_t)split * PART;
+  if (tid < G) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sML[(ww * 8 + h) * 2]);
+    for (int ww = 0; ww < NW; ++ww) mx = fmaxf(mx, sML[(ww * 8 + tid) * 2]);
     const float ms = mx == -INFINITY ? 0.f : mx;
-    float v = 0.f;
+    float l = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
-      const float mw = sML[(ww * 8 + h) * 2];
+      const float mw = sML[(ww * 8 + tid) * 2];
       const float sc = mw == -INFINITY ? 0.f : exp2f(mw - ms);
-      if (k == 1) v += sc * sML[(ww * 8 + h) * 2 + 1];
-      else if (k >= 2) v += sc * sO[(ww * 8 + h) * D + (k - 2)];
+      sWt[ww * 8 + tid] = sc;
+      l += sc * sML[(ww * 8 + tid) * 2 + 1];
     }
-    if (k == 0) v = mx;
-    float* part = a.part + (((int64_t)b * a.hq + g * G + h) * a.s_total + split) * PART;
-    part[k < 2 ? k : PO + (k - 2)] = v;
+    float* ph = part + (int64_t)tid * a.s_total * PART;
+    ph[0] = mx;
+    ph[1] = l;
+  }
+  __syncthreads();
+  if (tid < G * (D / 4)) {
+    const int h = tid / (D / 4), cq = tid % (D / 4);
+    f4 v = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww)
+      v += sWt[ww * 8 + h] * *reinterpret_cast<const f4*>(sO + (ww * 8 + h) * D + 4 * cq);
+    *reinterpret_cast<f4*>(part + (int64_t)h * a.s_total * PART + PO + 4 * cq) = v;
   }
 }
 
