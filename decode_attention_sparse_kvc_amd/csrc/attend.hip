@@ -40,8 +40,10 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int NW = 4;          // waves per workgroup
-constexpr int NT = 64 * NW;
+// Waves per workgroup.  One workgroup per CU either way; the 1-bit layer's
+// per-group work is arithmetic more than bytes, so it runs two waves per SIMD
+// to overlap one wave's latencies with another's work.
+constexpr int waves_per_wg(int fmt) { return fmt == KVC_FMT_INT1 ? 8 : 4; }
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.69314718055994531f;
 constexpr int PART = 4 + D;    // floats per split partial: m (log2 units), l, pad, o[128]
@@ -590,6 +592,7 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
   const bool hi_lane = hv && col < 8;
   // the waves of (b, g) take groups round-robin, so at any moment they read
   // one window of adjacent groups (long runs for the DRAM pages)
+  constexpr int NW = waves_per_wg(FMT);
   const int W = a.s_q * NW;
   const int ga = split * NW + w;
   const int nmine = ga < ngroups ? (ngroups - 1 - ga) / W + 1 : 0;
@@ -751,6 +754,7 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
   int np;
   if (a.mode == KVC_ATTEND_DENSE) np = n - nq;
   else np = a.n_sink + a.k_max + a.n_window + (a.mode == KVC_ATTEND_KEEP ? GS : 0);
+  constexpr int NW = waves_per_wg(FMT);
   const int pa = (rsplit * NW + w) * a.ppw;
   const int pb = min(pa + a.ppw, np);
   const bool drop = a.mode == KVC_ATTEND_DROP;
@@ -881,7 +885,9 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
 }
 
 template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED>
-__global__ __launch_bounds__(NT, 2) void attend_kernel(AttendArgs a) {
+__global__ __launch_bounds__(64 * waves_per_wg(FMT), waves_per_wg(FMT) < 8 ? 8 / waves_per_wg(FMT) : 1)
+void attend_kernel(AttendArgs a) {
+  constexpr int NW = waves_per_wg(FMT);
   __shared__ float sO[NW * 8 * D];
   __shared__ float sML[NW * 8 * 2];
   __shared__ __align__(16) uint16_t sKm[NW * 256];
@@ -1026,6 +1032,7 @@ int env_int(const char* name, int dflt) {
 
 Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window) {
   Plan p{0, 0, 1, TILE};
+  const int NW = waves_per_wg(c.format);
   const int pairs = c.batch * c.num_kv_heads;
   const bool quant = c.format != KVC_FMT_FP16;
   // one four-wave workgroup per CU: measured on the 128K layers, fewer
@@ -1059,18 +1066,18 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
 template <int F, bool DN, bool LG>
 void launch_inst(dim3 grid, hipStream_t s, const AttendArgs& a, bool pk, bool tiled) {
   if constexpr (F == KVC_FMT_FP16) {
-    attend_kernel<F, DN, LG, false, false><<<grid, NT, 0, s>>>(a);
+    attend_kernel<F, DN, LG, false, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
   } else if constexpr (F == KVC_FMT_INT4) {
     if (tiled) {
-      if (pk) attend_kernel<F, DN, LG, true, true><<<grid, NT, 0, s>>>(a);
-      else attend_kernel<F, DN, LG, false, true><<<grid, NT, 0, s>>>(a);
+      if (pk) attend_kernel<F, DN, LG, true, true><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
+      else attend_kernel<F, DN, LG, false, true><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
     } else {
-      if (pk) attend_kernel<F, DN, LG, true, false><<<grid, NT, 0, s>>>(a);
-      else attend_kernel<F, DN, LG, false, false><<<grid, NT, 0, s>>>(a);
+      if (pk) attend_kernel<F, DN, LG, true, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
+      else attend_kernel<F, DN, LG, false, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
     }
   } else {
-    if (pk) attend_kernel<F, DN, LG, true, false><<<grid, NT, 0, s>>>(a);
-    else attend_kernel<F, DN, LG, false, false><<<grid, NT, 0, s>>>(a);
+    if (pk) attend_kernel<F, DN, LG, true, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
+    else attend_kernel<F, DN, LG, false, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
   }
 }
 template <int F>
