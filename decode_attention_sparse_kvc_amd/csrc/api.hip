@@ -56,7 +56,8 @@ kvc_status check_attend_args(const kvc_cache* c, int32_t hq, int32_t mode, const
   if (mode < KVC_ATTEND_DENSE || mode > KVC_ATTEND_KEEP) return KVC_ERR_INVALID;
   if (mode != KVC_ATTEND_DENSE) {
     if (k_max < 0 || n_sink < 0 || n_window < 0) return KVC_ERR_INVALID;
-    if ((int64_t)n_sink + k_max + n_window + KVC_GROUP > (int64_t)INT32_MAX / 2) return KVC_ERR_SHAPE;
+    // positions of the fp16-rows role; its plan (8 bytes each) is addressed with 32-bit offsets
+    if ((int64_t)n_sink + k_max + n_window + KVC_GROUP > ((int64_t)1 << 28)) return KVC_ERR_SHAPE;
     if (k_max > 0 && !sel && !sizing_only) return KVC_ERR_INVALID;
     if (sel && !aligned(sel, 4)) return KVC_ERR_INVALID;
   }

@@ -62,6 +62,8 @@ struct AttendArgs {
   float* part;                // [B][Hq][s_total][PART]
   uint32_t* sbits;            // drop/keep: [B][Hkv][max_tokens/32] valid sel entries as bits
   int32_t* spre;              // drop/keep: [B][Hkv][max_tokens/32] sel index of the word's first token
+  int2* rplan;                // drop/keep: [B][Hkv][np] fp16-rows role plan entries
+  int np;                     // drop/keep: positions per (sequence, KV head) of the fp16-rows role
   int s_q, s_total;
   int ppw;                    // rows role: positions per wave (multiple of 16)
   PageDiv pd;                 // token -> page division of the cache
@@ -681,201 +683,264 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
 }
 
 // ---------------------------------------------------------------- fp16-rows role
-struct RowRef {
-  int t;          // token index (logits position in dense / keep mode)
-  int pos;        // logits position in drop mode
-  int64_t off;    // element offset of the row (k16/v16 slot * D, or tail row)
-  bool tail;      // row lives in k_tail/v_tail
-  bool ok;        // this role attends the position
-  bool none;      // drop mode: the position attends no token at all
-};
+// Row plan entry of one position of the fp16-rows role, {code, slot}:
+//   code >= 0   token `code`, fp16 row `slot` of k16/v16;
+//   code == -1  nothing to attend (another role owns the token, or no token);
+//   code == -2  drop mode: the position holds no token (its logit is -inf);
+//   code <= -3  token -3 - code, row `slot` of k_tail/v_tail.
+// Slots fit in 32 bits: 2^31 fp16 rows would take 512 GB.
+constexpr int ROW_SKIP = -1, ROW_NONE = -2;
+__device__ inline int tail_code(int t) { return -3 - t; }
+__device__ inline bool row_on(int code) { return code >= 0 || code <= -3; }
 
-template <int FMT>
-__device__ inline RowRef resolve(const AttendArgs& a, int b, int g, int n, int nq, int p) {
-  const kvc_cache& c = a.c;
-  RowRef r{0, p, 0, false, false, false};
-  const bool quant = FMT != KVC_FMT_FP16;
-  const int Hkv = c.num_kv_heads;
-  if (a.mode == KVC_ATTEND_DENSE) {
-    r.t = nq + p;
-    r.ok = r.t < n;
-    r.tail = quant;
-  } else {
-    const int nset = a.n_sink + a.k_max + a.n_window;
-    const int w0 = window_start(n, a.n_sink, a.n_window);
-    if (p < nset) {
-      if (p < a.n_sink) {
-        r.t = p;
-        r.ok = p < n;
-      } else if (p < a.n_sink + a.k_max) {
-        const int e = a.sel[((int64_t)b * Hkv + g) * a.k_max + (p - a.n_sink)];
-        r.t = e;
-        r.ok = e >= a.n_sink && e < n - a.n_window;
-      } else {
-        r.t = w0 + (p - a.n_sink - a.k_max);
-        r.ok = r.t < n;
-      }
-      r.none = !r.ok;
-      if (a.mode == KVC_ATTEND_DROP && quant) {
-        r.ok = r.ok && r.t >= nq;      // older tokens come from the codes
-        r.tail = true;
-      }
-    } else {  // keep mode: tail tokens outside the keep set
-      r.t = nq + (p - nset);
-      r.tail = true;
-      r.ok = r.t < n && r.t >= a.n_sink && r.t < w0;
-      if (r.ok) {
-        const uint32_t word = a.sbits[((int64_t)b * Hkv + g) * (c.max_tokens / 32) + (r.t >> 5)];
-        if ((word >> (r.t & 31)) & 1u) r.ok = false;
-      }
-    }
-  }
-  if (!r.ok) return r;
-  if (r.tail) {
-    r.off = (((int64_t)b * Hkv + g) * GS + (r.t - nq)) * D;
-  } else {
-    const int64_t s = slot_fast(c, a.pd, b, g, r.t);
-    if (s < 0) { r.ok = false; return r; }
-    r.off = s * D;
-  }
-  return r;
+// True when token t is an entry of the ascending selection sel[0, k).
+__device__ inline bool in_sel(const int32_t* sel, int k, int t) {
+  const int i = lower_bound_sel(sel, k, t);
+  return i < k && sel[i] == t;
 }
 
-template <int FMT>
+// Plan entry of drop/keep position p of (b, g): the sinks, the selected
+// tokens and the recent window (TailorKV article section 2.3, StreamingLLM /
+// H2O survey section 3), then, in keep mode, the fp16 tail tokens outside the
+// keep set.
+template <bool QUANT>
+__device__ inline int2 plan_entry(const AttendArgs& a, int b, int g, int n, int p) {
+  const kvc_cache& c = a.c;
+  const int nq = QUANT ? (n & ~(GS - 1)) : 0;
+  const int nset = a.n_sink + a.k_max + a.n_window;
+  const int w0 = window_start(n, a.n_sink, a.n_window);
+  const int32_t* sel = a.k_max > 0 ? a.sel + ((int64_t)b * c.num_kv_heads + g) * a.k_max : nullptr;
+  const int tail_row = (b * c.num_kv_heads + g) * GS;
+  if (p < nset) {
+    int t;
+    bool ok;
+    if (p < a.n_sink) {
+      t = p;
+      ok = p < n;
+    } else if (p < a.n_sink + a.k_max) {
+      t = sel[p - a.n_sink];
+      ok = t >= a.n_sink && t < n - a.n_window;
+    } else {
+      t = w0 + (p - a.n_sink - a.k_max);
+      ok = t < n;
+    }
+    if (!ok) return int2{a.mode == KVC_ATTEND_DROP ? ROW_NONE : ROW_SKIP, 0};
+    if (a.mode == KVC_ATTEND_DROP && QUANT)   // older tokens come from the codes
+      return t >= nq ? int2{tail_code(t), tail_row + (t - nq)} : int2{ROW_SKIP, 0};
+    const int64_t sl = slot_fast(c, a.pd, b, g, t);
+    return sl < 0 ? int2{ROW_SKIP, 0} : int2{t, (int)sl};
+  }
+  // keep mode: tail tokens outside the keep set
+  const int t = nq + (p - nset);
+  const bool ok = t < n && t >= a.n_sink && t < w0 && !in_sel(sel, a.k_max, t);
+  return ok ? int2{tail_code(t), tail_row + (t - nq)} : int2{ROW_SKIP, 0};
+}
+
+// One 16-row tile in registers: lane (row, kb) holds K channels [32kb, 32kb+32)
+// of its row (the matrix-core A operand); every lane holds V channels
+// 2*lane, 2*lane + 1 of all 16 rows (the vector-unit P.V operand).
+struct RowTile {
+  uint4 k[4];
+  uint32_t v[TILE];
+};
+
+// fp16-rows role: positions [pa, pb) of (b, g) in 16-row tiles, software
+// pipelined -- the plan entries of tile i + 2 and the rows of tile i + 1 are
+// in flight while tile i computes.  Plan entries come from the plan kernel
+// (drop / keep) or, in dense mode, from the token index (fp16 caches read the
+// page table here).  Every load is unconditional (buffer loads with empty
+// ranges, or a valid row for an empty slot), so the compiler's waits count
+// them exactly.
+// GH: head slots of the vector P.V (4 when G <= 4, else 8); slots >= G carry p = 0.
+template <int FMT, bool DENSE, bool LOGITS, int GH>
 __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int rsplit, int lane, int w,
-                          float* sO, float* sML, float* sP, int* sTok, int64_t* sOff,
-                          float* sAl) {
+                                          float* sO, float* sML, float* sP, int* sTok, float* sAl) {
+  constexpr bool QUANT = FMT != KVC_FMT_FP16;
+  constexpr int NW = waves_per_wg(FMT);
   const kvc_cache& c = a.c;
   const int n = max(c.seq_lens[b], 0);
-  const int nq = FMT == KVC_FMT_FP16 ? 0 : (n & ~(GS - 1));
+  const int nq = QUANT ? (n & ~(GS - 1)) : 0;
   const int G = a.G;
   const int col = lane & 15, kb = lane >> 4;
   const bool hv = col < G;
-  int np;
-  if (a.mode == KVC_ATTEND_DENSE) np = n - nq;
-  else np = a.n_sink + a.k_max + a.n_window + (a.mode == KVC_ATTEND_KEEP ? GS : 0);
-  constexpr int NW = waves_per_wg(FMT);
+  const int np = DENSE ? n - nq : a.np;
   const int pa = (rsplit * NW + w) * a.ppw;
   const int pb = min(pa + a.ppw, np);
   const bool drop = a.mode == KVC_ATTEND_DROP;
-
-  h8 qb[4];
-  {
-    uint4 raw[4] = {};
-    if (hv) {
-      const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + col) * D + 32 * kb);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) raw[k] = qp[k];
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) qb[k] = bc<h8>(raw[k]);
-  }
+  const int ntiles = pb > pa ? (pb - pa + TILE - 1) / TILE : 0;
 
   float m = -INFINITY, l = 0.f;
-  float o[8][2];
+  float o[GH][2];
 #pragma unroll
-  for (int h = 0; h < 8; ++h) o[h][0] = o[h][1] = 0.f;
-  float* P = sP + w * 16 * 8;
-  int* tok = sTok + w * 16;
-  int64_t* roff = sOff + w * 16;
-  float* al = sAl + w * 8;
+  for (int h = 0; h < GH; ++h) o[h][0] = o[h][1] = 0.f;
 
-  for (int p0 = pa; p0 < pb; p0 += TILE) {
-    const int p = p0 + (lane & 15);
-    RowRef r = p < pb ? resolve<FMT>(a, b, g, n, nq, p) : RowRef{0, p, 0, false, false, false};
-    if (drop && r.none && a.logits && kb < G)   // lanes (row, kb) cover heads kb, kb + 4
-      for (int h = kb; h < G; h += 4)
-        a.logits[((int64_t)b * a.hq + g * G + h) * a.logits_stride + p] = -INFINITY;
-    h8 ka[4];
+  if (ntiles > 0) {
+    h8 qb[4];
     {
       uint4 raw[4] = {};
-      if (r.ok) {
-        const uint16_t* kbase = (r.tail ? c.k_tail : c.k16) + r.off + 32 * kb;
+      if (hv) {
+        const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + col) * D + 32 * kb);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) raw[k] = reinterpret_cast<const uint4*>(kbase)[k];
+        for (int k = 0; k < 4; ++k) raw[k] = qp[k];
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) ka[k] = bc<h8>(raw[k]);
+      for (int k = 0; k < 4; ++k) qb[k] = bc<h8>(raw[k]);
     }
-    if (lane < 16) {
-      tok[lane] = r.ok ? (r.tail ? -2 - r.t : r.t) : -1;   // -1: none; <= -2: tail row
-      roff[lane] = r.off;
-    }
-    f4 s = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) s = mfma32(ka[k], qb[k], s);
-    wave_sync_lds();
+    float* P = sP + w * 16 * 8;
+    float* al = sAl + w * 8;
+    int* tok0 = sTok + w * 32;
+    int* tok1 = tok0 + 16;
+    const int row = lane & 15;
+    const int Hkv = c.num_kv_heads;
+    const int64_t pair = (int64_t)b * Hkv + g;
 
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tv = tok[4 * kb + i];
-      const bool on = tv != -1;
-      x[i] = on ? s[i] * a.sm2 : -INFINITY;
-      if (a.logits && hv && on) {
-        const int t = tv <= -2 ? -2 - tv : tv;
-        const int pos = drop ? p0 + 4 * kb + i : t;
-        a.logits[((int64_t)b * a.hq + g * G + col) * a.logits_stride + pos] = s[i] * a.sm;
+    // raw plan word(s) of this lane's row in tile i (one buffer load)
+    const Buf rplan = DENSE ? make_buf(c.block_table + (int64_t)b * c.max_pages,
+                                       (!QUANT && c.page_size > 0) ? c.max_pages * 4u : 0u)
+                            : make_buf(a.rplan + pair * a.np, (uint32_t)a.np * 8u);
+    auto plan_load = [&](int i) -> uint2 {
+      const int p = pa + TILE * i + row;
+      if constexpr (DENSE) {
+        const int page = (!QUANT && c.page_size > 0) ? page_of(a.pd, nq + p) : 0;
+        return uint2{bc<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rplan, (int)(4u * (uint32_t)page), 0, 0)), 0u};
+      } else {
+        return buf_load8(rplan, 8u * (uint32_t)p);
       }
-    }
-    float gmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    gmax = max_kb(gmax);
-    const float m_new = fmaxf(m, gmax);
-    const float ms = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = ex2(m - ms);
-    m = m_new;
-    l *= alpha;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pi = ex2(x[i] - ms);
-      l += pi;
-      if (hv) P[(4 * kb + i) * 8 + col] = pi;
-    }
-    if (hv && kb == 0) al[col] = alpha;
-    wave_sync_lds();
-
-    // VALU P.V: lane owns channels 2*lane, 2*lane + 1 for every head
-#pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      if (h < G) {
-        const float ah = al[h];
-        o[h][0] *= ah;
-        o[h][1] *= ah;
+    };
+    auto plan_decode = [&](uint2 raw, int i) -> int2 {
+      const int p = pa + TILE * i + row;
+      if (p >= pb) return int2{ROW_SKIP, 0};
+      if constexpr (!DENSE) {
+        return int2{(int)raw.x, (int)raw.y};
+      } else {
+        const int t = nq + p;
+        if (QUANT) return int2{tail_code(t), (int)(pair * GS) + p};
+        if (c.page_size == 0) return int2{t, (int)(pair * c.max_tokens + t)};
+        const int page = page_of(a.pd, t);
+        const int phys = (int)raw.x;
+        if (page >= c.max_pages || phys < 0 || phys >= c.num_pages) return int2{ROW_SKIP, 0};
+        return int2{t, (phys * Hkv + g) * a.pd.P + (t - page * a.pd.P)};
       }
-    }
-    // all 16 rows' loads in flight before any use; empty rows read a valid
-    // address and are zeroed afterwards (their p is 0 as well)
+    };
+    const uint16_t* ksafe = c.k16 ? c.k16 : c.k_tail;
     const uint16_t* vsafe = c.v16 ? c.v16 : c.v_tail;
-    uint32_t vraw[TILE];
+    auto load_rows = [&](int2 e, RowTile& d, int* tok) {
+      const bool on = row_on(e.x);
+      const uint16_t* kp = on ? (e.x <= -3 ? c.k_tail : c.k16) + (int64_t)e.y * D : ksafe;
+      const uint4* kq = reinterpret_cast<const uint4*>(kp + 32 * kb);
 #pragma unroll
-    for (int i = 0; i < TILE; ++i) {
-      const int tv = tok[i];
-      const uint16_t* vrow = tv == -1 ? vsafe : (tv <= -2 ? c.v_tail : c.v16) + roff[i];
-      vraw[i] = *reinterpret_cast<const uint32_t*>(vrow + 2 * lane);
-    }
+      for (int k = 0; k < 4; ++k) d.k[k] = kq[k];
 #pragma unroll
-    for (int i = 0; i < TILE; ++i) {
-      const h2 v = bc<h2>(tok[i] == -1 ? 0u : vraw[i]);
-      const float v0 = (float)v.x, v1 = (float)v.y;
+      for (int i = 0; i < TILE; ++i) {
+        const int ci = __builtin_amdgcn_readlane(e.x, i);
+        const int si = __builtin_amdgcn_readlane(e.y, i);
+        const uint16_t* vp = row_on(ci) ? (ci <= -3 ? c.v_tail : c.v16) + (int64_t)si * D : vsafe;
+        d.v[i] = reinterpret_cast<const uint32_t*>(vp)[lane];
+      }
+      if (lane < TILE) tok[lane] = e.x;
+    };
+    auto compute = [&](int i, const RowTile& d, const int* tok) {
+      const int p0 = pa + TILE * i;
+      wave_sync_lds();
+      int tk[TILE];   // codes of the tile's 16 rows (LDS broadcast reads)
 #pragma unroll
-      for (int h = 0; h < 8; ++h) {
-        if (h < G) {
-          const float ph = P[i * 8 + h];
-          o[h][0] = fmaf(ph, v0, o[h][0]);
-          o[h][1] = fmaf(ph, v1, o[h][1]);
+      for (int r = 0; r < TILE; r += 4) {
+        const int4 t4 = *reinterpret_cast<const int4*>(tok + r);
+        tk[r] = t4.x;
+        tk[r + 1] = t4.y;
+        tk[r + 2] = t4.z;
+        tk[r + 3] = t4.w;
+      }
+      bool any = false;
+#pragma unroll
+      for (int r = 0; r < TILE; ++r) any = any || row_on(tk[r]) || (LOGITS && drop && tk[r] == ROW_NONE);
+      if (!any) return;   // a tile of empty positions (past a shorter selection)
+      f4 sc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sc = mfma32(bc<h8>(d.k[k]), qb[k], sc);
+      float x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tv = tk[4 * kb + j];
+        const bool on = row_on(tv);
+        x[j] = on ? sc[j] * a.sm2 : -INFINITY;
+        if constexpr (LOGITS) {
+          if (hv && (on || (drop && tv == ROW_NONE))) {
+            const int t = tv <= -3 ? -3 - tv : tv;
+            const int pos = drop ? p0 + 4 * kb + j : t;
+            a.logits[((int64_t)b * a.hq + g * G + col) * a.logits_stride + pos] =
+                on ? sc[j] * a.sm : -INFINITY;
+          }
         }
       }
+      float gmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      gmax = max_kb(gmax);
+      const float m_new = fmaxf(m, gmax);
+      const float ms = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = ex2(m - ms);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pj = ex2(x[j] - ms);
+        l += pj;
+        if (col < GH) P[(4 * kb + j) * 8 + col] = hv ? pj : 0.f;
+      }
+      if (kb == 0 && col < GH) al[col] = alpha;
+      wave_sync_lds();
+      // P.V on the vector unit: lane owns channels 2*lane, 2*lane + 1 of every head slot
+      float ah[GH];
+#pragma unroll
+      for (int h = 0; h < GH; h += 4) {
+        const f4 a4 = *reinterpret_cast<const f4*>(al + h);
+        ah[h] = a4[0];
+        ah[h + 1] = a4[1];
+        ah[h + 2] = a4[2];
+        ah[h + 3] = a4[3];
+      }
+#pragma unroll
+      for (int h = 0; h < GH; ++h) {
+        o[h][0] *= ah[h];
+        o[h][1] *= ah[h];
+      }
+#pragma unroll
+      for (int r = 0; r < TILE; ++r) {
+        const h2 v = bc<h2>(row_on(tk[r]) ? d.v[r] : 0u);   // empty rows: p = 0 and v = 0
+        const float v0 = (float)v.x, v1 = (float)v.y;
+#pragma unroll
+        for (int h = 0; h < GH; h += 4) {
+          const f4 p4 = *reinterpret_cast<const f4*>(P + r * 8 + h);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            o[h + u][0] = fmaf(p4[u], v0, o[h + u][0]);
+            o[h + u][1] = fmaf(p4[u], v1, o[h + u][1]);
+          }
+        }
+      }
+    };
+
+    RowTile dA, dB;
+    uint2 eA = plan_load(0), eB = plan_load(1);
+    load_rows(plan_decode(eA, 0), dA, tok0);
+    eA = plan_load(2);
+    int i = 0;
+    for (; i + 2 <= ntiles; i += 2) {   // pairs of tiles, no exit inside a trip
+      load_rows(plan_decode(eB, i + 1), dB, tok1);
+      eB = plan_load(i + 3);
+      compute(i, dA, tok0);
+      load_rows(plan_decode(eA, i + 2), dA, tok0);
+      eA = plan_load(i + 4);
+      compute(i + 1, dB, tok1);
     }
-    wave_sync_lds();
+    if (i < ntiles) compute(i, dA, tok0);
   }
 
   l = sum_kb(l);
 #pragma unroll
-  for (int h = 0; h < 8; ++h) {
+  for (int h = 0; h < GH; ++h) {
     if (h < G) {
       float* oh = sO + (w * 8 + h) * D;
-      oh[2 * lane] = o[h][0];
-      oh[2 * lane + 1] = o[h][1];
+      *reinterpret_cast<float2*>(oh + 2 * lane) = float2{o[h][0], o[h][1]};
     }
   }
   if (hv && kb == 0) {
@@ -888,14 +953,13 @@ template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED>
 __global__ __launch_bounds__(64 * waves_per_wg(FMT), waves_per_wg(FMT) < 8 ? 8 / waves_per_wg(FMT) : 1)
 void attend_kernel(AttendArgs a) {
   constexpr int NW = waves_per_wg(FMT);
-  __shared__ float sO[NW * 8 * D];
+  __shared__ __align__(16) float sO[NW * 8 * D];
   __shared__ float sML[NW * 8 * 2];
   __shared__ __align__(16) uint16_t sKm[NW * 256];
   __shared__ __align__(16) uint16_t sVm[NW * 256];
-  __shared__ float sP[NW * 16 * 8];
-  __shared__ int sTok[NW * 16];
-  __shared__ int64_t sOff[NW * 16];
-  __shared__ float sAl[NW * 8];
+  __shared__ __align__(16) float sP[NW * 16 * 8];
+  __shared__ __align__(16) int sTok[NW * 32];
+  __shared__ __align__(16) float sAl[NW * 8];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -907,9 +971,9 @@ void attend_kernel(AttendArgs a) {
     if (split < a.s_q)
       quant_role<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, split, lane, w, sO, sML, sKm, sVm);
     else
-      rows_role<FMT>(a, b, g, split - a.s_q, lane, w, sO, sML, sP, sTok, sOff, sAl);
+      rows_role<FMT, DENSE, LOGITS, PACK ? 4 : 8>(a, b, g, split - a.s_q, lane, w, sO, sML, sP, sTok, sAl);
   } else {
-    rows_role<FMT>(a, b, g, split, lane, w, sO, sML, sP, sTok, sOff, sAl);
+    rows_role<FMT, DENSE, LOGITS, PACK ? 4 : 8>(a, b, g, split, lane, w, sO, sML, sP, sTok, sAl);
   }
   __syncthreads();
 
@@ -947,26 +1011,31 @@ void attend_kernel(AttendArgs a) {
 }
 
 // ---------------------------------------------------------------- selection plan
-// One thread per 32-token word of (sequence, KV head): which valid sel entries
-// fall in the word (bits) and the sel index of the first entry at or after the
-// word's first token (prefix).  Every word is written, so no clearing is needed.
-__global__ __launch_bounds__(256) void sel_plan_kernel(AttendArgs a) {
+// Drop / keep modes, one thread per (32-token word, position) of (sequence,
+// KV head): for quantized caches, which valid sel entries fall in the word
+// (bits) and the sel index of the first entry at or after the word's first
+// token (prefix); for every cache, the fp16-rows role's plan entry of the
+// position.  Every word and entry is written, so no clearing is needed.
+template <bool QUANT>
+__global__ __launch_bounds__(256) void plan_kernel(AttendArgs a) {
   const int g = blockIdx.y, b = blockIdx.z;
-  const int wd = blockIdx.x * 256 + threadIdx.x;
+  const int e = blockIdx.x * 256 + threadIdx.x;
   const int words = a.c.max_tokens / 32;
-  if (wd >= words) return;
   const int64_t pi = (int64_t)b * a.c.num_kv_heads + g;
   const int n = max(a.c.seq_lens[b], 0);
-  const int32_t* sel = a.k_max > 0 ? a.sel + pi * a.k_max : nullptr;
-  const int lo = lower_bound_sel(sel, a.k_max, 32 * wd);
-  const int hi = lower_bound_sel(sel, a.k_max, 32 * wd + 32);
-  uint32_t bits = 0u;
-  for (int i = lo; i < hi; ++i) {
-    const int e = sel[i];
-    if (e >= a.n_sink && e < n - a.n_window) bits |= 1u << (e & 31);
+  if (QUANT && e < words) {
+    const int32_t* sel = a.k_max > 0 ? a.sel + pi * a.k_max : nullptr;
+    const int lo = lower_bound_sel(sel, a.k_max, 32 * e);
+    const int hi = lower_bound_sel(sel, a.k_max, 32 * e + 32);
+    uint32_t bits = 0u;
+    for (int i = lo; i < hi; ++i) {
+      const int t = sel[i];
+      if (t >= a.n_sink && t < n - a.n_window) bits |= 1u << (t & 31);
+    }
+    a.sbits[pi * words + e] = bits;
+    a.spre[pi * words + e] = lo;
   }
-  a.sbits[pi * words + wd] = bits;
-  a.spre[pi * words + wd] = lo;
+  if (e < a.np) a.rplan[pi * a.np + e] = plan_entry<QUANT>(a, b, g, n, e);
 }
 
 // ---------------------------------------------------------------- split merge
@@ -1030,6 +1099,11 @@ int env_int(const char* name, int dflt) {
   return v && *v ? atoi(v) : dflt;
 }
 
+// Positions of the fp16-rows role per (sequence, KV head) in drop / keep mode.
+int rows_positions(int mode, int k_max, int n_sink, int n_window) {
+  return n_sink + k_max + n_window + (mode == KVC_ATTEND_KEEP ? GS : 0);
+}
+
 Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window) {
   Plan p{0, 0, 1, TILE};
   const int NW = waves_per_wg(c.format);
@@ -1066,7 +1140,8 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
 template <int F, bool DN, bool LG>
 void launch_inst(dim3 grid, hipStream_t s, const AttendArgs& a, bool pk, bool tiled) {
   if constexpr (F == KVC_FMT_FP16) {
-    attend_kernel<F, DN, LG, false, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
+    if (pk) attend_kernel<F, DN, LG, true, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
+    else attend_kernel<F, DN, LG, false, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
   } else if constexpr (F == KVC_FMT_INT4) {
     if (tiled) {
       if (pk) attend_kernel<F, DN, LG, true, true><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
@@ -1100,6 +1175,8 @@ size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, i
   size_t bytes = (size_t)c.batch * hq * (p.s_q + p.s_r) * PART * sizeof(float);
   if (mode != KVC_ATTEND_DENSE && c.format != KVC_FMT_FP16)   // selection bitmap + prefix
     bytes += 2 * (size_t)c.batch * c.num_kv_heads * (c.max_tokens / 32) * sizeof(uint32_t);
+  if (mode != KVC_ATTEND_DENSE)                               // fp16-rows role plan
+    bytes += (size_t)c.batch * c.num_kv_heads * rows_positions(mode, k_max, n_sink, n_window) * sizeof(int2);
   return bytes;
 }
 
@@ -1126,27 +1203,35 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   a.pd = make_page_div(c);
   a.sbits = nullptr;
   a.spre = nullptr;
-  const size_t part_bytes = (size_t)c.batch * hq * (p.s_q + p.s_r) * PART * sizeof(float);
+  a.rplan = nullptr;
+  a.np = mode == KVC_ATTEND_DENSE ? 0 : rows_positions(mode, k_max, n_sink, n_window);
+  const bool quant = c.format != KVC_FMT_FP16;
+  char* wp = static_cast<char*>(ws) + (size_t)c.batch * hq * (p.s_q + p.s_r) * PART * sizeof(float);
   const size_t sel_words = (size_t)c.batch * c.num_kv_heads * (c.max_tokens / 32);
-  if (mode != KVC_ATTEND_DENSE && c.format != KVC_FMT_FP16) {
-    a.sbits = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + part_bytes);
+  if (mode != KVC_ATTEND_DENSE && quant) {
+    a.sbits = reinterpret_cast<uint32_t*>(wp);
     a.spre = reinterpret_cast<int32_t*>(a.sbits + sel_words);
+    wp += 2 * sel_words * sizeof(uint32_t);
   }
+  if (mode != KVC_ATTEND_DENSE) a.rplan = reinterpret_cast<int2*>(wp);
   a.s_q = p.s_q;
   a.s_total = p.s_q + p.s_r;
   a.ppw = p.ppw;
   const dim3 grid(a.s_total, c.num_kv_heads, c.batch);
-  if (mode != KVC_ATTEND_DENSE && c.format != KVC_FMT_FP16) {   // k_max == 0: all-zero bits
-    const int words = c.max_tokens / 32;
-    sel_plan_kernel<<<dim3((words + 255) / 256, c.num_kv_heads, c.batch), 256, 0, s>>>(a);
+  if (mode != KVC_ATTEND_DENSE) {   // k_max == 0: all-zero bits
+    const int items = std::max(quant ? c.max_tokens / 32 : 0, a.np);
+    const dim3 pg((items + 255) / 256, c.num_kv_heads, c.batch);
+    if (quant) plan_kernel<true><<<pg, 256, 0, s>>>(a);
+    else plan_kernel<false><<<pg, 256, 0, s>>>(a);
   }
   const bool dense = mode == KVC_ATTEND_DENSE, lg = logits != nullptr;
-  const bool pk = a.G <= 4;   // packed softmax (quantized role only)
+  // G <= 4: packed softmax in the quantized role, four head slots in the fp16-rows role
+  const bool pk = a.G <= 4;
   const bool tiled = c.page_size % GS != 0;   // INT4 on pages of 16 or 32 tokens
   switch (c.format) {
     case KVC_FMT_INT4: launch_fmt<KVC_FMT_INT4>(grid, s, a, dense, lg, pk, tiled); break;
     case KVC_FMT_INT1: launch_fmt<KVC_FMT_INT1>(grid, s, a, dense, lg, pk, false); break;
-    default: launch_fmt<KVC_FMT_FP16>(grid, s, a, dense, lg, false, false); break;
+    default: launch_fmt<KVC_FMT_FP16>(grid, s, a, dense, lg, pk, false); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
