@@ -66,6 +66,8 @@ struct AttendArgs {
   int np;                     // drop/keep: positions per (sequence, KV head) of the fp16-rows role
   int s_q, s_total;
   int ppw;                    // rows role: positions per wave (multiple of 16)
+  int gpw;                    // quantized role: planned groups per wave
+  int pairs;                  // B * Hkv
   PageDiv pd;                 // token -> page division of the cache
 };
 
@@ -221,15 +223,27 @@ __device__ inline const __attribute__((address_space(4))) T* scalar_ptr(const T*
   return (const __attribute__((address_space(4))) T*)p;
 }
 
-// Slot of token t (the same t in every lane); -1 for a page outside the pool.
-__device__ inline int64_t slot_uniform(const kvc_cache& c, const PageDiv& d, int b, int g, int t) {
+// Page-table words for group gi of sequence b: the entries of the group's
+// first page and the three after it, one 16-byte load through a buffer over
+// the sequence's table row (a contiguous cache has an empty range: zeros).
+// The quantized role issues it a group ahead of the group's code loads, so
+// the table lookup is off the loads' critical path.
+__device__ inline uint4 group_table(const AttendArgs& a, Buf rtab, int gi) {
+  const int page0 = a.c.page_size > 0 ? page_of(a.pd, gi * GS) : 0;
+  return bc<uint4>(__builtin_amdgcn_raw_buffer_load_b128(rtab, (int)(4u * (uint32_t)page0), 0, 0));
+}
+
+// Slot of token t of group gi (t in the group, the same t in every lane) from
+// the group's table words; -1 for a page outside the pool.
+__device__ inline int64_t group_slot(const AttendArgs& a, int b, int g, int gi, int t, uint4 tw) {
+  const kvc_cache& c = a.c;
   if (c.page_size == 0) return ((int64_t)b * c.num_kv_heads + g) * (int64_t)c.max_tokens + t;
-  const int page = page_of(d, t);
-  const int off = t - page * d.P;
-  const int pg = min(page, c.max_pages - 1);
-  const int64_t phys = scalar_ptr(c.block_table)[(int64_t)b * c.max_pages + pg];
+  const int page = page_of(a.pd, t);
+  const int e = page - page_of(a.pd, gi * GS);   // 0..3
+  const uint32_t w = e == 0 ? tw.x : e == 1 ? tw.y : e == 2 ? tw.z : tw.w;
+  const int phys = (int)__builtin_amdgcn_readfirstlane(w);
   const bool ok = page < c.max_pages && phys >= 0 && phys < c.num_pages;
-  return ok ? (phys * c.num_kv_heads + g) * (int64_t)d.P + off : -1;
+  return ok ? ((int64_t)phys * c.num_kv_heads + g) * (int64_t)a.pd.P + (t - page * a.pd.P) : -1;
 }
 
 // Loads of group gi: a fixed set of vector loads with no branch between them,
@@ -238,12 +252,12 @@ __device__ inline int64_t slot_uniform(const kvc_cache& c, const PageDiv& d, int
 // pool give empty ranges: the loads read zero without touching memory.
 template <int FMT, bool DENSE, bool TILED>
 __device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, int gi, bool live,
-                                           int lane, GroupData<FMT, TILED>& d) {
+                                           uint4 tw, int lane, GroupData<FMT, TILED>& d) {
   const kvc_cache& c = a.c;
   const int t0 = gi * GS;
   const uint32_t l16 = 16u * lane, l8 = 8u * lane;
   if constexpr (!TILED) {   // 64 consecutive slots: one range per array
-    const int64_t s0 = slot_uniform(c, a.pd, b, g, t0);
+    const int64_t s0 = group_slot(a, b, g, gi, t0, tw);
     const bool ok = live && s0 >= 0;
     const int64_t sl = ok ? s0 : 0;
     const int64_t unit = FMT == KVC_FMT_INT4 ? (sl >> 4) : (sl >> 6);
@@ -261,7 +275,7 @@ __device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, in
     bool ok[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      st[j] = slot_uniform(c, a.pd, b, g, t0 + TILE * j);
+      st[j] = group_slot(a, b, g, gi, t0 + TILE * j, tw);
       ok[j] = live && st[j] >= 0;
       if (!ok[j]) st[j] = 0;
     }
@@ -595,9 +609,13 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
   // the waves of (b, g) take groups round-robin, so at any moment they read
   // one window of adjacent groups (long runs for the DRAM pages)
   constexpr int NW = waves_per_wg(FMT);
-  const int W = a.s_q * NW;
+  // dense: all of the pair's waves share its groups; drop / keep (ragged
+  // batches): a pair uses only the waves its length needs at the planned
+  // groups per wave, so short sequences free their workgroups at once
+  int W = a.s_q * NW;
+  if (!DENSE) W = min(W, NW * ((ngroups + NW * a.gpw - 1) / (NW * a.gpw)));
   const int ga = split * NW + w;
-  const int nmine = ga < ngroups ? (ngroups - 1 - ga) / W + 1 : 0;
+  const int nmine = ga < ngroups && ga < W ? (ngroups - 1 - ga) / W + 1 : 0;
   // k-th group of this wave; past the last one the loads of the last repeat
   // with empty ranges (no memory traffic), so every load is unconditional and
   // the compiler's wait before a group counts exactly (a wave with no group
@@ -612,9 +630,14 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
 #pragma unroll
     for (int k = 0; k < 4; ++k) raw[k] = qp[k];
   }
+  const Buf rtab = make_buf(c.block_table + (int64_t)b * c.max_pages,
+                            c.page_size > 0 ? (uint32_t)c.max_pages * 4u : 0u);
   GroupData<FMT, TILED> d0, d1;
-  load_group<FMT, DENSE, TILED>(a, b, g, gid(0), nmine > 0, lane, d0);
-  load_group<FMT, DENSE, TILED>(a, b, g, gid(1), nmine > 1, lane, d1);
+  uint4 t0w = group_table(a, rtab, gid(0)), t1w = group_table(a, rtab, gid(1));
+  load_group<FMT, DENSE, TILED>(a, b, g, gid(0), nmine > 0, t0w, lane, d0);
+  t0w = group_table(a, rtab, gid(2));
+  load_group<FMT, DENSE, TILED>(a, b, g, gid(1), nmine > 1, t1w, lane, d1);
+  t1w = group_table(a, rtab, gid(3));
   // q is in registers before the group loop (so no wait inside the loop, where
   // the next group's loads are in flight, is spent on it); the memory clobber
   // keeps the group loads above issued first
@@ -645,9 +668,11 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
   int k = 0;
   for (; k + 2 <= nmine; k += 2) {
     group_body<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, gid(k), lane, w, n, d0, st, qv, dc, sKm, sVm);
-    load_group<FMT, DENSE, TILED>(a, b, g, gid(k + 2), k + 2 < nmine, lane, d0);
+    load_group<FMT, DENSE, TILED>(a, b, g, gid(k + 2), k + 2 < nmine, t0w, lane, d0);
+    t0w = group_table(a, rtab, gid(k + 4));
     group_body<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, gid(k + 1), lane, w, n, d1, st, qv, dc, sKm, sVm);
-    load_group<FMT, DENSE, TILED>(a, b, g, gid(k + 3), k + 3 < nmine, lane, d1);
+    load_group<FMT, DENSE, TILED>(a, b, g, gid(k + 3), k + 3 < nmine, t1w, lane, d1);
+    t1w = group_table(a, rtab, gid(k + 5));
   }
   if (k < nmine)
     group_body<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, gid(k), lane, w, n, d0, st, qv, dc, sKm, sVm);
@@ -961,7 +986,20 @@ void attend_kernel(AttendArgs a) {
   __shared__ __align__(16) int sTok[NW * 32];
   __shared__ __align__(16) float sAl[NW * 8];
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // one-dimensional grid: every quantized-role workgroup (s_q per pair) comes
+  // before every fp16-rows workgroup (s_r per pair), so the longer quantized
+  // runs are dispatched first
+  int id = blockIdx.x, pair, split;
+  if (id < a.s_q * a.pairs) {
+    pair = id / a.s_q;
+    split = id - pair * a.s_q;
+  } else {
+    id -= a.s_q * a.pairs;
+    const int s_r = a.s_total - a.s_q;
+    pair = id / s_r;
+    split = a.s_q + (id - pair * s_r);
+  }
+  const int b = pair / a.c.num_kv_heads, g = pair - b * a.c.num_kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform per wave
   const int G = a.G;
@@ -1113,8 +1151,10 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   // concurrent streams keep the DRAM pages open longer and beat two per CU
   const int target = env_int("KVC_ATTEND_TARGET_WG", 256);
   if (quant) {
+    // dense: every pair is planned at capacity; drop / keep: four times the
+    // workgroups, of which a pair uses what its length needs
     const int groups = c.max_tokens / GS;
-    const int64_t waves = (int64_t)target * NW;
+    const int64_t waves = (int64_t)(mode == KVC_ATTEND_DENSE ? target : 4 * target) * NW;
     p.gpw = (int)std::max<int64_t>(1, ((int64_t)groups * pairs + waves - 1) / waves);
     p.s_q = (groups + NW * p.gpw - 1) / (NW * p.gpw);
   }
@@ -1217,7 +1257,9 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   a.s_q = p.s_q;
   a.s_total = p.s_q + p.s_r;
   a.ppw = p.ppw;
-  const dim3 grid(a.s_total, c.num_kv_heads, c.batch);
+  a.gpw = p.gpw;
+  a.pairs = c.batch * c.num_kv_heads;
+  const dim3 grid((unsigned)((int64_t)a.s_total * a.pairs));
   if (mode != KVC_ATTEND_DENSE) {   // k_max == 0: all-zero bits
     const int items = std::max(quant ? c.max_tokens / 32 : 0, a.np);
     const dim3 pg((items + 255) / 256, c.num_kv_heads, c.batch);
