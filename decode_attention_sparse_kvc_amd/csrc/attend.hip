@@ -761,13 +761,19 @@ __device__ inline int2 plan_entry(const AttendArgs& a, int b, int g, int n, int 
   return ok ? int2{tail_code(t), tail_row + (t - nq)} : int2{ROW_SKIP, 0};
 }
 
-// One 16-row tile in registers: lane (row, kb) holds K channels [32kb, 32kb+32)
-// of its row (the matrix-core A operand); every lane holds V channels
-// 2*lane, 2*lane + 1 of all 16 rows (the vector-unit P.V operand).
+// One 16-row tile in registers: lane (row, kb) holds channels [32kb, 32kb+32)
+// of its row, of K (the matrix-core A operand of S = K q) and of V (staged
+// through LDS into the transposed A operand of O^T = V^T P^T).
 struct RowTile {
   uint4 k[4];
-  uint32_t v[TILE];
+  uint4 v[4];
 };
+constexpr int ROWS_AHEAD = 2;   // row tiles held in registers by the fp16-rows role
+
+// V tile staging in LDS: row t's 16-byte chunk j lives at chunk j ^ (t >> 2)
+// of the row, so the four 16-lane groups of a transposed read (rows 4 apart)
+// hit different banks.
+__device__ inline int vt_off(int t, int chunk) { return t * D + ((chunk ^ (t >> 2)) << 3); }
 
 // fp16-rows role: positions [pa, pb) of (b, g) in 16-row tiles, software
 // pipelined -- the plan entries of tile i + 2 and the rows of tile i + 1 are
@@ -776,10 +782,9 @@ struct RowTile {
 // page table here).  Every load is unconditional (buffer loads with empty
 // ranges, or a valid row for an empty slot), so the compiler's waits count
 // them exactly.
-// GH: head slots of the vector P.V (4 when G <= 4, else 8); slots >= G carry p = 0.
-template <int FMT, bool DENSE, bool LOGITS, int GH>
+template <int FMT, bool DENSE, bool LOGITS>
 __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int rsplit, int lane, int w,
-                                          float* sO, float* sML, float* sP, int* sTok, float* sAl) {
+                                          float* sO, float* sML, int* sTok) {
   constexpr bool QUANT = FMT != KVC_FMT_FP16;
   constexpr int NW = waves_per_wg(FMT);
   const kvc_cache& c = a.c;
@@ -794,10 +799,10 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
   const bool drop = a.mode == KVC_ATTEND_DROP;
   const int ntiles = pb > pa ? (pb - pa + TILE - 1) / TILE : 0;
 
-  float m = -INFINITY, l = 0.f;
-  float o[GH][2];
+  float m = -INFINITY, l = 0.f;   // per head (lane column), log2 units
+  f4 acc[8];                       // O^T channel tiles: lane holds channels 16ct + 4kb + i of head col
 #pragma unroll
-  for (int h = 0; h < GH; ++h) o[h][0] = o[h][1] = 0.f;
+  for (int ct = 0; ct < 8; ++ct) acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
 
   if (ntiles > 0) {
     h8 qb[4];
@@ -811,10 +816,8 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
 #pragma unroll
       for (int k = 0; k < 4; ++k) qb[k] = bc<h8>(raw[k]);
     }
-    float* P = sP + w * 16 * 8;
-    float* al = sAl + w * 8;
-    int* tok0 = sTok + w * 32;
-    int* tok1 = tok0 + 16;
+    uint16_t* vt = reinterpret_cast<uint16_t*>(sO + w * 8 * D);   // 16 x 128 halves (sO is free until the end)
+    int* tok0 = sTok + w * TILE * ROWS_AHEAD;   // codes of the tiles in registers
     const int row = lane & 15;
     const int Hkv = c.num_kv_heads;
     const int64_t pair = (int64_t)b * Hkv + g;
@@ -851,42 +854,34 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
     const uint16_t* vsafe = c.v16 ? c.v16 : c.v_tail;
     auto load_rows = [&](int2 e, RowTile& d, int* tok) {
       const bool on = row_on(e.x);
-      const uint16_t* kp = on ? (e.x <= -3 ? c.k_tail : c.k16) + (int64_t)e.y * D : ksafe;
-      const uint4* kq = reinterpret_cast<const uint4*>(kp + 32 * kb);
+      const int64_t off = (int64_t)e.y * D + 32 * kb;
+      const uint4* kq = reinterpret_cast<const uint4*>(on ? (e.x <= -3 ? c.k_tail : c.k16) + off : ksafe);
+      const uint4* vq = reinterpret_cast<const uint4*>(on ? (e.x <= -3 ? c.v_tail : c.v16) + off : vsafe);
 #pragma unroll
       for (int k = 0; k < 4; ++k) d.k[k] = kq[k];
 #pragma unroll
-      for (int i = 0; i < TILE; ++i) {
-        const int ci = __builtin_amdgcn_readlane(e.x, i);
-        const int si = __builtin_amdgcn_readlane(e.y, i);
-        const uint16_t* vp = row_on(ci) ? (ci <= -3 ? c.v_tail : c.v16) + (int64_t)si * D : vsafe;
-        d.v[i] = reinterpret_cast<const uint32_t*>(vp)[lane];
-      }
+      for (int k = 0; k < 4; ++k) d.v[k] = vq[k];
       if (lane < TILE) tok[lane] = e.x;
     };
     auto compute = [&](int i, const RowTile& d, const int* tok) {
       const int p0 = pa + TILE * i;
       wave_sync_lds();
-      int tk[TILE];   // codes of the tile's 16 rows (LDS broadcast reads)
+      const int4 own = *reinterpret_cast<const int4*>(tok + 4 * kb);   // codes of this lane's S rows
+      const int tk[4] = {own.x, own.y, own.z, own.w};
+      const int mine = tok[row];                                      // code of the row this lane stages
+      if (__ballot(row_on(mine) || (LOGITS && drop && mine == ROW_NONE)) == 0)
+        return;   // a tile of empty positions (past a shorter selection)
+      // stage V (empty rows were read from a valid row; their p is 0)
 #pragma unroll
-      for (int r = 0; r < TILE; r += 4) {
-        const int4 t4 = *reinterpret_cast<const int4*>(tok + r);
-        tk[r] = t4.x;
-        tk[r + 1] = t4.y;
-        tk[r + 2] = t4.z;
-        tk[r + 3] = t4.w;
-      }
-      bool any = false;
-#pragma unroll
-      for (int r = 0; r < TILE; ++r) any = any || row_on(tk[r]) || (LOGITS && drop && tk[r] == ROW_NONE);
-      if (!any) return;   // a tile of empty positions (past a shorter selection)
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<uint4*>(vt + vt_off(row, 4 * kb + k)) = row_on(mine) ? d.v[k] : uint4{0u, 0u, 0u, 0u};
       f4 sc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < 4; ++k) sc = mfma32(bc<h8>(d.k[k]), qb[k], sc);
       float x[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int tv = tk[4 * kb + j];
+        const int tv = tk[j];
         const bool on = row_on(tv);
         x[j] = on ? sc[j] * a.sm2 : -INFINITY;
         if constexpr (LOGITS) {
@@ -901,72 +896,66 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
       float gmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       gmax = max_kb(gmax);
       const float m_new = fmaxf(m, gmax);
-      const float ms = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = ex2(m - ms);
-      m = m_new;
-      l *= alpha;
+      if (__any(m_new > m)) {   // rescale only when some head's maximum grows
+        const float alpha = m == -INFINITY ? 0.f : ex2(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) acc[ct] *= alpha;
+        m = m_new;
+      }
+      const float ms = m == -INFINITY ? 0.f : m;
+      h4 pt;   // P^T as the B operand: k = the lane's four rows, column = head
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float pj = ex2(x[j] - ms);
         l += pj;
-        if (col < GH) P[(4 * kb + j) * 8 + col] = hv ? pj : 0.f;
+        pt[j] = (_Float16)pj;
       }
-      if (kb == 0 && col < GH) al[col] = alpha;
       wave_sync_lds();
-      // P.V on the vector unit: lane owns channels 2*lane, 2*lane + 1 of every head slot
-      float ah[GH];
+      // O^T += V^T P^T: A = V^T (row = channel 16ct + col, k = rows 4kb..4kb+3)
 #pragma unroll
-      for (int h = 0; h < GH; h += 4) {
-        const f4 a4 = *reinterpret_cast<const f4*>(al + h);
-        ah[h] = a4[0];
-        ah[h + 1] = a4[1];
-        ah[h + 2] = a4[2];
-        ah[h + 3] = a4[3];
-      }
+      for (int ct = 0; ct < 8; ++ct) {
+        const int chunk = 2 * ct + (col >> 3);
+        h4 va;
 #pragma unroll
-      for (int h = 0; h < GH; ++h) {
-        o[h][0] *= ah[h];
-        o[h][1] *= ah[h];
-      }
-#pragma unroll
-      for (int r = 0; r < TILE; ++r) {
-        const h2 v = bc<h2>(row_on(tk[r]) ? d.v[r] : 0u);   // empty rows: p = 0 and v = 0
-        const float v0 = (float)v.x, v1 = (float)v.y;
-#pragma unroll
-        for (int h = 0; h < GH; h += 4) {
-          const f4 p4 = *reinterpret_cast<const f4*>(P + r * 8 + h);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            o[h + u][0] = fmaf(p4[u], v0, o[h + u][0]);
-            o[h + u][1] = fmaf(p4[u], v1, o[h + u][1]);
-          }
-        }
+        for (int j = 0; j < 4; ++j) va[j] = bc<_Float16>(vt[vt_off(4 * kb + j, chunk) + (col & 7)]);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pt, acc[ct], 0, 0, 0);
       }
     };
 
-    RowTile dA, dB;
-    uint2 eA = plan_load(0), eB = plan_load(1);
-    load_rows(plan_decode(eA, 0), dA, tok0);
-    eA = plan_load(2);
-    int i = 0;
-    for (; i + 2 <= ntiles; i += 2) {   // pairs of tiles, no exit inside a trip
-      load_rows(plan_decode(eB, i + 1), dB, tok1);
-      eB = plan_load(i + 3);
-      compute(i, dA, tok0);
-      load_rows(plan_decode(eA, i + 2), dA, tok0);
-      eA = plan_load(i + 4);
-      compute(i + 1, dB, tok1);
+    // ROWS_AHEAD tiles in registers: while tile i computes, tiles i + 1 ..
+    // i + ROWS_AHEAD - 1 are in flight; tile t lives in buffer t % ROWS_AHEAD,
+    // and its plan entry is loaded ROWS_AHEAD tiles before its rows
+    RowTile d[ROWS_AHEAD];
+    uint2 e[ROWS_AHEAD];
+#pragma unroll
+    for (int j = 0; j < ROWS_AHEAD; ++j) e[j] = plan_load(j);
+#pragma unroll
+    for (int j = 0; j < ROWS_AHEAD - 1; ++j) {
+      load_rows(plan_decode(e[j], j), d[j], tok0 + TILE * j);
+      e[j] = plan_load(j + ROWS_AHEAD);
     }
-    if (i < ntiles) compute(i, dA, tok0);
+    int i = 0;
+    for (; i + ROWS_AHEAD <= ntiles; i += ROWS_AHEAD) {   // whole rounds, no exit inside a trip
+#pragma unroll
+      for (int j = 0; j < ROWS_AHEAD; ++j) {
+        const int jl = (j + ROWS_AHEAD - 1) % ROWS_AHEAD;
+        load_rows(plan_decode(e[jl], i + j + ROWS_AHEAD - 1), d[jl], tok0 + TILE * jl);
+        e[jl] = plan_load(i + j + 2 * ROWS_AHEAD - 1);
+        compute(i + j, d[j], tok0 + TILE * j);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < ROWS_AHEAD - 1; ++j)
+      if (i + j < ntiles) compute(i + j, d[j], tok0 + TILE * j);
   }
 
   l = sum_kb(l);
+  wave_sync_lds();   // the V staging area in sO is read before the output lands there
+  if (hv) {
+    float* oh = sO + (w * 8 + col) * D;
 #pragma unroll
-  for (int h = 0; h < GH; ++h) {
-    if (h < G) {
-      float* oh = sO + (w * 8 + h) * D;
-      *reinterpret_cast<float2*>(oh + 2 * lane) = float2{o[h][0], o[h][1]};
-    }
+    for (int ct = 0; ct < 8; ++ct) *reinterpret_cast<f4*>(oh + 16 * ct + 4 * kb) = acc[ct];
   }
   if (hv && kb == 0) {
     sML[(w * 8 + col) * 2] = m;
@@ -982,8 +971,7 @@ void attend_kernel(AttendArgs a) {
   __shared__ float sML[NW * 8 * 2];
   __shared__ __align__(16) uint16_t sKm[NW * 256];
   __shared__ __align__(16) uint16_t sVm[NW * 256];
-  __shared__ __align__(16) float sP[NW * 16 * 8];
-  __shared__ __align__(16) int sTok[NW * 32];
+  __shared__ __align__(16) int sTok[NW * TILE * ROWS_AHEAD];
   __shared__ __align__(16) float sAl[NW * 8];
 
   // one-dimensional grid: every quantized-role workgroup (s_q per pair) comes
@@ -1009,16 +997,16 @@ void attend_kernel(AttendArgs a) {
     if (split < a.s_q)
       quant_role<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, split, lane, w, sO, sML, sKm, sVm);
     else
-      rows_role<FMT, DENSE, LOGITS, PACK ? 4 : 8>(a, b, g, split - a.s_q, lane, w, sO, sML, sP, sTok, sAl);
+      rows_role<FMT, DENSE, LOGITS>(a, b, g, split - a.s_q, lane, w, sO, sML, sTok);
   } else {
-    rows_role<FMT, DENSE, LOGITS, PACK ? 4 : 8>(a, b, g, split, lane, w, sO, sML, sP, sTok, sAl);
+    rows_role<FMT, DENSE, LOGITS>(a, b, g, split, lane, w, sO, sML, sTok);
   }
   __syncthreads();
 
   // ---- combine the waves and write this split's partial per query head:
   // thread h < G finds the head's maximum and each wave's weight, then thread
   // (h, channel quad) sums the weighted outputs
-  float* sWt = sAl;   // NW * 8 weights (the rows role is done with sAl)
+  float* sWt = sAl;   // NW * 8 wave weights
   float* part = a.part + ((int64_t)b * a.hq + g * G) * a.s_total * PART + (int64_t)split * PART;
   if (tid < G) {
     float mx = -INFINITY;
@@ -1180,8 +1168,7 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
 template <int F, bool DN, bool LG>
 void launch_inst(dim3 grid, hipStream_t s, const AttendArgs& a, bool pk, bool tiled) {
   if constexpr (F == KVC_FMT_FP16) {
-    if (pk) attend_kernel<F, DN, LG, true, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
-    else attend_kernel<F, DN, LG, false, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
+    attend_kernel<F, DN, LG, false, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
   } else if constexpr (F == KVC_FMT_INT4) {
     if (tiled) {
       if (pk) attend_kernel<F, DN, LG, true, true><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
@@ -1267,13 +1254,12 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
     else plan_kernel<false><<<pg, 256, 0, s>>>(a);
   }
   const bool dense = mode == KVC_ATTEND_DENSE, lg = logits != nullptr;
-  // G <= 4: packed softmax in the quantized role, four head slots in the fp16-rows role
-  const bool pk = a.G <= 4;
+  const bool pk = a.G <= 4;   // packed softmax (quantized role only)
   const bool tiled = c.page_size % GS != 0;   // INT4 on pages of 16 or 32 tokens
   switch (c.format) {
     case KVC_FMT_INT4: launch_fmt<KVC_FMT_INT4>(grid, s, a, dense, lg, pk, tiled); break;
     case KVC_FMT_INT1: launch_fmt<KVC_FMT_INT1>(grid, s, a, dense, lg, pk, false); break;
-    default: launch_fmt<KVC_FMT_FP16>(grid, s, a, dense, lg, pk, false); break;
+    default: launch_fmt<KVC_FMT_FP16>(grid, s, a, dense, lg, false, false); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
