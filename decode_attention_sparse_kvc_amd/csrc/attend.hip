@@ -225,11 +225,12 @@ __device__ inline const __attribute__((address_space(4))) T* scalar_ptr(const T*
 
 // Page-table words for group gi of sequence b: the entries of the group's
 // first page and the three after it, one 16-byte load through a buffer over
-// the sequence's table row (a contiguous cache has an empty range: zeros).
+// the sequence's table row (a contiguous cache has none).
 // The quantized role issues it a group ahead of the group's code loads, so
 // the table lookup is off the loads' critical path.
 __device__ inline uint4 group_table(const AttendArgs& a, Buf rtab, int gi) {
-  const int page0 = a.c.page_size > 0 ? page_of(a.pd, gi * GS) : 0;
+  if (a.c.page_size == 0) return uint4{0u, 0u, 0u, 0u};   // (uniform: no load at all)
+  const int page0 = page_of(a.pd, gi * GS);
   return bc<uint4>(__builtin_amdgcn_raw_buffer_load_b128(rtab, (int)(4u * (uint32_t)page0), 0, 0));
 }
 
@@ -622,18 +623,20 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
   // names group 0, whose selection words are in range)
   auto gid = [&](int k) { return nmine > 0 ? ga + min(k, nmine - 1) * W : 0; };
 
-  // q of this lane's head, channels [32kb, 32kb + 32), as fp16 pairs (zero
-  // off-head); the first two groups' loads go out before q is waited for
+  // page-table words of the first groups, then q of this lane's head
+  // (channels [32kb, 32kb + 32) as fp16 pairs, zero off-head), then the first
+  // two groups' code loads, all before q is waited for; the table words are
+  // issued first so that waiting for them leaves q in flight
+  const Buf rtab = make_buf(c.block_table + (int64_t)b * c.max_pages,
+                            c.page_size > 0 ? (uint32_t)c.max_pages * 4u : 0u);
+  uint4 t0w = group_table(a, rtab, gid(0)), t1w = group_table(a, rtab, gid(1));
   uint4 raw[4] = {};
   if (hv) {
     const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + head) * D + 32 * kb);
 #pragma unroll
     for (int k = 0; k < 4; ++k) raw[k] = qp[k];
   }
-  const Buf rtab = make_buf(c.block_table + (int64_t)b * c.max_pages,
-                            c.page_size > 0 ? (uint32_t)c.max_pages * 4u : 0u);
   GroupData<FMT, TILED> d0, d1;
-  uint4 t0w = group_table(a, rtab, gid(0)), t1w = group_table(a, rtab, gid(1));
   load_group<FMT, DENSE, TILED>(a, b, g, gid(0), nmine > 0, t0w, lane, d0);
   t0w = group_table(a, rtab, gid(2));
   load_group<FMT, DENSE, TILED>(a, b, g, gid(1), nmine > 1, t1w, lane, d1);
@@ -974,11 +977,15 @@ void attend_kernel(AttendArgs a) {
   __shared__ __align__(16) int sTok[NW * TILE * ROWS_AHEAD];
   __shared__ __align__(16) float sAl[NW * 8];
 
-  // one-dimensional grid: every quantized-role workgroup (s_q per pair) comes
-  // before every fp16-rows workgroup (s_r per pair), so the longer quantized
-  // runs are dispatched first
+  // one-dimensional grid.  Dense: pair-major, a pair's splits adjacent.
+  // Drop / keep: every quantized-role workgroup (s_q per pair) before every
+  // fp16-rows workgroup (s_r per pair), so the longer quantized runs of a
+  // ragged batch are dispatched first.
   int id = blockIdx.x, pair, split;
-  if (id < a.s_q * a.pairs) {
+  if (DENSE) {
+    pair = id / a.s_total;
+    split = id - pair * a.s_total;
+  } else if (id < a.s_q * a.pairs) {
     pair = id / a.s_q;
     split = id - pair * a.s_q;
   } else {
