@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "llama8b_layer_int4_dense_128k"
 CODE_BYTES = {"int4": 144, "int1": 48}      # per token per KV head, incl. amortized K meta
+GRAPH_CALLS = 8                             # at least this many steps (or calls) per replayed graph
 
 
 def parse():
@@ -160,7 +161,7 @@ def main():
 
     w = W.FULL[args.workload]()
     dev = torch.device("cuda")
-    extra = args.warmup + 2 * args.steps + 64      # room for the tokens the steps append
+    extra = args.warmup + 2 * args.steps + 2 * GRAPH_CALLS + 64   # room for the tokens the steps append
     cap = ((int(w.seq_lens.max()) + extra + 63) // 64) * 64
     table, num_pages = None, 0
     if w.page_size:   # shuffled pages covering the grown capacity of every sequence
@@ -240,14 +241,16 @@ def main():
     # The timed steps, replicas in rotation: step s uses replica (warmup + s) % nrep.
     order = [(args.warmup + s_) % nrep for s_ in range(args.steps)]
     graph = not args.no_graph
+    # a replayed graph holds whole passes over the replicas, at least
+    # GRAPH_CALLS steps (as one graph would hold every layer of a model's
+    # decode step), so the graph launch is amortized as it would be there;
+    # a remainder of fewer steps replays single-step graphs
+    per = nrep * -(-GRAPH_CALLS // nrep)
     if graph:
-        # one graph holds one pass over every replica (nrep consecutive steps),
-        # as one graph would hold every layer of a model's decode step; a
-        # remainder of fewer than nrep steps replays single-step graphs
-        rounds = args.steps // nrep
-        seq = order[:nrep]
+        rounds = args.steps // per
+        seq = order[:per]
         pass_graph = capture(lambda st: [step(r, st) for r in seq]) if rounds else None
-        tail_graphs = {r: capture(lambda st, r=r: step(r, st)) for r in order[rounds * nrep:]}
+        tail_graphs = {r: capture(lambda st, r=r: step(r, st)) for r in order[rounds * per:]}
         torch.cuda.synchronize()
 
     # host bookkeeping of the timed steps, done before the timed region
@@ -264,7 +267,7 @@ def main():
     if graph:
         for _ in range(rounds):
             pass_graph.replay()
-        for r in order[rounds * nrep:]:
+        for r in order[rounds * per:]:
             tail_graphs[r].replay()
     else:
         for r in order:
@@ -274,14 +277,15 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
-    # ---- per-op durations: each op alone, one graph call per replica, replayed
-    # until `steps` calls have run, bracketed by events on the launch stream
+    # ---- per-op durations: each op alone, `per` calls per graph (whole passes
+    # over the replicas), replayed until at least `steps` calls have run,
+    # bracketed by events on the launch stream
     per_op_us = {}
     for nm in names:
         if graph:
-            g = capture(lambda st: [ops[nm](r, st) for r in range(nrep)])
+            g = capture(lambda st: [ops[nm](i % nrep, st) for i in range(per)])
             torch.cuda.synchronize()
-        reps_needed = -(-args.steps // nrep)
+        reps_needed = -(-args.steps // per)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -289,14 +293,14 @@ def main():
             if graph:
                 g.replay()
             else:
-                for r in range(nrep):
-                    ops[nm](r, stream)
+                for i in range(per):
+                    ops[nm](i % nrep, stream)
         e1.record(stream)
         torch.cuda.synchronize()
-        per_op_us[nm] = e0.elapsed_time(e1) / (reps_needed * nrep) * 1e3
+        per_op_us[nm] = e0.elapsed_time(e1) / (reps_needed * per) * 1e3
         if nm == "append":
             for r in range(nrep):
-                lens[r] += reps_needed
+                lens[r] += reps_needed * (per // nrep)
     attend_us = per_op_us["attend"]
     attend_calls_bytes = sum(attend_bytes(w, lens[r], w.top_k if sparse else None)
                              for r in range(nrep)) / nrep
