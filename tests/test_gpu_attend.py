@@ -257,3 +257,35 @@ def test_full_size_dense(make):
         assert_close(out[0, 4 * g:4 * g + 4], res.o[0, 4 * g:4 * g + 4], f"o g={g}")
         assert_close(lse[0, 4 * g:4 * g + 4], res.lse[0, 4 * g:4 * g + 4], f"lse g={g}")
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+@pytest.mark.parametrize("make,pairs", [
+    (lambda: W.batched_joint(), [(0, 0), (7, 3), (15, 7)]),
+    (lambda: W.sparse_crit8(), [(0, 0), (0, 6)]),
+], ids=["batch16_keep", "crit8_drop_128k"])
+def test_full_size_sparse(make, pairs):
+    """The benchmark's keep / drop workloads at full size: the GPU Top-K feeds the GPU
+    attention (as in a step); on sampled pairs the selection must equal the oracle's and
+    o / lse / logits must match it."""
+    from test_gpu_topk import run_topk
+    w = make()
+    res = ST.decode_step(w, append=False, pairs=pairs)
+    cache = cache_for(w)
+    prefill(cache, w)
+    k_max = int(w.top_k.max())
+    idx, _, _ = run_topk(cache, w, k_max, scores=False)
+    for (b, g), ref_sel in res.sel.items():
+        want = np.full(k_max, -1, np.int64)
+        want[: len(ref_sel)] = ref_sel[:k_max]
+        assert np.array_equal(idx[b, g], want), f"selection b={b} g={g}"
+    out, lse, lg, stride = run_attend(cache, w, idx.astype(np.int32), k_max)
+    G = w.group
+    for (b, g) in pairs:
+        hs = slice(g * G, (g + 1) * G)
+        assert_close(out[b, hs], res.o[b, hs], f"o b={b} g={g}")
+        assert_close(lse[b, hs], res.lse[b, hs], f"lse b={b} g={g}")
+    # logits of the sampled pairs (o / lse were compared above; the rest of res is unsampled)
+    sampled = ST.StepResult(res.caches, res.channels, res.scores, res.sel, res.tokens, res.logits,
+                            out, lse, None)
+    check_against_oracle(w, sampled, out, lse, lg, k_max, stride)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
