@@ -53,6 +53,7 @@ struct TopkArgs {
   uint64_t* prefix;    // [B][Hkv] key prefix of the bytes chosen so far (radix state)
   int32_t* krem;       // [B][Hkv] keys still to take from the current bucket
   int32_t* done;       // [B][Hkv] 0, or 8p once pass p found its bucket taken whole
+  int hist_words;      // histogram words per pair that prep clears (all passes, or pass 0 only)
 };
 
 __device__ inline uint64_t order_key(double d) {
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(D) void prep_kernel(TopkArgs a) {
   const int g = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
   const int64_t pi = pair_index(a, b, g);
   uint4* h = reinterpret_cast<uint4*>(a.hist + pi * HSTRIDE);
-  for (int e = c; e < HSTRIDE / 4; e += D) h[e] = uint4{0u, 0u, 0u, 0u};
+  for (int e = c; e < a.hist_words / 4; e += D) h[e] = uint4{0u, 0u, 0u, 0u};
   if (c == 0) a.done[pi] = 0;
   __shared__ double s[D];
   __shared__ int chosen[D];
@@ -467,6 +468,139 @@ __global__ __launch_bounds__(ET) void emit_kernel(TopkArgs a) {
   for (int e = total + tid; e < a.k_max; e += ET) out[e] = -1;
 }
 
+// ------------------------------------------------------------------ select (one workgroup per pair)
+// After the score kernel, the remaining radix passes, the threshold and the
+// ascending output of one (sequence, KV head) in one 1024-thread workgroup:
+// the pass-0 histogram is summed from its copies into LDS, the candidates'
+// keys are staged in LDS (re-read from L2 each pass if they do not fit), and
+// each pass histograms its byte with LDS atomics.  Same passes and tie rule as
+// radix / mark / emit above, without their launches; used when a pair's
+// candidate range is short.
+constexpr int SELT = 1024;
+constexpr int SEL_LDS_KEYS = 12288;   // 96 KB of keys in LDS
+
+// Byte of the current pass among 256 LDS bins (threads < 256 scan; every
+// thread calls): the bucket holding the krem-th largest key; results through
+// s_prefix / s_krem (bucket size in s_krem[1]).
+__device__ void select_byte_lds(const uint32_t* bins, uint64_t prefix, int krem, uint64_t* s_prefix,
+                                int* s_krem, uint32_t* s_scan) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t x = tid < 256 ? bins[255 - tid] : 0u;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (tid < 256 && lane == 63) s_scan[256 + wv] = x;
+  __syncthreads();
+  if (tid < 256) {
+    for (int k = 0; k < wv; ++k) x += s_scan[256 + k];
+    s_scan[255 - tid] = x;   // keys in buckets >= d
+  }
+  __syncthreads();
+  if (tid < 256) {
+    const uint32_t ge = s_scan[tid];
+    const uint32_t gt = tid < 255 ? s_scan[tid + 1] : 0u;
+    if (ge >= (uint32_t)krem && gt < (uint32_t)krem) {
+      s_prefix[0] = (prefix << 8) | (uint64_t)tid;
+      s_krem[0] = krem - (int)gt;
+      s_krem[1] = (int)(ge - gt);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(SELT) void select_kernel(TopkArgs a) {
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t pi = pair_index(a, b, g);
+  __shared__ uint64_t skeys[SEL_LDS_KEYS];
+  __shared__ uint32_t bins[256];
+  __shared__ uint32_t s_scan[256 + 4];
+  __shared__ uint64_t s_prefix[1];
+  __shared__ int s_krem[2];
+  __shared__ int s_tot[SELT / 64];
+  int lo, hi, k;
+  cand_range(a, b, lo, hi, k);
+  int32_t* out = a.out_idx + pi * a.k_max;
+  int written = 0;
+  if (k > 0) {
+    const uint64_t* gkeys = a.keys + pi * a.c.max_tokens;
+    const int nc = hi - lo;
+    const bool in_lds = nc <= SEL_LDS_KEYS;
+    if (in_lds)
+      for (int i = tid; i < nc; i += SELT) skeys[i] = gkeys[lo + i];
+    if (tid < 256) {
+      uint32_t x = 0;
+      const uint32_t* h = a.hist + pi * HSTRIDE;
+#pragma unroll
+      for (int r = 0; r < HREP; ++r) x += h[r * 256 + tid];
+      bins[tid] = x;
+    }
+    __syncthreads();
+    auto key_at = [&](int i) -> uint64_t { return in_lds ? skeys[i] : gkeys[lo + i]; };
+
+    // ---- passes: pick each byte; stop once a bucket is taken whole
+    uint64_t prefix = 0;
+    int krem = k, bits = 0;
+    for (int p = 0; p < PASSES; ++p) {
+      select_byte_lds(bins, prefix, krem, s_prefix, s_krem, s_scan);
+      prefix = s_prefix[0];
+      krem = s_krem[0];
+      if (s_krem[1] == krem) {
+        bits = 8 * (p + 1);
+        break;
+      }
+      if (p == PASSES - 1) break;
+      if (tid < 256) bins[tid] = 0u;
+      __syncthreads();
+      const int shift = 56 - 8 * p;   // bits above the next byte
+      for (int i = tid; i < nc; i += SELT) {
+        const uint64_t key = key_at(i);
+        if (key && (key >> shift) == prefix) atomicAdd(&bins[(key >> (shift - 8)) & 255u], 1u);
+      }
+      __syncthreads();
+    }
+
+    // ---- selected = above the threshold, plus the first krem keys equal to it
+    // by index (bits > 0: every key whose top `bits` bits reach the prefix)
+    const uint64_t T = prefix;
+    int eq_taken = 0;
+    for (int c0 = 0; c0 < nc; c0 += SELT) {
+      const int i = c0 + tid;
+      const uint64_t key = i < nc ? key_at(i) : 0ull;
+      const bool ab = key != 0 && (bits ? (key >> (64 - bits)) >= T : key > T);
+      const bool eq = key != 0 && !bits && key == T;
+      const uint64_t eb = __ballot(eq);
+      if (lane == 0) s_tot[wv] = __popcll(eb);
+      __syncthreads();
+      int eq_before = eq_taken, eq_chunk = 0;
+      for (int x = 0; x < SELT / 64; ++x) {
+        const int v = s_tot[x];
+        eq_before += x < wv ? v : 0;
+        eq_chunk += v;
+      }
+      eq_before += __popcll(eb & ((1ull << lane) - 1ull));
+      const bool take = ab || (eq && eq_before < krem);
+      __syncthreads();
+      const uint64_t tb = __ballot(take);
+      if (lane == 0) s_tot[wv] = __popcll(tb);
+      __syncthreads();
+      int pos = written, chunk = 0;
+      for (int x = 0; x < SELT / 64; ++x) {
+        const int v = s_tot[x];
+        pos += x < wv ? v : 0;
+        chunk += v;
+      }
+      pos += __popcll(tb & ((1ull << lane) - 1ull));
+      if (take && pos < a.k_max) out[pos] = lo + i;
+      written += chunk;
+      eq_taken += eq_chunk;
+      __syncthreads();
+    }
+  }
+  for (int e = written + tid; e < a.k_max; e += SELT) out[e] = -1;
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(const kvc_cache& c) {
@@ -519,6 +653,11 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   a.done = reinterpret_cast<int32_t*>(p);
 
   const int Hkv = c.num_kv_heads, B = c.batch;
+  // candidate ranges whose keys fit in LDS: one selection workgroup per pair
+  // after scoring, instead of seven radix launches, mark and emit (measured:
+  // longer ranges re-read from L2 by one workgroup lose to the radix kernels)
+  const bool one_wg = c.max_tokens <= SEL_LDS_KEYS;
+  a.hist_words = one_wg ? HREP * 256 : HSTRIDE;
   prep_kernel<<<dim3(Hkv, B), D, 0, s>>>(a);
   const dim3 sgrid((c.max_tokens + ST - 1) / ST, Hkv, B);
   const bool exact = mode == KVC_SCORE_EXACT;
@@ -543,6 +682,10 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   else KVC_SCORE_G(KVC_FMT_FP16, false);
 #undef KVC_SCORE_G
 #undef KVC_SCORE_E
+  if (one_wg) {
+    select_kernel<<<dim3(Hkv, B), SELT, 0, s>>>(a);
+    return hipGetLastError();
+  }
   const dim3 rgrid((c.max_tokens + TPB - 1) / TPB, Hkv, B);
   for (int pass = 1; pass < PASSES; ++pass) radix_kernel<<<rgrid, ST, 0, s>>>(a, pass);
   mark_kernel<<<rgrid, ST, 0, s>>>(a);
