@@ -117,18 +117,22 @@ constexpr int CB_EXACT = 32;   // (every channel)
 // channel at a time in ascending order.  The loads of CB channels are issued
 // together, then their q values are read from LDS, then the adds run.  GT is
 // the query group size when it is known at compile time (0: up to GMAX).
-template <int GT, int CB, typename Load, typename Aux, typename Value>
-__device__ inline double token_score(int G, int nch, const int* sch, const double* sq, Load load,
+// ALL: the list is every channel in order (exact mode), known at compile time,
+// so loads of channels that share a code word are issued once.
+template <int GT, int CB, bool ALL = false, typename Load, typename Aux, typename Value>
+__device__ inline double token_score(int G, int nch_, const int* sch, const double* sq, Load load,
                                      Aux aux, Value value) {
   constexpr int GN = GT > 0 ? GT : GMAX;
+  const int nch = ALL ? D : nch_;
   double acc[GN];
 #pragma unroll
   for (int hh = 0; hh < GN; ++hh) acc[hh] = 0.0;
-  for (int k0 = 0; k0 < nch; k0 += CB) {
+#pragma unroll
+  for (int k0 = 0; k0 < (ALL ? D : nch); k0 += CB) {
     int ch[CB];
     uint32_t raw[CB], mx[CB];
 #pragma unroll
-    for (int u = 0; u < CB; ++u) ch[u] = sch[min(k0 + u, nch - 1)];
+    for (int u = 0; u < CB; ++u) ch[u] = ALL ? k0 + u : sch[min(k0 + u, nch - 1)];
 #pragma unroll
     for (int u = 0; u < CB; ++u) raw[u] = load(ch[u]);   // global loads, all in flight
 #pragma unroll
@@ -213,13 +217,13 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
           };
           auto aux = [&](int) -> uint32_t { return 0u; };
           auto value = [&](int, uint32_t raw, uint32_t) { return (double)h2f((uint16_t)raw); };
-          r = token_score<GT, CB>(G, nch, sch, sq, load, aux, value);
+          r = token_score<GT, CB, EXACT && FMT != KVC_FMT_INT1>(G, nch, sch, sq, load, aux, value);
         } else if (t >= nq) {   // fp16 tail row of a quantized cache
           const uint16_t* row = c.k_tail + (bg * GS + (t - nq)) * D;
           auto load = [&](int ch) -> uint32_t { return row[ch]; };
           auto aux = [&](int) -> uint32_t { return 0u; };
           auto value = [&](int, uint32_t raw, uint32_t) { return (double)h2f((uint16_t)raw); };
-          r = token_score<GT, CB>(G, nch, sch, sq, load, aux, value);
+          r = token_score<GT, CB, EXACT && FMT != KVC_FMT_INT1>(G, nch, sch, sq, load, aux, value);
         } else {
           const uint32_t* meta = smeta + (tid / GS) * D;
           const int n16 = FMT == KVC_FMT_INT4 ? (int)(slot % TILE) : (int)(slot % GS) % 16;
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
             return __dadd_rn(__dmul_rn((double)code, (double)h2f((uint16_t)(m & 0xFFFFu))),
                              (double)h2f((uint16_t)(m >> 16)));
           };
-          r = token_score<GT, CB>(G, nch, sch, sq, load, aux, value);
+          r = token_score<GT, CB, EXACT && FMT != KVC_FMT_INT1>(G, nch, sch, sq, load, aux, value);
         }
       }
     }
