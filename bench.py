@@ -48,11 +48,15 @@ def parse():
 
 
 def src_digest() -> str:
+    """Digest of the sources the attend call is built from (its kernels, their
+    shared header and the ABI header): counter summaries taken with other
+    sources stay valid for it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "decode_attention_sparse_kvc_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+    for path in (os.path.join(csrc, "attend.hip"), os.path.join(csrc, "internal.h"),
+                 os.path.join(ROOT, "include", "kvc.h")):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + f.read())
     return h.hexdigest()[:16]
 
 
