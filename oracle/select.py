@@ -27,6 +27,20 @@ Readings taken (each listed in the design doc):
     min(K, #candidates), and returns indices ascending, padded with -1.
   * Sinks and the recent window are kept outside the Top-K: candidates are the
     tokens in [n_sink, n - n_window).
+
+Block-granular selection (meeting-LLM article, part 2, section 1.1, and its
+section 8.1: importance is averaged over 64- or 128-token blocks and the top
+P% of blocks are kept, trading a little accuracy for contiguous reads).
+Readings taken:
+  * A block is a 64-token quantization group (the smaller of the two sizes,
+    and the unit the codes are stored in); only complete blocks are
+    candidates, and only those lying wholly inside [n_sink, n - n_window).
+  * A block's importance is the mean of its tokens' ranking scores (the same
+    per-token score as above): an fp64 sum over its tokens in ascending order
+    from +0.0, divided by 64 (exact: a power of two), plus +0.0.
+  * The kept blocks are the top k by (mean desc, block index asc), returned
+    ascending and -1 padded, like the token Top-K; the attended set is the
+    sinks, every token of the kept blocks, and the recent window.
 """
 from __future__ import annotations
 
@@ -80,10 +94,13 @@ def attended_tokens(mode: str, n: int, n_sink: int, n_window: int, sel) -> np.nd
     """Token ids attended in one step, ascending.
 
     dense / keep: every cached token; drop: sinks U selected U recent window
-    (selected ids outside [n_sink, n - n_window) and -1 padding are ignored).
+    (selected ids outside [n_sink, n - n_window) and -1 padding are ignored);
+    blocks: sel holds block ids (see block_tokens).
     """
     if mode in ("dense", "keep"):
         return np.arange(n)
+    if mode == "blocks":
+        return block_tokens(n, n_sink, n_window, sel)
     sinks = np.arange(min(n_sink, n))
     w0 = max(n - n_window, 0)
     window = np.arange(max(w0, min(n_sink, n)), n)
@@ -97,3 +114,41 @@ def keep_set(n: int, n_sink: int, n_window: int, sel) -> np.ndarray:
     m = np.zeros(n, dtype=bool)
     m[attended_tokens("drop", n, n_sink, n_window, sel)] = True
     return m
+
+
+BLOCK = 64
+
+
+def block_range(n: int, n_sink: int, n_window: int):
+    """Candidate blocks [lo, hi): complete 64-token blocks inside [n_sink, n - n_window)."""
+    lo = -(-max(n_sink, 0) // BLOCK)
+    hi = max(n - n_window, 0) // BLOCK
+    return lo, max(hi, lo)
+
+
+def block_scores(r: np.ndarray, lo: int, hi: int) -> np.ndarray:
+    """Mean token score of each candidate block, indexed by block id ([0, hi); -inf below lo).
+
+    Each block's tokens are added one at a time in ascending order from +0.0
+    (vectorized over blocks only), then divided by 64.
+    """
+    out = np.full(max(hi, 0), -np.inf)
+    if hi <= lo:
+        return out
+    blocks = np.arange(lo, hi)
+    acc = np.zeros(blocks.size, dtype=np.float64)
+    for i in range(BLOCK):
+        acc = acc + r[BLOCK * blocks + i]
+    out[lo:hi] = acc / BLOCK + 0.0
+    return out
+
+
+def block_tokens(n: int, n_sink: int, n_window: int, blocks) -> np.ndarray:
+    """Sinks, every token of the kept candidate blocks, and the recent window, ascending."""
+    lo, hi = block_range(n, n_sink, n_window)
+    b = np.asarray(blocks, dtype=np.int64)
+    b = b[(b >= lo) & (b < hi)]
+    toks = (BLOCK * b[:, None] + np.arange(BLOCK)[None, :]).reshape(-1)
+    sinks = np.arange(min(n_sink, n))
+    window = np.arange(max(max(n - n_window, 0), min(n_sink, n)), n)
+    return np.unique(np.concatenate([sinks, toks, window]).astype(np.int64))

@@ -127,6 +127,9 @@ def decode_step(w, append: bool = True, pairs=None, k_max: Optional[int] = None)
                 res.channels[(b, g)] = ch
                 keys, _ = token_rows(hc)
                 r = S.token_scores(q_grp, keys, ch)
+            if w.granule == "block":   # rank 64-token blocks by their mean score
+                lo, hi = S.block_range(n, w.n_sink, w.n_window)
+                r = S.block_scores(r, lo, hi)
             res.scores[(b, g)] = r
             sel = S.topk_indices(r, lo, hi, kk, km)
             res.sel[(b, g)] = sel

@@ -52,8 +52,9 @@ class Workload:
     k_new: np.ndarray
     v_new: np.ndarray
     seq_lens: np.ndarray
-    mode: str = "dense"      # attend mode: "dense" | "drop" | "keep"
+    mode: str = "dense"      # attend mode: "dense" | "drop" | "keep" | "blocks"
     score: Optional[str] = None  # "exact" | "critical" | "external" | None
+    granule: str = "token"   # what Top-K ranks: "token" or "block" (64-token blocks)
     n_sink: int = 0
     n_window: int = 0
     top_k: Optional[np.ndarray] = None   # [B] int32 tokens to select per sequence
@@ -234,6 +235,24 @@ def sparse_crit8(n_ctx: int = 131072, seed: int = 3, n_planted: int = 512,
         max_tokens=_capacity(n_ctx, 64), kT=True)
 
 
+def sparse_blocks(n_ctx: int = 131072, fmt: str = "fp16", top_blocks: int = 61,
+                  seed: int = 3) -> Workload:
+    """Block-granular selection on the sparsity-friendly layer: the draws of
+    ``sparse_crit8`` (same seed, same order), scored on 8 critical channels,
+    ranked by the mean score of each 64-token block, the top ``top_blocks``
+    blocks kept (61 = 3% of the 2048 blocks at 128K), then attended (with the
+    H2O update).  fmt "int4" stores the same keys and values as INT4 codes."""
+    w = sparse_crit8(n_ctx, seed=seed)
+    tag = "128k" if n_ctx == 131072 else str(n_ctx)
+    w.name = f"llama8b_layer_{fmt}_crit8_block{top_blocks}_{tag}"
+    w.fmt = fmt
+    w.mode = "blocks"
+    w.granule = "block"
+    w.top_k = np.array([top_blocks], np.int32)
+    w.kT = fmt == "fp16"
+    return w
+
+
 def batched_joint(batch: int = 16, lo: int = 8192, hi: int = 32768, seed: int = 4,
                   page: int = 16, n_sink: int = 4, n_window: int = 2048) -> Workload:
     """Batched joint compression over a paged INT4 cache with an fp16 keep set.
@@ -287,4 +306,6 @@ FULL = {
     "llama8b_layer_int1_dense_128k": lambda: int1_dense(131072),
     "llama8b_layer_fp16_crit8_top4096_128k": lambda: sparse_crit8(131072),
     "batch16_ragged_paged_int4_keep_fp16": lambda: batched_joint(),
+    "llama8b_layer_fp16_crit8_block61_128k": lambda: sparse_blocks(131072, "fp16"),
+    "llama8b_layer_int4_crit8_block61_128k": lambda: sparse_blocks(131072, "int4"),
 }
