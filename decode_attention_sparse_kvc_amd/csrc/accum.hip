@@ -23,17 +23,25 @@ __global__ __launch_bounds__(AT) void accum_kernel(kvc_cache c, int hq, const fl
   const int n = max(c.seq_lens[b], 0);
   int t;
   bool ok;
-  if (mode == KVC_ATTEND_DROP) {
+  if (mode == KVC_ATTEND_DROP || mode == KVC_ATTEND_BLOCKS) {
     const int w0 = max(n - n_window, min(n_sink, n));
+    const int nsel = mode == KVC_ATTEND_BLOCKS ? GS * k_max : k_max;
     if (p < n_sink) {
       t = p;
       ok = p < n;
-    } else if (p < n_sink + k_max) {
-      t = sel[((int64_t)b * c.num_kv_heads + g) * k_max + (p - n_sink)];
-      ok = t >= n_sink && t < n - n_window;
+    } else if (p < n_sink + nsel) {
+      const int32_t* s = sel + ((int64_t)b * c.num_kv_heads + g) * k_max;
+      if (mode == KVC_ATTEND_BLOCKS) {   // token (p - n_sink) % 64 of kept block (p - n_sink) / 64
+        const int blk = s[(p - n_sink) / GS];
+        t = blk * GS + (p - n_sink) % GS;
+        ok = blk >= (n_sink + GS - 1) / GS && blk < max(n - n_window, 0) / GS;
+      } else {
+        t = s[p - n_sink];
+        ok = t >= n_sink && t < n - n_window;
+      }
     } else {
-      t = w0 + (p - n_sink - k_max);
-      ok = p < n_sink + k_max + n_window && t < n;
+      t = w0 + (p - n_sink - nsel);
+      ok = p < n_sink + nsel + n_window && t < n;
     }
   } else {
     t = p;
@@ -53,7 +61,9 @@ __global__ __launch_bounds__(AT) void accum_kernel(kvc_cache c, int hq, const fl
 hipError_t launch_accum(const kvc_cache& c, int hq, const float* logits, int64_t stride,
                         const float* lse, int mode, const int32_t* sel, int k_max, int n_sink,
                         int n_window, float* acc, hipStream_t s) {
-  const int64_t np = mode == KVC_ATTEND_DROP ? (int64_t)n_sink + k_max + n_window : c.max_tokens;
+  const int64_t np = mode == KVC_ATTEND_DROP ? (int64_t)n_sink + k_max + n_window
+                    : mode == KVC_ATTEND_BLOCKS ? (int64_t)n_sink + (int64_t)GS * k_max + n_window
+                                                : c.max_tokens;
   if (np <= 0) return hipSuccess;
   const dim3 grid((unsigned)((np + AT - 1) / AT), c.num_kv_heads, c.batch);
   accum_kernel<<<grid, AT, 0, s>>>(c, hq, logits, stride, lse, mode, sel, k_max, n_sink, n_window, acc);

@@ -53,15 +53,17 @@ kvc_status check_attend_args(const kvc_cache* c, int32_t hq, int32_t mode, const
   if (hq < 1 || hq % c->num_kv_heads) return KVC_ERR_SHAPE;
   const int G = hq / c->num_kv_heads;
   if (G > KVC_MAX_GQA) return KVC_ERR_UNSUPPORTED;
-  if (mode < KVC_ATTEND_DENSE || mode > KVC_ATTEND_KEEP) return KVC_ERR_INVALID;
+  if (mode < KVC_ATTEND_DENSE || mode > KVC_ATTEND_BLOCKS) return KVC_ERR_INVALID;
   if (mode != KVC_ATTEND_DENSE) {
     if (k_max < 0 || n_sink < 0 || n_window < 0) return KVC_ERR_INVALID;
     // positions of the fp16-rows role; its plan (8 bytes each) is addressed with 32-bit offsets
-    if ((int64_t)n_sink + k_max + n_window + KVC_GROUP > ((int64_t)1 << 28)) return KVC_ERR_SHAPE;
+    const int64_t nsel = mode == KVC_ATTEND_BLOCKS ? (int64_t)KVC_GROUP * k_max : k_max;
+    if ((int64_t)n_sink + nsel + n_window + KVC_GROUP > ((int64_t)1 << 28)) return KVC_ERR_SHAPE;
     if (k_max > 0 && !sel && !sizing_only) return KVC_ERR_INVALID;
     if (sel && !aligned(sel, 4)) return KVC_ERR_INVALID;
   }
   if (mode == KVC_ATTEND_KEEP && (c->format == KVC_FMT_FP16 || !c->k16)) return KVC_ERR_UNSUPPORTED;
+  if (!attend_plan_ok(*c, mode, k_max, n_sink, n_window)) return KVC_ERR_UNSUPPORTED;
   return KVC_OK;
 }
 
@@ -105,17 +107,18 @@ kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num
   if (st != KVC_OK) return st;
   if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads) return KVC_ERR_SHAPE;
   if (num_q_heads / cache->num_kv_heads > 16) return KVC_ERR_UNSUPPORTED;
-  if (score_mode < KVC_SCORE_EXACT || score_mode > KVC_SCORE_EXTERNAL) return KVC_ERR_INVALID;
+  const int32_t base_mode = score_mode & ~KVC_SCORE_BLOCKS;
+  if (base_mode < KVC_SCORE_EXACT || base_mode > KVC_SCORE_EXTERNAL) return KVC_ERR_INVALID;
   if (n_sink < 0 || n_window < 0 || k_max < 0) return KVC_ERR_INVALID;
   if (!out_idx || !aligned(out_idx, 4)) return KVC_ERR_INVALID;
   if (k_per_seq && !aligned(k_per_seq, 4)) return KVC_ERR_INVALID;
   if (out_scores && !aligned(out_scores, 8)) return KVC_ERR_INVALID;
-  if (score_mode == KVC_SCORE_EXTERNAL) {
+  if (base_mode == KVC_SCORE_EXTERNAL) {
     if (!ext || !aligned(ext, 4)) return KVC_ERR_INVALID;
   } else {
     if (!q || !aligned(q, 2)) return KVC_ERR_INVALID;
   }
-  if (score_mode == KVC_SCORE_CRITICAL) {
+  if (base_mode == KVC_SCORE_CRITICAL) {
     if (n_crit < 1 || n_crit > KVC_HEAD_DIM) return KVC_ERR_INVALID;
     if (!cache->k_absmax) return KVC_ERR_INVALID;
     if (out_channels && !aligned(out_channels, 4)) return KVC_ERR_INVALID;
@@ -143,7 +146,8 @@ kvc_status kvc_attend_decode(const kvc_cache* cache, const uint16_t* q, int32_t 
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return KVC_ERR_INVALID;
   if (logits) {
     const int64_t need = mode == KVC_ATTEND_DROP ? (int64_t)n_sink + k_max + n_window
-                                                 : (int64_t)cache->max_tokens;
+                         : mode == KVC_ATTEND_BLOCKS ? (int64_t)n_sink + (int64_t)KVC_GROUP * k_max + n_window
+                                                     : (int64_t)cache->max_tokens;
     if (logits_stride < need) return KVC_ERR_SHAPE;
   }
   const size_t ws = attend_workspace_bytes(*cache, num_q_heads, mode, k_max, n_sink, n_window);
@@ -163,7 +167,8 @@ kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const f
   if (!logits || !lse || !acc || !aligned(logits, 4) || !aligned(lse, 4) || !aligned(acc, 4))
     return KVC_ERR_INVALID;
   const int64_t need = mode == KVC_ATTEND_DROP ? (int64_t)n_sink + k_max + n_window
-                                               : (int64_t)cache->max_tokens;
+                       : mode == KVC_ATTEND_BLOCKS ? (int64_t)n_sink + (int64_t)KVC_GROUP * k_max + n_window
+                                                   : (int64_t)cache->max_tokens;
   if (logits_stride < need) return KVC_ERR_SHAPE;
   return hip_status(launch_accum(*cache, num_q_heads, logits, logits_stride, lse, mode, sel, k_max,
                                  n_sink, n_window, acc, stream));

@@ -64,6 +64,9 @@ struct AttendArgs {
   int32_t* spre;              // drop/keep: [B][Hkv][max_tokens/32] sel index of the word's first token
   int2* rplan;                // drop/keep: [B][Hkv][np] fp16-rows role plan entries
   int np;                     // drop/keep: positions per (sequence, KV head) of the fp16-rows role
+  int nsel;                   // positions of the selection (k_max; 64 k_max in blocks mode)
+  int32_t* glist;             // blocks mode, INT4/INT1: [B][Hkv][max_tokens/64] groups to walk
+  int32_t* gcount;            // blocks mode, INT4/INT1: [B][Hkv] their number
   int s_q, s_total;
   int ppw;                    // rows role: positions per wave (multiple of 16)
   int gpw;                    // quantized role: planned groups per wave
@@ -148,6 +151,10 @@ __device__ inline int lower_bound_sel(const int32_t* sel, int k, int t) {
   }
   return lo;
 }
+
+// Drop and blocks modes attend a compact set (sinks, selection, window) whose
+// logits positions follow the selection; keep mode attends every token.
+__device__ inline bool compact(int mode) { return mode == KVC_ATTEND_DROP || mode == KVC_ATTEND_BLOCKS; }
 
 // Window start of the drop/keep sets.
 __device__ inline int window_start(int n, int n_sink, int n_window) {
@@ -334,7 +341,7 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
   if constexpr (!DENSE) {
     const int tl = t0 + lane;
     const uint64_t inset = __ballot(tl < a.n_sink || tl >= w0) | selm;
-    att = a.mode == KVC_ATTEND_DROP ? inset : ~inset;
+    att = a.mode != KVC_ATTEND_KEEP ? inset : ~inset;
     if (att == 0) return;
   }
 
@@ -418,7 +425,7 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
   // ---- logits (natural units) of the attended tokens
   if constexpr (LOGITS) {
     int32_t pre0 = 0, pre1 = 0;   // sel index of the group's two 32-token words (drop mode)
-    if (!DENSE && a.mode == KVC_ATTEND_DROP) {
+    if (!DENSE && compact(a.mode)) {
       const auto* sp = scalar_ptr(a.spre + ((int64_t)b * a.c.num_kv_heads + g) * (a.c.max_tokens / 32) + 2 * gi);
       pre0 = sp[0];
       pre1 = sp[1];
@@ -431,12 +438,12 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
         const bool on = DENSE || ((att >> bit) & 1ull);
         if (hi_lane && on) {
           int pos = t0 + bit;
-          if (a.mode == KVC_ATTEND_DROP) {
+          if (compact(a.mode)) {
             const int t = t0 + bit;
             if (t < a.n_sink) {
               pos = t;
             } else if (t >= w0) {
-              pos = a.n_sink + a.k_max + (t - w0);
+              pos = a.n_sink + a.nsel + (t - w0);
             } else {
               const uint32_t word = (bit >> 5) ? d.bits.y : d.bits.x;
               const int32_t base = (bit >> 5) ? pre1 : pre0;
@@ -602,7 +609,11 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
                            float* sO, float* sML, uint16_t* sKm, uint16_t* sVm) {
   const kvc_cache& c = a.c;
   const int n = max(c.seq_lens[b], 0);
-  const int ngroups = n >> 6;
+  // blocks mode walks the plan's list of groups (sink groups, kept blocks,
+  // window groups); the other modes walk every complete group
+  const bool listed = !DENSE && a.mode == KVC_ATTEND_BLOCKS;
+  const int64_t pair = (int64_t)b * c.num_kv_heads + g;
+  const int ngroups = listed ? *scalar_ptr(a.gcount + pair) : n >> 6;
   const int G = a.G;
   const int col = lane & 15, kb = lane >> 4, head = col & 7;
   const bool hv = head < G;
@@ -616,12 +627,21 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
   int W = a.s_q * NW;
   if (!DENSE) W = min(W, NW * ((ngroups + NW * a.gpw - 1) / (NW * a.gpw)));
   const int ga = split * NW + w;
-  const int nmine = ga < ngroups && ga < W ? (ngroups - 1 - ga) / W + 1 : 0;
+  int nmine = ga < ngroups && ga < W ? (ngroups - 1 - ga) / W + 1 : 0;
+  if (listed) nmine = min(nmine, 64);   // (the planner keeps it there)
   // k-th group of this wave; past the last one the loads of the last repeat
   // with empty ranges (no memory traffic), so every load is unconditional and
   // the compiler's wait before a group counts exactly (a wave with no group
   // names group 0, whose selection words are in range)
-  auto gid = [&](int k) { return nmine > 0 ? ga + min(k, nmine - 1) * W : 0; };
+  // (blocks mode: the k-th entry comes from lane k of vlist, one load per wave;
+  // the planner keeps nmine <= 64)
+  int vlist = 0;
+  if (listed && lane < nmine) vlist = a.glist[pair * (c.max_tokens / GS) + ga + lane * W];
+  auto gid = [&](int k) {
+    if (nmine <= 0) return 0;
+    const int kk = min(k, nmine - 1);
+    return listed ? __builtin_amdgcn_readlane(vlist, kk) : ga + kk * W;
+  };
 
   // page-table words of the first groups, then q of this lane's head
   // (channels [32kb, 32kb + 32) as fp16 pairs, zero off-head), then the first
@@ -735,7 +755,7 @@ template <bool QUANT>
 __device__ inline int2 plan_entry(const AttendArgs& a, int b, int g, int n, int p) {
   const kvc_cache& c = a.c;
   const int nq = QUANT ? (n & ~(GS - 1)) : 0;
-  const int nset = a.n_sink + a.k_max + a.n_window;
+  const int nset = a.n_sink + a.nsel + a.n_window;
   const int w0 = window_start(n, a.n_sink, a.n_window);
   const int32_t* sel = a.k_max > 0 ? a.sel + ((int64_t)b * c.num_kv_heads + g) * a.k_max : nullptr;
   const int tail_row = (b * c.num_kv_heads + g) * GS;
@@ -745,15 +765,21 @@ __device__ inline int2 plan_entry(const AttendArgs& a, int b, int g, int n, int 
     if (p < a.n_sink) {
       t = p;
       ok = p < n;
-    } else if (p < a.n_sink + a.k_max) {
-      t = sel[p - a.n_sink];
-      ok = t >= a.n_sink && t < n - a.n_window;
+    } else if (p < a.n_sink + a.nsel) {
+      if (a.mode == KVC_ATTEND_BLOCKS) {   // token (p - n_sink) % 64 of kept block (p - n_sink) / 64
+        const int blk = sel[(p - a.n_sink) / GS];
+        ok = blk >= (a.n_sink + GS - 1) / GS && blk < max(n - a.n_window, 0) / GS;
+        t = ok ? blk * GS + (p - a.n_sink) % GS : 0;
+      } else {
+        t = sel[p - a.n_sink];
+        ok = t >= a.n_sink && t < n - a.n_window;
+      }
     } else {
-      t = w0 + (p - a.n_sink - a.k_max);
+      t = w0 + (p - a.n_sink - a.nsel);
       ok = t < n;
     }
-    if (!ok) return int2{a.mode == KVC_ATTEND_DROP ? ROW_NONE : ROW_SKIP, 0};
-    if (a.mode == KVC_ATTEND_DROP && QUANT)   // older tokens come from the codes
+    if (!ok) return int2{compact(a.mode) ? ROW_NONE : ROW_SKIP, 0};
+    if (compact(a.mode) && QUANT)   // older tokens come from the codes
       return t >= nq ? int2{tail_code(t), tail_row + (t - nq)} : int2{ROW_SKIP, 0};
     const int64_t sl = slot_fast(c, a.pd, b, g, t);
     return sl < 0 ? int2{ROW_SKIP, 0} : int2{t, (int)sl};
@@ -799,7 +825,7 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
   const int np = DENSE ? n - nq : a.np;
   const int pa = (rsplit * NW + w) * a.ppw;
   const int pb = min(pa + a.ppw, np);
-  const bool drop = a.mode == KVC_ATTEND_DROP;
+  const bool drop = compact(a.mode);
   const int ntiles = pb > pa ? (pb - pa + TILE - 1) / TILE : 0;
 
   float m = -INFINITY, l = 0.f;   // per head (lane column), log2 units
@@ -1056,8 +1082,16 @@ __global__ __launch_bounds__(256) void plan_kernel(AttendArgs a) {
   const int words = a.c.max_tokens / 32;
   const int64_t pi = (int64_t)b * a.c.num_kv_heads + g;
   const int n = max(a.c.seq_lens[b], 0);
-  if (QUANT && e < words) {
-    const int32_t* sel = a.k_max > 0 ? a.sel + pi * a.k_max : nullptr;
+  const int32_t* sel = a.k_max > 0 ? a.sel + pi * a.k_max : nullptr;
+  const int blo = (a.n_sink + GS - 1) / GS, bhi = max(n - a.n_window, 0) / GS;   // candidate blocks
+  if (QUANT && e < words && a.mode == KVC_ATTEND_BLOCKS) {
+    // every token of a kept block; its logits positions start at 64 x its sel index
+    const int j = e >> 1;
+    const int i = lower_bound_sel(sel, a.k_max, j);
+    const bool kept = i < a.k_max && sel[i] == j && j >= blo && j < bhi;
+    a.sbits[pi * words + e] = kept ? ~0u : 0u;
+    a.spre[pi * words + e] = GS * i + 32 * (e & 1);
+  } else if (QUANT && e < words) {
     const int lo = lower_bound_sel(sel, a.k_max, 32 * e);
     const int hi = lower_bound_sel(sel, a.k_max, 32 * e + 32);
     uint32_t bits = 0u;
@@ -1067,6 +1101,26 @@ __global__ __launch_bounds__(256) void plan_kernel(AttendArgs a) {
     }
     a.sbits[pi * words + e] = bits;
     a.spre[pi * words + e] = lo;
+  }
+  if (QUANT && a.mode == KVC_ATTEND_BLOCKS) {
+    // groups the quantized role walks, ascending and disjoint: those holding
+    // sink tokens, the kept blocks, those holding window tokens (complete
+    // groups only; a kept block lies wholly between the sinks and the window)
+    const int groups = a.c.max_tokens / GS, ng = n >> 6;
+    const int ns = min((a.n_sink + GS - 1) / GS, ng);
+    const int l0 = lower_bound_sel(sel, a.k_max, blo), l1 = lower_bound_sel(sel, a.k_max, max(bhi, blo));
+    const int nl = l1 - l0;
+    const int ws = max(window_start(n, a.n_sink, a.n_window) / GS, ns);
+    const int nw = max(0, ng - ws);
+    // (a selection that is not strictly ascending, which the interface rules
+    // out, may list more groups or other ids: the count is capped and every
+    // id clamped into the candidate range, so the walk stays in bounds)
+    const int cnt = min(ns + nl + nw, groups);
+    if (e < cnt)
+      a.glist[pi * groups + e] = e < ns ? e
+                                 : e < ns + nl ? min(max(sel[l0 + e - ns], blo), bhi - 1)
+                                               : ws + (e - ns - nl);
+    if (e == 0) a.gcount[pi] = cnt;
   }
   if (e < a.np) a.rplan[pi * a.np + e] = plan_entry<QUANT>(a, b, g, n, e);
 }
@@ -1122,6 +1176,7 @@ __global__ __launch_bounds__(MT) void merge_kernel(const float* __restrict__ par
 }
 
 constexpr int MAX_SPLITS = 2048;
+constexpr int LIST_MAX = 64;   // blocks mode: groups per wave (one list entry per lane)
 
 struct Plan {
   int s_q, s_r, gpw, ppw;
@@ -1134,7 +1189,8 @@ int env_int(const char* name, int dflt) {
 
 // Positions of the fp16-rows role per (sequence, KV head) in drop / keep mode.
 int rows_positions(int mode, int k_max, int n_sink, int n_window) {
-  return n_sink + k_max + n_window + (mode == KVC_ATTEND_KEEP ? GS : 0);
+  const int nsel = mode == KVC_ATTEND_BLOCKS ? GS * k_max : k_max;
+  return n_sink + nsel + n_window + (mode == KVC_ATTEND_KEEP ? GS : 0);
 }
 
 Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window) {
@@ -1151,11 +1207,13 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
     const int groups = c.max_tokens / GS;
     const int64_t waves = (int64_t)(mode == KVC_ATTEND_DENSE ? target : 4 * target) * NW;
     p.gpw = (int)std::max<int64_t>(1, ((int64_t)groups * pairs + waves - 1) / waves);
+    // blocks mode: a wave's list entries fit in one register (<= 64 groups)
+    if (mode == KVC_ATTEND_BLOCKS) p.gpw = std::min(p.gpw, LIST_MAX);
     p.s_q = (groups + NW * p.gpw - 1) / (NW * p.gpw);
   }
   int64_t np;
   if (mode == KVC_ATTEND_DENSE) np = quant ? GS : c.max_tokens;
-  else np = (int64_t)n_sink + k_max + n_window + (mode == KVC_ATTEND_KEEP ? GS : 0);
+  else np = rows_positions(mode, k_max, n_sink, n_window);
   const int64_t tiles = std::max<int64_t>(1, (np + TILE - 1) / TILE);
   // a dense quantized cache leaves only its tail (< 64 tokens) to this role
   const int64_t rwaves = (quant && mode == KVC_ATTEND_DENSE) ? (int64_t)pairs * NW
@@ -1164,8 +1222,9 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   p.ppw = (int)(tpw * TILE);
   p.s_r = (int)((tiles + NW * tpw - 1) / (NW * tpw));
   while (p.s_q + p.s_r > MAX_SPLITS) {   // bound the merge's work per query head
-    if (p.s_q >= p.s_r) { p.gpw *= 2; p.s_q = (c.max_tokens / GS + NW * p.gpw - 1) / (NW * p.gpw); }
-    else { p.ppw *= 2; p.s_r = (int)((tiles * TILE + (int64_t)NW * p.ppw - 1) / ((int64_t)NW * p.ppw)); }
+    if (p.s_q >= p.s_r && (mode != KVC_ATTEND_BLOCKS || 2 * p.gpw <= LIST_MAX)) { p.gpw *= 2; p.s_q = (c.max_tokens / GS + NW * p.gpw - 1) / (NW * p.gpw); }
+    else if (p.s_r > 1) { p.ppw *= 2; p.s_r = (int)((tiles * TILE + (int64_t)NW * p.ppw - 1) / ((int64_t)NW * p.ppw)); }
+    else break;   // (blocks mode on a cache too long for its list registers: rejected by the caller)
   }
   return p;
 }
@@ -1211,7 +1270,17 @@ size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, i
     bytes += 2 * (size_t)c.batch * c.num_kv_heads * (c.max_tokens / 32) * sizeof(uint32_t);
   if (mode != KVC_ATTEND_DENSE)                               // fp16-rows role plan
     bytes += (size_t)c.batch * c.num_kv_heads * rows_positions(mode, k_max, n_sink, n_window) * sizeof(int2);
+  if (mode == KVC_ATTEND_BLOCKS && c.format != KVC_FMT_FP16)   // group list + count
+    bytes += (size_t)c.batch * c.num_kv_heads * (c.max_tokens / GS + 1) * sizeof(int32_t);
   return bytes;
+}
+
+bool attend_plan_ok(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window) {
+  const Plan p = plan_attend(c, mode, k_max, n_sink, n_window);
+  if (p.s_q + p.s_r > MAX_SPLITS) return false;
+  if (mode == KVC_ATTEND_BLOCKS && c.format != KVC_FMT_FP16)
+    return (int64_t)p.s_q * waves_per_wg(c.format) * LIST_MAX >= c.max_tokens / GS;
+  return true;
 }
 
 hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm_scale, int mode,
@@ -1239,6 +1308,9 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   a.spre = nullptr;
   a.rplan = nullptr;
   a.np = mode == KVC_ATTEND_DENSE ? 0 : rows_positions(mode, k_max, n_sink, n_window);
+  a.nsel = mode == KVC_ATTEND_BLOCKS ? GS * k_max : k_max;
+  a.glist = nullptr;
+  a.gcount = nullptr;
   const bool quant = c.format != KVC_FMT_FP16;
   char* wp = static_cast<char*>(ws) + (size_t)c.batch * hq * (p.s_q + p.s_r) * PART * sizeof(float);
   const size_t sel_words = (size_t)c.batch * c.num_kv_heads * (c.max_tokens / 32);
@@ -1247,7 +1319,14 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
     a.spre = reinterpret_cast<int32_t*>(a.sbits + sel_words);
     wp += 2 * sel_words * sizeof(uint32_t);
   }
-  if (mode != KVC_ATTEND_DENSE) a.rplan = reinterpret_cast<int2*>(wp);
+  if (mode != KVC_ATTEND_DENSE) {
+    a.rplan = reinterpret_cast<int2*>(wp);
+    wp += (size_t)c.batch * c.num_kv_heads * a.np * sizeof(int2);
+  }
+  if (mode == KVC_ATTEND_BLOCKS && quant) {
+    a.glist = reinterpret_cast<int32_t*>(wp);
+    a.gcount = a.glist + (size_t)c.batch * c.num_kv_heads * (c.max_tokens / GS);
+  }
   a.s_q = p.s_q;
   a.s_total = p.s_q + p.s_r;
   a.ppw = p.ppw;

@@ -94,6 +94,7 @@ hipError_t launch_append(const kvc_cache& c, const uint16_t* k_new, const uint16
                          const int32_t* n_new, int32_t n_new_max, int32_t* overflow,
                          hipStream_t s);
 
+bool attend_plan_ok(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window);
 size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, int n_sink,
                               int n_window);
 hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm_scale, int mode,

@@ -18,6 +18,11 @@
 //   mark    bitmaps of keys above the k-th largest key T and equal to T.
 //   emit    one workgroup per (sequence, KV head): the first k - #above keys
 //           equal to T by index, then every selected index in ascending order.
+// Block mode (meeting-LLM article, section 8.1: importance averaged over
+// 64-token blocks, the top blocks kept): score writes each token's fp64 score
+// and no key; block_key averages every candidate block's 64 scores into the
+// block's key (item j of the pair's key row) and histograms it; the passes
+// above then select blocks instead of tokens.
 
 #include <math.h>
 
@@ -54,6 +59,8 @@ struct TopkArgs {
   int32_t* krem;       // [B][Hkv] keys still to take from the current bucket
   int32_t* done;       // [B][Hkv] 0, or 8p once pass p found its bucket taken whole
   int hist_words;      // histogram words per pair that prep clears (all passes, or pass 0 only)
+  bool blocks;         // rank 64-token blocks (items = block ids)
+  double* tscore;      // block mode: [B][Hkv][max_tokens] token scores
 };
 
 __device__ inline uint64_t order_key(double d) {
@@ -65,11 +72,18 @@ __device__ inline int64_t pair_index(const TopkArgs& a, int b, int g) {
   return (int64_t)b * a.c.num_kv_heads + g;
 }
 
-// Number of tokens to select and the candidate range of (sequence b).
+// Number of items to select and the candidate range of (sequence b): tokens
+// [n_sink, n - n_window), or in block mode the complete 64-token blocks
+// wholly inside that range.
 __device__ inline void cand_range(const TopkArgs& a, int b, int& lo, int& hi, int& k) {
   const int n = max(a.c.seq_lens[b], 0);
-  lo = a.n_sink;
-  hi = n - a.n_window;
+  if (a.blocks) {
+    lo = (a.n_sink + GS - 1) / GS;
+    hi = max(lo, max(n - a.n_window, 0) / GS);
+  } else {
+    lo = a.n_sink;
+    hi = n - a.n_window;
+  }
   const int ncand = max(0, hi - lo);
   int want = a.k_per_seq ? a.k_per_seq[b] : a.k_max;
   want = min(max(want, 0), a.k_max);
@@ -197,6 +211,10 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
 
   int lo, hi, kk;
   cand_range(a, b, lo, hi, kk);
+  if (a.blocks) {   // every token of the candidate blocks
+    lo *= GS;
+    hi *= GS;
+  }
   const int n = max(c.seq_lens[b], 0);
   const bool in = t < c.max_tokens;
   uint64_t key = 0;
@@ -246,11 +264,53 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
       }
     }
     r = __dadd_rn(r, 0.0);
-    key = order_key(r);
-    if (a.out_scores) a.out_scores[pi * c.max_tokens + t] = r;
+    if (a.blocks) {
+      a.tscore[pi * c.max_tokens + t] = r;
+    } else {
+      key = order_key(r);
+      if (a.out_scores) a.out_scores[pi * c.max_tokens + t] = r;
+    }
   }
   if (in) a.keys[pi * c.max_tokens + t] = key;
   if (key) atomicAdd(&sh[key >> 56], 1u);
+  __syncthreads();
+  if (sh[tid]) atomicAdd(&a.hist[pi * HSTRIDE + (blockIdx.x % HREP) * 256 + tid], sh[tid]);
+}
+
+// ------------------------------------------------------------------ block keys
+// Block mode: 64 candidate blocks a workgroup.  Their 64 x 64 token scores are
+// staged in LDS with coalesced loads, then thread j adds block j's scores one
+// at a time in ascending token order from +0.0, divides by 64 (exact), and
+// writes the block's key and its pass-0 histogram entry.  Items that are not
+// candidates keep the zero key the score kernel wrote.
+constexpr int BPW = 64;
+__global__ __launch_bounds__(ST) void block_key_kernel(TopkArgs a) {
+  const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int64_t pi = pair_index(a, b, g);
+  __shared__ double ss[BPW * GS];
+  __shared__ uint32_t sh[256];
+  int lo, hi, kk;
+  cand_range(a, b, lo, hi, kk);
+  const int j0 = blockIdx.x * BPW;
+  const double* ts = a.tscore + pi * a.c.max_tokens;
+  sh[tid] = 0u;
+  for (int e = tid; e < BPW * GS; e += ST) {
+    const int j = j0 + e / GS;
+    ss[e] = j >= lo && j < hi ? ts[(int64_t)j0 * GS + e] : 0.0;
+  }
+  __syncthreads();
+  if (tid < BPW) {
+    const int j = j0 + tid;
+    if (j >= lo && j < hi) {
+      double sum = 0.0;
+      for (int i = 0; i < GS; ++i) sum = __dadd_rn(sum, ss[tid * GS + i]);
+      const double r = __dadd_rn(__ddiv_rn(sum, (double)GS), 0.0);
+      const uint64_t key = order_key(r);
+      a.keys[pi * a.c.max_tokens + j] = key;
+      if (a.out_scores) a.out_scores[pi * a.c.max_tokens + j] = r;
+      atomicAdd(&sh[key >> 56], 1u);
+    }
+  }
   __syncthreads();
   if (sh[tid]) atomicAdd(&a.hist[pi * HSTRIDE + (blockIdx.x % HREP) * 256 + tid], sh[tid]);
 }
@@ -610,7 +670,7 @@ __global__ __launch_bounds__(SELT) void select_kernel(TopkArgs a) {
 size_t topk_workspace_bytes(const kvc_cache& c) {
   const size_t pairs = (size_t)c.batch * c.num_kv_heads;
   const size_t words = c.max_tokens / 32;
-  size_t bytes = pairs * c.max_tokens * sizeof(uint64_t);
+  size_t bytes = 2 * pairs * c.max_tokens * sizeof(uint64_t);   // keys, block-mode token scores
   bytes += pairs * HSTRIDE * sizeof(uint32_t);
   bytes += 2 * pairs * words * sizeof(uint32_t);
   bytes += pairs * D * sizeof(int32_t);
@@ -627,6 +687,8 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   a.q = q;
   a.hq = hq;
   a.G = hq / c.num_kv_heads;
+  a.blocks = (mode & KVC_SCORE_BLOCKS) != 0;
+  mode &= ~KVC_SCORE_BLOCKS;
   a.mode = mode;
   a.n_crit = n_crit;
   a.ext = ext;
@@ -642,6 +704,8 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   char* p = static_cast<char*>(ws);
   a.keys = reinterpret_cast<uint64_t*>(p);
   p += pairs * c.max_tokens * sizeof(uint64_t);
+  a.tscore = reinterpret_cast<double*>(p);
+  p += pairs * c.max_tokens * sizeof(double);
   a.hist = reinterpret_cast<uint32_t*>(p);
   p += pairs * HSTRIDE * sizeof(uint32_t);
   a.above = reinterpret_cast<uint32_t*>(p);
@@ -660,7 +724,7 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   // candidate ranges whose keys fit in LDS: one selection workgroup per pair
   // after scoring, instead of seven radix launches, mark and emit (measured:
   // longer ranges re-read from L2 by one workgroup lose to the radix kernels)
-  const bool one_wg = c.max_tokens <= SEL_LDS_KEYS;
+  const bool one_wg = (a.blocks ? c.max_tokens / GS : c.max_tokens) <= SEL_LDS_KEYS;
   a.hist_words = one_wg ? HREP * 256 : HSTRIDE;
   prep_kernel<<<dim3(Hkv, B), D, 0, s>>>(a);
   const dim3 sgrid((c.max_tokens + ST - 1) / ST, Hkv, B);
@@ -686,6 +750,8 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   else KVC_SCORE_G(KVC_FMT_FP16, false);
 #undef KVC_SCORE_G
 #undef KVC_SCORE_E
+  if (a.blocks)
+    block_key_kernel<<<dim3((c.max_tokens / GS + BPW - 1) / BPW, Hkv, B), ST, 0, s>>>(a);
   if (one_wg) {
     select_kernel<<<dim3(Hkv, B), SELT, 0, s>>>(a);
     return hipGetLastError();

@@ -21,7 +21,8 @@ HEAD_DIM = 128
 GROUP = 64
 FMT = {"fp16": 0, "int4": 1, "int1": 2}
 SCORE = {"exact": 0, "critical": 1, "external": 2}
-MODE = {"dense": 0, "drop": 1, "keep": 2}
+SCORE_BLOCKS = 16   # OR'ed into a score mode: rank 64-token blocks
+MODE = {"dense": 0, "drop": 1, "keep": 2, "blocks": 3}
 OP_SCORE_TOPK, OP_ATTEND = 1, 2
 
 

@@ -64,7 +64,9 @@ enum {
 
 enum { KVC_FMT_FP16 = 0, KVC_FMT_INT4 = 1, KVC_FMT_INT1 = 2 };
 enum { KVC_SCORE_EXACT = 0, KVC_SCORE_CRITICAL = 1, KVC_SCORE_EXTERNAL = 2 };
-enum { KVC_ATTEND_DENSE = 0, KVC_ATTEND_DROP = 1, KVC_ATTEND_KEEP = 2 };
+/* OR'ed into a score mode: rank 64-token blocks instead of tokens ([MTG] 8.1) */
+enum { KVC_SCORE_BLOCKS = 16 };
+enum { KVC_ATTEND_DENSE = 0, KVC_ATTEND_DROP = 1, KVC_ATTEND_KEEP = 2, KVC_ATTEND_BLOCKS = 3 };
 enum { KVC_OP_SCORE_TOPK = 1, KVC_OP_ATTEND = 2 };
 
 /*
@@ -186,6 +188,17 @@ kvc_status kvc_quantize_append(const kvc_cache* cache, const uint16_t* k_new,
  *   out_channels optional int32 [B][Hkv][n_crit]: ascending critical channels.
  *   workspace   kvc_workspace_bytes(KVC_OP_SCORE_TOPK, ...) bytes.
  * Hq/Hkv must be 1..16; n_crit 1..128.
+ *
+ * With KVC_SCORE_BLOCKS in score_mode (block-granular selection, [MTG] 8.1
+ * and its part 2 section 1.1: importance averaged over blocks, the top blocks
+ * kept for contiguous reads), the items ranked are the complete 64-token
+ * blocks j lying wholly inside [n_sink, n - n_window), i.e. j in
+ * [ceil(n_sink/64), floor((n - n_window)/64)); block j's score is the mean of
+ * its 64 token scores r_t (their fp64 sum in ascending t from +0.0, / 64,
+ * + 0.0).  k_per_seq / k_max count blocks; out_idx holds block ids (ascending,
+ * -1 padded, ties to the lower block); out_scores, if given, receives the
+ * block means at index j of each (sequence, KV head) row (other entries are
+ * left as they were).
  */
 kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num_q_heads,
                           int32_t score_mode, int32_t n_crit, const float* ext,
@@ -203,6 +216,13 @@ kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num
  *           the window [max(n - n_window, n_sink), n); other tokens dropped.
  *         KVC_ATTEND_KEEP (INT4/INT1 with k16/v16): every token; those of the
  *           DROP set read from the fp16 rows, the rest from codes or tail.
+ *         KVC_ATTEND_BLOCKS ([MTG] 8.1): sel holds block ids (as written by
+ *           kvc_score_topk with KVC_SCORE_BLOCKS, strictly ascending among
+ *           the valid ones); the sinks, all 64 tokens of every valid block,
+ *           and the window.  Valid blocks are those wholly inside
+ *           [n_sink, n - n_window).  INT4/INT1 read only the groups of kept
+ *           blocks, sinks and window.  KVC_ERR_UNSUPPORTED when a quantized
+ *           cache is too long for the per-wave block list (over 2^23 tokens).
  *   sel   int32 [B][Hkv][k_max], ascending, -1 padded (kvc_score_topk's
  *         out_idx); entries outside [n_sink, n - n_window) are ignored.
  *   out   float32 [B][Hq][128];  lse  float32 [B][Hq] (natural log; -inf and
@@ -210,8 +230,10 @@ kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num
  *   logits optional float32, row (b, h) at logits + (b*Hq + h)*logits_stride:
  *         DENSE/KEEP: position t = token t (t < n); DROP: position j with
  *         j < n_sink -> token j, j - n_sink < k_max -> sel entry, then window
- *         token max(n - n_window, n_sink) + (j - n_sink - k_max); positions
- *         that attend nothing hold -inf.  Values are q.k~ * sm_scale.
+ *         token max(n - n_window, n_sink) + (j - n_sink - k_max); BLOCKS: as
+ *         DROP with 64 positions per sel entry (token 64 sel[i] + r at
+ *         position n_sink + 64 i + r) and the window after n_sink + 64 k_max;
+ *         positions that attend nothing hold -inf.  Values are q.k~ * sm_scale.
  *   workspace  kvc_workspace_bytes(KVC_OP_ATTEND, ...) bytes: split partials
  *         (and, for DROP/KEEP on INT4/INT1, the selection bitmap); contents
  *         on entry are ignored.

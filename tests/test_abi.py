@@ -112,6 +112,8 @@ def test_score_topk_and_accum_argument_checks():
     assert call(idx=None) == 1
     assert call(wsb=16) == 4 and call(ws=None) == 4
     assert call(mode=2) == 1             # external scores need ext
+    assert call(mode=1 | 16, kmax=0) == 0   # block ranking is a flag on a score mode
+    assert call(mode=3 | 16) == 1 and call(mode=32) == 1
     assert call(kmax=0) == 0             # nothing to select: no launch
     d.k_absmax = None
     assert call() == 1                   # critical channels need max|K|
@@ -127,4 +129,6 @@ def test_workspace_sizes():
     t = kvc.kvc_workspace_bytes(kvc.OP_SCORE_TOPK, d, 4)
     assert a1 > 0 and a2 > 0 and t >= 4096 * 8
     assert kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 4, 7, 0, 0, 0) == 0      # bad mode
+    a3 = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 4, 3, 61, 4, 64)          # blocks mode
+    assert a3 > a2                       # its plan spans 64 positions per kept block
     assert kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 36, 0, 0, 0, 0) == 0     # G = 36 > 8

@@ -242,7 +242,7 @@ def sparse_blocks(n_ctx: int = 131072, fmt: str = "fp16", top_blocks: int = 61,
     ranked by the mean score of each 64-token block, the top ``top_blocks``
     blocks kept (61 = 3% of the 2048 blocks at 128K), then attended (with the
     H2O update).  fmt "int4" stores the same keys and values as INT4 codes."""
-    w = sparse_crit8(n_ctx, seed=seed)
+    w = sparse_crit8(n_ctx, seed=seed, n_planted=min(512, n_ctx))
     tag = "128k" if n_ctx == 131072 else str(n_ctx)
     w.name = f"llama8b_layer_{fmt}_crit8_block{top_blocks}_{tag}"
     w.fmt = fmt
