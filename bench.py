@@ -87,6 +87,10 @@ def attend_bytes(w, lens, k_sel) -> int:
             w0 = max(n - w.n_window, min(w.n_sink, n))
             attended = min(w.n_sink, n) + int(k_sel[b]) + (n - w0)
             per_head = attended * (512 if fmt == "fp16" else CODE_BYTES[fmt])
+        elif w.mode == "blocks":   # k_sel blocks of 64 tokens (every candidate range holds them)
+            w0 = max(n - w.n_window, min(w.n_sink, n))
+            attended = min(w.n_sink, n) + 64 * int(k_sel[b]) + (n - w0)
+            per_head = attended * (512 if fmt == "fp16" else CODE_BYTES[fmt])
         else:   # keep: fp16 keep set, codes for the rest (tail rows fp16)
             w0 = max(n - w.n_window, min(w.n_sink, n))
             keep = min(w.n_sink, n) + int(k_sel[b]) + (n - w0)
@@ -94,7 +98,9 @@ def attend_bytes(w, lens, k_sel) -> int:
             per_head = keep * 512 + rest * CODE_BYTES[fmt]
         total += hkv * per_head
         if w.accumulate:                          # logits written
-            total += hq * (n if w.mode != "drop" else w.n_sink + int(w.top_k.max()) + w.n_window) * 4
+            pos = {"drop": w.n_sink + int(w.top_k.max()) + w.n_window,
+                   "blocks": w.n_sink + 64 * int(w.top_k.max()) + w.n_window}.get(w.mode, n)
+            total += hq * pos * 4
     total += B * hq * 128 * 2           # q
     total += B * hq * (128 + 1) * 4     # out + lse
     return total
@@ -202,16 +208,19 @@ def main():
         acc0 = np.zeros((w.batch, w.hkv, cap), np.float32)
         acc0[:, :, : w.acc.shape[2]] = w.acc[:, :, :cap]
         accs = [torch.from_numpy(acc0).to(dev) for _ in reps]
-        stride = w.n_sink + k_max + w.n_window if w.mode == "drop" else cap
+        stride = (w.n_sink + k_max + w.n_window if w.mode == "drop"
+                  else w.n_sink + 64 * k_max + w.n_window if w.mode == "blocks" else cap)
         logits = torch.empty(w.batch, w.hq, stride, device=dev)
     names = ["append"] + (["score_topk"] if sparse else []) + ["attend"] + (["accum"] if accs else [])
 
     def op_append(r, st):
         kvc.kvc_quantize_append(reps[r].desc, k_new, v_new, None, 1, None, st)
 
+    score_mode = (kvc.SCORE[w.score] | (kvc.SCORE_BLOCKS if w.granule == "block" else 0)) if sparse else 0
+
     def op_score_topk(r, st):
         ext = accs[r] if w.score == "external" else None
-        kvc.kvc_score_topk(reps[r].desc, q, w.hq, kvc.SCORE[w.score], w.n_crit, ext, w.n_sink,
+        kvc.kvc_score_topk(reps[r].desc, q, w.hq, score_mode, w.n_crit, ext, w.n_sink,
                            w.n_window, k_per_seq, k_max, sel, None, None, tk_ws, tk_bytes, st)
 
     def op_attend(r, st):

@@ -754,6 +754,10 @@ __device__ inline bool in_sel(const int32_t* sel, int k, int t) {
 template <bool QUANT>
 __device__ inline int2 plan_entry(const AttendArgs& a, int b, int g, int n, int p) {
   const kvc_cache& c = a.c;
+  // blocks mode on codes: the kept blocks are the quantized role's, so this
+  // role's positions are the sinks and the window only (position p past the
+  // sinks stands for logits position p + 64 k_max)
+  if (QUANT && a.mode == KVC_ATTEND_BLOCKS && p >= a.n_sink) p += a.nsel;
   const int nq = QUANT ? (n & ~(GS - 1)) : 0;
   const int nset = a.n_sink + a.nsel + a.n_window;
   const int w0 = window_start(n, a.n_sink, a.n_window);
@@ -916,7 +920,8 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
         if constexpr (LOGITS) {
           if (hv && (on || (drop && tv == ROW_NONE))) {
             const int t = tv <= -3 ? -3 - tv : tv;
-            const int pos = drop ? p0 + 4 * kb + j : t;
+            const int pp = p0 + 4 * kb + j;
+            const int pos = !drop ? t : (QUANT && a.mode == KVC_ATTEND_BLOCKS && pp >= a.n_sink) ? pp + a.nsel : pp;
             a.logits[((int64_t)b * a.hq + g * G + col) * a.logits_stride + pos] =
                 on ? sc[j] * a.sm : -INFINITY;
           }
@@ -1121,6 +1126,16 @@ __global__ __launch_bounds__(256) void plan_kernel(AttendArgs a) {
                                  : e < ns + nl ? min(max(sel[l0 + e - ns], blo), bhi - 1)
                                                : ws + (e - ns - nl);
     if (e == 0) a.gcount[pi] = cnt;
+    // logits positions of sel entries that name no candidate block attend nothing
+    if (a.logits) {
+      const int G = a.G;
+      for (int q = e; q < GS * a.k_max; q += gridDim.x * 256) {
+        const int blk = sel[q / GS];
+        if (blk >= blo && blk < bhi) continue;
+        for (int h = 0; h < G; ++h)
+          a.logits[((int64_t)b * a.hq + g * G + h) * a.logits_stride + a.n_sink + q] = -INFINITY;
+      }
+    }
   }
   if (e < a.np) a.rplan[pi * a.np + e] = plan_entry<QUANT>(a, b, g, n, e);
 }
@@ -1187,10 +1202,18 @@ int env_int(const char* name, int dflt) {
   return v && *v ? atoi(v) : dflt;
 }
 
-// Positions of the fp16-rows role per (sequence, KV head) in drop / keep mode.
-int rows_positions(int mode, int k_max, int n_sink, int n_window) {
-  const int nsel = mode == KVC_ATTEND_BLOCKS ? GS * k_max : k_max;
+// Positions of the fp16-rows role per (sequence, KV head) in drop / keep /
+// blocks mode (blocks mode on codes: sinks and window only).
+int rows_positions(int mode, int k_max, int n_sink, int n_window, bool quant) {
+  const int nsel = mode != KVC_ATTEND_BLOCKS ? k_max : quant ? 0 : GS * k_max;
   return n_sink + nsel + n_window + (mode == KVC_ATTEND_KEEP ? GS : 0);
+}
+
+int walk_groups(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window) {
+  const int all = c.max_tokens / GS;
+  if (mode != KVC_ATTEND_BLOCKS) return all;
+  const int64_t w = (int64_t)k_max + (n_sink + GS - 1) / GS + (n_window + GS - 1) / GS + 1;
+  return (int)std::min<int64_t>(all, w);
 }
 
 Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window) {
@@ -1201,10 +1224,12 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   // one four-wave workgroup per CU: measured on the 128K layers, fewer
   // concurrent streams keep the DRAM pages open longer and beat two per CU
   const int target = env_int("KVC_ATTEND_TARGET_WG", 256);
+  // groups the quantized role may walk per pair: every group, or in blocks
+  // mode the kept blocks plus the groups holding sinks or window tokens
+  const int groups = walk_groups(c, mode, k_max, n_sink, n_window);
   if (quant) {
     // dense: every pair is planned at capacity; drop / keep: four times the
     // workgroups, of which a pair uses what its length needs
-    const int groups = c.max_tokens / GS;
     const int64_t waves = (int64_t)(mode == KVC_ATTEND_DENSE ? target : 4 * target) * NW;
     p.gpw = (int)std::max<int64_t>(1, ((int64_t)groups * pairs + waves - 1) / waves);
     // blocks mode: a wave's list entries fit in one register (<= 64 groups)
@@ -1213,7 +1238,7 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   }
   int64_t np;
   if (mode == KVC_ATTEND_DENSE) np = quant ? GS : c.max_tokens;
-  else np = rows_positions(mode, k_max, n_sink, n_window);
+  else np = rows_positions(mode, k_max, n_sink, n_window, quant);
   const int64_t tiles = std::max<int64_t>(1, (np + TILE - 1) / TILE);
   // a dense quantized cache leaves only its tail (< 64 tokens) to this role
   const int64_t rwaves = (quant && mode == KVC_ATTEND_DENSE) ? (int64_t)pairs * NW
@@ -1222,7 +1247,7 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   p.ppw = (int)(tpw * TILE);
   p.s_r = (int)((tiles + NW * tpw - 1) / (NW * tpw));
   while (p.s_q + p.s_r > MAX_SPLITS) {   // bound the merge's work per query head
-    if (p.s_q >= p.s_r && (mode != KVC_ATTEND_BLOCKS || 2 * p.gpw <= LIST_MAX)) { p.gpw *= 2; p.s_q = (c.max_tokens / GS + NW * p.gpw - 1) / (NW * p.gpw); }
+    if (p.s_q >= p.s_r && (mode != KVC_ATTEND_BLOCKS || 2 * p.gpw <= LIST_MAX)) { p.gpw *= 2; p.s_q = (groups + NW * p.gpw - 1) / (NW * p.gpw); }
     else if (p.s_r > 1) { p.ppw *= 2; p.s_r = (int)((tiles * TILE + (int64_t)NW * p.ppw - 1) / ((int64_t)NW * p.ppw)); }
     else break;   // (blocks mode on a cache too long for its list registers: rejected by the caller)
   }
@@ -1269,7 +1294,8 @@ size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, i
   if (mode != KVC_ATTEND_DENSE && c.format != KVC_FMT_FP16)   // selection bitmap + prefix
     bytes += 2 * (size_t)c.batch * c.num_kv_heads * (c.max_tokens / 32) * sizeof(uint32_t);
   if (mode != KVC_ATTEND_DENSE)                               // fp16-rows role plan
-    bytes += (size_t)c.batch * c.num_kv_heads * rows_positions(mode, k_max, n_sink, n_window) * sizeof(int2);
+    bytes += (size_t)c.batch * c.num_kv_heads *
+             rows_positions(mode, k_max, n_sink, n_window, c.format != KVC_FMT_FP16) * sizeof(int2);
   if (mode == KVC_ATTEND_BLOCKS && c.format != KVC_FMT_FP16)   // group list + count
     bytes += (size_t)c.batch * c.num_kv_heads * (c.max_tokens / GS + 1) * sizeof(int32_t);
   return bytes;
@@ -1279,7 +1305,7 @@ bool attend_plan_ok(const kvc_cache& c, int mode, int k_max, int n_sink, int n_w
   const Plan p = plan_attend(c, mode, k_max, n_sink, n_window);
   if (p.s_q + p.s_r > MAX_SPLITS) return false;
   if (mode == KVC_ATTEND_BLOCKS && c.format != KVC_FMT_FP16)
-    return (int64_t)p.s_q * waves_per_wg(c.format) * LIST_MAX >= c.max_tokens / GS;
+    return (int64_t)p.s_q * waves_per_wg(c.format) * LIST_MAX >= walk_groups(c, mode, k_max, n_sink, n_window);
   return true;
 }
 
@@ -1307,7 +1333,7 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   a.sbits = nullptr;
   a.spre = nullptr;
   a.rplan = nullptr;
-  a.np = mode == KVC_ATTEND_DENSE ? 0 : rows_positions(mode, k_max, n_sink, n_window);
+  a.np = mode == KVC_ATTEND_DENSE ? 0 : rows_positions(mode, k_max, n_sink, n_window, c.format != KVC_FMT_FP16);
   a.nsel = mode == KVC_ATTEND_BLOCKS ? GS * k_max : k_max;
   a.glist = nullptr;
   a.gcount = nullptr;
