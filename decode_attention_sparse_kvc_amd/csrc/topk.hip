@@ -59,6 +59,8 @@ struct TopkArgs {
   int32_t* krem;       // [B][Hkv] keys still to take from the current bucket
   int32_t* done;       // [B][Hkv] 0, or 8p once pass p found its bucket taken whole
   int hist_words;      // histogram words per pair that prep clears (all passes, or pass 0 only)
+  double* qsel;        // critical mode: [B][Hkv][GMAX][128] q of the group's heads on the
+                       // channel list (slot k = k-th critical channel), fp64
   bool blocks;         // rank 64-token blocks (items = block ids)
   double* tscore;      // block mode: [B][Hkv][max_tokens] token scores
 };
@@ -101,29 +103,47 @@ __global__ __launch_bounds__(D) void prep_kernel(TopkArgs a) {
   __shared__ double s[D];
   __shared__ int chosen[D];
   if (a.mode == KVC_SCORE_CRITICAL) {
-    double qm = 0.0;
+    // every load is issued before any is used: heads past the group re-read
+    // head 0 (the maximum is unchanged), so no load sits behind a branch
+    const float kabs_f = a.c.k_absmax[pi * D + c];
     const uint16_t* qg = a.q + ((int64_t)b * a.hq + g * a.G) * D + c;
+    uint16_t qh[GMAX_PREP];
 #pragma unroll
-    for (int hh = 0; hh < GMAX_PREP; ++hh)   // the group's loads issued together
-      if (hh < a.G) qm = fmax(qm, fabs((double)h2f(qg[hh * D])));
-    const double kabs = (double)a.c.k_absmax[pi * D + c];
+    for (int hh = 0; hh < GMAX_PREP; ++hh) qh[hh] = qg[(hh < a.G ? hh : 0) * D];
+    double qm = 0.0;
+#pragma unroll
+    for (int hh = 0; hh < GMAX_PREP; ++hh) qm = fmax(qm, fabs((double)h2f(qh[hh])));
+    const double kabs = (double)kabs_f;
     s[c] = __dmul_rn(qm, kabs);
     __syncthreads();
+    // rank of channel c under (s desc, c asc); the LDS reads are independent
+    const double sc = s[c];
     int rank = 0;
-    for (int o = 0; o < D; ++o) rank += (s[o] > s[c]) || (s[o] == s[c] && o < c);
-    chosen[c] = rank < a.n_crit;
+#pragma unroll 32
+    for (int o = 0; o < D; ++o) {
+      const double so = s[o];
+      rank += (so > sc) || (so == sc && o < c);
+    }
+    // position in the ascending list: chosen channels below c (ballots of the two waves)
+    const bool mine = rank < a.n_crit;
+    const uint64_t bal = __ballot(mine);
+    if ((c & 63) == 0) chosen[c >> 6] = __popcll(bal);
     __syncthreads();
-    if (chosen[c]) {
-      int pos = 0;
-      for (int o = 0; o < c; ++o) pos += chosen[o];
+    if (mine) {
+      const int pos = __popcll(bal & ((1ull << (c & 63)) - 1ull)) + (c >= 64 ? chosen[0] : 0);
       a.channels[pi * D + pos] = c;
       if (a.out_channels) a.out_channels[pi * a.n_crit + pos] = c;
+      // the scoring kernel's q operands, so it needs no gather through the list
+#pragma unroll
+      for (int hh = 0; hh < GMAX_PREP; ++hh)
+        if (hh < a.G) a.qsel[(pi * GMAX_PREP + hh) * D + pos] = (double)h2f(qh[hh]);
     }
   }
 }
 
 // ------------------------------------------------------------------ score
 constexpr int GMAX = 16;       // query heads per KV head supported by scoring
+static_assert(GMAX == GMAX_PREP, "prep writes the q operands the scoring kernel reads");
 constexpr int CB_CRIT = 8;     // channels whose loads are issued together (critical channels)
 constexpr int CB_EXACT = 32;   // (every channel)
 
@@ -202,10 +222,12 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
     smeta[(tid / 64) * D + 2 * j] = (s2 & 0xFFFFu) | (z2 << 16);
     smeta[(tid / 64) * D + 2 * j + 1] = (s2 >> 16) | (z2 & 0xFFFF0000u);
   }
-  __syncthreads();
+  // q on the channel list: gathered by prep (critical mode) or channel k itself
   for (int e = tid; e < G * nch; e += ST) {
     const int hh = e / nch, k = e % nch;
-    sq[hh * D + k] = (double)h2f(a.q[((int64_t)b * a.hq + g * G + hh) * D + sch[k]]);
+    sq[hh * D + k] = a.mode == KVC_SCORE_CRITICAL
+                         ? a.qsel[(pi * GMAX + hh) * D + k]
+                         : (double)h2f(a.q[((int64_t)b * a.hq + g * G + hh) * D + k]);
   }
   __syncthreads();
 
@@ -473,6 +495,7 @@ __device__ inline int block_exclusive_scan(int v, int* s, int& total) {
   return before + x - v;
 }
 
+constexpr int EPR = 8;   // bitmap words a thread loads at once
 __global__ __launch_bounds__(ET) void emit_kernel(TopkArgs a) {
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int64_t pi = pair_index(a, b, g);
@@ -485,12 +508,39 @@ __global__ __launch_bounds__(ET) void emit_kernel(TopkArgs a) {
   const uint32_t* ab = a.above + pi * words;
   const uint32_t* eq = a.equal + pi * words;
   int32_t* out = a.out_idx + pi * a.k_max;
-  // how many equal keys to take: k - #above
+  // how many equal keys to take: k - #above.  A thread's words are read
+  // EPR at a time with every load issued before any is used; the first EPR
+  // (all of them for caches up to 256K tokens) are read once and kept in
+  // registers for the three passes below.
+  typedef uint32_t Words[EPR];
+  auto load_chunk = [&](int base, Words& x, Words& y) {
+#pragma unroll
+    for (int i = 0; i < EPR; ++i) {
+      x[i] = base + i < wb ? ab[base + i] : 0u;
+      y[i] = base + i < wb ? eq[base + i] : 0u;
+    }
+  };
+  Words ab0, eq0;
+  load_chunk(wa, ab0, eq0);
+  auto for_chunks = [&](auto&& f) {
+    for (int base = wa; base < wb; base += EPR) {
+      if (base == wa) {
+        f(base, ab0, eq0);
+      } else {
+        Words x, y;
+        load_chunk(base, x, y);
+        f(base, x, y);
+      }
+    }
+  };
   int n_ab = 0, n_eq = 0;
-  for (int wd = wa; wd < wb; ++wd) {
-    n_ab += __popc(ab[wd]);
-    n_eq += __popc(eq[wd]);
-  }
+  for_chunks([&](int, Words& abw, Words& eqw) {
+#pragma unroll
+    for (int i = 0; i < EPR; ++i) {
+      n_ab += __popc(abw[i]);
+      n_eq += __popc(eqw[i]);
+    }
+  });
   int tot_ab, tot_eq;
   block_exclusive_scan(n_ab, s, tot_ab);
   const int eq_before = block_exclusive_scan(n_eq, s, tot_eq);
@@ -498,37 +548,43 @@ __global__ __launch_bounds__(ET) void emit_kernel(TopkArgs a) {
   // selected = above | (first take_eq equal bits by index)
   int n_sel = 0;
   int eq_seen = eq_before;
-  for (int wd = wa; wd < wb; ++wd) {
-    uint32_t e = eq[wd];
-    uint32_t keep = 0u;
-    while (e && eq_seen < take_eq) {
-      const uint32_t bit = e & (0u - e);
-      keep |= bit;
-      e ^= bit;
-      ++eq_seen;
+  for_chunks([&](int, Words& abw, Words& eqw) {
+#pragma unroll
+    for (int i = 0; i < EPR; ++i) {
+      uint32_t e = eqw[i];
+      uint32_t keep = 0u;
+      while (e && eq_seen < take_eq) {
+        const uint32_t bit = e & (0u - e);
+        keep |= bit;
+        e ^= bit;
+        ++eq_seen;
+      }
+      n_sel += __popc(abw[i] | keep);
     }
-    n_sel += __popc(ab[wd] | keep);
-  }
+  });
   int total;
   int pos = block_exclusive_scan(n_sel, s, total);
   eq_seen = eq_before;
-  for (int wd = wa; wd < wb; ++wd) {
-    uint32_t e = eq[wd];
-    uint32_t keep = 0u;
-    while (e && eq_seen < take_eq) {
-      const uint32_t bit = e & (0u - e);
-      keep |= bit;
-      e ^= bit;
-      ++eq_seen;
+  for_chunks([&](int base, Words& abw, Words& eqw) {
+#pragma unroll
+    for (int i = 0; i < EPR; ++i) {
+      uint32_t e = eqw[i];
+      uint32_t keep = 0u;
+      while (e && eq_seen < take_eq) {
+        const uint32_t bit = e & (0u - e);
+        keep |= bit;
+        e ^= bit;
+        ++eq_seen;
+      }
+      uint32_t m = abw[i] | keep;
+      while (m) {
+        const int j = __ffs(m) - 1;
+        m &= m - 1;
+        if (pos < a.k_max) out[pos] = (base + i) * 32 + j;
+        ++pos;
+      }
     }
-    uint32_t m = ab[wd] | keep;
-    while (m) {
-      const int i = __ffs(m) - 1;
-      m &= m - 1;
-      if (pos < a.k_max) out[pos] = wd * 32 + i;
-      ++pos;
-    }
-  }
+  });
   for (int e = total + tid; e < a.k_max; e += ET) out[e] = -1;
 }
 
@@ -671,6 +727,7 @@ size_t topk_workspace_bytes(const kvc_cache& c) {
   const size_t pairs = (size_t)c.batch * c.num_kv_heads;
   const size_t words = c.max_tokens / 32;
   size_t bytes = 2 * pairs * c.max_tokens * sizeof(uint64_t);   // keys, block-mode token scores
+  bytes += pairs * GMAX * D * sizeof(double);                    // critical-mode q operands
   bytes += pairs * HSTRIDE * sizeof(uint32_t);
   bytes += 2 * pairs * words * sizeof(uint32_t);
   bytes += pairs * D * sizeof(int32_t);
@@ -706,6 +763,8 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   p += pairs * c.max_tokens * sizeof(uint64_t);
   a.tscore = reinterpret_cast<double*>(p);
   p += pairs * c.max_tokens * sizeof(double);
+  a.qsel = reinterpret_cast<double*>(p);
+  p += pairs * GMAX * D * sizeof(double);
   a.hist = reinterpret_cast<uint32_t*>(p);
   p += pairs * HSTRIDE * sizeof(uint32_t);
   a.above = reinterpret_cast<uint32_t*>(p);
