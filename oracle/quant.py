@@ -104,3 +104,57 @@ def dequant_values(code, s, z) -> np.ndarray:
     rep_s = np.repeat(s, GROUP, axis=1)
     rep_z = np.repeat(z, GROUP, axis=1)
     return dequantize(code, rep_s, rep_z)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) warm tier.  Meeting-LLM article, section 6.2: the warm (L2) tier
+# prefers FP8 E4M3/E5M2 over INT4 where the hardware supports it natively; KV
+# compression survey, section 2: an FP8 E4M3/E5M2 KV cache halves memory and
+# doubles bandwidth without reworking the dequantization.
+# Readings taken (listed in the design doc):
+#   * E4M3 as the OCP 8-bit format: 1 sign, 4 exponent (bias 7), 3 mantissa
+#     bits, subnormals, no infinities, largest finite 448.
+#   * A plain per-element cast (no scale: the pages need no new dequantization),
+#     round to nearest with ties to the even code, saturating at +-448; the sign
+#     of zero is kept.
+#   * Every token is encoded when appended (no groups, no fp16 tail).
+# ---------------------------------------------------------------------------
+
+def _fp8_magnitudes() -> np.ndarray:
+    """Exact value of every non-negative finite E4M3 code 0x00..0x7E (index = code)."""
+    vals = []
+    for c in range(0x7F):
+        e, m = c >> 3, c & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (8 + m) * 2.0 ** (e - 10))
+    return np.array(vals, dtype=np.float64)
+
+
+FP8_MAG = _fp8_magnitudes()
+
+
+def encode_fp8(x16: np.ndarray) -> np.ndarray:
+    """fp16 -> E4M3 code: the nearest grid value, ties to the even code, saturating.
+
+    A brute-force search over the 127 magnitudes (exact in fp64: every fp16 and
+    every E4M3 value is a short dyadic rational).
+    """
+    x = np.asarray(x16, dtype=np.float16)
+    assert np.all(np.isfinite(x))
+    a = np.abs(x.astype(np.float64)).reshape(-1)
+    d = np.abs(a[:, None] - FP8_MAG[None, :])                  # [n, 127]
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best                                             # one or two nearest codes
+    codes = np.arange(0x7F)
+    odd = (codes & 1).astype(bool)[None, :]
+    pick = np.where(cand & ~odd, codes[None, :], 0x7F).min(axis=1)   # an even nearest code
+    pick = np.where(pick == 0x7F, np.where(cand, codes[None, :], 0x7F).min(axis=1), pick)
+    pick = np.where(a > FP8_MAG[-1], 0x7E, pick)                # saturate
+    sign = np.signbit(x).reshape(-1).astype(np.int64) << 7
+    return (pick | sign).astype(np.uint8).reshape(x.shape)
+
+
+def decode_fp8(code: np.ndarray) -> np.ndarray:
+    """E4M3 code -> exact value (fp64)."""
+    c = np.asarray(code, dtype=np.int64)
+    mag = FP8_MAG[np.minimum(c & 0x7F, 0x7E)]
+    return np.where(c & 0x80, -mag, mag)

@@ -12,6 +12,7 @@ buffer beside an fp16 buffer of the key tokens):
   * fp16 format: every token is fp16.
   * int4 / int1, dense or drop mode: tokens of complete 64-token groups are
     dequantized codes, the incomplete last group is fp16.
+  * fp8: every token is its E4M3 codes, decoded (encoded when appended).
   * keep mode: sinks, selected tokens and the recent window are fp16; the rest
     as in dense mode.
 """
@@ -50,7 +51,9 @@ def build_head_cache(k16: np.ndarray, v16: np.ndarray, fmt: str) -> HeadCache:
     n = k16.shape[0]
     kabs = np.abs(k16).max(axis=0) if n else np.zeros(k16.shape[1], np.float16)
     hc = HeadCache(n=n, nq=n, k16=k16, v16=v16, kabs=kabs.astype(np.float16))
-    if fmt in BITS:
+    if fmt == "fp8":
+        hc.k_code, hc.v_code = Q.encode_fp8(k16), Q.encode_fp8(v16)
+    elif fmt in BITS:
         b = BITS[fmt]
         hc.k_code, hc.k_scale, hc.k_zero = Q.quantize_keys(k16, b)
         hc.v_code, hc.v_scale, hc.v_zero = Q.quantize_values(v16, b)
@@ -62,7 +65,10 @@ def token_rows(hc: HeadCache, fp16_mask: Optional[np.ndarray] = None) -> Tuple[n
     """fp64 K~, V~ [n, D]: dequantized for quantized tokens, fp16 values otherwise."""
     keys = hc.k16.astype(np.float64)
     vals = hc.v16.astype(np.float64)
-    if hc.k_code is not None and hc.nq:
+    if hc.k_code is not None and hc.k_scale is None:   # fp8: every row from its codes
+        keys = Q.decode_fp8(hc.k_code)
+        vals = Q.decode_fp8(hc.v_code)
+    elif hc.k_code is not None and hc.nq:
         kq = Q.dequant_keys(hc.k_code, hc.k_scale, hc.k_zero)
         vq = Q.dequant_values(hc.v_code, hc.v_scale, hc.v_zero)
         quant = np.ones(hc.nq, dtype=bool)

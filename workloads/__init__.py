@@ -42,7 +42,7 @@ class Workload:
     """
     name: str
     seed: int
-    fmt: str                 # "int4" | "int1" | "fp16"
+    fmt: str                 # "int4" | "int1" | "fp16" | "fp8"
     batch: int
     hq: int
     hkv: int
@@ -189,6 +189,13 @@ def int4_dense(n_ctx: int = 32768, seed: int = 1) -> Workload:
     return _llama_dense(f"llama8b_layer_int4_dense_{tag}", "int4", n_ctx, seed, True)
 
 
+def fp8_dense(n_ctx: int = 131072, seed: int = 1) -> Workload:
+    """FP8 (E4M3) warm tier: the INT4 layer's draws (seed 1, same outliers) stored
+    as E4M3 codes, dense decode."""
+    tag = "32k" if n_ctx == 32768 else ("128k" if n_ctx == 131072 else str(n_ctx))
+    return _llama_dense(f"llama8b_layer_fp8_dense_{tag}", "fp8", n_ctx, seed, True)
+
+
 def int1_dense(n_ctx: int = 131072, seed: int = 2) -> Workload:
     """TailorKV quantization-friendly layer: 1-bit K and V, dense decode (seed 2)."""
     tag = "128k" if n_ctx == 131072 else str(n_ctx)
@@ -308,4 +315,5 @@ FULL = {
     "batch16_ragged_paged_int4_keep_fp16": lambda: batched_joint(),
     "llama8b_layer_fp16_crit8_block61_128k": lambda: sparse_blocks(131072, "fp16"),
     "llama8b_layer_int4_crit8_block61_128k": lambda: sparse_blocks(131072, "int4"),
+    "llama8b_layer_fp8_dense_128k": lambda: fp8_dense(131072),
 }
