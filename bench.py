@@ -26,7 +26,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "llama8b_layer_int4_dense_128k"
-CODE_BYTES = {"int4": 144, "int1": 48}      # per token per KV head, incl. amortized K meta
+CODE_BYTES = {"int4": 144, "int1": 48, "fp8": 256}   # per token per KV head, incl. amortized K meta
 GRAPH_CALLS = 8                             # at least this many steps (or calls) per replayed graph
 
 
@@ -80,7 +80,7 @@ def attend_bytes(w, lens, k_sel) -> int:
     total = 0
     for b, n in enumerate(lens):
         n = int(n)
-        nq = (n // 64) * 64
+        nq = (n // 64) * 64 if fmt != "fp8" else n     # fp8 has no fp16 tail
         if w.mode == "dense":
             per_head = nq * CODE_BYTES[fmt] + (n - nq) * 512 if fmt != "fp16" else n * 512
         elif w.mode == "drop":

@@ -13,11 +13,11 @@ import torch
 
 from . import kvc
 
-_BYTES_PER_SLOT = {"int4": 64, "int1": 16}   # code bytes per token per KV head (K or V)
+_BYTES_PER_SLOT = {"int4": 64, "int1": 16, "fp8": 128}   # code bytes per token per KV head (K or V)
 
 
 class KvcCache:
-    """Buffers + descriptor.  ``fmt`` in {"fp16", "int4", "int1"}.
+    """Buffers + descriptor.  ``fmt`` in {"fp16", "int4", "int1", "fp8"}.
 
     page_size 0 is a contiguous cache; otherwise ``block_table`` [B, max_pages]
     (int32, physical page ids) and ``num_pages`` describe the page pools.
@@ -48,7 +48,10 @@ class KvcCache:
         self.seq_lens = torch.zeros(batch, dtype=torch.int32, **z)
         self.k_codes = self.v_codes = self.k_meta = self.v_meta = None
         self.k_tail = self.v_tail = self.k16 = self.v16 = self.kT = None
-        if fmt != "fp16":
+        if fmt == "fp8":   # E4M3 rows only: no groups, metadata or tail
+            self.k_codes = torch.zeros(slots * _BYTES_PER_SLOT[fmt], dtype=torch.uint8, **z)
+            self.v_codes = torch.zeros_like(self.k_codes)
+        elif fmt != "fp16":
             nb = slots * _BYTES_PER_SLOT[fmt]
             self.k_codes = torch.zeros(nb, dtype=torch.uint8, **z)
             self.v_codes = torch.zeros(nb, dtype=torch.uint8, **z)

@@ -15,7 +15,7 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 kvc_status check_cache(const kvc_cache* c) {
   if (!c) return KVC_ERR_INVALID;
   if (c->abi_version != KVC_ABI_VERSION) return KVC_ERR_INVALID;
-  if (c->format < KVC_FMT_FP16 || c->format > KVC_FMT_INT1) return KVC_ERR_UNSUPPORTED;
+  if (c->format < KVC_FMT_FP16 || c->format > KVC_FMT_FP8) return KVC_ERR_UNSUPPORTED;
   if (c->head_dim != KVC_HEAD_DIM || c->group_size != KVC_GROUP) return KVC_ERR_UNSUPPORTED;
   if (c->batch < 1 || c->num_kv_heads < 1) return KVC_ERR_SHAPE;
   if (c->max_tokens < KVC_GROUP || c->max_tokens % KVC_GROUP) return KVC_ERR_SHAPE;
@@ -30,6 +30,9 @@ kvc_status check_cache(const kvc_cache* c) {
   }
   if (c->format == KVC_FMT_FP16) {
     if (!c->k16 || !c->v16) return KVC_ERR_INVALID;
+  } else if (c->format == KVC_FMT_FP8) {
+    if (!c->k_codes || !c->v_codes || !aligned(c->k_codes, 16) || !aligned(c->v_codes, 16))
+      return KVC_ERR_INVALID;
   } else {
     if (!c->k_codes || !c->v_codes || !c->k_meta || !c->v_meta || !c->k_tail || !c->v_tail)
       return KVC_ERR_INVALID;
@@ -62,7 +65,7 @@ kvc_status check_attend_args(const kvc_cache* c, int32_t hq, int32_t mode, const
     if (k_max > 0 && !sel && !sizing_only) return KVC_ERR_INVALID;
     if (sel && !aligned(sel, 4)) return KVC_ERR_INVALID;
   }
-  if (mode == KVC_ATTEND_KEEP && (c->format == KVC_FMT_FP16 || !c->k16)) return KVC_ERR_UNSUPPORTED;
+  if (mode == KVC_ATTEND_KEEP && (!grouped(c->format) || !c->k16)) return KVC_ERR_UNSUPPORTED;
   if (!attend_plan_ok(*c, mode, k_max, n_sink, n_window)) return KVC_ERR_UNSUPPORTED;
   return KVC_OK;
 }

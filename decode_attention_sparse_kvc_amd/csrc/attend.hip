@@ -794,6 +794,24 @@ __device__ inline int2 plan_entry(const AttendArgs& a, int b, int g, int n, int 
   return ok ? int2{tail_code(t), tail_row + (t - nq)} : int2{ROW_SKIP, 0};
 }
 
+// 32 E4M3 codes (two 16-byte words, channels in byte order) -> 32 fp16 values
+// / 256 in four 16-byte words: a byte permute spreads two codes into the low
+// bytes of the two halves of a dword, then one shift-mask pair per field.
+__device__ inline uint32_t fp8_pair(uint32_t x) {   // x = [c0, 0, c1, 0]
+  return ((x & 0x007F007Fu) << 7) | ((x & 0x00800080u) << 8);
+}
+__device__ inline void fp8_row_decode(uint4 r0, uint4 r1, uint4* out) {
+  const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = w[2 * i], b = w[2 * i + 1];
+    out[i] = uint4{fp8_pair(__builtin_amdgcn_perm(0u, a, 0x0c010c00u)),
+                   fp8_pair(__builtin_amdgcn_perm(0u, a, 0x0c030c02u)),
+                   fp8_pair(__builtin_amdgcn_perm(0u, b, 0x0c010c00u)),
+                   fp8_pair(__builtin_amdgcn_perm(0u, b, 0x0c030c02u))};
+  }
+}
+
 // One 16-row tile in registers: lane (row, kb) holds channels [32kb, 32kb+32)
 // of its row, of K (the matrix-core A operand of S = K q) and of V (staged
 // through LDS into the transposed A operand of O^T = V^T P^T).
@@ -818,7 +836,11 @@ __device__ inline int vt_off(int t, int chunk) { return t * D + ((chunk ^ (t >> 
 template <int FMT, bool DENSE, bool LOGITS>
 __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int rsplit, int lane, int w,
                                           float* sO, float* sML, int* sTok) {
-  constexpr bool QUANT = FMT != KVC_FMT_FP16;
+  constexpr bool QUANT = grouped(FMT);
+  constexpr bool FP8 = FMT == KVC_FMT_FP8;
+  // FP8 rows enter the matrix cores as value / 256 (exact fp16); scores and
+  // outputs are scaled back by 256
+  constexpr float RS = FP8 ? 256.f : 1.f;
   constexpr int NW = waves_per_wg(FMT);
   const kvc_cache& c = a.c;
   const int n = max(c.seq_lens[b], 0);
@@ -887,13 +909,23 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
     const uint16_t* vsafe = c.v16 ? c.v16 : c.v_tail;
     auto load_rows = [&](int2 e, RowTile& d, int* tok) {
       const bool on = row_on(e.x);
-      const int64_t off = (int64_t)e.y * D + 32 * kb;
-      const uint4* kq = reinterpret_cast<const uint4*>(on ? (e.x <= -3 ? c.k_tail : c.k16) + off : ksafe);
-      const uint4* vq = reinterpret_cast<const uint4*>(on ? (e.x <= -3 ? c.v_tail : c.v16) + off : vsafe);
+      if constexpr (FP8) {   // 32 codes of the row: two 16-byte loads each for K and V
+        const int64_t off = (int64_t)e.y * D + 32 * kb;
+        const uint4* kq = reinterpret_cast<const uint4*>(c.k_codes + (on ? off : 0));
+        const uint4* vq = reinterpret_cast<const uint4*>(c.v_codes + (on ? off : 0));
+        d.k[0] = kq[0];
+        d.k[1] = kq[1];
+        d.v[0] = vq[0];
+        d.v[1] = vq[1];
+      } else {
+        const int64_t off = (int64_t)e.y * D + 32 * kb;
+        const uint4* kq = reinterpret_cast<const uint4*>(on ? (e.x <= -3 ? c.k_tail : c.k16) + off : ksafe);
+        const uint4* vq = reinterpret_cast<const uint4*>(on ? (e.x <= -3 ? c.v_tail : c.v16) + off : vsafe);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) d.k[k] = kq[k];
+        for (int k = 0; k < 4; ++k) d.k[k] = kq[k];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) d.v[k] = vq[k];
+        for (int k = 0; k < 4; ++k) d.v[k] = vq[k];
+      }
       if (lane < TILE) tok[lane] = e.x;
     };
     auto compute = [&](int i, const RowTile& d, const int* tok) {
@@ -904,13 +936,25 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
       const int mine = tok[row];                                      // code of the row this lane stages
       if (__ballot(row_on(mine) || (LOGITS && drop && mine == ROW_NONE)) == 0)
         return;   // a tile of empty positions (past a shorter selection)
+      uint4 kr[4], vr[4];   // the tile's fp16 operands (FP8: decoded here, not at load)
+      if constexpr (FP8) {
+        fp8_row_decode(d.k[0], d.k[1], kr);
+        fp8_row_decode(d.v[0], d.v[1], vr);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          kr[k] = d.k[k];
+          vr[k] = d.v[k];
+        }
+      }
       // stage V (empty rows were read from a valid row; their p is 0)
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<uint4*>(vt + vt_off(row, 4 * kb + k)) = row_on(mine) ? d.v[k] : uint4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<uint4*>(vt + vt_off(row, 4 * kb + k)) = row_on(mine) ? vr[k] : uint4{0u, 0u, 0u, 0u};
       f4 sc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) sc = mfma32(bc<h8>(d.k[k]), qb[k], sc);
+      for (int k = 0; k < 4; ++k) sc = mfma32(bc<h8>(kr[k]), qb[k], sc);
+      if constexpr (FP8) sc *= RS;
       float x[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -989,7 +1033,7 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
   if (hv) {
     float* oh = sO + (w * 8 + col) * D;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) *reinterpret_cast<f4*>(oh + 16 * ct + 4 * kb) = acc[ct];
+    for (int ct = 0; ct < 8; ++ct) *reinterpret_cast<f4*>(oh + 16 * ct + 4 * kb) = acc[ct] * RS;
   }
   if (hv && kb == 0) {
     sML[(w * 8 + col) * 2] = m;
@@ -1031,7 +1075,7 @@ void attend_kernel(AttendArgs a) {
   const int G = a.G;
   // (every wave of either role writes its sO / sML slots of heads < G)
 
-  if constexpr (FMT != KVC_FMT_FP16) {
+  if constexpr (grouped(FMT)) {
     if (split < a.s_q)
       quant_role<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, split, lane, w, sO, sML, sKm, sVm);
     else
@@ -1220,7 +1264,7 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   Plan p{0, 0, 1, TILE};
   const int NW = waves_per_wg(c.format);
   const int pairs = c.batch * c.num_kv_heads;
-  const bool quant = c.format != KVC_FMT_FP16;
+  const bool quant = grouped(c.format);
   // one four-wave workgroup per CU: measured on the 128K layers, fewer
   // concurrent streams keep the DRAM pages open longer and beat two per CU
   const int target = env_int("KVC_ATTEND_TARGET_WG", 256);
@@ -1258,7 +1302,7 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
 // caches have no quantized role, and only INT4 has 16-token tiles.
 template <int F, bool DN, bool LG>
 void launch_inst(dim3 grid, hipStream_t s, const AttendArgs& a, bool pk, bool tiled) {
-  if constexpr (F == KVC_FMT_FP16) {
+  if constexpr (!grouped(F)) {
     attend_kernel<F, DN, LG, false, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
   } else if constexpr (F == KVC_FMT_INT4) {
     if (tiled) {
@@ -1291,12 +1335,12 @@ size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, i
                               int n_window) {
   const Plan p = plan_attend(c, mode, k_max, n_sink, n_window);
   size_t bytes = (size_t)c.batch * hq * (p.s_q + p.s_r) * PART * sizeof(float);
-  if (mode != KVC_ATTEND_DENSE && c.format != KVC_FMT_FP16)   // selection bitmap + prefix
+  if (mode != KVC_ATTEND_DENSE && grouped(c.format))   // selection bitmap + prefix
     bytes += 2 * (size_t)c.batch * c.num_kv_heads * (c.max_tokens / 32) * sizeof(uint32_t);
   if (mode != KVC_ATTEND_DENSE)                               // fp16-rows role plan
     bytes += (size_t)c.batch * c.num_kv_heads *
-             rows_positions(mode, k_max, n_sink, n_window, c.format != KVC_FMT_FP16) * sizeof(int2);
-  if (mode == KVC_ATTEND_BLOCKS && c.format != KVC_FMT_FP16)   // group list + count
+             rows_positions(mode, k_max, n_sink, n_window, grouped(c.format)) * sizeof(int2);
+  if (mode == KVC_ATTEND_BLOCKS && grouped(c.format))   // group list + count
     bytes += (size_t)c.batch * c.num_kv_heads * (c.max_tokens / GS + 1) * sizeof(int32_t);
   return bytes;
 }
@@ -1304,7 +1348,7 @@ size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, i
 bool attend_plan_ok(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window) {
   const Plan p = plan_attend(c, mode, k_max, n_sink, n_window);
   if (p.s_q + p.s_r > MAX_SPLITS) return false;
-  if (mode == KVC_ATTEND_BLOCKS && c.format != KVC_FMT_FP16)
+  if (mode == KVC_ATTEND_BLOCKS && grouped(c.format))
     return (int64_t)p.s_q * waves_per_wg(c.format) * LIST_MAX >= walk_groups(c, mode, k_max, n_sink, n_window);
   return true;
 }
@@ -1333,11 +1377,11 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   a.sbits = nullptr;
   a.spre = nullptr;
   a.rplan = nullptr;
-  a.np = mode == KVC_ATTEND_DENSE ? 0 : rows_positions(mode, k_max, n_sink, n_window, c.format != KVC_FMT_FP16);
+  a.np = mode == KVC_ATTEND_DENSE ? 0 : rows_positions(mode, k_max, n_sink, n_window, grouped(c.format));
   a.nsel = mode == KVC_ATTEND_BLOCKS ? GS * k_max : k_max;
   a.glist = nullptr;
   a.gcount = nullptr;
-  const bool quant = c.format != KVC_FMT_FP16;
+  const bool quant = grouped(c.format);
   char* wp = static_cast<char*>(ws) + (size_t)c.batch * hq * (p.s_q + p.s_r) * PART * sizeof(float);
   const size_t sel_words = (size_t)c.batch * c.num_kv_heads * (c.max_tokens / 32);
   if (mode != KVC_ATTEND_DENSE && quant) {
@@ -1371,6 +1415,7 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   switch (c.format) {
     case KVC_FMT_INT4: launch_fmt<KVC_FMT_INT4>(grid, s, a, dense, lg, pk, tiled); break;
     case KVC_FMT_INT1: launch_fmt<KVC_FMT_INT1>(grid, s, a, dense, lg, pk, false); break;
+    case KVC_FMT_FP8: launch_fmt<KVC_FMT_FP8>(grid, s, a, dense, lg, false, false); break;
     default: launch_fmt<KVC_FMT_FP16>(grid, s, a, dense, lg, false, false); break;
   }
   hipError_t e = hipGetLastError();

@@ -86,6 +86,44 @@ __host__ __device__ constexpr int v1_code(int ct, int i) {
   return 2 * (4 * ((ct >> 2) * 2 + (i >> 1)) + (ct & 3)) + (i & 1);
 }
 
+// Formats stored as 64-token groups of codes with scale/zero metadata and an
+// fp16 tail (INT4, INT1), as opposed to per-token rows (fp16, FP8).
+__host__ __device__ constexpr bool grouped(int fmt) { return fmt == KVC_FMT_INT4 || fmt == KVC_FMT_INT1; }
+
+// FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals,
+// largest finite 448) of fp16 bits h: the nearest value, ties to the even
+// code, saturating at +-448, sign kept.  In units of 2^-24 an fp16 magnitude
+// is V = m (subnormal) or (1024 + m) << (e - 1); the E4M3 quantum is
+// 2^(e - 25 + 7) in the normal range (keep 3 of 10 mantissa bits, which with
+// the exponent field is a shift of the magnitude bits by 7 and a rebias) and
+// 2^-9 = 2^15 units below it.
+__device__ inline uint32_t fp8_encode(uint32_t h) {
+  const uint32_t s = (h >> 8) & 0x80u;
+  const uint32_t a = h & 0x7FFFu;
+  if (a >= 0x5F00u) return s | 0x7Eu;          // >= 448 (fp16 0x5F00): saturate
+  const uint32_t e = a >> 10, m = a & 0x3FFu;
+  uint32_t r;
+  if (e >= 9) {                                 // E4M3 normal: exponent e - 8 >= 1
+    r = a >> 7;
+    const uint32_t rem = a & 0x7Fu;
+    if (rem > 0x40u || (rem == 0x40u && (r & 1u))) ++r;
+    r -= 8u << 3;                               // rebias (a carry into the exponent is exact)
+  } else {                                      // E4M3 subnormal or zero: quantum 2^-9
+    const uint32_t V = e ? (1024u + m) << (e - 1) : m;
+    r = V >> 15;
+    const uint32_t rem = V & 0x7FFFu;
+    if (rem > 0x4000u || (rem == 0x4000u && (r & 1u))) ++r;
+  }
+  return s | r;
+}
+
+// E4M3 code c -> fp16 bits of value / 256, exactly: sign to bit 15 and the
+// exponent and mantissa fields shifted into fp16's (bias 15 = 7 + 8, and an
+// E4M3 subnormal lands on the matching fp16 subnormal).
+__host__ __device__ inline uint32_t fp8_h16_over256(uint32_t c) {
+  return ((c & 0x80u) << 8) | ((c & 0x7Fu) << 7);
+}
+
 __device__ inline float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 __device__ inline uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
 

@@ -8,6 +8,8 @@
 //   s = fp16((max - min) / (2^b - 1) + 0), z = fp16(min + 0),
 //   code = s == 0 ? 0 : clamp(rint((x - z) / s), 0, 2^b - 1) in fp32.
 // The packed code tiles follow the lane/dword layout of include/kvc.h.
+// FP8 (E4M3) caches encode every appended row at once (no groups, no tail);
+// the channel-major copy then holds the decoded values.
 // A second, per-sequence kernel then rewrites the fp16 tail and seq_lens.
 
 #include "internal.h"
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
 
   // Old rows [g0, L) are read back from the tail only when this append completes
   // the group of a quantized cache (nothing else needs them; an fp16 cache has no tail).
-  const bool complete = FMT != KVC_FMT_FP16 && hi == g0 + GS;
+  const bool complete = grouped(FMT) && hi == g0 + GS;
   const int r0 = complete ? 0 : lo - g0;
 
   // ---- stage rows [g0 + r0, hi) in LDS: 16 threads per row, 8 halves each
@@ -94,10 +96,28 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
       *reinterpret_cast<uint4*>(c.v16 + slot * D + ch) = *reinterpret_cast<const uint4*>(&sV[r][ch]);
     }
   }
+  if constexpr (FMT == KVC_FMT_FP8) {   // E4M3 rows: 16 threads per row, 8 codes each
+    for (int e = tid; e < (hi - lo) * 16; e += NT) {
+      const int r = lo - g0 + (e >> 4), ch = (e & 15) * 8;
+      const int64_t slot = slot_of(c, b, g, g0 + r);
+      if (slot < 0) continue;
+      uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        kw[j >> 2] |= fp8_encode(sK[r][ch + j]) << (8 * (j & 3));
+        vw[j >> 2] |= fp8_encode(sV[r][ch + j]) << (8 * (j & 3));
+      }
+      *reinterpret_cast<uint2*>(c.k_codes + slot * D + ch) = uint2{kw[0], kw[1]};
+      *reinterpret_cast<uint2*>(c.v_codes + slot * D + ch) = uint2{vw[0], vw[1]};
+    }
+  }
   if (c.kT) {  // channel-major: consecutive lanes write consecutive tokens of one channel
     for (int e = tid; e < (hi - lo) * D; e += NT) {
       const int ch = e / (hi - lo), r = lo - g0 + e % (hi - lo);
-      c.kT[(((int64_t)b * Hkv + g) * D + ch) * c.max_tokens + g0 + r] = sK[r][ch];
+      uint16_t x = sK[r][ch];
+      if constexpr (FMT == KVC_FMT_FP8)   // the decoded value (exact in fp16)
+        x = f2h(h2f((uint16_t)fp8_h16_over256(fp8_encode(x))) * 256.0f);
+      c.kT[(((int64_t)b * Hkv + g) * D + ch) * c.max_tokens + g0 + r] = x;
     }
   }
   if (c.k_absmax && tid < D) {
@@ -107,7 +127,7 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
               __float_as_uint(m));
   }
 
-  if constexpr (FMT == KVC_FMT_FP16) {
+  if constexpr (!grouped(FMT)) {
     return;
   } else {
     if (!complete) return;  // group not complete yet: it stays in the tail
@@ -229,7 +249,7 @@ __global__ __launch_bounds__(NT) void append_finish_kernel(
     if (tid == 0 && overflow) *overflow = 1;
     return;
   }
-  const bool quantized = c.format != KVC_FMT_FP16;
+  const bool quantized = grouped(c.format);
   if (quantized) {
     const int nq_old = L & ~(GS - 1), nq_new = (L + n) & ~(GS - 1);
     const int t0 = nq_new > nq_old ? nq_new : L;  // first token to place in the tail
@@ -260,6 +280,9 @@ hipError_t launch_append(const kvc_cache& c, const uint16_t* k_new, const uint16
       break;
     case KVC_FMT_INT1:
       append_groups_kernel<KVC_FMT_INT1><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max);
+      break;
+    case KVC_FMT_FP8:
+      append_groups_kernel<KVC_FMT_FP8><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max);
       break;
     default:
       append_groups_kernel<KVC_FMT_FP16><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max);

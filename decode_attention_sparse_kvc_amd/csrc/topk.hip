@@ -203,14 +203,14 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
   __shared__ double sq[GMAX * D];   // q as fp64, [head][channel slot]
   __shared__ int sch[D];
   __shared__ uint32_t sh[256];
-  __shared__ uint32_t smeta[FMT == KVC_FMT_FP16 ? 1 : (ST / GS) * D];   // (scale | zero << 16) per channel
+  __shared__ uint32_t smeta[grouped(FMT) ? (ST / GS) * D : 1];   // (scale | zero << 16) per channel
   const int G = a.G;
   const kvc_cache& c = a.c;
   const int nch = a.mode == KVC_SCORE_CRITICAL ? a.n_crit : (a.mode == KVC_SCORE_EXACT ? D : 0);
   for (int e = tid; e < nch; e += ST)
     sch[e] = a.mode == KVC_SCORE_CRITICAL ? a.channels[pi * D + e] : e;
   sh[tid] = 0u;
-  if (FMT != KVC_FMT_FP16 && nch > 0) {   // K metadata of the block's groups, channel pairs a thread
+  if (grouped(FMT) && nch > 0) {   // K metadata of the block's groups, channel pairs a thread
     const int groups = c.max_tokens / GS;
     const int gq = blockIdx.x * (ST / GS) + tid / 64, j = tid % 64;
     uint32_t s2 = 0u, z2 = 0u;
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
     if (a.mode == KVC_SCORE_EXTERNAL) {
       r = (double)a.ext[pi * c.max_tokens + t];
     } else {
-      const int nq = FMT == KVC_FMT_FP16 ? n : (n & ~(GS - 1));
+      const int nq = grouped(FMT) ? (n & ~(GS - 1)) : n;
       const int64_t slot = slot_of(c, b, g, t);
       r = -INFINITY;
       if (slot >= 0) {
@@ -258,6 +258,14 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
           auto aux = [&](int) -> uint32_t { return 0u; };
           auto value = [&](int, uint32_t raw, uint32_t) { return (double)h2f((uint16_t)raw); };
           r = token_score<GT, CB, EXACT && FMT != KVC_FMT_INT1>(G, nch, sch, sq, load, aux, value);
+        } else if (FMT == KVC_FMT_FP8) {   // E4M3 row, decoded exactly
+          const uint8_t* row = c.k_codes + slot * D;
+          auto load = [&](int ch) -> uint32_t { return row[ch]; };
+          auto aux = [&](int) -> uint32_t { return 0u; };
+          auto value = [&](int, uint32_t raw, uint32_t) {
+            return (double)h2f((uint16_t)fp8_h16_over256(raw)) * 256.0;
+          };
+          r = token_score<GT, CB, EXACT>(G, nch, sch, sq, load, aux, value);
         } else if (t >= nq) {   // fp16 tail row of a quantized cache
           const uint16_t* row = c.k_tail + (bg * GS + (t - nq)) * D;
           auto load = [&](int ch) -> uint32_t { return row[ch]; };
@@ -805,7 +813,8 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   } while (0)
   if (c.format == KVC_FMT_INT4) KVC_SCORE_G(KVC_FMT_INT4, false);
   else if (c.format == KVC_FMT_INT1) KVC_SCORE_G(KVC_FMT_INT1, false);
-  else if (c.kT && c.page_size == 0) KVC_SCORE_G(KVC_FMT_FP16, true);
+  else if (c.kT && c.page_size == 0) KVC_SCORE_G(KVC_FMT_FP16, true);   // (FP8: kT holds decoded values)
+  else if (c.format == KVC_FMT_FP8) KVC_SCORE_G(KVC_FMT_FP8, false);
   else KVC_SCORE_G(KVC_FMT_FP16, false);
 #undef KVC_SCORE_G
 #undef KVC_SCORE_E

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(PKG, "libkvc.so")
 ABI_VERSION = 1
 HEAD_DIM = 128
 GROUP = 64
-FMT = {"fp16": 0, "int4": 1, "int1": 2}
+FMT = {"fp16": 0, "int4": 1, "int1": 2, "fp8": 3}
 SCORE = {"exact": 0, "critical": 1, "external": 2}
 SCORE_BLOCKS = 16   # OR'ed into a score mode: rank 64-token blocks
 MODE = {"dense": 0, "drop": 1, "keep": 2, "blocks": 3}

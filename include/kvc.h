@@ -62,7 +62,7 @@ enum {
   KVC_ERR_HIP = 5           /* a kernel launch failed (hipGetLastError) */
 };
 
-enum { KVC_FMT_FP16 = 0, KVC_FMT_INT4 = 1, KVC_FMT_INT1 = 2 };
+enum { KVC_FMT_FP16 = 0, KVC_FMT_INT4 = 1, KVC_FMT_INT1 = 2, KVC_FMT_FP8 = 3 };
 enum { KVC_SCORE_EXACT = 0, KVC_SCORE_CRITICAL = 1, KVC_SCORE_EXTERNAL = 2 };
 /* OR'ed into a score mode: rank 64-token blocks instead of tokens ([MTG] 8.1) */
 enum { KVC_SCORE_BLOCKS = 16 };
@@ -114,6 +114,15 @@ enum { KVC_OP_SCORE_TOPK = 1, KVC_OP_ATTEND = 2 };
  *     0-63, zero of 64-127.
  *   k_tail, v_tail  fp16 [B][Hkv][64][128]: row r holds token 64*floor(n/64) + r
  *     of the incomplete group (n = seq_lens[b]).
+ *
+ * FP8 store (format FP8: the warm tier in E4M3, [MTG] 6.2, [SRV] 2).  Every
+ * appended element is cast to E4M3 (1 sign, 4 exponent bits of bias 7, 3
+ * mantissa bits, subnormals, largest finite 448): the nearest value, ties to
+ * the even code, saturating at +-448, sign kept; no scale.
+ *   k_codes, v_codes  uint8 [slot][128]: the codes of channel c at byte c of
+ *     the slot's row.  k_meta, v_meta, k_tail, v_tail are unused (may be NULL);
+ *     tokens never wait in a tail.  kT, if given, holds the decoded values.
+ *   KVC_ATTEND_KEEP is not supported on FP8.
  *
  * fp16 rows (format FP16: the main store; INT4/INT1: an optional full copy of
  * every appended token, required by KVC_ATTEND_KEEP; [MTG] 3.1 hot tier,

@@ -135,20 +135,19 @@ FP8_MAG = _fp8_magnitudes()
 def encode_fp8(x16: np.ndarray) -> np.ndarray:
     """fp16 -> E4M3 code: the nearest grid value, ties to the even code, saturating.
 
-    A brute-force search over the 127 magnitudes (exact in fp64: every fp16 and
-    every E4M3 value is a short dyadic rational).
+    The two grid magnitudes around |x| are compared (exact in fp64: every fp16
+    and every E4M3 value is a short dyadic rational).
     """
     x = np.asarray(x16, dtype=np.float16)
     assert np.all(np.isfinite(x))
     a = np.abs(x.astype(np.float64)).reshape(-1)
-    d = np.abs(a[:, None] - FP8_MAG[None, :])                  # [n, 127]
-    best = d.min(axis=1, keepdims=True)
-    cand = d == best                                             # one or two nearest codes
-    codes = np.arange(0x7F)
-    odd = (codes & 1).astype(bool)[None, :]
-    pick = np.where(cand & ~odd, codes[None, :], 0x7F).min(axis=1)   # an even nearest code
-    pick = np.where(pick == 0x7F, np.where(cand, codes[None, :], 0x7F).min(axis=1), pick)
-    pick = np.where(a > FP8_MAG[-1], 0x7E, pick)                # saturate
+    hi = np.minimum(np.searchsorted(FP8_MAG, a), 0x7E)        # first magnitude >= |x| (capped)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - FP8_MAG[lo]
+    d_hi = FP8_MAG[hi] - a
+    pick = np.where(d_hi < d_lo, hi, lo)
+    pick = np.where(d_hi == d_lo, np.where(hi % 2 == 0, hi, lo), pick)   # tie: the even code
+    pick = np.where(a >= FP8_MAG[-1], 0x7E, pick)             # 448 and beyond: saturate
     sign = np.signbit(x).reshape(-1).astype(np.int64) << 7
     return (pick | sign).astype(np.uint8).reshape(x.shape)
 
