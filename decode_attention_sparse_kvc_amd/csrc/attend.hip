@@ -795,20 +795,18 @@ __device__ inline int2 plan_entry(const AttendArgs& a, int b, int g, int n, int 
 }
 
 // 32 E4M3 codes (two 16-byte words, channels in byte order) -> 32 fp16 values
-// / 256 in four 16-byte words: a byte permute spreads two codes into the low
-// bytes of the two halves of a dword, then one shift-mask pair per field.
-__device__ inline uint32_t fp8_pair(uint32_t x) {   // x = [c0, 0, c1, 0]
-  return ((x & 0x007F007Fu) << 7) | ((x & 0x00800080u) << 8);
+// in four 16-byte words, two codes per conversion instruction (scale 1: every
+// E4M3 value is exact in fp16).
+template <bool HI>
+__device__ inline uint32_t fp8_pair(uint32_t w) {
+  return bc<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
 }
 __device__ inline void fp8_row_decode(uint4 r0, uint4 r1, uint4* out) {
   const uint32_t w[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t a = w[2 * i], b = w[2 * i + 1];
-    out[i] = uint4{fp8_pair(__builtin_amdgcn_perm(0u, a, 0x0c010c00u)),
-                   fp8_pair(__builtin_amdgcn_perm(0u, a, 0x0c030c02u)),
-                   fp8_pair(__builtin_amdgcn_perm(0u, b, 0x0c010c00u)),
-                   fp8_pair(__builtin_amdgcn_perm(0u, b, 0x0c030c02u))};
+    out[i] = uint4{fp8_pair<false>(a), fp8_pair<true>(a), fp8_pair<false>(b), fp8_pair<true>(b)};
   }
 }
 
@@ -842,9 +840,6 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
                                           float* sO, float* sML, int* sTok) {
   constexpr bool QUANT = grouped(FMT);
   constexpr bool FP8 = FMT == KVC_FMT_FP8;
-  // FP8 rows enter the matrix cores as value / 256 (exact fp16); scores and
-  // outputs are scaled back by 256
-  constexpr float RS = FP8 ? 256.f : 1.f;
   constexpr int NW = waves_per_wg(FMT);
   const kvc_cache& c = a.c;
   const int n = max(c.seq_lens[b], 0);
@@ -958,7 +953,6 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
       f4 sc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < 4; ++k) sc = mfma32(bc<h8>(kr[k]), qb[k], sc);
-      if constexpr (FP8) sc *= RS;
       float x[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1037,7 +1031,7 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
   if (hv) {
     float* oh = sO + (w * 8 + col) * D;
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) *reinterpret_cast<f4*>(oh + 16 * ct + 4 * kb) = acc[ct] * RS;
+    for (int ct = 0; ct < 8; ++ct) *reinterpret_cast<f4*>(oh + 16 * ct + 4 * kb) = acc[ct];
   }
   if (hv && kb == 0) {
     sML[(w * 8 + col) * 2] = m;
