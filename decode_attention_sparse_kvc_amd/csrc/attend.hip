@@ -1055,7 +1055,13 @@ void attend_kernel(AttendArgs a) {
   // fp16-rows workgroup (s_r per pair), so the longer quantized runs of a
   // ragged batch are dispatched first.
   int id = blockIdx.x, pair, split;
-  if (DENSE) {
+  if (DENSE && a.pairs % 8 == 0) {
+    // split-major: workgroup ids go round-robin over the eight XCDs, so every
+    // split of a pair runs on the XCD whose L2 then holds the pair's partials
+    // for the merge (whose workgroups follow the same order)
+    split = id / a.pairs;
+    pair = id - split * a.pairs;
+  } else if (DENSE) {
     pair = id / a.s_total;
     split = id - pair * a.s_total;
   } else if (id < a.s_q * a.pairs) {
@@ -1191,10 +1197,13 @@ __global__ __launch_bounds__(256) void plan_kernel(AttendArgs a) {
 // wait on one another; the 8 replicas are then combined through LDS.
 constexpr int MT = 256;
 __global__ __launch_bounds__(MT) void merge_kernel(const float* __restrict__ part, int s_total,
-                                                   float* __restrict__ out, float* __restrict__ lse) {
+                                                   float* __restrict__ out, float* __restrict__ lse,
+                                                   int pairs, int G) {
   __shared__ f4 sacc[MT];
   __shared__ float sml[2 * MT];
-  const int bh = blockIdx.x, tid = threadIdx.x, cq = tid & 31, r = tid >> 5;
+  // workgroup j * pairs + p merges query head j of pair p (on pair p's XCD)
+  const int p = blockIdx.x % pairs, j = blockIdx.x / pairs;
+  const int bh = p * G + j, tid = threadIdx.x, cq = tid & 31, r = tid >> 5;
   const float* pp = part + (int64_t)bh * s_total * PART;
   float mr = -INFINITY, lr = 0.f;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
@@ -1418,7 +1427,7 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  merge_kernel<<<c.batch * hq, MT, 0, s>>>(a.part, a.s_total, out, lse);
+  merge_kernel<<<c.batch * hq, MT, 0, s>>>(a.part, a.s_total, out, lse, a.pairs, a.G);
   return hipGetLastError();
 }
 
