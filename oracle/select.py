@@ -152,3 +152,29 @@ def block_tokens(n: int, n_sink: int, n_window: int, blocks) -> np.ndarray:
     sinks = np.arange(min(n_sink, n))
     window = np.arange(max(max(n - n_window, 0), min(n_sink, n)), n)
     return np.unique(np.concatenate([sinks, toks, window]).astype(np.int64))
+
+
+def topk_mass(probs: np.ndarray, k: int) -> float:
+    """Sum of the k largest attention probabilities of one query row (fp64).
+
+    TailorKV article, section 2.1 (dense preference score): for each of the last
+    n_q queries, the top-k entries of its softmax row are taken and their
+    probabilities summed.  The sum does not depend on which of several equal
+    entries count as the k-th.
+    """
+    p = np.sort(np.asarray(probs, dtype=np.float64))[::-1]
+    return float(p[: max(0, min(int(k), p.size))].sum())
+
+
+def dense_preference(masses) -> float:
+    """P = n_q - sum over the n_q queries of their top-k probability mass."""
+    m = np.asarray(masses, dtype=np.float64)
+    return float(m.size - m.sum())
+
+
+def quantization_friendly(P: float, tau: float = 0.2) -> bool:
+    """A layer whose attention spreads beyond its top-k entries (P above tau) is
+    quantization-friendly; one that concentrates in them is sparsity-friendly.
+    (The comparison sign is lost in the page's text; this reading matches its
+    example, where the dense layer 0 scores 0.7178 and layer 16 0.0473.)"""
+    return bool(P > tau)
