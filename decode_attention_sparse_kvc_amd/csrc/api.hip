@@ -177,6 +177,19 @@ kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const f
                                  n_sink, n_window, acc, stream));
 }
 
+kvc_status kvc_topk_mass(const kvc_cache* cache, int32_t num_q_heads, const float* logits,
+                         int64_t logits_stride, const float* lse, int32_t k, float* out,
+                         hipStream_t stream) {
+  kvc_status st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads) return KVC_ERR_SHAPE;
+  if (!logits || !lse || !out || !aligned(logits, 4) || !aligned(lse, 4) || !aligned(out, 4))
+    return KVC_ERR_INVALID;
+  if (k < 0) return KVC_ERR_INVALID;
+  if (logits_stride < cache->max_tokens) return KVC_ERR_SHAPE;
+  return hip_status(launch_topk_mass(*cache, num_q_heads, logits, logits_stride, lse, k, out, stream));
+}
+
 size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t mode,
                            int32_t k_max, int32_t n_sink, int32_t n_window) {
   if (check_cache(cache) != KVC_OK) return 0;

@@ -76,6 +76,8 @@ def _load():
     lib.kvc_accum_scores.restype = c_int32
     lib.kvc_accum_scores.argtypes = [P, c_int32, c_void_p, c_int64, c_void_p, c_int32, c_void_p,
                                      c_int32, c_int32, c_int32, c_void_p, c_void_p]
+    lib.kvc_topk_mass.restype = c_int32
+    lib.kvc_topk_mass.argtypes = [P, c_int32, c_void_p, c_int64, c_void_p, c_int32, c_void_p, c_void_p]
     lib.kvc_workspace_bytes.restype = c_size_t
     lib.kvc_workspace_bytes.argtypes = [c_int32, P, c_int32, c_int32, c_int32, c_int32, c_int32]
     if lib.kvc_abi_version() != ABI_VERSION:
@@ -148,6 +150,13 @@ def kvc_accum_scores(cache, num_q_heads: int, logits, logits_stride: int, lse, m
     _check("kvc_accum_scores", lib().kvc_accum_scores(
         ctypes.byref(cache), num_q_heads, _ptr(logits), logits_stride, _ptr(lse), mode, _ptr(sel),
         k_max, n_sink, n_window, _ptr(acc), _stream(stream)))
+
+
+def kvc_topk_mass(cache, num_q_heads: int, logits, logits_stride: int, lse, k: int, out,
+                  stream=None):
+    _check("kvc_topk_mass", lib().kvc_topk_mass(
+        ctypes.byref(cache), num_q_heads, _ptr(logits), logits_stride, _ptr(lse), k, _ptr(out),
+        _stream(stream)))
 
 
 def kvc_workspace_bytes(op: int, cache, num_q_heads: int, mode: int = 0, k_max: int = 0,

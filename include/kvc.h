@@ -264,6 +264,24 @@ kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const f
                             const int32_t* sel, int32_t k_max, int32_t n_sink, int32_t n_window,
                             float* acc, hipStream_t stream);
 
+/*
+ * kvc_topk_mass -- top-k attention probability mass of each query head's row
+ * ([TKV] 2.1: the dense preference score P = n_q - sum over the last n_q
+ * query rows of their top-k softmax entries; a layer with P above tau = 0.2
+ * is quantization-friendly, one below it sparsity-friendly).
+ *   logits, lse  a dense kvc_attend_decode's outputs for one query: row
+ *                (b, h) at logits + (b*Hq + h)*logits_stride, position t =
+ *                token t for t < n = seq_lens[b]; logits_stride >= max_tokens.
+ *   k            entries per row (k_b = min(k, n)); k >= 0.
+ *   out          float32 [B][Hq]: sum over the k_b largest logits of
+ *                exp(logit - lse) (fp32 sums; 0 when k_b = 0).  The value does
+ *                not depend on which of several equal entries are counted.
+ * The caller sums 1 - out over its n_q recent queries to form P.
+ */
+kvc_status kvc_topk_mass(const kvc_cache* cache, int32_t num_q_heads, const float* logits,
+                         int64_t logits_stride, const float* lse, int32_t k, float* out,
+                         hipStream_t stream);
+
 /* Workspace bytes for op (KVC_OP_*) called with these arguments (mode is the
  * attend mode; it is ignored for KVC_OP_SCORE_TOPK); 0 on invalid arguments.
  * Host only. */

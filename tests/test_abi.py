@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     lib = kvc.lib()
     names = declared_functions()
     assert {"kvc_quantize_append", "kvc_score_topk", "kvc_attend_decode", "kvc_accum_scores",
-            "kvc_workspace_bytes", "kvc_status_str", "kvc_abi_version"} <= set(names)
+            "kvc_topk_mass", "kvc_workspace_bytes", "kvc_status_str", "kvc_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert kvc.kvc_abi_version() == kvc.ABI_VERSION
@@ -132,3 +132,16 @@ def test_workspace_sizes():
     a3 = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 4, 3, 61, 4, 64)          # blocks mode
     assert a3 > 0
     assert kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 36, 0, 0, 0, 0) == 0     # G = 36 > 8
+
+
+def test_topk_mass_argument_checks():
+    d = _desc(max_tokens=4096, num_kv_heads=2)
+    L = kvc.lib()
+
+    def call(hq=8, logits=0x10000, stride=4096, lse=0x20000, k=16, out=0x30000):
+        return L.kvc_topk_mass(ctypes.byref(d), hq, logits, stride, lse, k, out, None)
+    assert call(hq=0) == 2 and call(hq=3) == 2
+    assert call(logits=None) == 1 and call(lse=None) == 1 and call(out=None) == 1
+    assert call(logits=0x10002) == 1
+    assert call(k=-1) == 1
+    assert call(stride=4095) == 2
