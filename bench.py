@@ -97,9 +97,13 @@ def attend_bytes(w, lens, k_sel) -> int:
             rest = n - keep
             per_head = keep * 512 + rest * CODE_BYTES[fmt]
         total += hkv * per_head
-        if w.accumulate:                          # logits written
-            pos = {"drop": w.n_sink + int(w.top_k.max()) + w.n_window,
-                   "blocks": w.n_sink + 64 * int(w.top_k.max()) + w.n_window}.get(w.mode, n)
+        if w.accumulate or w.prefer_k:            # logits written
+            if w.mode == "drop":
+                pos = w.n_sink + int(w.top_k.max()) + w.n_window
+            elif w.mode == "blocks":
+                pos = w.n_sink + 64 * int(w.top_k.max()) + w.n_window
+            else:
+                pos = n
             total += hq * pos * 4
     total += B * hq * 128 * 2           # q
     total += B * hq * (128 + 1) * 4     # out + lse
@@ -211,7 +215,13 @@ def main():
         stride = (w.n_sink + k_max + w.n_window if w.mode == "drop"
                   else w.n_sink + 64 * k_max + w.n_window if w.mode == "blocks" else cap)
         logits = torch.empty(w.batch, w.hq, stride, device=dev)
-    names = ["append"] + (["score_topk"] if sparse else []) + ["attend"] + (["accum"] if accs else [])
+    if w.prefer_k and not w.accumulate:   # the attention rows the top-k mass reads
+        stride = cap
+        logits = torch.empty(w.batch, w.hq, stride, device=dev)
+    mass = torch.empty(w.batch, w.hq, device=dev)
+    want_logits = bool(accs) or w.prefer_k > 0
+    names = (["append"] + (["score_topk"] if sparse else []) + ["attend"] + (["accum"] if accs else [])
+             + (["topk_mass"] if w.prefer_k else []))
 
     def op_append(r, st):
         kvc.kvc_quantize_append(reps[r].desc, k_new, v_new, None, 1, None, st)
@@ -225,14 +235,18 @@ def main():
 
     def op_attend(r, st):
         kvc.kvc_attend_decode(reps[r].desc, q, w.hq, w.sm_scale, mode, sel if sparse else None,
-                              k_max, w.n_sink, w.n_window, out, lse, logits if accs else None,
-                              stride if accs else 0, ws, nbytes, st)
+                              k_max, w.n_sink, w.n_window, out, lse, logits if want_logits else None,
+                              stride if want_logits else 0, ws, nbytes, st)
 
     def op_accum(r, st):
         kvc.kvc_accum_scores(reps[r].desc, w.hq, logits, stride, lse, mode, sel if sparse else None,
                              k_max, w.n_sink, w.n_window, accs[r], st)
 
-    ops = {"append": op_append, "score_topk": op_score_topk, "attend": op_attend, "accum": op_accum}
+    def op_topk_mass(r, st):
+        kvc.kvc_topk_mass(reps[r].desc, w.hq, logits, stride, lse, w.prefer_k, mass, st)
+
+    ops = {"append": op_append, "score_topk": op_score_topk, "attend": op_attend, "accum": op_accum,
+           "topk_mass": op_topk_mass}
 
     def step(r, st):
         for nm in names:
@@ -323,7 +337,8 @@ def main():
     step_desc = " + ".join({"append": "kvc_quantize_append(1 token)",
                             "score_topk": f"kvc_score_topk({w.score})",
                             "attend": f"kvc_attend_decode({w.mode})",
-                            "accum": "kvc_accum_scores"}[nm] for nm in names)
+                            "accum": "kvc_accum_scores",
+                            "topk_mass": f"kvc_topk_mass(k={w.prefer_k})"}[nm] for nm in names)
 
     result = {
         "metric": "decode attention context-tokens/s per layer at 128K; achieved HBM GB/s vs peak",

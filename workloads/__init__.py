@@ -67,6 +67,7 @@ class Workload:
     max_tokens: int = 0                  # per-sequence capacity (multiple of 64)
     kT: bool = False                     # keep a channel-major K copy (fp16 caches)
     fp16_shadow: bool = False            # keep full fp16 rows beside quantized codes
+    prefer_k: int = 0                    # > 0: also the top-k probability mass of each row
 
     @property
     def group(self) -> int:
@@ -306,6 +307,14 @@ def batched_joint(batch: int = 16, lo: int = 8192, hi: int = 32768, seed: int = 
 
 
 # Full-size workloads by name (the benchmark and the full-size parity tests).
+def _with_prefer(w: Workload, k: int) -> Workload:
+    """The same layer with the dense preference score's top-k mass per row
+    (TailorKV article, section 2.1) computed from the step's attention."""
+    w.prefer_k = k
+    w.name += f"_topmass{k}"
+    return w
+
+
 FULL = {
     "single_head_int4_exact_top128": lambda: single_head_4k(),
     "llama8b_layer_int4_dense_32k": lambda: int4_dense(32768),
@@ -316,4 +325,5 @@ FULL = {
     "llama8b_layer_fp16_crit8_block61_128k": lambda: sparse_blocks(131072, "fp16"),
     "llama8b_layer_int4_crit8_block61_128k": lambda: sparse_blocks(131072, "int4"),
     "llama8b_layer_fp8_dense_128k": lambda: fp8_dense(131072),
+    "llama8b_layer_int1_dense_128k_topmass3pct": lambda: _with_prefer(int1_dense(131072), 3932),
 }
