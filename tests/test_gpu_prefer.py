@@ -83,3 +83,12 @@ def test_full_size_layers_decision():
         assert abs(p_gpu - p_ref) <= 1e-3 + 2e-3 * abs(p_ref), (name, p_gpu, p_ref)
         if abs(p_ref - 0.2) > 1e-2:
             assert S.quantization_friendly(p_gpu) == S.quantization_friendly(p_ref), name
+
+
+def test_bucket_larger_than_lds():
+    """40000 equal logits share one top-byte bucket, more than the kernel stages in
+    LDS: the row is re-read from memory, and the mass is k / n."""
+    w = W.int4_dense(40000)
+    w.fmt = "fp16"
+    w.k[0, :, 1] = w.k[0, 0, 1]
+    mass_case(w, [1, 3000, 40000], pairs=[(0, 1)])
