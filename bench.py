@@ -10,7 +10,7 @@ with the cache already resident in HBM:
 heads, all sequences).  Cache replicas are rotated so that the working set
 exceeds the 256 MB Infinity Cache and bytes come from HBM.
 
-Prints one JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on
+Prints one JSON line.  ``--gpus N`` with N > 1 is refused: the benchmark runs on
 one GPU.
 """
 from __future__ import annotations
@@ -158,7 +158,7 @@ def cpu_baseline(w, seconds: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only; the path shards by (sequence, KV head) "
+        print("bench.py: measures one GPU only; the path shards by (sequence, KV head) "
               "with no exchange, so N-GPU throughput is N times the 1-GPU figure by construction "
               "and is not measured here.", file=sys.stderr)
         sys.exit(2)

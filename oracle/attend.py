@@ -13,7 +13,7 @@ Sources:
   * StreamingLLM / H2O survey, section 3.2 (H2O): cumulative attention scores
     per token, accumulated over decode steps.
 
-Readings (listed in DESIGN.md):
+Readings:
   * GQA: query head h reads KV head floor(h / G), G = Hq / Hkv (pages silent;
     Llama convention).
   * The scale is 1/sqrt(128) passed as a float32 value; lse is the natural log.

@@ -8,7 +8,7 @@ channel and the value cache per token; its section 5.2 asks for group sizes that
 are multiples of 64.  The on-device KV article, section 3.1, gives INT4 keys
 asymmetric per channel with a zero point and INT4 values in groups of 32/64.
 
-Readings taken where the pages are silent or garbled (each listed in the design doc):
+Readings taken where the pages are silent or garbled:
   * b-bit generalization: the printed denominator 2**1 - 1 becomes 2**b - 1.
   * The printed code takes one min/max over its whole input; we take it per
     64-element group (the ``group_size`` argument it never uses).
@@ -111,7 +111,7 @@ def dequant_values(code, s, z) -> np.ndarray:
 # prefers FP8 E4M3/E5M2 over INT4 where the hardware supports it natively; KV
 # compression survey, section 2: an FP8 E4M3/E5M2 KV cache halves memory and
 # doubles bandwidth without reworking the dequantization.
-# Readings taken (listed in the design doc):
+# Readings taken:
 #   * E4M3 as the OCP 8-bit format: 1 sign, 4 exponent (bias 7), 3 mantissa
 #     bits, subnormals, no infinities, largest finite 448.
 #   * A plain per-element cast (no scale: the pages need no new dequantization),

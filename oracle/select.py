@@ -12,7 +12,7 @@ Sources:
     and a recent window (e.g. 2048 tokens); section 3.2: H2O keeps tokens with
     high cumulative attention score.
 
-Readings taken (each listed in the design doc):
+Readings taken:
   * GQA: a KV head serves G query heads; the channel importance uses the max
     over the group of |q_{h,c}|, and a token's score is the max over the group
     of the per-head scores.  Max is order-free, so the result is exact.
