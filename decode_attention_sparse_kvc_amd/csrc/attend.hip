@@ -65,6 +65,8 @@ struct AttendArgs {
   int2* rplan;                // drop/keep: [B][Hkv][np] fp16-rows role plan entries
   int np;                     // drop/keep: positions per (sequence, KV head) of the fp16-rows role
   int nsel;                   // positions of the selection (k_max; 64 k_max in blocks mode)
+  int inline_plan;            // drop / blocks on a contiguous fp16 / FP8 cache: the rows role
+                              // derives its positions from sel itself (no plan kernel)
   int32_t* glist;             // blocks mode, INT4/INT1: [B][Hkv][max_tokens/64] groups to walk
   int32_t* gcount;            // blocks mode, INT4/INT1: [B][Hkv] their number
   int s_q, s_total;
@@ -876,16 +878,25 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
     const int Hkv = c.num_kv_heads;
     const int64_t pair = (int64_t)b * Hkv + g;
 
-    // raw plan word(s) of this lane's row in tile i (one buffer load)
+    // raw plan word(s) of this lane's row in tile i (one buffer load): the page
+    // table word (dense), the sel entry (inline plan), or the plan kernel's entry
+    const bool inl = !DENSE && a.inline_plan;
     const Buf rplan = DENSE ? make_buf(c.block_table + (int64_t)b * c.max_pages,
                                        (!QUANT && c.page_size > 0) ? c.max_pages * 4u : 0u)
-                            : make_buf(a.rplan + pair * a.np, (uint32_t)a.np * 8u);
+                    : inl ? make_buf(a.sel + pair * a.k_max, (uint32_t)a.k_max * 4u)
+                          : make_buf(a.rplan + pair * a.np, (uint32_t)a.np * 8u);
+    const bool blocks = a.mode == KVC_ATTEND_BLOCKS;
     auto plan_load = [&](int i) -> uint2 {
       const int p = pa + TILE * i + row;
       if constexpr (DENSE) {
         const int page = (!QUANT && c.page_size > 0) ? page_of(a.pd, nq + p) : 0;
         return uint2{bc<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rplan, (int)(4u * (uint32_t)page), 0, 0)), 0u};
       } else {
+        if (inl) {   // sel entry of the position (outside the sel region: past the range, reads 0)
+          const int q = p - a.n_sink;
+          const int si = q < 0 ? INT_MAX / 8 : (blocks ? q / GS : q);
+          return uint2{bc<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rplan, (int)(4u * (uint32_t)min(si, INT_MAX / 8)), 0, 0)), 0u};
+        }
         return buf_load8(rplan, 8u * (uint32_t)p);
       }
     };
@@ -893,6 +904,27 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
       const int p = pa + TILE * i + row;
       if (p >= pb) return int2{ROW_SKIP, 0};
       if constexpr (!DENSE) {
+        if (inl) {   // as plan_entry for drop / blocks on a contiguous row store
+          int t;
+          bool ok;
+          if (p < a.n_sink) {
+            t = p;
+            ok = p < n;
+          } else if (p < a.n_sink + a.nsel) {
+            const int e = (int)raw.x;
+            if (blocks) {
+              ok = e >= (a.n_sink + GS - 1) / GS && e < max(n - a.n_window, 0) / GS;
+              t = ok ? e * GS + (p - a.n_sink) % GS : 0;
+            } else {
+              t = e;
+              ok = t >= a.n_sink && t < n - a.n_window;
+            }
+          } else {
+            t = window_start(n, a.n_sink, a.n_window) + (p - a.n_sink - a.nsel);
+            ok = t < n;
+          }
+          return ok ? int2{t, (int)(pair * c.max_tokens + t)} : int2{ROW_NONE, 0};
+        }
         return int2{(int)raw.x, (int)raw.y};
       } else {
         const int t = nq + p;
@@ -1391,6 +1423,8 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   a.rplan = nullptr;
   a.np = mode == KVC_ATTEND_DENSE ? 0 : rows_positions(mode, k_max, n_sink, n_window, grouped(c.format));
   a.nsel = mode == KVC_ATTEND_BLOCKS ? GS * k_max : k_max;
+  a.inline_plan = !grouped(c.format) && c.page_size == 0 &&
+                  (mode == KVC_ATTEND_DROP || mode == KVC_ATTEND_BLOCKS);
   a.glist = nullptr;
   a.gcount = nullptr;
   const bool quant = grouped(c.format);
@@ -1415,7 +1449,7 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   a.gpw = p.gpw;
   a.pairs = c.batch * c.num_kv_heads;
   const dim3 grid((unsigned)((int64_t)a.s_total * a.pairs));
-  if (mode != KVC_ATTEND_DENSE) {   // k_max == 0: all-zero bits
+  if (mode != KVC_ATTEND_DENSE && !a.inline_plan) {   // k_max == 0: all-zero bits
     const int items = std::max(quant ? c.max_tokens / 32 : 0, a.np);
     const dim3 pg((items + 255) / 256, c.num_kv_heads, c.batch);
     if (quant) plan_kernel<true><<<pg, 256, 0, s>>>(a);
