@@ -196,6 +196,23 @@ def test_drop_fp16_gather(n_sink, n_window):
     check_against_oracle(w, res, out, lse, lg, k_max, stride)
 
 
+@pytest.mark.parametrize("fmt", ["fp16", "fp8"])
+def test_drop_paged_rows(fmt):
+    """Drop mode on a paged fp16 / FP8 row store (positions planned by the plan kernel,
+    rows found through the page table) against the contiguous case's inline planning."""
+    w = W.sparse_crit8(n_ctx=3000, n_planted=40, top_k=200)
+    w.fmt, w.kT = fmt, False
+    w.n_sink, w.n_window = 4, 100
+    page = 16
+    per = w.max_tokens // page
+    w.page_size, w.num_pages = page, per
+    w.block_table = np.random.default_rng(12).permutation(per).astype(np.int32)[None]
+    res, cache = oracle_and_cache(w)
+    k_max = 256
+    out, lse, lg, stride = run_attend(cache, w, sel_tensor(res, w, k_max), k_max)
+    check_against_oracle(w, res, out, lse, lg, k_max, stride)
+
+
 def test_drop_int1_and_out_of_range_entries():
     """Drop mode on a 1-bit cache; sel entries inside the sink/window ranges are ignored."""
     w = W.int1_dense(900)

@@ -146,3 +146,15 @@ def test_blocks_full_size(fmt):
     selection and attention against the oracle on two sampled pairs."""
     w = W.FULL[f"llama8b_layer_{fmt}_crit8_block61_128k"]()
     block_case(w, pairs=[(0, 0), (0, 5)])
+
+
+def test_blocks_paged_fp16():
+    """Blocks mode on a paged fp16 store (plan kernel, page table) with sinks and window."""
+    w = W.sparse_blocks(n_ctx=3000, fmt="fp16", top_blocks=6)
+    w.kT = False
+    w.n_sink, w.n_window = 4, 70
+    page = 16
+    per = w.max_tokens // page
+    w.page_size, w.num_pages = page, per
+    w.block_table = np.random.default_rng(13).permutation(per).astype(np.int32)[None]
+    block_case(w, pairs=[(0, 3)])
