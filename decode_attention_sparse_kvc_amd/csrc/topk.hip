@@ -179,7 +179,7 @@ __device__ inline double token_score(int G, int nch_, const int* sch, const doub
 #pragma unroll
       for (int hh = 0; hh < GN; ++hh) {
         if (GT > 0 || hh < G) {
-          const double nx = __dadd_rn(acc[hh], __dmul_rn(sq[hh * D + kq], v));
+          const double nx = __dadd_rn(acc[hh], __dmul_rn(sq[hh * (ALL ? D : nch) + kq], v));
           acc[hh] = on ? nx : acc[hh];
         }
       }
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
   const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int t = blockIdx.x * ST + tid;
   const int64_t pi = pair_index(a, b, g);
-  __shared__ double sq[GMAX * D];   // q as fp64, [head][channel slot]
+  extern __shared__ double sq[];    // q as fp64, [head][channel slot], G x nch (sized at launch)
   __shared__ int sch[D];
   __shared__ uint32_t sh[256];
   __shared__ uint32_t smeta[grouped(FMT) ? (ST / GS) * D : 1];   // (scale | zero << 16) per channel
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
   // q on the channel list: gathered by prep (critical mode) or channel k itself
   for (int e = tid; e < G * nch; e += ST) {
     const int hh = e / nch, k = e % nch;
-    sq[hh * D + k] = a.mode == KVC_SCORE_CRITICAL
+    sq[hh * nch + k] = a.mode == KVC_SCORE_CRITICAL
                          ? a.qsel[(pi * GMAX + hh) * D + k]
                          : (double)h2f(a.q[((int64_t)b * a.hq + g * G + hh) * D + k]);
   }
@@ -796,10 +796,13 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   prep_kernel<<<dim3(Hkv, B), D, 0, s>>>(a);
   const dim3 sgrid((c.max_tokens + ST - 1) / ST, Hkv, B);
   const bool exact = mode == KVC_SCORE_EXACT;
+  // the scorer's q operands in LDS: G heads x the channels it sums over
+  const int nch = mode == KVC_SCORE_CRITICAL ? n_crit : (exact ? D : 0);
+  const size_t sq_bytes = (size_t)std::max(1, a.G * nch) * sizeof(double);
 #define KVC_SCORE_E(F, KT, GG)                                                \
   do {                                                                        \
-    if (exact) score_kernel<F, KT, GG, true><<<sgrid, ST, 0, s>>>(a);         \
-    else score_kernel<F, KT, GG, false><<<sgrid, ST, 0, s>>>(a);              \
+    if (exact) score_kernel<F, KT, GG, true><<<sgrid, ST, sq_bytes, s>>>(a);  \
+    else score_kernel<F, KT, GG, false><<<sgrid, ST, sq_bytes, s>>>(a);       \
   } while (0)
 #define KVC_SCORE_G(F, KT)                                                    \
   do {                                                                        \
