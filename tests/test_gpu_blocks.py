@@ -158,3 +158,19 @@ def test_blocks_paged_fp16():
     w.page_size, w.num_pages = page, per
     w.block_table = np.random.default_rng(13).permutation(per).astype(np.int32)[None]
     block_case(w, pairs=[(0, 3)])
+
+
+def test_blocks_no_selection():
+    """k_max = 0: only the sinks and the window are attended (quantized and fp16)."""
+    for fmt in ["int4", "fp16"]:
+        w = W.sparse_blocks(n_ctx=2000, fmt=fmt, top_blocks=0)
+        w.n_sink, w.n_window = 4, 200
+        w.score = None
+        res = ST.decode_step(w, append=False, pairs=[(0, 1)])
+        cache = cache_for(w)
+        prefill(cache, w)
+        sel = np.zeros((1, w.hkv, 1), np.int32)
+        out, lse, lg, stride, _ = run_block_attend(cache, w, sel, 0)
+        G = w.group
+        assert_close(out[0, G:2 * G], res.o[0, G:2 * G], f"o {fmt}")
+        assert_close(lse[0, G:2 * G], res.lse[0, G:2 * G], f"lse {fmt}")

@@ -120,3 +120,33 @@ def test_full_size_dense():
         sl = slice(g * G, (g + 1) * G)
         assert_close(out[b, sl], res.o[b, sl], f"o g={g}")
         assert_close(lse[b, sl], res.lse[b, sl], f"lse g={g}")
+
+
+def test_ragged_paged_appends():
+    """Three sequences on a shared, shuffled 16-token page pool appended in ragged
+    steps: every slot's codes equal the oracle's cast of the appended value."""
+    rng = np.random.default_rng(21)
+    B, hkv, page, cap = 3, 2, 16, 256
+    per = cap // page
+    table = torch.from_numpy(rng.permutation(B * per).astype(np.int32).reshape(B, per))
+    cache = KvcCache("fp8", B, hkv, cap, page_size=page, block_table=table, num_pages=B * per)
+    rows = [np.zeros((0, hkv, 128), np.float16) for _ in range(B)]
+    for step in range(4):
+        n_new = rng.integers(0, 70, size=B).astype(np.int32)
+        m = int(n_new.max())
+        k = (rng.normal(size=(B, max(m, 1), hkv, 128)) * 30).astype(np.float16)
+        v = rng.normal(size=(B, max(m, 1), hkv, 128)).astype(np.float16)
+        cache.append(dev(k), dev(v), dev(n_new))
+        for b in range(B):
+            rows[b] = np.concatenate([rows[b], k[b, : n_new[b]]])
+    torch.cuda.synchronize()
+    lens = host(cache.seq_lens)
+    kc = host(cache.k_codes).reshape(-1, 128)
+    tab = table.numpy()
+    for b in range(B):
+        assert lens[b] == rows[b].shape[0]
+        for t in range(int(lens[b])):
+            phys = tab[b, t // page]
+            for g in range(hkv):
+                slot = (phys * hkv + g) * page + t % page
+                assert np.array_equal(kc[slot], Q.encode_fp8(rows[b][t, g])), (b, t, g)

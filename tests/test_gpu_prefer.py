@@ -92,3 +92,22 @@ def test_bucket_larger_than_lds():
     w.fmt = "fp16"
     w.k[0, :, 1] = w.k[0, 0, 1]
     mass_case(w, [1, 3000, 40000], pairs=[(0, 1)])
+
+
+def test_wider_logits_stride():
+    """Rows further apart than the cache capacity (logits_stride > max_tokens)."""
+    w = W.int4_dense(700)
+    w.fmt = "fp16"
+    res = ST.decode_step(w, append=False, pairs=[(0, 4)])
+    cache = cache_for(w)
+    prefill(cache, w)
+    out, lse, lg, stride = run_attend(cache, w)
+    wide = np.full((1, w.hq, stride + 40), -1e30, np.float32)
+    wide[:, :, :stride] = lg
+    m = torch.full((1, w.hq), float("nan"), device="cuda")
+    kvc.kvc_topk_mass(cache.desc, w.hq, dev(wide), stride + 40, dev(lse), 33, m)
+    torch.cuda.synchronize()
+    for j in range(w.group):
+        h = 4 * w.group + j
+        p = np.exp(res.logits[(0, 4)][j] - res.lse[0, h])
+        assert_close(host(m)[0, h], S.topk_mass(p, 33), f"h={h}")
