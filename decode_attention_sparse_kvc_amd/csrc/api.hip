@@ -44,6 +44,12 @@ kvc_status check_cache(const kvc_cache* c) {
       (c->kT && !aligned(c->kT, 16)) || (c->k_absmax && !aligned(c->k_absmax, 16)))
     return KVC_ERR_INVALID;
   if ((c->k16 == nullptr) != (c->v16 == nullptr)) return KVC_ERR_INVALID;
+  if (c->n_outlier < 0 || c->n_outlier > KVC_MAX_OUTLIERS) return KVC_ERR_INVALID;
+  if (c->n_outlier > 0) {
+    if (c->format != KVC_FMT_INT4) return KVC_ERR_UNSUPPORTED;
+    if (!c->outlier_ch || !c->k_outlier || !aligned(c->outlier_ch, 16) || !aligned(c->k_outlier, 8))
+      return KVC_ERR_INVALID;
+  }
   return KVC_OK;
 }
 

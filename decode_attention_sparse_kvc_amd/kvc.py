@@ -16,9 +16,10 @@ from ctypes import POINTER, c_double, c_float, c_int32, c_int64, c_size_t, c_voi
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkvc.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 HEAD_DIM = 128
 GROUP = 64
+MAX_OUTLIERS = 4
 FMT = {"fp16": 0, "int4": 1, "int1": 2, "fp8": 3}
 SCORE = {"exact": 0, "critical": 1, "external": 2}
 SCORE_BLOCKS = 16   # OR'ed into a score mode: rank 64-token blocks
@@ -45,6 +46,7 @@ class kvc_cache(ctypes.Structure):
         ("k_tail", c_void_p), ("v_tail", c_void_p),
         ("k16", c_void_p), ("v16", c_void_p), ("kT", c_void_p),
         ("k_absmax", c_void_p),
+        ("n_outlier", c_int32), ("outlier_ch", c_void_p), ("k_outlier", c_void_p),
     ]
 
 

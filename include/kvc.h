@@ -47,10 +47,11 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 #define KVC_HEAD_DIM 128
 #define KVC_GROUP 64
 #define KVC_MAX_GQA 8          /* query heads per KV head supported by attend */
+#define KVC_MAX_OUTLIERS 4     /* fp16 outlier K channels per KV head (INT4) */
 
 typedef int32_t kvc_status;
 enum {
@@ -135,6 +136,19 @@ enum { KVC_OP_SCORE_TOPK = 1, KVC_OP_ATTEND = 2 };
  *             tokens (fp16-exact values); zero-filled by the caller at creation.
  *   seq_lens  int32 [B]: tokens cached per sequence; updated by
  *             kvc_quantize_append.
+ *
+ * Outlier channels (INT4 only; [MTG] 8.2: the few channels of very large
+ * magnitude are found offline by their variance and kept at full precision
+ * beside the quantized main store).  With n_outlier = m in 1..4, channels
+ * outlier_ch[4*g + j] (j < m; ascending, distinct, 0..127) of KV head g are
+ * K outlier channels.  When a group is quantized their K scale and zero are
+ * stored as 0 (so their codes are 0) and their fp16 values go to
+ *   k_outlier  fp16 [slot][4]: entry j holds channel outlier_ch[4*g + j]
+ *              (entries j >= m hold 0).
+ * Dequantized K is then code*s + z on the other channels and the fp16 value
+ * on the outlier channels; V is quantized as before.  The channel list is the
+ * caller's (an offline analysis) and must not change over the cache's life.
+ * n_outlier = 0 ignores outlier_ch and k_outlier.
  */
 typedef struct kvc_cache {
   int32_t abi_version;     /* KVC_ABI_VERSION */
@@ -159,6 +173,9 @@ typedef struct kvc_cache {
   uint16_t* v16;
   uint16_t* kT;
   float* k_absmax;
+  int32_t n_outlier;         /* 0..KVC_MAX_OUTLIERS fp16 K channels (INT4 only) */
+  const int32_t* outlier_ch; /* int32 [Hkv][4] outlier channel ids */
+  uint16_t* k_outlier;       /* fp16 [slot][4] their K values */
 } kvc_cache;
 
 /*

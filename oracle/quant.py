@@ -107,6 +107,61 @@ def dequant_values(code, s, z) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Outlier channels.  Meeting-LLM article, section 8.2: after LayerNorm a very
+# few channels carry values of very large magnitude; an offline analysis ranks
+# each head's channels by their variance and marks the top ones as outliers;
+# at run time the main cache holds the other channels quantized (with scale
+# and zero point) and a separate store holds the outlier channels at their
+# original precision; one fused kernel combines both into the full K vector.
+# Readings taken:
+#   * Variance: the population variance of each channel over the calibration
+#     rows, compared exactly (fp16 values are integers times 2^-24, so
+#     N * sum(x^2) - (sum x)^2 = N^2 * variance is an exact integer in those
+#     units); ranking by (variance desc, channel asc); the list is returned
+#     ascending.  The count is a parameter (0.5% of 128 channels is
+#     less than one; the synthetic layers plant 3 outlier channels per head).
+#   * Keys only: the outlier store holds K's outlier channels; V is quantized
+#     as before (its groups are per token across channels).
+#   * In the main store an outlier channel's K scale and zero point are 0, so
+#     its codes are 0 and it contributes nothing; its value comes from the
+#     fp16 store instead.
+# ---------------------------------------------------------------------------
+
+def outlier_channels(k16_calib: np.ndarray, m: int) -> np.ndarray:
+    """The m channels of largest variance over the rows k16_calib [N, D], ascending."""
+    x = np.asarray(k16_calib, dtype=np.float16).astype(np.float64) * 2.0 ** 24   # exact integers
+    n, d = x.shape
+    spread = []                                  # N^2 * variance per channel, exact
+    for c in range(d):
+        col = [int(v) for v in x[:, c]]
+        spread.append(n * sum(v * v for v in col) - sum(col) ** 2)
+    order = sorted(range(d), key=lambda c: (-spread[c], c))   # variance desc, channel asc
+    return np.array(sorted(order[:m]), dtype=np.int32)
+
+
+def quantize_keys_outliers(k16: np.ndarray, bits: int, out_ch: np.ndarray):
+    """quantize_keys with the channels out_ch kept at fp16.
+
+    Returns (codes, scale, zero, k_out) where codes/scale/zero are 0 on the
+    outlier channels and k_out [nq, m] holds their fp16 values.
+    """
+    code, s, z = quantize_keys(k16, bits)
+    ch = np.asarray(out_ch, dtype=np.int64)
+    code[:, ch] = 0
+    s[:, ch] = np.float16(0.0)
+    z[:, ch] = np.float16(0.0)
+    k_out = np.ascontiguousarray(k16[: code.shape[0]][:, ch])
+    return code, s, z, k_out
+
+
+def dequant_keys_outliers(code, s, z, out_ch, k_out) -> np.ndarray:
+    """fp64 K~ [nq, D]: dequantized codes, with the outlier channels' fp16 values."""
+    k = dequant_keys(code, s, z)
+    k[:, np.asarray(out_ch, dtype=np.int64)] = k_out.astype(np.float64)
+    return k
+
+
+# ---------------------------------------------------------------------------
 # FP8 (E4M3) warm tier.  Meeting-LLM article, section 6.2: the warm (L2) tier
 # prefers FP8 E4M3/E5M2 over INT4 where the hardware supports it natively; KV
 # compression survey, section 2: an FP8 E4M3/E5M2 KV cache halves memory and

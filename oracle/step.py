@@ -44,10 +44,16 @@ class HeadCache:
     v_code: Optional[np.ndarray] = None   # [nq, D] uint8
     v_scale: Optional[np.ndarray] = None  # [nq, D/64] f16
     v_zero: Optional[np.ndarray] = None
+    out_ch: Optional[np.ndarray] = None   # [m] K outlier channels (int4), ascending
+    k_out: Optional[np.ndarray] = None    # [nq, m] f16 their values
 
 
-def build_head_cache(k16: np.ndarray, v16: np.ndarray, fmt: str) -> HeadCache:
-    """Cache contents after appending the fp16 rows k16, v16 [n, D]."""
+def build_head_cache(k16: np.ndarray, v16: np.ndarray, fmt: str,
+                     out_ch: Optional[np.ndarray] = None) -> HeadCache:
+    """Cache contents after appending the fp16 rows k16, v16 [n, D].
+
+    out_ch: K channels kept at fp16 beside the INT4 codes (outlier channels).
+    """
     n = k16.shape[0]
     kabs = np.abs(k16).max(axis=0) if n else np.zeros(k16.shape[1], np.float16)
     hc = HeadCache(n=n, nq=n, k16=k16, v16=v16, kabs=kabs.astype(np.float16))
@@ -55,7 +61,12 @@ def build_head_cache(k16: np.ndarray, v16: np.ndarray, fmt: str) -> HeadCache:
         hc.k_code, hc.v_code = Q.encode_fp8(k16), Q.encode_fp8(v16)
     elif fmt in BITS:
         b = BITS[fmt]
-        hc.k_code, hc.k_scale, hc.k_zero = Q.quantize_keys(k16, b)
+        if out_ch is not None and len(out_ch):
+            assert fmt == "int4"
+            hc.out_ch = np.asarray(out_ch, dtype=np.int32)
+            hc.k_code, hc.k_scale, hc.k_zero, hc.k_out = Q.quantize_keys_outliers(k16, b, hc.out_ch)
+        else:
+            hc.k_code, hc.k_scale, hc.k_zero = Q.quantize_keys(k16, b)
         hc.v_code, hc.v_scale, hc.v_zero = Q.quantize_values(v16, b)
         hc.nq = hc.k_code.shape[0]
     return hc
@@ -69,7 +80,10 @@ def token_rows(hc: HeadCache, fp16_mask: Optional[np.ndarray] = None) -> Tuple[n
         keys = Q.decode_fp8(hc.k_code)
         vals = Q.decode_fp8(hc.v_code)
     elif hc.k_code is not None and hc.nq:
-        kq = Q.dequant_keys(hc.k_code, hc.k_scale, hc.k_zero)
+        if hc.out_ch is not None:
+            kq = Q.dequant_keys_outliers(hc.k_code, hc.k_scale, hc.k_zero, hc.out_ch, hc.k_out)
+        else:
+            kq = Q.dequant_keys(hc.k_code, hc.k_scale, hc.k_zero)
         vq = Q.dequant_values(hc.v_code, hc.v_scale, hc.v_zero)
         quant = np.ones(hc.nq, dtype=bool)
         if fp16_mask is not None:
@@ -114,7 +128,8 @@ def decode_step(w, append: bool = True, pairs=None, k_max: Optional[int] = None)
             k16 = np.concatenate([k16, w.k_new[b, :, g]])
             v16 = np.concatenate([v16, w.v_new[b, :, g]])
         n = k16.shape[0]
-        hc = build_head_cache(k16, v16, w.fmt)
+        oc = None if getattr(w, "outlier_ch", None) is None else w.outlier_ch[g]
+        hc = build_head_cache(k16, v16, w.fmt, oc)
         res.caches[(b, g)] = hc
         q_grp = w.q[b, g * G:(g + 1) * G]
 

@@ -48,7 +48,7 @@ def test_struct_field_count_matches_header():
 
 def _desc(**kw):
     d = kvc.kvc_cache()
-    base = dict(abi_version=1, format=1, batch=1, num_kv_heads=1, head_dim=128, group_size=64,
+    base = dict(abi_version=2, format=1, batch=1, num_kv_heads=1, head_dim=128, group_size=64,
                 page_size=0, max_tokens=64, max_pages=0, num_pages=0,
                 seq_lens=0x1000, k_codes=0x2000, v_codes=0x3000, k_meta=0x4000, v_meta=0x5000,
                 k_tail=0x6000, v_tail=0x7000, k_absmax=0x8000)
@@ -59,7 +59,7 @@ def _desc(**kw):
 
 
 BAD = [
-    (dict(abi_version=2), 1), (dict(format=7), 3), (dict(head_dim=64), 3), (dict(group_size=32), 3),
+    (dict(abi_version=1), 1), (dict(format=7), 3), (dict(head_dim=64), 3), (dict(group_size=32), 3),
     (dict(batch=0), 2), (dict(max_tokens=100), 2), (dict(seq_lens=None), 1),
     (dict(k_codes=None), 1), (dict(k_meta=0x4004), 1), (dict(k_codes=0x2008), 1),
     (dict(page_size=8, max_tokens=64, max_pages=8, num_pages=8, block_table=0x9000), 2),
@@ -67,6 +67,12 @@ BAD = [
     (dict(page_size=16, max_tokens=64, max_pages=2, num_pages=4, block_table=0x9000), 2),
     (dict(page_size=16, max_tokens=64, max_pages=4, num_pages=4), 1),
     (dict(format=0), 1),   # fp16 cache without k16/v16
+    (dict(n_outlier=5, outlier_ch=0xA000, k_outlier=0xB000), 1),
+    (dict(n_outlier=-1), 1),
+    (dict(n_outlier=2, outlier_ch=0xA000), 1),                        # no outlier store
+    (dict(n_outlier=2, outlier_ch=0xA004, k_outlier=0xB000), 1),      # misaligned list
+    (dict(n_outlier=2, outlier_ch=0xA000, k_outlier=0xB004), 1),      # misaligned store
+    (dict(format=2, n_outlier=1, outlier_ch=0xA000, k_outlier=0xB000), 3),   # INT4 only
 ]
 
 

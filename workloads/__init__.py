@@ -68,6 +68,8 @@ class Workload:
     kT: bool = False                     # keep a channel-major K copy (fp16 caches)
     fp16_shadow: bool = False            # keep full fp16 rows beside quantized codes
     prefer_k: int = 0                    # > 0: also the top-k probability mass of each row
+    outlier_ch: Optional[np.ndarray] = None   # [Hkv, m] int4: K channels kept at fp16
+    planted: Optional[np.ndarray] = None      # [Hkv, m] the K channels the generator scaled
 
     @property
     def group(self) -> int:
@@ -171,23 +173,37 @@ def _llama_dense(name: str, fmt: str, n_ctx: int, seed: int, outliers: bool) -> 
     hq, hkv = 32, 8
     k = _bulk_normal(s_k, (1, n_ctx, hkv, HEAD_DIM))
     v = _bulk_normal(s_v, (1, n_ctx, hkv, HEAD_DIM))
+    planted = None
     if outliers:
+        planted = np.zeros((hkv, 3), np.int32)
         for g in range(hkv):
             out = rng.choice(HEAD_DIM, 3, replace=False)
             k[:, :, g, out] *= np.float32(8.0)
+            planted[g] = np.sort(out)
     q = _normal(rng, (1, hq, HEAD_DIM))
     k_new, v_new = _new_token(rng, 1, hkv)
     return Workload(
         name=name, seed=seed, fmt=fmt, batch=1, hq=hq, hkv=hkv,
         k=_f16(k), v=_f16(v), q=q.astype(np.float16),
         k_new=k_new, v_new=v_new, seq_lens=np.array([n_ctx], np.int32),
-        mode="dense", max_tokens=_capacity(n_ctx, 64))
+        mode="dense", max_tokens=_capacity(n_ctx, 64), planted=planted)
 
 
 def int4_dense(n_ctx: int = 32768, seed: int = 1) -> Workload:
     """INT4 K per-channel / V group-64, dense; 2% outlier K channels x8 (seed 1)."""
     tag = "32k" if n_ctx == 32768 else ("128k" if n_ctx == 131072 else str(n_ctx))
     return _llama_dense(f"llama8b_layer_int4_dense_{tag}", "int4", n_ctx, seed, True)
+
+
+def int4_outlier_dense(n_ctx: int = 131072, seed: int = 1) -> Workload:
+    """The INT4 layer (seed 1) with its outlier K channels kept at fp16 beside the
+    codes.  The channel list stands in for the offline variance analysis: it is
+    the generator's planted channels (x8, so 64x the variance of the others)."""
+    w = int4_dense(n_ctx, seed)
+    tag = "32k" if n_ctx == 32768 else ("128k" if n_ctx == 131072 else str(n_ctx))
+    w.name = f"llama8b_layer_int4_outlier3_dense_{tag}"
+    w.outlier_ch = w.planted.copy()
+    return w
 
 
 def fp8_dense(n_ctx: int = 131072, seed: int = 1) -> Workload:
@@ -325,5 +341,6 @@ FULL = {
     "llama8b_layer_fp16_crit8_block61_128k": lambda: sparse_blocks(131072, "fp16"),
     "llama8b_layer_int4_crit8_block61_128k": lambda: sparse_blocks(131072, "int4"),
     "llama8b_layer_fp8_dense_128k": lambda: fp8_dense(131072),
+    "llama8b_layer_int4_outlier3_dense_128k": lambda: int4_outlier_dense(131072),
     "llama8b_layer_int1_dense_128k_topmass3pct": lambda: _with_prefer(int1_dense(131072), 3932),
 }
