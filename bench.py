@@ -78,24 +78,27 @@ def attend_bytes(w, lens, k_sel) -> int:
     K/V (codes + metadata, or fp16 rows), q, out, lse and logits written."""
     fmt, hkv, hq, B = w.fmt, w.hkv, w.hq, w.batch
     total = 0
+    # quantized tokens of a cache with outlier K channels also read their
+    # 8-byte outlier-store entry
+    code = dict(CODE_BYTES, int4=CODE_BYTES["int4"] + (8 if w.outlier_ch is not None else 0))
     for b, n in enumerate(lens):
         n = int(n)
         nq = (n // 64) * 64 if fmt != "fp8" else n     # fp8 has no fp16 tail
         if w.mode == "dense":
-            per_head = nq * CODE_BYTES[fmt] + (n - nq) * 512 if fmt != "fp16" else n * 512
+            per_head = nq * code[fmt] + (n - nq) * 512 if fmt != "fp16" else n * 512
         elif w.mode == "drop":
             w0 = max(n - w.n_window, min(w.n_sink, n))
             attended = min(w.n_sink, n) + int(k_sel[b]) + (n - w0)
-            per_head = attended * (512 if fmt == "fp16" else CODE_BYTES[fmt])
+            per_head = attended * (512 if fmt == "fp16" else code[fmt])
         elif w.mode == "blocks":   # k_sel blocks of 64 tokens (every candidate range holds them)
             w0 = max(n - w.n_window, min(w.n_sink, n))
             attended = min(w.n_sink, n) + 64 * int(k_sel[b]) + (n - w0)
-            per_head = attended * (512 if fmt == "fp16" else CODE_BYTES[fmt])
+            per_head = attended * (512 if fmt == "fp16" else code[fmt])
         else:   # keep: fp16 keep set, codes for the rest (tail rows fp16)
             w0 = max(n - w.n_window, min(w.n_sink, n))
             keep = min(w.n_sink, n) + int(k_sel[b]) + (n - w0)
             rest = n - keep
-            per_head = keep * 512 + rest * CODE_BYTES[fmt]
+            per_head = keep * 512 + rest * code[fmt]
         total += hkv * per_head
         if w.accumulate or w.prefer_k:            # logits written
             if w.mode == "drop":
@@ -183,8 +186,9 @@ def main():
         num_pages = w.batch * per
         perm = np.random.default_rng(w.seed).permutation(num_pages).astype(np.int32)
         table = torch.from_numpy(perm.reshape(w.batch, per))
+    oc = torch.from_numpy(w.outlier_ch) if w.outlier_ch is not None else None
     base = KvcCache(w.fmt, w.batch, w.hkv, cap, page_size=w.page_size, block_table=table,
-                    num_pages=num_pages, fp16_rows=w.fp16_shadow, kT=w.kT)
+                    num_pages=num_pages, fp16_rows=w.fp16_shadow, kT=w.kT, outlier_ch=oc)
     base.append(torch.from_numpy(w.k).to(dev), torch.from_numpy(w.v).to(dev),
                 torch.from_numpy(w.seq_lens).to(dev))
     torch.cuda.synchronize()

@@ -167,10 +167,13 @@ __device__ inline int window_start(int n, int n_sink, int n_window) {
 // Raw loads of one 64-token group: code tiles, metadata words, selection bits.
 // TILED: the group's four 16-token tiles are addressed one by one (pages of
 // 16 or 32 tokens); otherwise the group is one contiguous run of slots.
-template <int FMT, bool TILED>
+// OUTL: INT4 with outlier channels; ko holds the outlier-store entries of
+// token l of the group in lane l.
+template <int FMT, bool TILED, bool OUTL = false>
 struct GroupData {
   uint4 k[FMT == KVC_FMT_INT4 ? 4 : 1];
   uint4 v[FMT == KVC_FMT_INT4 ? 4 : 1];
+  uint2 ko;
   uint2 km;
   uint2 vm[TILED ? 4 : 1];   // TILED: tile j's words in lanes 16j..16j+15, zero elsewhere
   uint2 bits;   // drop/keep: selected tokens of the group (two 32-token words)
@@ -260,12 +263,13 @@ __device__ inline int64_t group_slot(const AttendArgs& a, int b, int g, int gi, 
 // so the wait before a group's first use leaves the next group's loads in
 // flight.  live == false (a group past the wave's last) and a page outside the
 // pool give empty ranges: the loads read zero without touching memory.
-template <int FMT, bool DENSE, bool TILED>
+template <int FMT, bool DENSE, bool TILED, bool OUTL = false>
 __device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, int gi, bool live,
-                                           uint4 tw, int lane, GroupData<FMT, TILED>& d) {
+                                           uint4 tw, int lane, GroupData<FMT, TILED, OUTL>& d) {
   const kvc_cache& c = a.c;
   const int t0 = gi * GS;
   const uint32_t l16 = 16u * lane, l8 = 8u * lane;
+  constexpr uint32_t OB = KVC_MAX_OUTLIERS * 2;   // outlier-store bytes per slot (= 8)
   if constexpr (!TILED) {   // 64 consecutive slots: one range per array
     const int64_t s0 = group_slot(a, b, g, gi, t0, tw);
     const bool ok = live && s0 >= 0;
@@ -280,6 +284,7 @@ __device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, in
       d.v[j] = buf_load16_stream(rv, l16 + j * UNIT_BYTES);
     }
     d.vm[0] = buf_load8(make_buf(c.v_meta + sl * 4, ok ? GS * 8u : 0u), l8);
+    if constexpr (OUTL) d.ko = buf_load8(make_buf(c.k_outlier + sl * KVC_MAX_OUTLIERS, ok ? GS * OB : 0u), l8);
   } else {                  // INT4 tiles on pages of 16 or 32 tokens
     int64_t st[4];
     bool ok[4];
@@ -298,6 +303,15 @@ __device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, in
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       d.vm[j] = buf_load8(make_buf(c.v_meta + st[j] * 4, ok[j] ? TILE * 8u : 0u), l8 - 128u * j);
+    if constexpr (OUTL) {   // (as the V metadata: lanes of other tiles read zero)
+      d.ko = uint2{0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint2 o = buf_load8(make_buf(c.k_outlier + st[j] * KVC_MAX_OUTLIERS, ok[j] ? TILE * OB : 0u),
+                                  l8 - TILE * OB * j);
+        d.ko = uint2{d.ko.x | o.x, d.ko.y | o.y};
+      }
+    }
   }
   const uint16_t* km = c.k_meta +
       ((((int64_t)b * c.num_kv_heads + g) * (c.max_tokens / GS) + gi) * 2) * D;
@@ -324,11 +338,11 @@ __device__ inline float ror4(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
 }
 
-template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED>
+template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED, bool OUTL = false>
 __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, int gi, int lane,
-                                           int w, int n, const GroupData<FMT, TILED>& d, QState& st,
-                                           const h2* qv, const Dec& dc, uint16_t* sKm,
-                                           uint16_t* sVm) {
+                                           int w, int n, const GroupData<FMT, TILED, OUTL>& d,
+                                           QState& st, const h2* qv, const h8& qo, const Dec& dc,
+                                           uint16_t* sKm, uint16_t* sVm) {
   const int G = a.G;
   const int col = lane & 15, kb = lane >> 4, head = col & 7;
   const bool hv = head < G;
@@ -401,11 +415,28 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
     }
   }
 
-  // ---- S^T = codes x q'^T per 16-token tile; hi + lo columns added (raw units)
+  // ---- S^T = codes x q'^T per 16-token tile; hi + lo columns added (raw units).
+  // Outlier channels (scale and zero 0 in the main store) add one more product
+  // per tile: A = the group's fp16 outlier entries (lane l: token l, in row
+  // l % 16 at k = 8 (l / 16) + e; entries past the list masked to 0), and
+  // B = q on those channels in the hi columns of the lanes whose k block is
+  // the tile (qo, zero elsewhere), so tile j's rows take only tokens 16j + n.
+  h8 ao = h8{};
+  if constexpr (OUTL) {
+    const int m = a.c.n_outlier;
+    const uint32_t om0 = m >= 2 ? 0xFFFFFFFFu : (m == 1 ? 0xFFFFu : 0u);
+    const uint32_t om1 = m >= 4 ? 0xFFFFFFFFu : (m == 3 ? 0xFFFFu : 0u);
+    ao = bc<h8>(uint4{d.ko.x & om0, d.ko.y & om1, 0u, 0u});
+  }
   float x[4][4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     f4 s = bias;
+    if constexpr (OUTL) {
+      const uint32_t sel = (lane >> 4) == j ? 0xFFFFFFFFu : 0u;
+      const uint4 qb = bc<uint4>(qo);
+      s = mfma32(ao, bc<h8>(uint4{qb.x & sel, qb.y & sel, 0u, 0u}), s);
+    }
     if constexpr (FMT == KVC_FMT_INT4) {
       s = mfma32(dec4k(d.k[j].x, dc), qp[0], s);
       s = mfma32(dec4k(d.k[j].y, dc), qp[1], s);
@@ -606,7 +637,7 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
   }
 }
 
-template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED>
+template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED, bool OUTL = false>
 __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, int split, int lane, int w,
                            float* sO, float* sML, uint16_t* sKm, uint16_t* sVm) {
   const kvc_cache& c = a.c;
@@ -658,10 +689,22 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
 #pragma unroll
     for (int k = 0; k < 4; ++k) raw[k] = qp[k];
   }
-  GroupData<FMT, TILED> d0, d1;
-  load_group<FMT, DENSE, TILED>(a, b, g, gid(0), nmine > 0, t0w, lane, d0);
+  // q on the outlier channels: B operand of the outlier product (the heads'
+  // hi columns, entries past the list 0)
+  h8 qo = h8{};
+  if constexpr (OUTL) {
+    if (hi_lane) {
+      const uint16_t* qh = a.q + ((int64_t)b * a.hq + g * G + head) * D;
+      const auto* oc = scalar_ptr(c.outlier_ch + g * KVC_MAX_OUTLIERS);
+#pragma unroll
+      for (int e = 0; e < KVC_MAX_OUTLIERS; ++e)
+        if (e < c.n_outlier) qo[e] = bc<_Float16>(qh[min(max((int)oc[e], 0), D - 1)]);
+    }
+  }
+  GroupData<FMT, TILED, OUTL> d0, d1;
+  load_group<FMT, DENSE, TILED, OUTL>(a, b, g, gid(0), nmine > 0, t0w, lane, d0);
   t0w = group_table(a, rtab, gid(2));
-  load_group<FMT, DENSE, TILED>(a, b, g, gid(1), nmine > 1, t1w, lane, d1);
+  load_group<FMT, DENSE, TILED, OUTL>(a, b, g, gid(1), nmine > 1, t1w, lane, d1);
   t1w = group_table(a, rtab, gid(3));
   // q is in registers before the group loop (so no wait inside the loop, where
   // the next group's loads are in flight, is spent on it); the memory clobber
@@ -692,15 +735,15 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
   // and its wait leaves the newer group's loads in flight.
   int k = 0;
   for (; k + 2 <= nmine; k += 2) {
-    group_body<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, gid(k), lane, w, n, d0, st, qv, dc, sKm, sVm);
-    load_group<FMT, DENSE, TILED>(a, b, g, gid(k + 2), k + 2 < nmine, t0w, lane, d0);
+    group_body<FMT, DENSE, LOGITS, PACK, TILED, OUTL>(a, b, g, gid(k), lane, w, n, d0, st, qv, qo, dc, sKm, sVm);
+    load_group<FMT, DENSE, TILED, OUTL>(a, b, g, gid(k + 2), k + 2 < nmine, t0w, lane, d0);
     t0w = group_table(a, rtab, gid(k + 4));
-    group_body<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, gid(k + 1), lane, w, n, d1, st, qv, dc, sKm, sVm);
-    load_group<FMT, DENSE, TILED>(a, b, g, gid(k + 3), k + 3 < nmine, t1w, lane, d1);
+    group_body<FMT, DENSE, LOGITS, PACK, TILED, OUTL>(a, b, g, gid(k + 1), lane, w, n, d1, st, qv, qo, dc, sKm, sVm);
+    load_group<FMT, DENSE, TILED, OUTL>(a, b, g, gid(k + 3), k + 3 < nmine, t1w, lane, d1);
     t1w = group_table(a, rtab, gid(k + 5));
   }
   if (k < nmine)
-    group_body<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, gid(k), lane, w, n, d0, st, qv, dc, sKm, sVm);
+    group_body<FMT, DENSE, LOGITS, PACK, TILED, OUTL>(a, b, g, gid(k), lane, w, n, d0, st, qv, qo, dc, sKm, sVm);
 
   // ---- finish: sums over the lanes of each head, bases and zero points
   float l = st.l, sz0 = st.sz0, sz1 = st.sz1;
@@ -1071,7 +1114,7 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
   }
 }
 
-template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED>
+template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED, bool OUTL = false>
 __global__ __launch_bounds__(64 * waves_per_wg(FMT), waves_per_wg(FMT) < 8 ? 8 / waves_per_wg(FMT) : 1)
 void attend_kernel(AttendArgs a) {
   constexpr int NW = waves_per_wg(FMT);
@@ -1113,7 +1156,7 @@ void attend_kernel(AttendArgs a) {
 
   if constexpr (grouped(FMT)) {
     if (split < a.s_q)
-      quant_role<FMT, DENSE, LOGITS, PACK, TILED>(a, b, g, split, lane, w, sO, sML, sKm, sVm);
+      quant_role<FMT, DENSE, LOGITS, PACK, TILED, OUTL>(a, b, g, split, lane, w, sO, sML, sKm, sVm);
     else
       rows_role<FMT, DENSE, LOGITS>(a, b, g, split - a.s_q, lane, w, sO, sML, sTok);
   } else {
@@ -1342,14 +1385,27 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   return p;
 }
 
-// Kernel instance for (format, mode, logits, packing, tile addressing); fp16
-// caches have no quantized role, and only INT4 has 16-token tiles.
+// Kernel instance for (format, mode, logits, packing, tile addressing, INT4
+// outlier channels); fp16 caches have no quantized role, and only INT4 has
+// 16-token tiles and outlier channels.
+template <int F, bool DN, bool LG, bool OUTL>
+void launch_tiles(dim3 grid, hipStream_t s, const AttendArgs& a, bool pk, bool tiled) {
+  if (tiled) {
+    if (pk) attend_kernel<F, DN, LG, true, true, OUTL><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
+    else attend_kernel<F, DN, LG, false, true, OUTL><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
+  } else {
+    if (pk) attend_kernel<F, DN, LG, true, false, OUTL><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
+    else attend_kernel<F, DN, LG, false, false, OUTL><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
+  }
+}
 template <int F, bool DN, bool LG>
 void launch_inst(dim3 grid, hipStream_t s, const AttendArgs& a, bool pk, bool tiled) {
   if constexpr (!grouped(F)) {
     attend_kernel<F, DN, LG, false, false><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
   } else if constexpr (F == KVC_FMT_INT4) {
-    if (tiled) {
+    if (a.c.n_outlier > 0) {
+      launch_tiles<F, DN, LG, true>(grid, s, a, pk, tiled);
+    } else if (tiled) {
       if (pk) attend_kernel<F, DN, LG, true, true><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
       else attend_kernel<F, DN, LG, false, true><<<grid, 64 * waves_per_wg(F), 0, s>>>(a);
     } else {

@@ -8,6 +8,8 @@
 //   s = fp16((max - min) / (2^b - 1) + 0), z = fp16(min + 0),
 //   code = s == 0 ? 0 : clamp(rint((x - z) / s), 0, 2^b - 1) in fp32.
 // The packed code tiles follow the lane/dword layout of include/kvc.h.
+// INT4 outlier channels (meeting-LLM article section 8.2) get scale and zero 0
+// in the main store and their fp16 values in the outlier store.
 // FP8 (E4M3) caches encode every appended row at once (no groups, no tail);
 // the channel-major copy then holds the decoded values.
 // A second, per-sequence kernel then rewrites the fp16 tail and seq_lens.
@@ -18,6 +20,7 @@ namespace kvc {
 namespace {
 
 constexpr int NT = 256;   // threads per workgroup
+static_assert(NT == GS * KVC_MAX_OUTLIERS, "one thread per (token, outlier entry) of a group");
 
 template <int BITS>
 struct GroupQuant {
@@ -145,6 +148,11 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
     __syncthreads();
     mn = fminf(sRed[0][ck], sRed[2][ck]);
     mx = fmaxf(sRed[1][ck], sRed[3][ck]);
+    // outlier channels (INT4): scale and zero 0, hence codes 0; their values
+    // go to the fp16 outlier store below
+    const int n_out = BITS == 4 ? c.n_outlier : 0;
+    for (int j = 0; j < n_out; ++j)
+      if (c.outlier_ch[g * KVC_MAX_OUTLIERS + j] == ck) mn = mx = 0.0f;
     float ks, kz;
     uint16_t ks16, kz16;
     GroupQuant<BITS>::params(mn, mx, ks, kz, ks16, kz16);
@@ -156,6 +164,15 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
     }
     for (int r = 32 * hk; r < 32 * hk + 32; ++r)
       sKc[r][ck] = (uint8_t)GroupQuant<BITS>::code(h2f(sK[r][ck]), ks, kz);
+
+    // ---- outlier store: thread (token r, entry j) writes the token's fp16
+    // value of outlier channel j (0 past the list)
+    if (n_out > 0) {
+      const int r = tid >> 2, j = tid & 3;
+      const int ch = min(max(c.outlier_ch[g * KVC_MAX_OUTLIERS + j], 0), D - 1);
+      const int64_t slot = slot_of(c, b, g, g0 + r);
+      if (slot >= 0) c.k_outlier[slot * KVC_MAX_OUTLIERS + j] = j < n_out ? sK[r][ch] : (uint16_t)0;
+    }
 
     // ---- V: per token over each 64-channel half.  Thread (token nv, quarter qv).
     const int nv = tid >> 2, qv = tid & 3, jv = qv >> 1, c0 = 32 * qv;

@@ -146,6 +146,7 @@ constexpr int GMAX = 16;       // query heads per KV head supported by scoring
 static_assert(GMAX == GMAX_PREP, "prep writes the q operands the scoring kernel reads");
 constexpr int CB_CRIT = 8;     // channels whose loads are issued together (critical channels)
 constexpr int CB_EXACT = 32;   // (every channel)
+constexpr uint32_t OUT_TAG = 0xFFFF0000u;   // staged K metadata word of an outlier channel
 
 // Scores of one token on the channel list: per query head, +0.0 then one
 // channel at a time in ascending order.  The loads of CB channels are issued
@@ -219,8 +220,16 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
       s2 = km[j];
       z2 = km[D / 2 + j];
     }
-    smeta[(tid / 64) * D + 2 * j] = (s2 & 0xFFFFu) | (z2 << 16);
-    smeta[(tid / 64) * D + 2 * j + 1] = (s2 >> 16) | (z2 & 0xFFFF0000u);
+    uint32_t m0 = (s2 & 0xFFFFu) | (z2 << 16), m1 = (s2 >> 16) | (z2 & 0xFFFF0000u);
+    // outlier channels (INT4): the word names the outlier store entry instead
+    // (a zero-point field of all ones is a NaN no quantized group stores)
+    for (int e = 0; e < c.n_outlier; ++e) {
+      const int oc = c.outlier_ch[g * KVC_MAX_OUTLIERS + e];
+      if (oc == 2 * j) m0 = OUT_TAG | e;
+      if (oc == 2 * j + 1) m1 = OUT_TAG | e;
+    }
+    smeta[(tid / 64) * D + 2 * j] = m0;
+    smeta[(tid / 64) * D + 2 * j + 1] = m1;
   }
   // q on the channel list: gathered by prep (critical mode) or channel k itself
   for (int e = tid; e < G * nch; e += ST) {
@@ -283,7 +292,10 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
             return unit[lane * 4 + (FMT == KVC_FMT_INT4 ? (ch % 32) / 8 : dsel)];
           };
           auto aux = [&](int ch) -> uint32_t { return meta[ch]; };
+          const bool has_out = FMT == KVC_FMT_INT4 && c.n_outlier > 0;
           auto value = [&](int ch, uint32_t raw, uint32_t m) {
+            if (has_out && (m & 0xFFFF0000u) == OUT_TAG)   // fp16 outlier store entry
+              return (double)h2f(c.k_outlier[slot * KVC_MAX_OUTLIERS + (m & 3u)]);
             const uint32_t code = FMT == KVC_FMT_INT4 ? (raw >> nib_pos(ch % 8)) & 15u
                                                       : (raw >> bit_pos(ch % 32)) & 1u;
             return __dadd_rn(__dmul_rn((double)code, (double)h2f((uint16_t)(m & 0xFFFFu))),

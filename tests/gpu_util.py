@@ -19,8 +19,10 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 def cache_for(w, max_tokens=None) -> KvcCache:
     table = torch.from_numpy(w.block_table) if w.block_table is not None else None
+    oc = torch.from_numpy(w.outlier_ch) if w.outlier_ch is not None else None
     return KvcCache(w.fmt, w.batch, w.hkv, max_tokens or w.max_tokens, page_size=w.page_size,
-                    block_table=table, num_pages=w.num_pages, fp16_rows=w.fp16_shadow, kT=w.kT)
+                    block_table=table, num_pages=w.num_pages, fp16_rows=w.fp16_shadow, kT=w.kT,
+                    outlier_ch=oc)
 
 
 def prefill(cache: KvcCache, w):

@@ -1,0 +1,139 @@
+"""GPU parity of INT4 caches with outlier K channels kept at fp16 (meeting-LLM
+article, section 8.2): main-store codes, scales, zeros and the outlier store bit
+for bit against the oracle; scores and Top-K bit for bit; attention (dense,
+drop, contiguous and paged) within 1e-3 + 2e-3 |ref|, including the 128K layer."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from decode_attention_sparse_kvc_amd import KvcCache
+from gpu_util import assert_close, cache_for, dev, host, prefill
+from kvc_layout import slots, unpack_codes
+from oracle import quant as Q
+from oracle import step as ST
+from test_gpu_attend import check_against_oracle, paged, run_attend, sel_tensor
+from test_gpu_topk import check_topk, run_topk, topk_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _u16(a):
+    return np.ascontiguousarray(a).view(np.uint16)
+
+
+@pytest.mark.parametrize("page,m", [(0, 3), (16, 1), (64, 4)])
+def test_store_after_ragged_appends(page, m):
+    """Two sequences appended in ragged steps (groups completed by prefill-sized
+    and single-token appends): main store and outlier store equal the oracle's."""
+    rng = np.random.default_rng(31 + m)
+    B, hkv, cap = 2, 2, 384
+    ch = np.stack([np.sort(rng.choice(128, m, replace=False)) for _ in range(hkv)]).astype(np.int32)
+    table, npages = None, 0
+    if page:
+        per = cap // page
+        npages = B * per
+        table = rng.permutation(npages).astype(np.int32).reshape(B, per)
+    cache = KvcCache("int4", B, hkv, cap, page_size=page,
+                     block_table=None if table is None else torch.from_numpy(table),
+                     num_pages=npages, outlier_ch=torch.from_numpy(ch))
+    rows_k = [np.zeros((0, hkv, 128), np.float16) for _ in range(B)]
+    rows_v = [np.zeros((0, hkv, 128), np.float16) for _ in range(B)]
+    for step, n_new in enumerate([[130, 64], [1, 63], [62, 1], [1, 1]]):
+        n_new = np.array(n_new, np.int32)
+        mx = int(n_new.max())
+        k = rng.normal(size=(B, mx, hkv, 128)).astype(np.float32)
+        for g in range(hkv):
+            k[:, :, g, ch[g]] *= 20.0
+        k = k.astype(np.float16)
+        v = rng.normal(size=(B, mx, hkv, 128)).astype(np.float16)
+        cache.append(dev(k), dev(v), dev(n_new))
+        for b in range(B):
+            rows_k[b] = np.concatenate([rows_k[b], k[b, : n_new[b]]])
+            rows_v[b] = np.concatenate([rows_v[b], v[b, : n_new[b]]])
+    torch.cuda.synchronize()
+    kc, km, ko = host(cache.k_codes), host(cache.k_meta), host(cache.k_outlier)
+    for b in range(B):
+        n = rows_k[b].shape[0]
+        for g in range(hkv):
+            hc = ST.build_head_cache(rows_k[b][:, g], rows_v[b][:, g], "int4", ch[g])
+            nq = hc.nq
+            sl = slots(b, g, np.arange(nq), hkv, cap, page, table)
+            where = f"b={b} g={g} n={n}"
+            assert np.array_equal(unpack_codes(kc, "int4", "k", sl), hc.k_code), "K codes " + where
+            assert np.array_equal(_u16(km[b, g, : nq // 64, 0]), _u16(hc.k_scale)), where
+            assert np.array_equal(_u16(km[b, g, : nq // 64, 1]), _u16(hc.k_zero)), where
+            assert np.array_equal(_u16(ko[sl, :m]), _u16(hc.k_out)), "outlier store " + where
+            assert not _u16(ko[sl, m:]).any(), where
+
+
+@pytest.mark.parametrize("n", [63, 777, 4095, 4097])
+def test_dense(n):
+    """Prefill n tokens, append the step's token (4095 + 1 completes a group on the
+    single-token path), attend over everything."""
+    w = W.int4_outlier_dense(n)
+    res = ST.decode_step(w, append=True, pairs=[(0, 0), (0, 3), (0, 7)])
+    cache = cache_for(w)
+    prefill(cache, w)
+    cache.append(dev(w.k_new), dev(w.v_new))
+    out, lse, lg, _ = run_attend(cache, w)
+    G = w.group
+    for (b, g), toks in res.tokens.items():
+        sl = slice(g * G, (g + 1) * G)
+        assert_close(out[b, sl], res.o[b, sl], f"o g={g}")
+        assert_close(lse[b, sl], res.lse[b, sl], f"lse g={g}")
+        assert_close(lg[b, sl][:, toks], res.logits[(b, g)], f"logits g={g}")
+
+
+@pytest.mark.parametrize("page", [16, 32, 64])
+def test_dense_paged(page):
+    w = paged(W.int4_outlier_dense(3000), page, seed=page)
+    res = ST.decode_step(w, append=False, pairs=[(0, 1), (0, 6)])
+    cache = cache_for(w)
+    prefill(cache, w)
+    out, lse, _, _ = run_attend(cache, w, logits=False)
+    G = w.group
+    for (b, g) in res.tokens:
+        sl = slice(g * G, (g + 1) * G)
+        assert_close(out[b, sl], res.o[b, sl], f"o g={g}")
+        assert_close(lse[b, sl], res.lse[b, sl], f"lse g={g}")
+
+
+def test_exact_topk_single_head():
+    """The 4K single-head case with its 4 outlier channels found by the offline
+    variance analysis: exact scores (which read the outlier store) and indices bit
+    for bit, then drop-mode attention over sinks + Top-128 + window."""
+    w = W.single_head_4k(2000)
+    w.outlier_ch = Q.outlier_channels(w.k[0, :, 0], 4)[None]
+    res, cache, idx = topk_case(w, append=True)
+    km = int(w.top_k.max())
+    out, lse, lg, stride = run_attend(cache, w, sel_tensor(res, w, km), km)
+    check_against_oracle(w, res, out, lse, lg, km, stride)
+
+
+def test_critical_topk_drop():
+    """Critical channels on an INT4 layer whose outlier channels are the planted
+    ones: scores, channels and indices bit for bit, attention in tolerance."""
+    w = W.sparse_crit8(n_ctx=3000, n_planted=40, top_k=200)
+    w.fmt = "int4"
+    w.outlier_ch = np.stack([Q.outlier_channels(w.k[0, :, g], 2) for g in range(w.hkv)])
+    res, cache, idx = topk_case(w)
+    km = int(w.top_k.max())
+    out, lse, lg, stride = run_attend(cache, w, sel_tensor(res, w, km), km)
+    check_against_oracle(w, res, out, lse, lg, km, stride)
+
+
+def test_full_size_dense():
+    """The 128K INT4 layer with its 3 outlier channels per KV head, in the
+    benchmark's launch configuration, sampled pairs."""
+    w = W.FULL["llama8b_layer_int4_outlier3_dense_128k"]()
+    res = ST.decode_step(w, append=True, pairs=[(0, 2), (0, 5)])
+    cache = cache_for(w)
+    prefill(cache, w)
+    cache.append(dev(w.k_new), dev(w.v_new))
+    out, lse, _, _ = run_attend(cache, w, logits=False)
+    G = w.group
+    for (b, g) in res.tokens:
+        sl = slice(g * G, (g + 1) * G)
+        assert_close(out[b, sl], res.o[b, sl], f"o g={g}")
+        assert_close(lse[b, sl], res.lse[b, sl], f"lse g={g}")
