@@ -1,7 +1,8 @@
 """GPU parity of INT4 caches with outlier K channels kept at fp16 (meeting-LLM
 article, section 8.2): main-store codes, scales, zeros and the outlier store bit
 for bit against the oracle; scores and Top-K bit for bit; attention (dense,
-drop, contiguous and paged) within 1e-3 + 2e-3 |ref|, including the 128K layer."""
+drop, keep, blocks; contiguous and paged) within 1e-3 + 2e-3 |ref|, including
+the 128K layer."""
 import numpy as np
 import pytest
 import torch
@@ -12,8 +13,9 @@ from gpu_util import assert_close, cache_for, dev, host, prefill
 from kvc_layout import slots, unpack_codes
 from oracle import quant as Q
 from oracle import step as ST
-from test_gpu_attend import check_against_oracle, paged, run_attend, sel_tensor
-from test_gpu_topk import check_topk, run_topk, topk_case
+from test_gpu_attend import check_against_oracle, oracle_and_cache, paged, run_attend, sel_tensor
+from test_gpu_blocks import block_case
+from test_gpu_topk import topk_case
 
 pytestmark = pytest.mark.gpu
 
@@ -137,3 +139,28 @@ def test_full_size_dense():
         sl = slice(g * G, (g + 1) * G)
         assert_close(out[b, sl], res.o[b, sl], f"o g={g}")
         assert_close(lse[b, sl], res.lse[b, sl], f"lse g={g}")
+
+
+@pytest.mark.parametrize("append", [False, True])
+def test_keep_paged_ragged(append):
+    """Joint tiers on 16-token pages with outlier channels: the keep set in fp16,
+    the rest from the codes plus the outlier store, H2O-ranked keep set."""
+    w = W.batched_joint(batch=3, lo=500, hi=900, n_window=128)
+    rng = np.random.default_rng(5)
+    w.outlier_ch = np.stack([np.sort(rng.choice(128, 3, replace=False)) for _ in range(w.hkv)]).astype(np.int32)
+    res, cache = oracle_and_cache(w, append=append)
+    if append:
+        cache.append(dev(w.k_new), dev(w.v_new))
+    k_max = int(w.top_k.max())
+    out, lse, lg, _ = run_attend(cache, w, sel_tensor(res, w, k_max), k_max)
+    check_against_oracle(w, res, out, lse, lg)
+
+
+def test_blocks_critical():
+    """Block-granular selection on an INT4 layer with outlier channels: block means
+    (from scores that read the outlier store) and kept blocks bit for bit, then
+    blocks-mode attention."""
+    w = W.sparse_blocks(n_ctx=3000, fmt="int4", top_blocks=7)
+    w.n_sink, w.n_window = 4, 200
+    w.outlier_ch = np.stack([Q.outlier_channels(w.k[0, :, g], 2) for g in range(w.hkv)])
+    block_case(w, append=True, pairs=[(0, 2), (0, 4)])
