@@ -78,9 +78,10 @@ def attend_bytes(w, lens, k_sel) -> int:
     K/V (codes + metadata, or fp16 rows), q, out, lse and logits written."""
     fmt, hkv, hq, B = w.fmt, w.hkv, w.hq, w.batch
     total = 0
-    # quantized tokens of a cache with outlier K channels also read their
-    # 8-byte outlier-store entry
-    code = dict(CODE_BYTES, int4=CODE_BYTES["int4"] + (8 if w.outlier_ch is not None else 0))
+    # quantized tokens of a cache with outlier channels also read their
+    # 8-byte outlier-store entries (K, and V when isolated)
+    extra = 0 if w.outlier_ch is None else (16 if w.outlier_v else 8)
+    code = dict(CODE_BYTES, int4=CODE_BYTES["int4"] + extra)
     for b, n in enumerate(lens):
         n = int(n)
         nq = (n // 64) * 64 if fmt != "fp8" else n     # fp8 has no fp16 tail
@@ -188,7 +189,8 @@ def main():
         table = torch.from_numpy(perm.reshape(w.batch, per))
     oc = torch.from_numpy(w.outlier_ch) if w.outlier_ch is not None else None
     base = KvcCache(w.fmt, w.batch, w.hkv, cap, page_size=w.page_size, block_table=table,
-                    num_pages=num_pages, fp16_rows=w.fp16_shadow, kT=w.kT, outlier_ch=oc)
+                    num_pages=num_pages, fp16_rows=w.fp16_shadow, kT=w.kT, outlier_ch=oc,
+                    outlier_v=w.outlier_v)
     base.append(torch.from_numpy(w.k).to(dev), torch.from_numpy(w.v).to(dev),
                 torch.from_numpy(w.seq_lens).to(dev))
     torch.cuda.synchronize()

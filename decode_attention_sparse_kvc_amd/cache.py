@@ -22,14 +22,16 @@ class KvcCache:
     page_size 0 is a contiguous cache; otherwise ``block_table`` [B, max_pages]
     (int32, physical page ids) and ``num_pages`` describe the page pools.
     ``fp16_rows``: keep k16/v16 (always true for fp16).  ``kT``: channel-major K.
-    ``outlier_ch``: int4 only, [Hkv, m] ascending K channels (m <= 4) kept at
-    fp16 in ``k_outlier`` beside the codes.
+    ``outlier_ch``: int4 only, [Hkv, m] ascending channels (m <= 4) whose K is
+    kept at fp16 in ``k_outlier`` beside the codes (and their V in
+    ``v_outlier`` when ``outlier_v``).
     """
 
     def __init__(self, fmt: str, batch: int, num_kv_heads: int, max_tokens: int,
                  page_size: int = 0, block_table: Optional[torch.Tensor] = None,
                  num_pages: int = 0, fp16_rows: bool = False, kT: bool = False,
-                 outlier_ch: Optional[torch.Tensor] = None, device="cuda"):
+                 outlier_ch: Optional[torch.Tensor] = None, outlier_v: bool = True,
+                 device="cuda"):
         assert fmt in kvc.FMT
         assert max_tokens % kvc.GROUP == 0
         self.fmt, self.batch, self.hkv, self.max_tokens = fmt, batch, num_kv_heads, max_tokens
@@ -68,7 +70,7 @@ class KvcCache:
         if kT:
             self.kT = torch.zeros(batch, num_kv_heads, D, max_tokens, dtype=torch.float16, **z)
         self.k_absmax = torch.zeros(batch, num_kv_heads, D, dtype=torch.float32, **z)
-        self.n_outlier, self.outlier_ch, self.k_outlier = 0, None, None
+        self.n_outlier, self.outlier_ch, self.k_outlier, self.v_outlier = 0, None, None, None
         if outlier_ch is not None and outlier_ch.shape[-1] > 0:
             assert fmt == "int4" and outlier_ch.shape[0] == num_kv_heads
             m = int(outlier_ch.shape[-1])
@@ -78,6 +80,8 @@ class KvcCache:
             self.n_outlier = m
             self.outlier_ch = ch.to(self.device)
             self.k_outlier = torch.zeros(slots, kvc.MAX_OUTLIERS, dtype=torch.float16, **z)
+            if outlier_v:
+                self.v_outlier = torch.zeros_like(self.k_outlier)
         self._refresh()
 
     def _refresh(self):
@@ -88,11 +92,11 @@ class KvcCache:
             p(self.block_table), p(self.seq_lens), p(self.k_codes), p(self.v_codes),
             p(self.k_meta), p(self.v_meta), p(self.k_tail), p(self.v_tail),
             p(self.k16), p(self.v16), p(self.kT), p(self.k_absmax),
-            self.n_outlier, p(self.outlier_ch), p(self.k_outlier))
+            self.n_outlier, p(self.outlier_ch), p(self.k_outlier), p(self.v_outlier))
 
     def tensors(self):
         names = ["block_table", "seq_lens", "k_codes", "v_codes", "k_meta", "v_meta", "k_tail",
-                 "v_tail", "k16", "v16", "kT", "k_absmax", "outlier_ch", "k_outlier"]
+                 "v_tail", "k16", "v16", "kT", "k_absmax", "outlier_ch", "k_outlier", "v_outlier"]
         return {n: getattr(self, n) for n in names if getattr(self, n) is not None}
 
     def clone(self) -> "KvcCache":

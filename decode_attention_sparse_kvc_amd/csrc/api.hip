@@ -47,7 +47,8 @@ kvc_status check_cache(const kvc_cache* c) {
   if (c->n_outlier < 0 || c->n_outlier > KVC_MAX_OUTLIERS) return KVC_ERR_INVALID;
   if (c->n_outlier > 0) {
     if (c->format != KVC_FMT_INT4) return KVC_ERR_UNSUPPORTED;
-    if (!c->outlier_ch || !c->k_outlier || !aligned(c->outlier_ch, 16) || !aligned(c->k_outlier, 8))
+    if (!c->outlier_ch || !c->k_outlier || !aligned(c->outlier_ch, 16) || !aligned(c->k_outlier, 8) ||
+        (c->v_outlier && !aligned(c->v_outlier, 8)))
       return KVC_ERR_INVALID;
   }
   return KVC_OK;

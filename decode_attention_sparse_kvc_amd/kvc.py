@@ -47,6 +47,7 @@ class kvc_cache(ctypes.Structure):
         ("k16", c_void_p), ("v16", c_void_p), ("kT", c_void_p),
         ("k_absmax", c_void_p),
         ("n_outlier", c_int32), ("outlier_ch", c_void_p), ("k_outlier", c_void_p),
+        ("v_outlier", c_void_p),
     ]
 
 

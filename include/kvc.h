@@ -146,9 +146,15 @@ enum { KVC_OP_SCORE_TOPK = 1, KVC_OP_ATTEND = 2 };
  *   k_outlier  fp16 [slot][4]: entry j holds channel outlier_ch[4*g + j]
  *              (entries j >= m hold 0).
  * Dequantized K is then code*s + z on the other channels and the fp16 value
- * on the outlier channels; V is quantized as before.  The channel list is the
- * caller's (an offline analysis) and must not change over the cache's life.
- * n_outlier = 0 ignores outlier_ch and k_outlier.
+ * on the outlier channels.  With v_outlier set, the same channels of V are
+ * isolated too: each token's V group range (min, max) is taken over the
+ * group's other channels, the outlier channels get code 0, and
+ *   v_outlier  fp16 [slot][4]: entry j holds V channel outlier_ch[4*g + j]
+ *              (entries j >= m hold 0),
+ * which dequantized V takes on those channels; v_outlier NULL leaves V as
+ * without outliers.  The channel list is the caller's (an offline analysis)
+ * and must not change over the cache's life.  n_outlier = 0 ignores
+ * outlier_ch, k_outlier and v_outlier.
  */
 typedef struct kvc_cache {
   int32_t abi_version;     /* KVC_ABI_VERSION */
@@ -176,6 +182,7 @@ typedef struct kvc_cache {
   int32_t n_outlier;         /* 0..KVC_MAX_OUTLIERS fp16 K channels (INT4 only) */
   const int32_t* outlier_ch; /* int32 [Hkv][4] outlier channel ids */
   uint16_t* k_outlier;       /* fp16 [slot][4] their K values */
+  uint16_t* v_outlier;       /* fp16 [slot][4] their V values, or NULL (V not isolated) */
 } kvc_cache;
 
 /*

@@ -120,11 +120,13 @@ def dequant_values(code, s, z) -> np.ndarray:
 #     units); ranking by (variance desc, channel asc); the list is returned
 #     ascending.  The count is a parameter (0.5% of 128 channels is
 #     less than one; the synthetic layers plant 3 outlier channels per head).
-#   * Keys only: the outlier store holds K's outlier channels; V is quantized
-#     as before (its groups are per token across channels).
+#   * One channel list per head serves K and V (the section isolates the
+#     head's outlier channels for both); storing the V side is optional.
 #   * In the main store an outlier channel's K scale and zero point are 0, so
 #     its codes are 0 and it contributes nothing; its value comes from the
-#     fp16 store instead.
+#     fp16 store instead.  V is grouped per token across channels: an outlier
+#     channel is left out of its group's min/max and gets code 0; its value
+#     comes from the fp16 store.
 # ---------------------------------------------------------------------------
 
 def outlier_channels(k16_calib: np.ndarray, m: int) -> np.ndarray:
@@ -152,6 +154,39 @@ def quantize_keys_outliers(k16: np.ndarray, bits: int, out_ch: np.ndarray):
     z[:, ch] = np.float16(0.0)
     k_out = np.ascontiguousarray(k16[: code.shape[0]][:, ch])
     return code, s, z, k_out
+
+
+def quantize_values_outliers(v16: np.ndarray, bits: int, out_ch: np.ndarray):
+    """quantize_values with the channels out_ch left out of every group's range.
+
+    Each outlier entry is replaced by the smallest of its group's other values
+    (which leaves min and max those of the other channels and gives code 0),
+    then the groups are quantized as usual.  Returns (codes, scale, zero, v_out)
+    with v_out [nq, m] the outlier channels' fp16 values.
+    """
+    n, d = v16.shape
+    nq = (n // GROUP) * GROUP
+    ch = np.asarray(out_ch, dtype=np.int64)
+    x = v16[:nq].copy()
+    other = np.ones(d, bool)
+    other[ch] = False
+    for h in range(d // GROUP):
+        cols = np.arange(h * GROUP, (h + 1) * GROUP)
+        mine = ch[(ch >= h * GROUP) & (ch < (h + 1) * GROUP)]
+        if len(mine) and nq:
+            low = x[:, cols[other[cols]]].min(axis=1)
+            x[:, mine] = low[:, None]
+    code, s, z = quantize_values(x, bits)
+    code[:, ch] = 0
+    v_out = np.ascontiguousarray(v16[:nq][:, ch])
+    return code, s, z, v_out
+
+
+def dequant_values_outliers(code, s, z, out_ch, v_out) -> np.ndarray:
+    """fp64 V~ [nq, D]: dequantized codes, with the outlier channels' fp16 values."""
+    v = dequant_values(code, s, z)
+    v[:, np.asarray(out_ch, dtype=np.int64)] = v_out.astype(np.float64)
+    return v
 
 
 def dequant_keys_outliers(code, s, z, out_ch, k_out) -> np.ndarray:

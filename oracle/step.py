@@ -45,14 +45,16 @@ class HeadCache:
     v_scale: Optional[np.ndarray] = None  # [nq, D/64] f16
     v_zero: Optional[np.ndarray] = None
     out_ch: Optional[np.ndarray] = None   # [m] K outlier channels (int4), ascending
-    k_out: Optional[np.ndarray] = None    # [nq, m] f16 their values
+    k_out: Optional[np.ndarray] = None    # [nq, m] f16 their K values
+    v_out: Optional[np.ndarray] = None    # [nq, m] f16 their V values (V isolated too)
 
 
 def build_head_cache(k16: np.ndarray, v16: np.ndarray, fmt: str,
-                     out_ch: Optional[np.ndarray] = None) -> HeadCache:
+                     out_ch: Optional[np.ndarray] = None, outlier_v: bool = True) -> HeadCache:
     """Cache contents after appending the fp16 rows k16, v16 [n, D].
 
-    out_ch: K channels kept at fp16 beside the INT4 codes (outlier channels).
+    out_ch: channels kept at fp16 beside the INT4 codes (outlier channels), for
+    K, and for V too when outlier_v.
     """
     n = k16.shape[0]
     kabs = np.abs(k16).max(axis=0) if n else np.zeros(k16.shape[1], np.float16)
@@ -67,7 +69,10 @@ def build_head_cache(k16: np.ndarray, v16: np.ndarray, fmt: str,
             hc.k_code, hc.k_scale, hc.k_zero, hc.k_out = Q.quantize_keys_outliers(k16, b, hc.out_ch)
         else:
             hc.k_code, hc.k_scale, hc.k_zero = Q.quantize_keys(k16, b)
-        hc.v_code, hc.v_scale, hc.v_zero = Q.quantize_values(v16, b)
+        if hc.out_ch is not None and outlier_v:
+            hc.v_code, hc.v_scale, hc.v_zero, hc.v_out = Q.quantize_values_outliers(v16, b, hc.out_ch)
+        else:
+            hc.v_code, hc.v_scale, hc.v_zero = Q.quantize_values(v16, b)
         hc.nq = hc.k_code.shape[0]
     return hc
 
@@ -84,7 +89,10 @@ def token_rows(hc: HeadCache, fp16_mask: Optional[np.ndarray] = None) -> Tuple[n
             kq = Q.dequant_keys_outliers(hc.k_code, hc.k_scale, hc.k_zero, hc.out_ch, hc.k_out)
         else:
             kq = Q.dequant_keys(hc.k_code, hc.k_scale, hc.k_zero)
-        vq = Q.dequant_values(hc.v_code, hc.v_scale, hc.v_zero)
+        if hc.v_out is not None:
+            vq = Q.dequant_values_outliers(hc.v_code, hc.v_scale, hc.v_zero, hc.out_ch, hc.v_out)
+        else:
+            vq = Q.dequant_values(hc.v_code, hc.v_scale, hc.v_zero)
         quant = np.ones(hc.nq, dtype=bool)
         if fp16_mask is not None:
             quant &= ~fp16_mask[: hc.nq]
@@ -129,7 +137,7 @@ def decode_step(w, append: bool = True, pairs=None, k_max: Optional[int] = None)
             v16 = np.concatenate([v16, w.v_new[b, :, g]])
         n = k16.shape[0]
         oc = None if getattr(w, "outlier_ch", None) is None else w.outlier_ch[g]
-        hc = build_head_cache(k16, v16, w.fmt, oc)
+        hc = build_head_cache(k16, v16, w.fmt, oc, getattr(w, "outlier_v", True))
         res.caches[(b, g)] = hc
         q_grp = w.q[b, g * G:(g + 1) * G]
 

@@ -22,7 +22,7 @@ def cache_for(w, max_tokens=None) -> KvcCache:
     oc = torch.from_numpy(w.outlier_ch) if w.outlier_ch is not None else None
     return KvcCache(w.fmt, w.batch, w.hkv, max_tokens or w.max_tokens, page_size=w.page_size,
                     block_table=table, num_pages=w.num_pages, fp16_rows=w.fp16_shadow, kT=w.kT,
-                    outlier_ch=oc)
+                    outlier_ch=oc, outlier_v=w.outlier_v)
 
 
 def prefill(cache: KvcCache, w):

@@ -72,6 +72,7 @@ BAD = [
     (dict(n_outlier=2, outlier_ch=0xA000), 1),                        # no outlier store
     (dict(n_outlier=2, outlier_ch=0xA004, k_outlier=0xB000), 1),      # misaligned list
     (dict(n_outlier=2, outlier_ch=0xA000, k_outlier=0xB004), 1),      # misaligned store
+    (dict(n_outlier=2, outlier_ch=0xA000, k_outlier=0xB000, v_outlier=0xC002), 1),
     (dict(format=2, n_outlier=1, outlier_ch=0xA000, k_outlier=0xB000), 3),   # INT4 only
 ]
 

@@ -1,6 +1,6 @@
-"""Pins for the oracle's outlier K channels (meeting-LLM article, section 8.2:
-channels chosen by variance offline, kept at full precision beside the INT4
-main store).  CPU only."""
+"""Pins for the oracle's outlier channels (meeting-LLM article, section 8.2:
+channels chosen by variance offline, their K and V kept at full precision beside
+the INT4 main store).  CPU only."""
 from fractions import Fraction
 
 import numpy as np
@@ -68,6 +68,53 @@ def test_outlier_channels_kept_exactly_and_others_unchanged():
     assert np.array_equal(kd[:, other], Q.dequant_keys(code0, s0, z0)[:, other])
 
 
+def test_value_outliers_leave_the_main_store_alone():
+    """V groups run per token across channels: whatever the outlier channels hold
+    (here huge values, then copies of a neighbour), every other channel's codes and
+    every group's scale and zero are the same, the outlier codes are 0, and the
+    dequantized outlier channels are the fp16 values."""
+    rng = np.random.default_rng(74)
+    v = rng.normal(size=(192, 128)).astype(np.float16)
+    ch = np.array([7, 64, 90])
+    big = v.copy()
+    big[:, ch] = (rng.normal(size=(192, 3)) * 3000).astype(np.float16)
+    tame = v.copy()
+    tame[:, ch] = v[:, ch + 1]          # values inside the other channels' range
+    c1, s1, z1, vo1 = Q.quantize_values_outliers(big, 4, ch)
+    c2, s2, z2, vo2 = Q.quantize_values_outliers(tame, 4, ch)
+    other = np.setdiff1d(np.arange(128), ch)
+    assert np.array_equal(c1[:, other], c2[:, other])
+    assert np.array_equal(s1.view(np.uint16), s2.view(np.uint16))
+    assert np.array_equal(z1.view(np.uint16), z2.view(np.uint16))
+    assert not c1[:, ch].any() and not c2[:, ch].any()
+    # with tame outliers the groups equal plain quantization's (the range is the same)
+    c0, s0, z0 = Q.quantize_values(tame, 4)
+    assert np.array_equal(c2[:, other], c0[:, other])
+    assert np.array_equal(s2.view(np.uint16), s0.view(np.uint16))
+    vd = Q.dequant_values_outliers(c1, s1, z1, ch, vo1)
+    assert np.array_equal(vd[:, ch], big[:, ch].astype(np.float64))
+    assert np.array_equal(vd[:, other], Q.dequant_values(c2, s2, z2)[:, other])
+
+
+def test_value_isolation_reduces_output_error():
+    """Planted V outlier channels (x20) blow up their token groups' scales; isolating
+    them brings the attention output closer to fp16 attention."""
+    rng = np.random.default_rng(75)
+    k = rng.normal(size=(1024, 128)).astype(np.float16)
+    v = rng.normal(size=(1024, 128)).astype(np.float32)
+    ch = np.array([11, 70])
+    v[:, ch] *= 20
+    v = v.astype(np.float16)
+    q = rng.normal(size=(4, 128)).astype(np.float16)
+    ref, _, _ = A.attend_group(q, k.astype(np.float64), v.astype(np.float64), SM)
+    err = {}
+    for name, oc, ov in (("plain", None, True), ("k_only", ch, False), ("k_and_v", ch, True)):
+        keys, vals = ST.token_rows(ST.build_head_cache(k, v, "int4", oc, ov))
+        o, _, _ = A.attend_group(q, keys, vals, SM)
+        err[name] = np.abs(o - ref).mean()
+    assert err["k_and_v"] < 0.5 * err["k_only"], err
+
+
 def test_outliers_with_lossless_main_reduce_to_dense_attention():
     """Main channels on an exact INT4 grid, outlier channels arbitrary fp16: the
     dequantized keys are the fp16 keys, so attention is textbook fp16 attention."""
@@ -81,15 +128,24 @@ def test_outliers_with_lossless_main_reduce_to_dense_attention():
     kf[:, ch] = rng.normal(size=(n, 3)).astype(np.float16).astype(np.float64) * 37.0
     k16 = kf.astype(np.float16)
     kf = k16.astype(np.float64)
-    v16 = rng.normal(size=(n, 128)).astype(np.float16)
+    cv = rng.integers(0, 16, size=(n, 128))
+    cv[:, 0] = 0
+    cv[:, 1] = 15
+    cv[:, 65] = 0
+    cv[:, 66] = 15
+    vf = cv * 0.125 - 1.0
+    vf[:, ch] = rng.normal(size=(n, 3)).astype(np.float16).astype(np.float64) * 50.0
+    v16 = vf.astype(np.float16)
     hc = ST.build_head_cache(k16, v16, "int4", ch)
-    keys, _ = ST.token_rows(hc)
+    keys, vals = ST.token_rows(hc)
     assert np.array_equal(keys, kf)
+    assert np.array_equal(vals, v16.astype(np.float64))
     hc_plain = ST.build_head_cache(k16, v16, "int4")
     assert not np.array_equal(ST.token_rows(hc_plain)[0], kf)   # without the store: lossy
+    assert not np.array_equal(ST.token_rows(hc_plain)[1], v16.astype(np.float64))
     q = rng.normal(size=(4, 128)).astype(np.float16)
     vv = v16.astype(np.float64)
-    o, _, _ = A.attend_group(q, keys, vv, SM)
+    o, _, _ = A.attend_group(q, keys, vals, SM)
     qt = torch.from_numpy(q.astype(np.float64))[None, :, None, :]
     kt = torch.from_numpy(kf)[None, None].expand(1, 4, -1, -1)
     vt = torch.from_numpy(vv)[None, None].expand(1, 4, -1, -1)
@@ -122,6 +178,7 @@ def test_step_uses_the_outlier_store():
     keys = Q.dequant_keys(hc.k_code, hc.k_scale, hc.k_zero)
     keys[:, hc.out_ch] = w.k[0, :640, 1][:, hc.out_ch].astype(np.float64)
     vals = Q.dequant_values(hc.v_code, hc.v_scale, hc.v_zero)
+    vals[:, hc.out_ch] = w.v[0, :640, 1][:, hc.out_ch].astype(np.float64)
     o, lse, _ = A.attend_group(w.q[0, 4:8], keys, vals, w.sm_scale)
     np.testing.assert_allclose(res.o[0, 4:8], o, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(res.lse[0, 4:8], lse, rtol=1e-13)

@@ -68,7 +68,8 @@ class Workload:
     kT: bool = False                     # keep a channel-major K copy (fp16 caches)
     fp16_shadow: bool = False            # keep full fp16 rows beside quantized codes
     prefer_k: int = 0                    # > 0: also the top-k probability mass of each row
-    outlier_ch: Optional[np.ndarray] = None   # [Hkv, m] int4: K channels kept at fp16
+    outlier_ch: Optional[np.ndarray] = None   # [Hkv, m] int4: channels kept at fp16
+    outlier_v: bool = True                    # isolate those channels of V too
     planted: Optional[np.ndarray] = None      # [Hkv, m] the K channels the generator scaled
 
     @property
