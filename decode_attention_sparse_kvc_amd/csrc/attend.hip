@@ -167,13 +167,13 @@ __device__ inline int window_start(int n, int n_sink, int n_window) {
 // Raw loads of one 64-token group: code tiles, metadata words, selection bits.
 // TILED: the group's four 16-token tiles are addressed one by one (pages of
 // 16 or 32 tokens); otherwise the group is one contiguous run of slots.
-// OUTL: INT4 with outlier channels; ko holds the outlier-store entries of
-// token l of the group in lane l.
+// OUTL: INT4 with outlier channels; ko / vo hold the K / V outlier-store
+// entries of token l of the group in lane l (vo zero without a V store).
 template <int FMT, bool TILED, bool OUTL = false>
 struct GroupData {
   uint4 k[FMT == KVC_FMT_INT4 ? 4 : 1];
   uint4 v[FMT == KVC_FMT_INT4 ? 4 : 1];
-  uint2 ko;
+  uint2 ko, vo;
   uint2 km;
   uint2 vm[TILED ? 4 : 1];   // TILED: tile j's words in lanes 16j..16j+15, zero elsewhere
   uint2 bits;   // drop/keep: selected tokens of the group (two 32-token words)
@@ -183,6 +183,7 @@ struct GroupData {
 // the raw score q.k~ for the lane's head; the rest is relative to exp2(m * sm2).
 struct QState {
   float m, l, sz0, sz1;
+  float vo[4];      // sum_t p_t * V outlier entry e (isolated V outlier channels)
   f4 acc[8];        // O^T, channel tiles 0..7 (lane column = head)
   f4 corr0, corr1;  // sum_t P'_t * base_t per V half, replicated over rows
 };
@@ -284,7 +285,11 @@ __device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, in
       d.v[j] = buf_load16_stream(rv, l16 + j * UNIT_BYTES);
     }
     d.vm[0] = buf_load8(make_buf(c.v_meta + sl * 4, ok ? GS * 8u : 0u), l8);
-    if constexpr (OUTL) d.ko = buf_load8(make_buf(c.k_outlier + sl * KVC_MAX_OUTLIERS, ok ? GS * OB : 0u), l8);
+    if constexpr (OUTL) {
+      d.ko = buf_load8(make_buf(c.k_outlier + sl * KVC_MAX_OUTLIERS, ok ? GS * OB : 0u), l8);
+      const bool vok = ok && c.v_outlier;
+      d.vo = buf_load8(make_buf((vok ? c.v_outlier : c.k_outlier) + sl * KVC_MAX_OUTLIERS, vok ? GS * OB : 0u), l8);
+    }
   } else {                  // INT4 tiles on pages of 16 or 32 tokens
     int64_t st[4];
     bool ok[4];
@@ -304,12 +309,16 @@ __device__ __forceinline__ void load_group(const AttendArgs& a, int b, int g, in
     for (int j = 0; j < 4; ++j)
       d.vm[j] = buf_load8(make_buf(c.v_meta + st[j] * 4, ok[j] ? TILE * 8u : 0u), l8 - 128u * j);
     if constexpr (OUTL) {   // (as the V metadata: lanes of other tiles read zero)
-      d.ko = uint2{0u, 0u};
+      d.ko = d.vo = uint2{0u, 0u};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint2 o = buf_load8(make_buf(c.k_outlier + st[j] * KVC_MAX_OUTLIERS, ok[j] ? TILE * OB : 0u),
                                   l8 - TILE * OB * j);
         d.ko = uint2{d.ko.x | o.x, d.ko.y | o.y};
+        const bool vok = ok[j] && c.v_outlier;
+        const uint2 u = buf_load8(make_buf((vok ? c.v_outlier : c.k_outlier) + st[j] * KVC_MAX_OUTLIERS,
+                                           vok ? TILE * OB : 0u), l8 - TILE * OB * j);
+        d.vo = uint2{d.vo.x | u.x, d.vo.y | u.y};
       }
     }
   }
@@ -338,11 +347,28 @@ __device__ inline float ror4(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
 }
 
+// Isolated V outlier channels: p_i times the four fp16 entries of token i of
+// a lane's quad of consecutive tokens (staged in LDS, 32 bytes) into the
+// running sums.
+__device__ inline void vo_accum(QState& st, const float* p, const uint16_t* quad) {
+  const uint4 e0 = *reinterpret_cast<const uint4*>(quad);
+  const uint4 e1 = *reinterpret_cast<const uint4*>(quad + 8);
+  const uint32_t w[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const h2 e01 = bc<h2>(w[2 * i]), e23 = bc<h2>(w[2 * i + 1]);
+    st.vo[0] = fmaf(p[i], (float)e01.x, st.vo[0]);
+    st.vo[1] = fmaf(p[i], (float)e01.y, st.vo[1]);
+    st.vo[2] = fmaf(p[i], (float)e23.x, st.vo[2]);
+    st.vo[3] = fmaf(p[i], (float)e23.y, st.vo[3]);
+  }
+}
+
 template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED, bool OUTL = false>
 __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, int gi, int lane,
                                            int w, int n, const GroupData<FMT, TILED, OUTL>& d,
                                            QState& st, const h2* qv, const h8& qo, const Dec& dc,
-                                           uint16_t* sKm, uint16_t* sVm) {
+                                           uint16_t* sKm, uint16_t* sVm, uint16_t* sVo) {
   const int G = a.G;
   const int col = lane & 15, kb = lane >> 4, head = col & 7;
   const bool hv = head < G;
@@ -376,6 +402,7 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
       for (int j = 1; j < 4; ++j) vm = uint2{vm.x | d.vm[j].x, vm.y | d.vm[j].y};
     }
     *reinterpret_cast<uint2*>(sVm + 256 * w + 4 * lane) = vm;
+    if constexpr (OUTL) *reinterpret_cast<uint2*>(sVo + 256 * w + 4 * lane) = d.vo;
   }
   wave_sync_lds();
 
@@ -490,6 +517,7 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
 
   const uint16_t* vmeta = sVm + 256 * w;
   h4 B0[4], B1[4];   // P' of each tile as the B operand of P.V (lane column = head)
+  float pv[PACK ? 4 : 16];   // OUTL: the probabilities, for the V outlier sums after P.V
   if constexpr (PACK) {
     // ---- pack the four tiles into all 64 lanes: lane (4j + h, kb) takes head h of tile j
     float y[4];
@@ -522,6 +550,10 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
       st.corr1 *= alpha;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= alpha;
+      if constexpr (OUTL) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.vo[e] *= alpha;
+      }
     }
     const float msc = st.m == -INFINITY ? 0.f : st.m * a.sm2;
     const uint4 m01 = *reinterpret_cast<const uint4*>(vmeta + 4 * (TILE * jj + 4 * kb));
@@ -538,6 +570,7 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
       A1[i] = (_Float16)(p * (float)s01.y);
       st.sz0 = fmaf(p, (float)z01.x, st.sz0);
       st.sz1 = fmaf(p, (float)z01.y, st.sz1);
+      if constexpr (OUTL) pv[i] = p;
     }
     // ---- unpack: tile j's P' back to lanes (h, kb)
     const uint2 a0 = bc<uint2>(A0), a1 = bc<uint2>(A1);
@@ -574,6 +607,10 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
       st.corr1 *= alpha;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) st.acc[ct] *= alpha;
+      if constexpr (OUTL) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.vo[e] *= alpha;
+      }
     }
     const float msc = st.m == -INFINITY ? 0.f : st.m * a.sm2;
 #pragma unroll
@@ -591,6 +628,7 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
         B1[j][i] = (_Float16)(p * (float)s01.y);
         st.sz0 = fmaf(p, (float)z01.x, st.sz0);
         st.sz1 = fmaf(p, (float)z01.y, st.sz1);
+        if constexpr (OUTL) pv[(4 * j + i) % (PACK ? 4 : 16)] = p;
       }
     }
   }
@@ -635,11 +673,20 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
       }
     }
   }
+  // isolated V outlier channels, while the matrix cores run the products above
+  if constexpr (OUTL) {
+    if constexpr (PACK) {
+      vo_accum(st, pv, sVo + 256 * w + 4 * (TILE * (col >> 2) + 4 * kb));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vo_accum(st, pv + 4 * j, sVo + 256 * w + 4 * (TILE * j + 4 * kb));
+    }
+  }
 }
 
 template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED, bool OUTL = false>
 __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, int split, int lane, int w,
-                           float* sO, float* sML, uint16_t* sKm, uint16_t* sVm) {
+                           float* sO, float* sML, uint16_t* sKm, uint16_t* sVm, uint16_t* sVo) {
   const kvc_cache& c = a.c;
   const int n = max(c.seq_lens[b], 0);
   // blocks mode walks the plan's list of groups (sink groups, kept blocks,
@@ -724,6 +771,8 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
   QState st;
   st.m = -INFINITY;
   st.l = st.sz0 = st.sz1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) st.vo[e] = 0.f;
   st.corr0 = st.corr1 = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) st.acc[ct] = f4{0.f, 0.f, 0.f, 0.f};
@@ -735,18 +784,19 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
   // and its wait leaves the newer group's loads in flight.
   int k = 0;
   for (; k + 2 <= nmine; k += 2) {
-    group_body<FMT, DENSE, LOGITS, PACK, TILED, OUTL>(a, b, g, gid(k), lane, w, n, d0, st, qv, qo, dc, sKm, sVm);
+    group_body<FMT, DENSE, LOGITS, PACK, TILED, OUTL>(a, b, g, gid(k), lane, w, n, d0, st, qv, qo, dc, sKm, sVm, sVo);
     load_group<FMT, DENSE, TILED, OUTL>(a, b, g, gid(k + 2), k + 2 < nmine, t0w, lane, d0);
     t0w = group_table(a, rtab, gid(k + 4));
-    group_body<FMT, DENSE, LOGITS, PACK, TILED, OUTL>(a, b, g, gid(k + 1), lane, w, n, d1, st, qv, qo, dc, sKm, sVm);
+    group_body<FMT, DENSE, LOGITS, PACK, TILED, OUTL>(a, b, g, gid(k + 1), lane, w, n, d1, st, qv, qo, dc, sKm, sVm, sVo);
     load_group<FMT, DENSE, TILED, OUTL>(a, b, g, gid(k + 3), k + 3 < nmine, t1w, lane, d1);
     t1w = group_table(a, rtab, gid(k + 5));
   }
   if (k < nmine)
-    group_body<FMT, DENSE, LOGITS, PACK, TILED, OUTL>(a, b, g, gid(k), lane, w, n, d0, st, qv, qo, dc, sKm, sVm);
+    group_body<FMT, DENSE, LOGITS, PACK, TILED, OUTL>(a, b, g, gid(k), lane, w, n, d0, st, qv, qo, dc, sKm, sVm, sVo);
 
   // ---- finish: sums over the lanes of each head, bases and zero points
   float l = st.l, sz0 = st.sz0, sz1 = st.sz1;
+  float vo[4] = {st.vo[0], st.vo[1], st.vo[2], st.vo[3]};
   if constexpr (PACK) {   // lanes h, h+4, h+8, h+12 of each row hold head h
     l += ror4(l);
     l += ror8(l);
@@ -754,10 +804,21 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
     sz0 += ror8(sz0);
     sz1 += ror4(sz1);
     sz1 += ror8(sz1);
+    if constexpr (OUTL) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vo[e] += ror4(vo[e]);
+        vo[e] += ror8(vo[e]);
+      }
+    }
   }
   l = sum_kb(l);
   sz0 = sum_kb(sz0);
   sz1 = sum_kb(sz1);
+  if constexpr (OUTL) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vo[e] = sum_kb(vo[e]);
+  }
   if (hi_lane) {
     float* o = sO + (w * 8 + head) * D;
     const float c0 = st.corr0[0], c1 = st.corr1[0];
@@ -767,6 +828,17 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
       const float corr = ct < 4 ? sz0 - scale * c0 : sz1 - scale * c1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[16 * ct + 4 * kb + i] = st.acc[ct][i] + corr;
+    }
+    // isolated V outlier channels: their output is the fp16 store's sum (the
+    // codes' value there, the group zero, is replaced; same wave, so the LDS
+    // stores land in program order)
+    if constexpr (OUTL) {
+      if (kb == 0 && c.v_outlier) {
+        const auto* oc = scalar_ptr(c.outlier_ch + g * KVC_MAX_OUTLIERS);
+#pragma unroll
+        for (int e = 0; e < KVC_MAX_OUTLIERS; ++e)
+          if (e < c.n_outlier) o[min(max((int)oc[e], 0), D - 1)] = vo[e];
+      }
     }
     if (kb == 0) {
       sML[(w * 8 + head) * 2] = st.m == -INFINITY ? -INFINITY : st.m * a.sm2;
@@ -1122,6 +1194,7 @@ void attend_kernel(AttendArgs a) {
   __shared__ float sML[NW * 8 * 2];
   __shared__ __align__(16) uint16_t sKm[NW * 256];
   __shared__ __align__(16) uint16_t sVm[NW * 256];
+  __shared__ __align__(16) uint16_t sVo[OUTL ? NW * 256 : 4];   // V outlier entries per wave
   __shared__ __align__(16) int sTok[NW * TILE * ROWS_AHEAD];
   __shared__ __align__(16) float sAl[NW * 8];
 
@@ -1156,7 +1229,7 @@ void attend_kernel(AttendArgs a) {
 
   if constexpr (grouped(FMT)) {
     if (split < a.s_q)
-      quant_role<FMT, DENSE, LOGITS, PACK, TILED, OUTL>(a, b, g, split, lane, w, sO, sML, sKm, sVm);
+      quant_role<FMT, DENSE, LOGITS, PACK, TILED, OUTL>(a, b, g, split, lane, w, sO, sML, sKm, sVm, sVo);
     else
       rows_role<FMT, DENSE, LOGITS>(a, b, g, split - a.s_q, lane, w, sO, sML, sTok);
   } else {

@@ -8,8 +8,10 @@
 //   s = fp16((max - min) / (2^b - 1) + 0), z = fp16(min + 0),
 //   code = s == 0 ? 0 : clamp(rint((x - z) / s), 0, 2^b - 1) in fp32.
 // The packed code tiles follow the lane/dword layout of include/kvc.h.
-// INT4 outlier channels (meeting-LLM article section 8.2) get scale and zero 0
-// in the main store and their fp16 values in the outlier store.
+// INT4 outlier channels (meeting-LLM article section 8.2) get K scale and zero
+// 0 in the main store and their fp16 K values in the outlier store; with a V
+// outlier store their V is left out of each token's group range (code 0) and
+// stored at fp16 too.
 // FP8 (E4M3) caches encode every appended row at once (no groups, no tail);
 // the channel-major copy then holds the decoded values.
 // A second, per-sequence kernel then rewrites the fp16 tail and seq_lens.
@@ -165,19 +167,30 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
     for (int r = 32 * hk; r < 32 * hk + 32; ++r)
       sKc[r][ck] = (uint8_t)GroupQuant<BITS>::code(h2f(sK[r][ck]), ks, kz);
 
-    // ---- outlier store: thread (token r, entry j) writes the token's fp16
-    // value of outlier channel j (0 past the list)
+    // ---- outlier stores: thread (token r, entry j) writes the token's fp16
+    // values of outlier channel j (0 past the list)
     if (n_out > 0) {
       const int r = tid >> 2, j = tid & 3;
       const int ch = min(max(c.outlier_ch[g * KVC_MAX_OUTLIERS + j], 0), D - 1);
       const int64_t slot = slot_of(c, b, g, g0 + r);
-      if (slot >= 0) c.k_outlier[slot * KVC_MAX_OUTLIERS + j] = j < n_out ? sK[r][ch] : (uint16_t)0;
+      if (slot >= 0) {
+        c.k_outlier[slot * KVC_MAX_OUTLIERS + j] = j < n_out ? sK[r][ch] : (uint16_t)0;
+        if (c.v_outlier) c.v_outlier[slot * KVC_MAX_OUTLIERS + j] = j < n_out ? sV[r][ch] : (uint16_t)0;
+      }
     }
 
     // ---- V: per token over each 64-channel half.  Thread (token nv, quarter qv).
+    // Isolated V outlier channels (bits of vout) stay out of the range and get code 0.
     const int nv = tid >> 2, qv = tid & 3, jv = qv >> 1, c0 = 32 * qv;
+    uint32_t vout = 0u;
+    if (n_out > 0 && c.v_outlier)
+      for (int j = 0; j < n_out; ++j) {
+        const int ch = c.outlier_ch[g * KVC_MAX_OUTLIERS + j] - c0;
+        if (ch >= 0 && ch < 32) vout |= 1u << ch;
+      }
     float vmn = INFINITY, vmx = -INFINITY;
     for (int i = 0; i < 32; ++i) {
+      if ((vout >> i) & 1u) continue;
       const float x = h2f(sV[nv][c0 + i]);
       vmn = fminf(vmn, x);
       vmx = fmaxf(vmx, x);
@@ -195,7 +208,7 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
       }
     }
     for (int i = 0; i < 32; ++i)
-      sVc[nv][c0 + i] = (uint8_t)GroupQuant<BITS>::code(h2f(sV[nv][c0 + i]), vs, vz);
+      sVc[nv][c0 + i] = (vout >> i) & 1u ? 0 : (uint8_t)GroupQuant<BITS>::code(h2f(sV[nv][c0 + i]), vs, vz);
     __syncthreads();
 
     // ---- pack codes into the lane/dword tile layout

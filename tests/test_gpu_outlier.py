@@ -1,6 +1,6 @@
-"""GPU parity of INT4 caches with outlier K channels kept at fp16 (meeting-LLM
-article, section 8.2): main-store codes, scales, zeros and the outlier store bit
-for bit against the oracle; scores and Top-K bit for bit; attention (dense,
+"""GPU parity of INT4 caches with outlier channels kept at fp16 (meeting-LLM
+article, section 8.2; K, and V unless its store is absent): main-store codes,
+scales, zeros and the outlier stores bit for bit against the oracle; scores and Top-K bit for bit; attention (dense,
 drop, keep, blocks; contiguous and paged) within 1e-3 + 2e-3 |ref|, including
 the 128K layer."""
 import numpy as np
@@ -45,16 +45,19 @@ def test_store_after_ragged_appends(page, m):
         n_new = np.array(n_new, np.int32)
         mx = int(n_new.max())
         k = rng.normal(size=(B, mx, hkv, 128)).astype(np.float32)
+        v = rng.normal(size=(B, mx, hkv, 128)).astype(np.float32)
         for g in range(hkv):
             k[:, :, g, ch[g]] *= 20.0
+            v[:, :, g, ch[g]] *= 30.0
         k = k.astype(np.float16)
-        v = rng.normal(size=(B, mx, hkv, 128)).astype(np.float16)
+        v = v.astype(np.float16)
         cache.append(dev(k), dev(v), dev(n_new))
         for b in range(B):
             rows_k[b] = np.concatenate([rows_k[b], k[b, : n_new[b]]])
             rows_v[b] = np.concatenate([rows_v[b], v[b, : n_new[b]]])
     torch.cuda.synchronize()
     kc, km, ko = host(cache.k_codes), host(cache.k_meta), host(cache.k_outlier)
+    vc, vm, vo = host(cache.v_codes), host(cache.v_meta), host(cache.v_outlier)
     for b in range(B):
         n = rows_k[b].shape[0]
         for g in range(hkv):
@@ -67,6 +70,11 @@ def test_store_after_ragged_appends(page, m):
             assert np.array_equal(_u16(km[b, g, : nq // 64, 1]), _u16(hc.k_zero)), where
             assert np.array_equal(_u16(ko[sl, :m]), _u16(hc.k_out)), "outlier store " + where
             assert not _u16(ko[sl, m:]).any(), where
+            assert np.array_equal(unpack_codes(vc, "int4", "v", sl), hc.v_code), "V codes " + where
+            assert np.array_equal(_u16(vm[sl, 0:2]), _u16(hc.v_scale)), where
+            assert np.array_equal(_u16(vm[sl, 2:4]), _u16(hc.v_zero)), where
+            assert np.array_equal(_u16(vo[sl, :m]), _u16(hc.v_out)), "V outlier store " + where
+            assert not _u16(vo[sl, m:]).any(), where
 
 
 @pytest.mark.parametrize("n", [63, 777, 4095, 4097])
@@ -85,6 +93,30 @@ def test_dense(n):
         assert_close(out[b, sl], res.o[b, sl], f"o g={g}")
         assert_close(lse[b, sl], res.lse[b, sl], f"lse g={g}")
         assert_close(lg[b, sl][:, toks], res.logits[(b, g)], f"logits g={g}")
+
+
+@pytest.mark.parametrize("outlier_v", [False, True])
+def test_dense_value_outliers(outlier_v):
+    """V channels scaled x30 on the outlier list: with the V store their output is
+    the fp16 values' (the codes' group zero replaced); without it (K only) V is
+    quantized with the outliers in range."""
+    w = W.int4_outlier_dense(2000)
+    w.v = w.v.astype(np.float32)
+    for g in range(w.hkv):
+        w.v[:, :, g, w.outlier_ch[g]] *= 30.0
+    w.v = w.v.astype(np.float16)
+    w.outlier_v = outlier_v
+    res = ST.decode_step(w, append=True, pairs=[(0, 1), (0, 4)])
+    cache = cache_for(w)
+    assert (cache.v_outlier is not None) == outlier_v
+    prefill(cache, w)
+    cache.append(dev(w.k_new), dev(w.v_new))
+    out, lse, lg, _ = run_attend(cache, w)
+    G = w.group
+    for (b, g), toks in res.tokens.items():
+        sl = slice(g * G, (g + 1) * G)
+        assert_close(out[b, sl], res.o[b, sl], f"o g={g}")
+        assert_close(lse[b, sl], res.lse[b, sl], f"lse g={g}")
 
 
 @pytest.mark.parametrize("page", [16, 32, 64])
