@@ -15,7 +15,7 @@ plain step at a time in the pages' order.
              printed ``quant_1bit`` generalized by its own 2**b - 1 levels);
              K per channel over 64-token groups, V per token over 64-channel
              groups (same section; on-device KV article, section 3.1);
-             outlier K channels kept at fp16 beside the codes, chosen by
+             outlier channels (K, optionally V) kept at fp16 beside the codes, chosen by
              variance (meeting-LLM article, section 8.2).
   select  -- critical channels and approximate scores (TailorKV, section 2.3),
              exact query-aware scores, Top-K with lower-index ties, sinks and
