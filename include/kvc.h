@@ -210,7 +210,8 @@ kvc_status kvc_quantize_append(const kvc_cache* cache, const uint16_t* k_new,
  *               (ties to the lower channel); KVC_SCORE_EXTERNAL: r_t = ext[t].
  *               Exact/critical score of token t: max over the group's heads of
  *               the fp64 sum, channel by channel in ascending order from +0.0,
- *               of q_{h,c} * k~_{t,c} (k~ = fp16 row or code*s + z), plus 0.0.
+ *               of q_{h,c} * k~_{t,c} (k~ = fp16 row, code*s + z, or the fp16
+ *               outlier-store value on an outlier channel), plus 0.0.
  *   ext         float32 [B][Hkv][max_tokens] (EXTERNAL only).
  *   candidates  tokens in [n_sink, n - n_window), n = seq_lens[b].
  *   k_per_seq   device int32 [B] or NULL (then k_max);
@@ -243,7 +244,9 @@ kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num
 /*
  * kvc_attend_decode -- softmax(q K~^T * sm_scale) V~ for every query head over
  * its attended tokens, dequantizing inside the kernel ([DEV] 3.2, [MTG] 8.1,
- * [TKV] 2.1); query head h reads KV head h / G, G = Hq / Hkv (1..8).
+ * [TKV] 2.1); query head h reads KV head h / G, G = Hq / Hkv (1..8).  On INT4
+ * caches with outlier channels K~ (and V~, with a V store) take the outlier
+ * stores' fp16 values on those channels ([MTG] 8.2).
  *   mode  KVC_ATTEND_DENSE: every cached token.
  *         KVC_ATTEND_DROP: sinks [0, n_sink), the valid entries of sel, and
  *           the window [max(n - n_window, n_sink), n); other tokens dropped.
