@@ -1337,8 +1337,6 @@ __global__ __launch_bounds__(256) void plan_kernel(AttendArgs a) {
 }
 
 // ---------------------------------------------------------------- split merge
-// One workgroup per (sequence, query head): log-sum-exp combination of the
-// split partials.  Thread t adds channel quad t % 32 over splits t / 32, +8, ...
 // Log-sum-exp merge of the split partials, one workgroup per (sequence, query
 // head).  Thread (quad cq, replica r) folds splits r, r + 8, ... into a running
 // (max, sum, o[4 cq .. 4 cq + 3]) with online rescaling, so its loads do not
