@@ -51,7 +51,7 @@ extern "C" {
 #define KVC_HEAD_DIM 128
 #define KVC_GROUP 64
 #define KVC_MAX_GQA 8          /* query heads per KV head supported by attend */
-#define KVC_MAX_OUTLIERS 4     /* fp16 outlier K channels per KV head (INT4) */
+#define KVC_MAX_OUTLIERS 4     /* fp16 outlier channels per KV head (INT4) */
 
 typedef int32_t kvc_status;
 enum {
@@ -141,16 +141,18 @@ enum { KVC_OP_SCORE_TOPK = 1, KVC_OP_ATTEND = 2 };
  * magnitude are found offline by their variance and kept at full precision
  * beside the quantized main store).  With n_outlier = m in 1..4, channels
  * outlier_ch[4*g + j] (j < m; ascending, distinct, 0..127) of KV head g are
- * K outlier channels.  When a group is quantized their K scale and zero are
- * stored as 0 (so their codes are 0) and their fp16 values go to
- *   k_outlier  fp16 [slot][4]: entry j holds channel outlier_ch[4*g + j]
- *              (entries j >= m hold 0).
+ * outlier channels; the list is device int32 [Hkv][4], 16-byte aligned (ids
+ * outside 0..127 are clamped where memory is indexed: undefined results, no
+ * out-of-bounds access).  When a group is quantized their K scale and zero
+ * are stored as 0 (so their codes are 0) and their fp16 values go to
+ *   k_outlier  fp16 [slot][4], 8-byte aligned: entry j holds channel
+ *              outlier_ch[4*g + j] (entries j >= m hold 0).
  * Dequantized K is then code*s + z on the other channels and the fp16 value
  * on the outlier channels.  With v_outlier set, the same channels of V are
  * isolated too: each token's V group range (min, max) is taken over the
  * group's other channels, the outlier channels get code 0, and
- *   v_outlier  fp16 [slot][4]: entry j holds V channel outlier_ch[4*g + j]
- *              (entries j >= m hold 0),
+ *   v_outlier  fp16 [slot][4], 8-byte aligned: entry j holds V channel
+ *              outlier_ch[4*g + j] (entries j >= m hold 0),
  * which dequantized V takes on those channels; v_outlier NULL leaves V as
  * without outliers.  The channel list is the caller's (an offline analysis)
  * and must not change over the cache's life.  n_outlier = 0 ignores
@@ -179,7 +181,7 @@ typedef struct kvc_cache {
   uint16_t* v16;
   uint16_t* kT;
   float* k_absmax;
-  int32_t n_outlier;         /* 0..KVC_MAX_OUTLIERS fp16 K channels (INT4 only) */
+  int32_t n_outlier;         /* 0..KVC_MAX_OUTLIERS fp16 outlier channels (INT4 only) */
   const int32_t* outlier_ch; /* int32 [Hkv][4] outlier channel ids */
   uint16_t* k_outlier;       /* fp16 [slot][4] their K values */
   uint16_t* v_outlier;       /* fp16 [slot][4] their V values, or NULL (V not isolated) */
