@@ -196,3 +196,26 @@ def test_blocks_critical():
     w.n_sink, w.n_window = 4, 200
     w.outlier_ch = np.stack([Q.outlier_channels(w.k[0, :, g], 2) for g in range(w.hkv)])
     block_case(w, append=True, pairs=[(0, 2), (0, 4)])
+
+
+@pytest.mark.parametrize("G,page", [(1, 0), (2, 16), (8, 0), (8, 32)])
+def test_group_sizes(G, page):
+    """Query groups of 1, 2 and 8 heads (8: the unpacked softmax path), with planted
+    K and V outliers on the list, contiguous and paged."""
+    w = W.int4_dense(900)
+    w.hkv = 32 // G if G < 8 else 4
+    w.hq = w.hkv * G
+    rng = np.random.default_rng(40 + G)
+    k = rng.standard_normal((1, 900, w.hkv, 128), dtype=np.float32)
+    v = rng.standard_normal((1, 900, w.hkv, 128), dtype=np.float32)
+    w.outlier_ch = np.stack([np.sort(rng.choice(128, 3, replace=False)) for _ in range(w.hkv)]).astype(np.int32)
+    for g in range(w.hkv):
+        k[:, :, g, w.outlier_ch[g]] *= 16.0
+        v[:, :, g, w.outlier_ch[g]] *= 16.0
+    w.k, w.v = k.astype(np.float16), v.astype(np.float16)
+    w.q = rng.standard_normal((1, w.hq, 128), dtype=np.float32).astype(np.float16)
+    if page:
+        paged(w, page, seed=G)
+    res, cache = oracle_and_cache(w)
+    out, lse, lg, _ = run_attend(cache, w)
+    check_against_oracle(w, res, out, lse, lg)
