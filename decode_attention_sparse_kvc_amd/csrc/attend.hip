@@ -482,36 +482,42 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
     for (int i = 0; i < 4; ++i) x[j][i] = s[i] + ror8(s[i]);
   }
 
-  // ---- logits (natural units) of the attended tokens
+  // ---- logits (natural units) of the attended tokens: one store per (token,
+  // head); with the packed softmax they are written from the packed scores
+  // below (all 64 lanes, four tokens each), otherwise here from the hi lanes
+  int32_t pre0 = 0, pre1 = 0;   // sel index of the group's two 32-token words (drop mode)
   if constexpr (LOGITS) {
-    int32_t pre0 = 0, pre1 = 0;   // sel index of the group's two 32-token words (drop mode)
     if (!DENSE && compact(a.mode)) {
       const auto* sp = scalar_ptr(a.spre + ((int64_t)b * a.c.num_kv_heads + g) * (a.c.max_tokens / 32) + 2 * gi);
       pre0 = sp[0];
       pre1 = sp[1];
     }
+  }
+  // logit of token t0 + bit for query head hh (bit attended)
+  auto put_logit = [&](int bit, int hh, float xv) {
+    int pos = t0 + bit;
+    if (compact(a.mode)) {
+      const int t = t0 + bit;
+      if (t < a.n_sink) {
+        pos = t;
+      } else if (t >= w0) {
+        pos = a.n_sink + a.nsel + (t - w0);
+      } else {
+        const uint32_t word = (bit >> 5) ? d.bits.y : d.bits.x;
+        const int32_t base = (bit >> 5) ? pre1 : pre0;
+        pos = a.n_sink + base + __popc(word & ((1u << (t & 31)) - 1u));
+      }
+    }
+    a.logits[((int64_t)b * a.hq + g * G + hh) * a.logits_stride + pos] = xv * a.sm;
+  };
+  if constexpr (LOGITS && !PACK) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int bit = TILE * j + 4 * kb + i;
         const bool on = DENSE || ((att >> bit) & 1ull);
-        if (hi_lane && on) {
-          int pos = t0 + bit;
-          if (compact(a.mode)) {
-            const int t = t0 + bit;
-            if (t < a.n_sink) {
-              pos = t;
-            } else if (t >= w0) {
-              pos = a.n_sink + a.nsel + (t - w0);
-            } else {
-              const uint32_t word = (bit >> 5) ? d.bits.y : d.bits.x;
-              const int32_t base = (bit >> 5) ? pre1 : pre0;
-              pos = a.n_sink + base + __popc(word & ((1u << (t & 31)) - 1u));
-            }
-          }
-          a.logits[((int64_t)b * a.hq + g * G + head) * a.logits_stride + pos] = x[j][i] * a.sm;
-        }
+        if (hi_lane && on) put_logit(bit, head, x[j][i]);
       }
   }
 
@@ -530,6 +536,14 @@ __device__ __forceinline__ void group_body(const AttendArgs& a, int b, int g, in
       y[i] = v;
     }
     const int jj = col >> 2;
+    if constexpr (LOGITS) {   // lane (4 jj + h, kb): head h's scores of tokens 16 jj + 4 kb + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int bit = TILE * jj + 4 * kb + i;
+        const bool on = DENSE || ((att >> bit) & 1ull);
+        if ((col & 3) < G && on) put_logit(bit, col & 3, y[i]);
+      }
+    }
     if constexpr (!DENSE) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
