@@ -168,7 +168,7 @@ def run_accum(cache, w, logits, stride, lse, sel, k_max):
     return host(acc)
 
 
-def accum_case(w, append=False):
+def accum_case(w, append=False, pad=0):
     res = ST.decode_step(w, append=append)
     cache = cache_for(w)
     prefill(cache, w)
@@ -178,7 +178,7 @@ def accum_case(w, append=False):
     sel = sel_tensor(res, w, km) if km else None
     mode = kvc.MODE[w.mode]
     B, hq = w.batch, w.hq
-    stride = w.n_sink + km + w.n_window if w.mode == "drop" else cache.max_tokens
+    stride = (w.n_sink + km + w.n_window if w.mode == "drop" else cache.max_tokens) + pad
     out = torch.empty(B, hq, 128, device="cuda")
     lse = torch.empty(B, hq, device="cuda")
     lg = torch.full((B, hq, stride), float("nan"), device="cuda")
@@ -211,8 +211,10 @@ def test_accum_keep_paged():
     accum_case(W.batched_joint(batch=3, lo=500, hi=900, n_window=128))
 
 
-def test_accum_dense():
-    w = W.int4_dense(1000)
+@pytest.mark.parametrize("n,pad", [(1000, 0), (1001, 0), (1003, 3)])
+def test_accum_dense(n, pad):
+    """Four tokens a thread with a ragged last quad, and (odd logits stride) one a thread."""
+    w = W.int4_dense(n)
     w.accumulate = True
-    w.acc = np.zeros((1, w.hkv, w.max_tokens), np.float32)
-    accum_case(w)
+    w.acc = np.random.default_rng(n).random((1, w.hkv, w.max_tokens)).astype(np.float32)
+    accum_case(w, pad=pad)
