@@ -58,8 +58,9 @@ inline kvc_status hip_status(hipError_t e) { return e == hipSuccess ? KVC_OK : K
 
 // Shared by kvc_attend_decode, kvc_accum_scores and the workspace query.
 kvc_status check_attend_args(const kvc_cache* c, int32_t hq, int32_t mode, const int32_t* sel,
-                             int32_t k_max, int32_t n_sink, int32_t n_window,
+                             int32_t k_max, int32_t n_sink, int32_t n_window, int32_t workgroups,
                              bool sizing_only = false) {
+  if (workgroups < 0 || workgroups > KVC_MAX_WORKGROUPS) return KVC_ERR_INVALID;
   if (hq < 1 || hq % c->num_kv_heads) return KVC_ERR_SHAPE;
   const int G = hq / c->num_kv_heads;
   if (G > KVC_MAX_GQA) return KVC_ERR_UNSUPPORTED;
@@ -73,7 +74,7 @@ kvc_status check_attend_args(const kvc_cache* c, int32_t hq, int32_t mode, const
     if (sel && !aligned(sel, 4)) return KVC_ERR_INVALID;
   }
   if (mode == KVC_ATTEND_KEEP && (!grouped(c->format) || !c->k16)) return KVC_ERR_UNSUPPORTED;
-  if (!attend_plan_ok(*c, mode, k_max, n_sink, n_window)) return KVC_ERR_UNSUPPORTED;
+  if (!attend_plan_ok(*c, mode, k_max, n_sink, n_window, workgroups)) return KVC_ERR_UNSUPPORTED;
   return KVC_OK;
 }
 
@@ -146,11 +147,11 @@ kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num
 kvc_status kvc_attend_decode(const kvc_cache* cache, const uint16_t* q, int32_t num_q_heads,
                              float sm_scale, int32_t mode, const int32_t* sel, int32_t k_max,
                              int32_t n_sink, int32_t n_window, float* out, float* lse,
-                             float* logits, int64_t logits_stride, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+                             float* logits, int64_t logits_stride, int32_t workgroups,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   kvc_status st = check_cache(cache);
   if (st != KVC_OK) return st;
-  st = check_attend_args(cache, num_q_heads, mode, sel, k_max, n_sink, n_window);
+  st = check_attend_args(cache, num_q_heads, mode, sel, k_max, n_sink, n_window, workgroups);
   if (st != KVC_OK) return st;
   if (!q || !aligned(q, 16) || !out || !lse) return KVC_ERR_INVALID;
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return KVC_ERR_INVALID;
@@ -160,10 +161,12 @@ kvc_status kvc_attend_decode(const kvc_cache* cache, const uint16_t* q, int32_t 
                                                      : (int64_t)cache->max_tokens;
     if (logits_stride < need) return KVC_ERR_SHAPE;
   }
-  const size_t ws = attend_workspace_bytes(*cache, num_q_heads, mode, k_max, n_sink, n_window);
+  const size_t ws = attend_workspace_bytes(*cache, num_q_heads, mode, k_max, n_sink, n_window,
+                                           workgroups);
   if (!workspace || workspace_bytes < ws || !aligned(workspace, 16)) return KVC_ERR_WORKSPACE;
   return hip_status(launch_attend(*cache, q, num_q_heads, sm_scale, mode, sel, k_max, n_sink,
-                                  n_window, out, lse, logits, logits_stride, workspace, stream));
+                                  n_window, out, lse, logits, logits_stride, workgroups, workspace,
+                                  stream));
 }
 
 kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const float* logits,
@@ -172,7 +175,7 @@ kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const f
                             float* acc, hipStream_t stream) {
   kvc_status st = check_cache(cache);
   if (st != KVC_OK) return st;
-  st = check_attend_args(cache, num_q_heads, mode, sel, k_max, n_sink, n_window);
+  st = check_attend_args(cache, num_q_heads, mode, sel, k_max, n_sink, n_window, 0);
   if (st != KVC_OK && !(st == KVC_ERR_UNSUPPORTED && mode == KVC_ATTEND_KEEP)) return st;
   if (!logits || !lse || !acc || !aligned(logits, 4) || !aligned(lse, 4) || !aligned(acc, 4))
     return KVC_ERR_INVALID;
@@ -198,12 +201,13 @@ kvc_status kvc_topk_mass(const kvc_cache* cache, int32_t num_q_heads, const floa
 }
 
 size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t mode,
-                           int32_t k_max, int32_t n_sink, int32_t n_window) {
+                           int32_t k_max, int32_t n_sink, int32_t n_window, int32_t workgroups) {
   if (check_cache(cache) != KVC_OK) return 0;
   if (op == KVC_OP_ATTEND) {
-    if (check_attend_args(cache, num_q_heads, mode, nullptr, k_max, n_sink, n_window, true) != KVC_OK)
+    if (check_attend_args(cache, num_q_heads, mode, nullptr, k_max, n_sink, n_window, workgroups,
+                          true) != KVC_OK)
       return 0;
-    return attend_workspace_bytes(*cache, num_q_heads, mode, k_max, n_sink, n_window);
+    return attend_workspace_bytes(*cache, num_q_heads, mode, k_max, n_sink, n_window, workgroups);
   }
   if (op == KVC_OP_SCORE_TOPK) return topk_workspace_bytes(*cache);
   return 0;

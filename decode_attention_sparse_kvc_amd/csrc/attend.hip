@@ -1402,16 +1402,15 @@ __global__ __launch_bounds__(MT) void merge_kernel(const float* __restrict__ par
 }
 
 constexpr int MAX_SPLITS = 2048;
+// Workgroups a call is planned for by default: one four-wave workgroup per
+// CU of an MI355X (measured on the 128K layers, fewer concurrent streams keep
+// the DRAM pages open longer and beat two per CU).
+constexpr int ATTEND_WG_DEFAULT = 256;
 constexpr int LIST_MAX = 64;   // blocks mode: groups per wave (one list entry per lane)
 
 struct Plan {
   int s_q, s_r, gpw, ppw;
 };
-
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
-}
 
 // Positions of the fp16-rows role per (sequence, KV head) in drop / keep /
 // blocks mode (blocks mode on codes: sinks and window only).
@@ -1427,14 +1426,12 @@ int walk_groups(const kvc_cache& c, int mode, int k_max, int n_sink, int n_windo
   return (int)std::min<int64_t>(all, w);
 }
 
-Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window) {
+// target: workgroups the launch is planned for (see attend_target)
+Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window, int target) {
   Plan p{0, 0, 1, TILE};
   const int NW = waves_per_wg(c.format);
   const int pairs = c.batch * c.num_kv_heads;
   const bool quant = grouped(c.format);
-  // one four-wave workgroup per CU: measured on the 128K layers, fewer
-  // concurrent streams keep the DRAM pages open longer and beat two per CU
-  const int target = env_int("KVC_ATTEND_TARGET_WG", 256);
   // groups the quantized role may walk per pair: every group, or in blocks
   // mode the kept blocks plus the groups holding sinks or window tokens
   const int groups = walk_groups(c, mode, k_max, n_sink, n_window);
@@ -1456,7 +1453,7 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   // the whole call; measured at 128K: FP8 dense 62.6 -> 59.5 us, fp16 Top-4096
   // drop 15.6 -> 13.9 us against four), four beside the quantized role of the
   // drop / keep modes (the ragged keep batch: 262 against 272 us with one)
-  const int rows_per_cu = env_int("KVC_ATTEND_ROWS_WG_PER_CU", quant ? 4 : 1);
+  const int rows_per_cu = quant ? 4 : 1;
   const int64_t rwaves = (quant && mode == KVC_ATTEND_DENSE) ? (int64_t)pairs * NW
                                                              : (int64_t)rows_per_cu * target * NW;
   const int64_t tpw = std::max<int64_t>(1, (tiles * pairs + rwaves - 1) / rwaves);
@@ -1516,9 +1513,11 @@ void launch_fmt(dim3 grid, hipStream_t s, const AttendArgs& a, bool dense, bool 
 
 }  // namespace
 
+int attend_target(int workgroups) { return workgroups > 0 ? workgroups : ATTEND_WG_DEFAULT; }
+
 size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, int n_sink,
-                              int n_window) {
-  const Plan p = plan_attend(c, mode, k_max, n_sink, n_window);
+                              int n_window, int workgroups) {
+  const Plan p = plan_attend(c, mode, k_max, n_sink, n_window, attend_target(workgroups));
   size_t bytes = (size_t)c.batch * hq * (p.s_q + p.s_r) * PART * sizeof(float);
   if (mode != KVC_ATTEND_DENSE && grouped(c.format))   // selection bitmap + prefix
     bytes += 2 * (size_t)c.batch * c.num_kv_heads * (c.max_tokens / 32) * sizeof(uint32_t);
@@ -1530,8 +1529,9 @@ size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, i
   return bytes;
 }
 
-bool attend_plan_ok(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window) {
-  const Plan p = plan_attend(c, mode, k_max, n_sink, n_window);
+bool attend_plan_ok(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window,
+                    int workgroups) {
+  const Plan p = plan_attend(c, mode, k_max, n_sink, n_window, attend_target(workgroups));
   if (p.s_q + p.s_r > MAX_SPLITS) return false;
   if (mode == KVC_ATTEND_BLOCKS && grouped(c.format))
     return (int64_t)p.s_q * waves_per_wg(c.format) * LIST_MAX >= walk_groups(c, mode, k_max, n_sink, n_window);
@@ -1540,9 +1540,9 @@ bool attend_plan_ok(const kvc_cache& c, int mode, int k_max, int n_sink, int n_w
 
 hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm_scale, int mode,
                          const int32_t* sel, int k_max, int n_sink, int n_window, float* out,
-                         float* lse, float* logits, int64_t logits_stride, void* ws,
-                         hipStream_t s) {
-  const Plan p = plan_attend(c, mode, k_max, n_sink, n_window);
+                         float* lse, float* logits, int64_t logits_stride, int workgroups,
+                         void* ws, hipStream_t s) {
+  const Plan p = plan_attend(c, mode, k_max, n_sink, n_window, attend_target(workgroups));
   AttendArgs a;
   a.c = c;
   a.q = q;

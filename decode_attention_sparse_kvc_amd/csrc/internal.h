@@ -132,13 +132,15 @@ hipError_t launch_append(const kvc_cache& c, const uint16_t* k_new, const uint16
                          const int32_t* n_new, int32_t n_new_max, int32_t* overflow,
                          hipStream_t s);
 
-bool attend_plan_ok(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window);
+// workgroups: the attention launch's planned workgroup count (0 = default)
+bool attend_plan_ok(const kvc_cache& c, int mode, int k_max, int n_sink, int n_window,
+                    int workgroups);
 size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, int n_sink,
-                              int n_window);
+                              int n_window, int workgroups);
 hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm_scale, int mode,
                          const int32_t* sel, int k_max, int n_sink, int n_window, float* out,
-                         float* lse, float* logits, int64_t logits_stride, void* ws,
-                         hipStream_t s);
+                         float* lse, float* logits, int64_t logits_stride, int workgroups,
+                         void* ws, hipStream_t s);
 
 size_t topk_workspace_bytes(const kvc_cache& c);
 hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int mode, int n_crit,

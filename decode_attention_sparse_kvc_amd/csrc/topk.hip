@@ -55,8 +55,8 @@ struct TopkArgs {
   uint32_t* above;     // [B][Hkv][max_tokens / 32]
   uint32_t* equal;     // [B][Hkv][max_tokens / 32]
   int32_t* channels;   // [B][Hkv][128]
-  uint64_t* prefix;    // [B][Hkv] key prefix of the bytes chosen so far (radix state)
-  int32_t* krem;       // [B][Hkv] keys still to take from the current bucket
+  uint64_t* prefix;    // [B][Hkv][PASSES] slot s: key prefix of the s + 1 bytes chosen by pass s
+  int32_t* krem;       // [B][Hkv][PASSES] slot s: keys still to take from pass s's bucket
   int32_t* done;       // [B][Hkv] 0, or 8p once pass p found its bucket taken whole
   int hist_words;      // histogram words per pair that prep clears (all passes, or pass 0 only)
   double* qsel;        // critical mode: [B][Hkv][GMAX][128] q of the group's heads on the
@@ -391,12 +391,14 @@ __device__ void select_byte(const uint32_t* hist_pp, uint64_t prefix, int krem, 
 }
 
 // State after pass p - 1 (prefix of p bytes) for (pair pi): pass 0's comes from
-// k alone; later ones from the state stored by the previous pass kernel.
+// k alone; later ones from the state the kernel of pass p - 1 stored in slot
+// p - 2.  Each pass writes its own slot, so the workgroups of one launch that
+// read the previous slot never see a value written in the same launch.
 __device__ void state_after(const TopkArgs& a, int64_t pi, int p, int k, uint64_t* s_prefix,
                             int* s_krem, uint32_t* s_scan) {
   const uint32_t* hist = a.hist + pi * HSTRIDE;
-  const uint64_t prefix = p == 1 ? 0ull : a.prefix[pi];
-  const int krem = p == 1 ? k : a.krem[pi];
+  const uint64_t prefix = p == 1 ? 0ull : a.prefix[pi * PASSES + p - 2];
+  const int krem = p == 1 ? k : a.krem[pi * PASSES + p - 2];
   select_byte(hist + (p - 1) * HREP * 256, prefix, krem, s_prefix, s_krem, s_scan);
 }
 
@@ -425,8 +427,8 @@ __global__ __launch_bounds__(ST) void radix_kernel(TopkArgs a, int p) {
   const uint64_t prefix = s_prefix[0];
   const bool whole = s_krem[1] == s_krem[0];   // every key of the bucket is taken: done
   if (blockIdx.x == 0 && tid == 0) {   // every workgroup derived the same state
-    a.prefix[pi] = prefix;
-    a.krem[pi] = s_krem[0];
+    a.prefix[pi * PASSES + p - 1] = prefix;
+    a.krem[pi * PASSES + p - 1] = s_krem[0];
     if (whole) a.done[pi] = 8 * p;
   }
   if (whole) return;
@@ -466,7 +468,7 @@ __global__ __launch_bounds__(ST) void mark_kernel(TopkArgs a) {
   if (k > 0) {
     bits = a.done[pi];
     if (bits) {
-      P = a.prefix[pi];
+      P = a.prefix[pi * PASSES + bits / 8 - 1];   // the prefix of the pass that found it whole
     } else {
       state_after(a, pi, PASSES, k, s_prefix, s_krem, s_scan);
       T = s_prefix[0];
@@ -751,7 +753,7 @@ size_t topk_workspace_bytes(const kvc_cache& c) {
   bytes += pairs * HSTRIDE * sizeof(uint32_t);
   bytes += 2 * pairs * words * sizeof(uint32_t);
   bytes += pairs * D * sizeof(int32_t);
-  bytes += pairs * (sizeof(uint64_t) + 2 * sizeof(int32_t));
+  bytes += pairs * PASSES * (sizeof(uint64_t) + sizeof(int32_t)) + pairs * sizeof(int32_t);
   return bytes;
 }
 
@@ -794,9 +796,9 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   a.channels = reinterpret_cast<int32_t*>(p);
   p += pairs * D * sizeof(int32_t);
   a.prefix = reinterpret_cast<uint64_t*>(p);
-  p += pairs * sizeof(uint64_t);
+  p += pairs * PASSES * sizeof(uint64_t);
   a.krem = reinterpret_cast<int32_t*>(p);
-  p += pairs * sizeof(int32_t);
+  p += pairs * PASSES * sizeof(int32_t);
   a.done = reinterpret_cast<int32_t*>(p);
 
   const int Hkv = c.num_kv_heads, B = c.batch;

@@ -16,7 +16,7 @@ from ctypes import POINTER, c_double, c_float, c_int32, c_int64, c_size_t, c_voi
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkvc.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 HEAD_DIM = 128
 GROUP = 64
 MAX_OUTLIERS = 4
@@ -75,14 +75,15 @@ def _load():
     lib.kvc_attend_decode.restype = c_int32
     lib.kvc_attend_decode.argtypes = [P, c_void_p, c_int32, c_float, c_int32, c_void_p, c_int32,
                                       c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int64,
-                                      c_void_p, c_size_t, c_void_p]
+                                      c_int32, c_void_p, c_size_t, c_void_p]
     lib.kvc_accum_scores.restype = c_int32
     lib.kvc_accum_scores.argtypes = [P, c_int32, c_void_p, c_int64, c_void_p, c_int32, c_void_p,
                                      c_int32, c_int32, c_int32, c_void_p, c_void_p]
     lib.kvc_topk_mass.restype = c_int32
     lib.kvc_topk_mass.argtypes = [P, c_int32, c_void_p, c_int64, c_void_p, c_int32, c_void_p, c_void_p]
     lib.kvc_workspace_bytes.restype = c_size_t
-    lib.kvc_workspace_bytes.argtypes = [c_int32, P, c_int32, c_int32, c_int32, c_int32, c_int32]
+    lib.kvc_workspace_bytes.argtypes = [c_int32, P, c_int32, c_int32, c_int32, c_int32, c_int32,
+                                        c_int32]
     if lib.kvc_abi_version() != ABI_VERSION:
         raise ImportError(f"{LIB_PATH}: ABI version {lib.kvc_abi_version()} != {ABI_VERSION}")
     _lib = lib
@@ -141,10 +142,11 @@ def kvc_score_topk(cache, q, num_q_heads: int, score_mode: int, n_crit: int, ext
 
 def kvc_attend_decode(cache, q, num_q_heads: int, sm_scale: float, mode: int, sel, k_max: int,
                       n_sink: int, n_window: int, out, lse, logits=None, logits_stride: int = 0,
-                      workspace=None, workspace_bytes: int = 0, stream=None):
+                      workspace=None, workspace_bytes: int = 0, stream=None, *,
+                      workgroups: int = 0):
     _check("kvc_attend_decode", lib().kvc_attend_decode(
         ctypes.byref(cache), _ptr(q), num_q_heads, sm_scale, mode, _ptr(sel), k_max, n_sink,
-        n_window, _ptr(out), _ptr(lse), _ptr(logits), logits_stride, _ptr(workspace),
+        n_window, _ptr(out), _ptr(lse), _ptr(logits), logits_stride, workgroups, _ptr(workspace),
         workspace_bytes, _stream(stream)))
 
 
@@ -163,6 +165,6 @@ def kvc_topk_mass(cache, num_q_heads: int, logits, logits_stride: int, lse, k: i
 
 
 def kvc_workspace_bytes(op: int, cache, num_q_heads: int, mode: int = 0, k_max: int = 0,
-                        n_sink: int = 0, n_window: int = 0) -> int:
+                        n_sink: int = 0, n_window: int = 0, workgroups: int = 0) -> int:
     return int(lib().kvc_workspace_bytes(op, ctypes.byref(cache), num_q_heads, mode, k_max,
-                                         n_sink, n_window))
+                                         n_sink, n_window, workgroups))

@@ -47,11 +47,12 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 #define KVC_HEAD_DIM 128
 #define KVC_GROUP 64
 #define KVC_MAX_GQA 8          /* query heads per KV head supported by attend */
 #define KVC_MAX_OUTLIERS 4     /* fp16 outlier channels per KV head (INT4) */
+#define KVC_MAX_WORKGROUPS 65536  /* largest workgroup count an attend call may be planned for */
 
 typedef int32_t kvc_status;
 enum {
@@ -272,6 +273,14 @@ kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num
  *         DROP with 64 positions per sel entry (token 64 sel[i] + r at
  *         position n_sink + 64 i + r) and the window after n_sink + 64 k_max;
  *         positions that attend nothing hold -inf.  Values are q.k~ * sm_scale.
+ *   workgroups  how many workgroups the attention launch is planned for: the
+ *         context of each (sequence, KV head) is split into partials that
+ *         many workgroups compute and a log-sum-exp merge combines ([MTG] 8.1
+ *         online softmax).  0 = the library's default (one per compute unit
+ *         of an MI355X); 1..KVC_MAX_WORKGROUPS otherwise (KVC_ERR_INVALID
+ *         outside).  Results agree within rounding for every value; the same
+ *         value must be passed to kvc_workspace_bytes.  Nothing else (no
+ *         environment variable, no global setting) changes the plan.
  *   workspace  kvc_workspace_bytes(KVC_OP_ATTEND, ...) bytes: split partials
  *         (and, for DROP/KEEP on INT4/INT1, the selection bitmap); contents
  *         on entry are ignored.
@@ -279,8 +288,8 @@ kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num
 kvc_status kvc_attend_decode(const kvc_cache* cache, const uint16_t* q, int32_t num_q_heads,
                              float sm_scale, int32_t mode, const int32_t* sel, int32_t k_max,
                              int32_t n_sink, int32_t n_window, float* out, float* lse,
-                             float* logits, int64_t logits_stride, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream);
+                             float* logits, int64_t logits_stride, int32_t workgroups,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kvc_accum_scores -- H2O cumulative scores ([SRV] 3.2): for every attended
@@ -311,11 +320,11 @@ kvc_status kvc_topk_mass(const kvc_cache* cache, int32_t num_q_heads, const floa
                          int64_t logits_stride, const float* lse, int32_t k, float* out,
                          hipStream_t stream);
 
-/* Workspace bytes for op (KVC_OP_*) called with these arguments (mode is the
- * attend mode; it is ignored for KVC_OP_SCORE_TOPK); 0 on invalid arguments.
- * Host only. */
+/* Workspace bytes for op (KVC_OP_*) called with these arguments (mode and
+ * workgroups are the attend call's; both are ignored for KVC_OP_SCORE_TOPK);
+ * 0 on invalid arguments.  Host only. */
 size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t mode,
-                           int32_t k_max, int32_t n_sink, int32_t n_window);
+                           int32_t k_max, int32_t n_sink, int32_t n_window, int32_t workgroups);
 
 /* Static description of a status code. */
 const char* kvc_status_str(kvc_status status);

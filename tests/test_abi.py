@@ -48,7 +48,7 @@ def test_struct_field_count_matches_header():
 
 def _desc(**kw):
     d = kvc.kvc_cache()
-    base = dict(abi_version=2, format=1, batch=1, num_kv_heads=1, head_dim=128, group_size=64,
+    base = dict(abi_version=kvc.ABI_VERSION, format=1, batch=1, num_kv_heads=1, head_dim=128, group_size=64,
                 page_size=0, max_tokens=64, max_pages=0, num_pages=0,
                 seq_lens=0x1000, k_codes=0x2000, v_codes=0x3000, k_meta=0x4000, v_meta=0x5000,
                 k_tail=0x6000, v_tail=0x7000, k_absmax=0x8000)
@@ -139,6 +139,13 @@ def test_workspace_sizes():
     a3 = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 4, 3, 61, 4, 64)          # blocks mode
     assert a3 > 0
     assert kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 36, 0, 0, 0, 0) == 0     # G = 36 > 8
+    # the planned workgroup count is an explicit argument: 0 is the default plan,
+    # more workgroups mean more split partials, out-of-range values are rejected
+    assert kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 4, 0, 0, 0, 0, 0) == a1
+    assert kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 4, 0, 0, 0, 0, 1) < a1
+    assert kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 4, 0, 0, 0, 0, 4096) >= a1
+    assert kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 4, 0, 0, 0, 0, -1) == 0
+    assert kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 4, 0, 0, 0, 0, 65537) == 0
 
 
 def test_topk_mass_argument_checks():

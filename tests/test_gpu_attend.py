@@ -23,18 +23,19 @@ def sel_tensor(res, w, k_max):
     return sel
 
 
-def run_attend(cache, w, sel=None, k_max=0, logits=True):
+def run_attend(cache, w, sel=None, k_max=0, logits=True, workgroups=0):
     mode = kvc.MODE[w.mode]
     B, hq = w.batch, w.hq
     out = torch.full((B, hq, 128), float("nan"), device="cuda")
     lse = torch.full((B, hq), float("nan"), device="cuda")
     stride = w.n_sink + k_max + w.n_window if w.mode == "drop" else cache.max_tokens
     lg = torch.full((B, hq, stride), float("nan"), device="cuda") if logits else None
-    nbytes = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, cache.desc, hq, mode, k_max, w.n_sink, w.n_window)
+    nbytes = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, cache.desc, hq, mode, k_max, w.n_sink, w.n_window,
+                                     workgroups)
     ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
     sel_t = dev(sel) if sel is not None else None
     kvc.kvc_attend_decode(cache.desc, dev(w.q), hq, w.sm_scale, mode, sel_t, k_max, w.n_sink,
-                          w.n_window, out, lse, lg, stride, ws, nbytes)
+                          w.n_window, out, lse, lg, stride, ws, nbytes, workgroups=workgroups)
     torch.cuda.synchronize()
     return host(out), host(lse), (host(lg) if logits else None), stride
 
@@ -121,24 +122,22 @@ def test_dense_paged(fmt, page):
     check_against_oracle(w, res, out, lse, lg)
 
 
-def test_workspace_reuse(monkeypatch):
+def test_workspace_reuse():
     """One workspace (holding stale partials of earlier calls) serves call after call, also
     when the split count changes between calls; repeated calls agree bit for bit."""
     w = W.int4_dense(3000)
     res, cache = oracle_and_cache(w)
     mode = kvc.MODE[w.mode]
     sizes = {}
-    for t in ["512", "3", "64"]:
-        monkeypatch.setenv("KVC_ATTEND_TARGET_WG", t)
-        sizes[t] = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, cache.desc, w.hq, mode, 0, 0, 0)
+    for t in [512, 3, 64]:
+        sizes[t] = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, cache.desc, w.hq, mode, 0, 0, 0, t)
     ws = torch.full((max(sizes.values()),), 255, dtype=torch.uint8, device="cuda")   # NaN bytes
     outs = []
-    for t in ["512", "3", "512", "64", "3"]:
-        monkeypatch.setenv("KVC_ATTEND_TARGET_WG", t)
+    for t in [512, 3, 512, 64, 3]:
         out = torch.full((w.batch, w.hq, 128), float("nan"), device="cuda")
         lse = torch.full((w.batch, w.hq), float("nan"), device="cuda")
         kvc.kvc_attend_decode(cache.desc, dev(w.q), w.hq, w.sm_scale, mode, None, 0, 0, 0,
-                              out, lse, None, 0, ws, ws.numel())
+                              out, lse, None, 0, ws, ws.numel(), workgroups=t)
         torch.cuda.synchronize()
         check_against_oracle(w, res, host(out), host(lse), None)
         outs.append((t, host(out), host(lse)))
@@ -251,13 +250,12 @@ def test_keep_paged_int4(append):
     check_against_oracle(w, res, out, lse, lg)
 
 
-@pytest.mark.parametrize("target", ["1", "64", "4096"])
-def test_split_count_invariance(monkeypatch, target):
+@pytest.mark.parametrize("target", [1, 64, 4096])
+def test_split_count_invariance(target):
     """The result does not depend on how the context is split across workgroups."""
-    monkeypatch.setenv("KVC_ATTEND_TARGET_WG", target)
     w = W.int4_dense(5000)
     res, cache = oracle_and_cache(w)
-    out, lse, lg, _ = run_attend(cache, w)
+    out, lse, lg, _ = run_attend(cache, w, workgroups=target)
     check_against_oracle(w, res, out, lse, lg)
 
 
