@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--replica-bytes", type=float, default=1.5 * 2**30,
                     help="total bytes of rotated cache replicas (defeats the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workgroups", type=int, default=0,
+                    help="workgroups the attend call is planned for (0: the library default)")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch every call from Python instead of replaying HIP graphs")
     ap.add_argument("--cpu-sample-seconds", type=float, default=15.0)
@@ -206,7 +208,8 @@ def main():
     k_max = int(w.top_k.max()) if sparse else 0
     out = torch.empty(w.batch, w.hq, 128, device=dev)
     lse = torch.empty(w.batch, w.hq, device=dev)
-    nbytes = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, base.desc, w.hq, mode, k_max, w.n_sink, w.n_window)
+    nbytes = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, base.desc, w.hq, mode, k_max, w.n_sink, w.n_window,
+                                     args.workgroups)
     ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
     if sparse:
         tk_bytes = kvc.kvc_workspace_bytes(kvc.OP_SCORE_TOPK, base.desc, w.hq)
@@ -242,7 +245,7 @@ def main():
     def op_attend(r, st):
         kvc.kvc_attend_decode(reps[r].desc, q, w.hq, w.sm_scale, mode, sel if sparse else None,
                               k_max, w.n_sink, w.n_window, out, lse, logits if want_logits else None,
-                              stride if want_logits else 0, ws, nbytes, st)
+                              stride if want_logits else 0, ws, nbytes, st, workgroups=args.workgroups)
 
     def op_accum(r, st):
         kvc.kvc_accum_scores(reps[r].desc, w.hq, logits, stride, lse, mode, sel if sparse else None,

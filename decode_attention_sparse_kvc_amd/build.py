@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import glob
+import hashlib
 import os
 import shutil
 import subprocess
@@ -23,6 +24,25 @@ FLAGS = [
 ]
 
 
+def source_files() -> list[str]:
+    """Every file the library is compiled from: the HIP sources, their shared
+    header and the ABI header."""
+    return (sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.h")))
+            + [os.path.join(ROOT, "include", "kvc.h")])
+
+
+def source_digest() -> str:
+    """16 hex digits of SHA-256 over the library's source files (name + bytes,
+    in a fixed order).  build() compiles it into libkvc.so, whose
+    kvc_build_digest() returns it, so a loader can tell a library built from
+    other sources."""
+    h = hashlib.sha256()
+    for path in source_files():
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -35,10 +55,11 @@ def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     cc = hipcc()
+    digest = source_digest()
 
     def compile_one(src):
         obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-        cmd = [cc, *FLAGS, "-c", src, "-o", obj]
+        cmd = [cc, *FLAGS, f'-DKVC_BUILD_DIGEST="{digest}"', "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -78,11 +78,42 @@ kvc_status check_attend_args(const kvc_cache* c, int32_t hq, int32_t mode, const
   return KVC_OK;
 }
 
+// Logits row length an attend call writes (its stride must be at least this).
+int64_t logits_positions(const kvc_cache* c, int32_t mode, int32_t k_max, int32_t n_sink,
+                         int32_t n_window) {
+  return mode == KVC_ATTEND_DROP ? (int64_t)n_sink + k_max + n_window
+         : mode == KVC_ATTEND_BLOCKS ? (int64_t)n_sink + (int64_t)KVC_GROUP * k_max + n_window
+                                     : (int64_t)c->max_tokens;
+}
+
+// Everything both attend entry points validate; *ws receives the workspace
+// bytes the call needs.
+kvc_status check_attend_call(const kvc_cache* cache, const uint16_t* q, int32_t num_q_heads,
+                             float sm_scale, int32_t mode, const int32_t* sel, int32_t k_max,
+                             int32_t n_sink, int32_t n_window, float* out, float* lse,
+                             float* logits, int64_t logits_stride, int32_t workgroups, size_t* ws) {
+  kvc_status st = check_cache(cache);
+  if (st != KVC_OK) return st;
+  st = check_attend_args(cache, num_q_heads, mode, sel, k_max, n_sink, n_window, workgroups);
+  if (st != KVC_OK) return st;
+  if (!q || !aligned(q, 16) || !out || !lse) return KVC_ERR_INVALID;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return KVC_ERR_INVALID;
+  if (logits && logits_stride < logits_positions(cache, mode, k_max, n_sink, n_window))
+    return KVC_ERR_SHAPE;
+  *ws = attend_workspace_bytes(*cache, num_q_heads, mode, k_max, n_sink, n_window, workgroups);
+  return KVC_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int32_t kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+#ifndef KVC_BUILD_DIGEST
+#define KVC_BUILD_DIGEST "unknown"
+#endif
+const char* kvc_build_digest(void) { return KVC_BUILD_DIGEST; }
 
 const char* kvc_status_str(kvc_status s) {
   switch (s) {
@@ -149,20 +180,11 @@ kvc_status kvc_attend_decode(const kvc_cache* cache, const uint16_t* q, int32_t 
                              int32_t n_sink, int32_t n_window, float* out, float* lse,
                              float* logits, int64_t logits_stride, int32_t workgroups,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  kvc_status st = check_cache(cache);
+  size_t ws = 0;
+  const kvc_status st = check_attend_call(cache, q, num_q_heads, sm_scale, mode, sel, k_max,
+                                          n_sink, n_window, out, lse, logits, logits_stride,
+                                          workgroups, &ws);
   if (st != KVC_OK) return st;
-  st = check_attend_args(cache, num_q_heads, mode, sel, k_max, n_sink, n_window, workgroups);
-  if (st != KVC_OK) return st;
-  if (!q || !aligned(q, 16) || !out || !lse) return KVC_ERR_INVALID;
-  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return KVC_ERR_INVALID;
-  if (logits) {
-    const int64_t need = mode == KVC_ATTEND_DROP ? (int64_t)n_sink + k_max + n_window
-                         : mode == KVC_ATTEND_BLOCKS ? (int64_t)n_sink + (int64_t)KVC_GROUP * k_max + n_window
-                                                     : (int64_t)cache->max_tokens;
-    if (logits_stride < need) return KVC_ERR_SHAPE;
-  }
-  const size_t ws = attend_workspace_bytes(*cache, num_q_heads, mode, k_max, n_sink, n_window,
-                                           workgroups);
   if (!workspace || workspace_bytes < ws || !aligned(workspace, 16)) return KVC_ERR_WORKSPACE;
   return hip_status(launch_attend(*cache, q, num_q_heads, sm_scale, mode, sel, k_max, n_sink,
                                   n_window, out, lse, logits, logits_stride, workgroups, workspace,
@@ -179,10 +201,7 @@ kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const f
   if (st != KVC_OK && !(st == KVC_ERR_UNSUPPORTED && mode == KVC_ATTEND_KEEP)) return st;
   if (!logits || !lse || !acc || !aligned(logits, 4) || !aligned(lse, 4) || !aligned(acc, 4))
     return KVC_ERR_INVALID;
-  const int64_t need = mode == KVC_ATTEND_DROP ? (int64_t)n_sink + k_max + n_window
-                       : mode == KVC_ATTEND_BLOCKS ? (int64_t)n_sink + (int64_t)KVC_GROUP * k_max + n_window
-                                                   : (int64_t)cache->max_tokens;
-  if (logits_stride < need) return KVC_ERR_SHAPE;
+  if (logits_stride < logits_positions(cache, mode, k_max, n_sink, n_window)) return KVC_ERR_SHAPE;
   return hip_status(launch_accum(*cache, num_q_heads, logits, logits_stride, lse, mode, sel, k_max,
                                  n_sink, n_window, acc, stream));
 }

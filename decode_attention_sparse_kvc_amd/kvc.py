@@ -3,9 +3,10 @@
 Argument marshalling only: every step of the decode path runs in the HIP
 kernels of libkvc.so.  Functions carry the C names and take torch tensors (or
 None for NULL); fp16 data is passed as the tensors' raw bits.  A non-zero
-status raises ``KvcError``.  If the library is missing it is built in-tree;
-if it cannot be loaded, importing this module fails loudly: there is no CPU
-fallback.
+status raises ``KvcError``.  If the library is missing it is built in-tree; a
+library whose embedded source digest differs from the sources beside it is
+refused (rebuild it with ``build.build()``); if it cannot be loaded, the first
+call fails loudly: there is no CPU fallback.
 """
 from __future__ import annotations
 
@@ -63,6 +64,12 @@ def _load():
         build()
     lib = ctypes.CDLL(LIB_PATH)
     P = POINTER(kvc_cache)
+    lib.kvc_build_digest.restype = ctypes.c_char_p
+    from .build import source_digest
+    built, here = lib.kvc_build_digest().decode(), source_digest()
+    if built != here:
+        raise ImportError(f"{LIB_PATH} was built from other sources (digest {built}, sources {here}); "
+                          "rebuild it: python -m decode_attention_sparse_kvc_amd.build")
     lib.kvc_abi_version.restype = c_int32
     lib.kvc_status_str.restype = ctypes.c_char_p
     lib.kvc_status_str.argtypes = [c_int32]
@@ -118,6 +125,10 @@ def _check(fn: str, status: int):
 
 def kvc_abi_version() -> int:
     return lib().kvc_abi_version()
+
+
+def kvc_build_digest() -> str:
+    return lib().kvc_build_digest().decode()
 
 
 def kvc_status_str(status: int) -> str:

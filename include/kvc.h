@@ -332,6 +332,12 @@ const char* kvc_status_str(kvc_status status);
 /* KVC_ABI_VERSION of the built library. */
 int32_t kvc_abi_version(void);
 
+/* Digest of the sources the library was compiled from (16 hex digits of
+ * SHA-256 over the HIP sources and headers, set by the build), or "unknown"
+ * when the build did not define it.  Static string; lets a loader refuse a
+ * library built from other sources. */
+const char* kvc_build_digest(void);
+
 #ifdef __cplusplus
 }
 #endif

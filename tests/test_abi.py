@@ -25,7 +25,8 @@ def test_library_exports_every_declared_symbol():
     lib = kvc.lib()
     names = declared_functions()
     assert {"kvc_quantize_append", "kvc_score_topk", "kvc_attend_decode", "kvc_accum_scores",
-            "kvc_topk_mass", "kvc_workspace_bytes", "kvc_status_str", "kvc_abi_version"} <= set(names)
+            "kvc_topk_mass", "kvc_workspace_bytes", "kvc_status_str", "kvc_abi_version",
+            "kvc_build_digest"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert kvc.kvc_abi_version() == kvc.ABI_VERSION
@@ -159,3 +160,10 @@ def test_topk_mass_argument_checks():
     assert call(logits=0x10002) == 1
     assert call(k=-1) == 1
     assert call(stride=4095) == 2
+
+
+def test_library_digest_names_its_sources():
+    """The loaded library was compiled from the sources beside it (a stale build is refused)."""
+    from decode_attention_sparse_kvc_amd.build import source_digest
+    assert kvc.kvc_build_digest() == source_digest()
+    assert len(source_digest()) == 16
