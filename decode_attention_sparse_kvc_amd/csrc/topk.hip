@@ -5,23 +5,26 @@
 // cumulative scores).
 //
 // Kernels, all on the caller's stream:
-//   prep    per (sequence, KV head): critical channels (exact fp64 products,
-//           rank with ties to the lower channel) and zeroed histograms.
-//   score   one thread per token: the fp64 score, summed channel by channel in
-//           ascending order from +0.0 (the order the interface fixes, so results
-//           are reproducible bit for bit), max over the query group, turned into
-//           an order-preserving 64-bit key (0 = not a candidate); histogram of
-//           the key's top byte.
-//   radix   passes 1..7: histogram of the next byte among keys that share the
-//           bytes chosen so far; each pass derives the byte of the previous
-//           pass from its histogram and the stored state of the pass before.
-//   mark    bitmaps of keys above the k-th largest key T and equal to T.
-//   emit    one workgroup per (sequence, KV head): the first k - #above keys
-//           equal to T by index, then every selected index in ascending order.
+//   prep     per (sequence, KV head): critical channels (exact fp64 products,
+//            rank with ties to the lower channel) and a zeroed histogram.
+//   score    one thread per token: the fp64 score, summed channel by channel in
+//            ascending order from +0.0 (the order the interface fixes, so results
+//            are reproducible bit for bit), max over the query group, turned into
+//            an order-preserving 64-bit key (0 = not a candidate); histogram of
+//            the keys' 12-bit coarse bins (sign, clamped exponent, 4 mantissa
+//            bits: a monotone function of the key).
+//   compact  (long ranges) per 4096 items: the coarse bin tb holding the k-th
+//            largest key (from the histogram); a bitmap of the items in bins
+//            above tb, and the items of bin tb (key, index) in index order.
+//   finish   one workgroup per (sequence, KV head): exact radix select among
+//            the keys of bin tb (LDS passes over 8-bit digits, from the first
+//            digit where they differ), lower index first among equal keys, then
+//            every selected index in ascending order.  Short ranges skip
+//            compact: finish reads the keys itself.
 // Block mode (meeting-LLM article, section 8.1: importance averaged over
 // 64-token blocks, the top blocks kept): score writes each token's fp64 score
 // and no key; block_key averages every candidate block's 64 scores into the
-// block's key (item j of the pair's key row) and histograms it; the passes
+// block's key (item j of the pair's key row) and histograms it; the kernels
 // above then select blocks instead of tokens.
 
 #include <math.h>
@@ -31,12 +34,17 @@
 namespace kvc {
 namespace {
 
-constexpr int ST = 256;        // threads of the scoring / radix workgroups
-constexpr int TPB = 1024;      // tokens per radix / mark workgroup
-constexpr int ET = 1024;       // threads of the emit workgroup
-constexpr int PASSES = 8;
-constexpr int HREP = 8;        // copies of each histogram (spread the global atomics)
-constexpr int HSTRIDE = PASSES * HREP * 256;   // histogram words per (sequence, KV head)
+constexpr int ST = 256;        // threads of the block-key and compaction workgroups
+constexpr int SCT = 1024;      // threads (= tokens) of a scoring workgroup
+constexpr int CBINS = 4096;    // coarse bins of the keys
+constexpr int HREP = 2;        // copies of the coarse histogram (spread the global atomics)
+constexpr int HW = CBINS * HREP;   // histogram words per (sequence, KV head)
+constexpr int CT = 4096;       // items per compaction workgroup
+constexpr int FT = 1024;       // threads of the finish workgroup
+constexpr int CAP = 8192;      // bin-tb items the finish workgroup holds in LDS
+constexpr int DIRECT_MAX = 8192;   // items up to which finish reads the keys itself (in LDS)
+constexpr int MAXR = 4096;     // compaction regions finish can index (items <= MAXR * CT)
+constexpr int EW = 4096;       // bitmap words per emission chunk (EW / FT words a thread)
 
 struct TopkArgs {
   kvc_cache c;
@@ -50,15 +58,14 @@ struct TopkArgs {
   double* out_scores;
   int32_t* out_channels;
   // workspace
-  uint64_t* keys;      // [B][Hkv][max_tokens]
-  uint32_t* hist;      // [B][Hkv][PASSES][HREP][256]
-  uint32_t* above;     // [B][Hkv][max_tokens / 32]
-  uint32_t* equal;     // [B][Hkv][max_tokens / 32]
+  uint64_t* keys;      // [B][Hkv][max_tokens] item keys (0: not a candidate)
+  uint32_t* hist;      // [B][Hkv][HREP][CBINS] coarse histogram
+  uint32_t* above;     // [B][Hkv][max_tokens / 32] items in bins above the threshold bin
+  uint64_t* ckey;      // [B][Hkv][nreg * CT] keys of the threshold bin, per compaction region
+  int32_t* cidx;       // [B][Hkv][nreg * CT] their item indices
+  int32_t* ccount;     // [B][Hkv][nreg] entries per region
+  int nreg;            // compaction regions per pair (ceil(items / CT))
   int32_t* channels;   // [B][Hkv][128]
-  uint64_t* prefix;    // [B][Hkv][PASSES] slot s: key prefix of the s + 1 bytes chosen by pass s
-  int32_t* krem;       // [B][Hkv][PASSES] slot s: keys still to take from pass s's bucket
-  int32_t* done;       // [B][Hkv] 0, or 8p once pass p found its bucket taken whole
-  int hist_words;      // histogram words per pair that prep clears (all passes, or pass 0 only)
   double* qsel;        // critical mode: [B][Hkv][GMAX][128] q of the group's heads on the
                        // channel list (slot k = k-th critical channel), fp64
   bool blocks;         // rank 64-token blocks (items = block ids)
@@ -68,6 +75,25 @@ struct TopkArgs {
 __device__ inline uint64_t order_key(double d) {
   const uint64_t u = (uint64_t)__double_as_longlong(d);
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// 12-bit coarse bin of a key: its top bit (the score's sign), its exponent
+// field clamped to a window of 128 binades (2^-64 .. 2^63 in magnitude; keys
+// outside it share the end bins), then the top 4 mantissa bits (0 below the
+// window, 15 above it).  Non-decreasing in the key, so every key in a higher
+// bin is larger than every key in a lower one.
+__device__ inline uint32_t coarse_of(uint64_t key) {
+  const uint32_t t = (uint32_t)(key >> 63);
+  const int e = (int)((key >> 52) & 0x7FFu) - (t ? 959 : 961);
+  const uint32_t m4 = (uint32_t)(key >> 48) & 15u;
+  const uint32_t e7 = e < 0 ? 0u : e > 127 ? 127u : (uint32_t)e;
+  const uint32_t mm = e < 0 ? 0u : e > 127 ? 15u : m4;
+  return (t << 11) | (e7 << 4) | mm;
+}
+
+// Items the selection runs over per (sequence, KV head): tokens, or blocks.
+__host__ __device__ inline int item_count(const kvc_cache& c, bool blocks) {
+  return blocks ? c.max_tokens / GS : c.max_tokens;
 }
 
 __device__ inline int64_t pair_index(const TopkArgs& a, int b, int g) {
@@ -97,9 +123,8 @@ constexpr int GMAX_PREP = 16;
 __global__ __launch_bounds__(D) void prep_kernel(TopkArgs a) {
   const int g = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
   const int64_t pi = pair_index(a, b, g);
-  uint4* h = reinterpret_cast<uint4*>(a.hist + pi * HSTRIDE);
-  for (int e = c; e < a.hist_words / 4; e += D) h[e] = uint4{0u, 0u, 0u, 0u};
-  if (c == 0) a.done[pi] = 0;
+  uint4* h = reinterpret_cast<uint4*>(a.hist + pi * HW);
+  for (int e = c; e < HW / 4; e += D) h[e] = uint4{0u, 0u, 0u, 0u};
   __shared__ double s[D];
   __shared__ int chosen[D];
   if (a.mode == KVC_SCORE_CRITICAL) {
@@ -162,7 +187,9 @@ __device__ inline double token_score(int G, int nch_, const int* sch, const doub
   double acc[GN];
 #pragma unroll
   for (int hh = 0; hh < GN; ++hh) acc[hh] = 0.0;
-#pragma unroll
+  // (batches stay a loop: unrolling the 128-channel exact sum over G heads
+  // leaves more live values than the registers hold)
+#pragma unroll 1
   for (int k0 = 0; k0 < (ALL ? D : nch); k0 += CB) {
     int ch[CB];
     uint32_t raw[CB], mx[CB];
@@ -194,26 +221,34 @@ __device__ inline double token_score(int G, int nch_, const int* sch, const doub
 }
 
 // One thread per token: the score on the channel list (max over the query
-// group), an order-preserving key, and the histogram of the key's top byte.
+// group), an order-preserving key, and the coarse histogram of the keys
+// (counted in LDS, then one global atomic per non-empty bin of the workgroup).
+// Workgroup size: 1024 tokens (one histogram flush per 1024 keys), except in
+// exact mode and for query groups of 8 or more heads, whose sums need the
+// registers of 256-thread groups.
+template <bool EXACT, int GT>
+constexpr int score_threads() { return EXACT || GT == 0 || GT >= 8 ? ST : SCT; }
+
 template <int FMT, bool KT, int GT, bool EXACT>
-__global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
+__global__ __launch_bounds__((score_threads<EXACT, GT>())) void score_kernel(TopkArgs a) {
+  constexpr int NT = score_threads<EXACT, GT>();
   constexpr int CB = EXACT ? CB_EXACT : CB_CRIT;
   const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int t = blockIdx.x * ST + tid;
+  const int t = blockIdx.x * NT + tid;
   const int64_t pi = pair_index(a, b, g);
   extern __shared__ double sq[];    // q as fp64, [head][channel slot], G x nch (sized at launch)
   __shared__ int sch[D];
-  __shared__ uint32_t sh[256];
-  __shared__ uint32_t smeta[grouped(FMT) ? (ST / GS) * D : 1];   // (scale | zero << 16) per channel
+  __shared__ uint32_t sh[CBINS];
+  __shared__ uint32_t smeta[grouped(FMT) ? (NT / GS) * D : 1];   // (scale | zero << 16) per channel
   const int G = a.G;
   const kvc_cache& c = a.c;
   const int nch = a.mode == KVC_SCORE_CRITICAL ? a.n_crit : (a.mode == KVC_SCORE_EXACT ? D : 0);
-  for (int e = tid; e < nch; e += ST)
+  for (int e = tid; e < nch; e += NT)
     sch[e] = a.mode == KVC_SCORE_CRITICAL ? a.channels[pi * D + e] : e;
-  sh[tid] = 0u;
+  for (int e = tid; e < CBINS; e += NT) sh[e] = 0u;
   if (grouped(FMT) && nch > 0) {   // K metadata of the block's groups, channel pairs a thread
     const int groups = c.max_tokens / GS;
-    const int gq = blockIdx.x * (ST / GS) + tid / 64, j = tid % 64;
+    const int gq = blockIdx.x * (NT / GS) + tid / 64, j = tid % 64;
     uint32_t s2 = 0u, z2 = 0u;
     if (gq < groups) {
       const uint32_t* km = reinterpret_cast<const uint32_t*>(c.k_meta + (pi * groups + gq) * 2 * D);
@@ -232,7 +267,7 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
     smeta[(tid / 64) * D + 2 * j + 1] = m1;
   }
   // q on the channel list: gathered by prep (critical mode) or channel k itself
-  for (int e = tid; e < G * nch; e += ST) {
+  for (int e = tid; e < G * nch; e += NT) {
     const int hh = e / nch, k = e % nch;
     sq[hh * nch + k] = a.mode == KVC_SCORE_CRITICAL
                          ? a.qsel[(pi * GMAX + hh) * D + k]
@@ -314,28 +349,30 @@ __global__ __launch_bounds__(ST) void score_kernel(TopkArgs a) {
     }
   }
   if (in) a.keys[pi * c.max_tokens + t] = key;
-  if (key) atomicAdd(&sh[key >> 56], 1u);
+  if (key) atomicAdd(&sh[coarse_of(key)], 1u);
   __syncthreads();
-  if (sh[tid]) atomicAdd(&a.hist[pi * HSTRIDE + (blockIdx.x % HREP) * 256 + tid], sh[tid]);
+  uint32_t* h = a.hist + pi * HW + (blockIdx.x % HREP) * CBINS;
+  for (int e = tid; e < CBINS; e += NT)
+    if (sh[e]) atomicAdd(&h[e], sh[e]);
 }
 
 // ------------------------------------------------------------------ block keys
 // Block mode: 64 candidate blocks a workgroup.  Their 64 x 64 token scores are
 // staged in LDS with coalesced loads, then thread j adds block j's scores one
 // at a time in ascending token order from +0.0, divides by 64 (exact), and
-// writes the block's key and its pass-0 histogram entry.  Items that are not
+// writes the block's key and its coarse histogram entry.  Items that are not
 // candidates keep the zero key the score kernel wrote.
 constexpr int BPW = 64;
 __global__ __launch_bounds__(ST) void block_key_kernel(TopkArgs a) {
   const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int64_t pi = pair_index(a, b, g);
   __shared__ double ss[BPW * GS];
-  __shared__ uint32_t sh[256];
+  __shared__ uint32_t sh[CBINS];
   int lo, hi, kk;
   cand_range(a, b, lo, hi, kk);
   const int j0 = blockIdx.x * BPW;
   const double* ts = a.tscore + pi * a.c.max_tokens;
-  sh[tid] = 0u;
+  for (int e = tid; e < CBINS; e += ST) sh[e] = 0u;
   for (int e = tid; e < BPW * GS; e += ST) {
     const int j = j0 + e / GS;
     ss[e] = j >= lo && j < hi ? ts[(int64_t)j0 * GS + e] : 0.0;
@@ -350,397 +387,394 @@ __global__ __launch_bounds__(ST) void block_key_kernel(TopkArgs a) {
       const uint64_t key = order_key(r);
       a.keys[pi * a.c.max_tokens + j] = key;
       if (a.out_scores) a.out_scores[pi * a.c.max_tokens + j] = r;
-      atomicAdd(&sh[key >> 56], 1u);
+      atomicAdd(&sh[coarse_of(key)], 1u);
     }
   }
   __syncthreads();
-  if (sh[tid]) atomicAdd(&a.hist[pi * HSTRIDE + (blockIdx.x % HREP) * 256 + tid], sh[tid]);
+  uint32_t* h = a.hist + pi * HW + (blockIdx.x % HREP) * CBINS;
+  for (int e = tid; e < CBINS; e += ST)
+    if (sh[e]) atomicAdd(&h[e], sh[e]);
 }
 
-// ------------------------------------------------------------------ radix passes
-// One selection step (256 threads; hist_pp holds HREP copies of the pass's
-// histogram; s_krem[1] receives the chosen bucket's size): given the prefix of the bytes chosen so far
-// and the number of keys still to take, pick the byte d of pass pp whose
-// bucket holds the krem-th largest key (suffix count of buckets >= d reaches
-// krem, of buckets > d does not).  Results through LDS.
-__device__ void select_byte(const uint32_t* hist_pp, uint64_t prefix, int krem, uint64_t* s_prefix,
-                            int* s_krem, uint32_t* s_scan) {
+// ------------------------------------------------------------------ selection helpers
+// Inclusive scan of x over the NT threads of the workgroup (wave scans, then
+// the wave totals through s_wsum[NT / 64]); *total receives the sum.
+template <int NT>
+__device__ inline uint32_t block_scan(uint32_t x, uint32_t* s_wsum, uint32_t* total) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // suffix sum over bins: inclusive scan of the reversed histogram (copies summed)
-  uint32_t x = 0;
-#pragma unroll
-  for (int r = 0; r < HREP; ++r) x += hist_pp[r * 256 + 255 - tid];
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const uint32_t y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
-  if (lane == 63) s_scan[256 + wv] = x;
+  if (lane == 63) s_wsum[wv] = x;
   __syncthreads();
-  for (int k = 0; k < wv; ++k) x += s_scan[256 + k];
-  s_scan[255 - tid] = x;   // s_scan[d] = keys in buckets >= d
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    const uint32_t v = s_wsum[k];
+    before += k < wv ? v : 0u;
+    all += v;
+  }
   __syncthreads();
-  const uint32_t ge = s_scan[tid];
-  const uint32_t gt = tid < 255 ? s_scan[tid + 1] : 0u;
-  if (ge >= (uint32_t)krem && gt < (uint32_t)krem) {
-    s_prefix[0] = (prefix << 8) | (uint64_t)tid;
-    s_krem[0] = krem - (int)gt;
-    s_krem[1] = (int)(ge - gt);   // keys in the chosen bucket
+  *total = all;
+  return before + x;
+}
+
+// The coarse bin tb holding the k-th largest key of the pair (1 <= k <= keys
+// counted) and n_gt, the keys in the bins above it, from the pair's histogram
+// copies: thread t sums bins [CBINS - BPT (t + 1), CBINS - BPT t) (the highest
+// bins first), a scan gives the keys above each thread's bins, and the thread
+// whose bins the k-th key falls in walks them.  Results in s_res[0] (tb) and
+// s_res[1] (n_gt).
+template <int NT>
+__device__ void coarse_threshold(const uint32_t* hist, int k, int* s_res, uint32_t* s_wsum) {
+  constexpr int BPT = CBINS / NT;
+  static_assert(BPT % 4 == 0, "bins a thread reads as 16-byte words");
+  const int top = CBINS - BPT * (int)threadIdx.x;   // bins [top - BPT, top)
+  uint32_t cnt[BPT];
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) cnt[i] = 0u;
+#pragma unroll
+  for (int r = 0; r < HREP; ++r) {
+#pragma unroll
+    for (int v = 0; v < BPT / 4; ++v) {
+      const uint4 w = *reinterpret_cast<const uint4*>(hist + r * CBINS + top - BPT + 4 * v);
+      cnt[4 * v] += w.x;
+      cnt[4 * v + 1] += w.y;
+      cnt[4 * v + 2] += w.z;
+      cnt[4 * v + 3] += w.w;
+    }
+  }
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) sum += cnt[i];
+  if (threadIdx.x == 0) {   // (k is at most the keys counted, so some thread overwrites these)
+    s_res[0] = 0;
+    s_res[1] = 0;
+  }
+  uint32_t total;
+  uint32_t run = block_scan<NT>(sum, s_wsum, &total) - sum;   // keys in the bins above
+#pragma unroll
+  for (int i = BPT - 1; i >= 0; --i) {   // bin top - BPT + i, highest first
+    if (run < (uint32_t)k && run + cnt[i] >= (uint32_t)k) {
+      s_res[0] = top - BPT + i;
+      s_res[1] = (int)run;
+    }
+    run += cnt[i];
   }
   __syncthreads();
 }
 
-// State after pass p - 1 (prefix of p bytes) for (pair pi): pass 0's comes from
-// k alone; later ones from the state the kernel of pass p - 1 stored in slot
-// p - 2.  Each pass writes its own slot, so the workgroups of one launch that
-// read the previous slot never see a value written in the same launch.
-__device__ void state_after(const TopkArgs& a, int64_t pi, int p, int k, uint64_t* s_prefix,
-                            int* s_krem, uint32_t* s_scan) {
-  const uint32_t* hist = a.hist + pi * HSTRIDE;
-  const uint64_t prefix = p == 1 ? 0ull : a.prefix[pi * PASSES + p - 2];
-  const int krem = p == 1 ? k : a.krem[pi * PASSES + p - 2];
-  select_byte(hist + (p - 1) * HREP * 256, prefix, krem, s_prefix, s_krem, s_scan);
-}
-
-__global__ __launch_bounds__(ST) void radix_kernel(TopkArgs a, int p) {
-  const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+// ------------------------------------------------------------------ compact
+// Long candidate ranges: CT items a workgroup (ST threads, CT / ST rounds).
+// Bits of the items whose coarse bin is above tb go to the `above` bitmap
+// (every word of the pair is written by some workgroup); the items of bin tb
+// go, in index order, to this workgroup's region of ckey / cidx, with their
+// count in ccount.
+__global__ __launch_bounds__(ST) void compact_kernel(TopkArgs a) {
+  const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t pi = pair_index(a, b, g);
-  __shared__ uint64_t s_prefix[1];
-  __shared__ int s_krem[2];
-  __shared__ uint32_t s_scan[256 + 4];
-  __shared__ uint32_t sh[256];
+  constexpr int R = CT / ST;   // rounds
+  __shared__ int s_res[2];
+  __shared__ uint32_t s_wsum[ST / 64];
+  __shared__ uint32_t s_cnt[R * (ST / 64)];
+  __shared__ uint32_t s_off[R * (ST / 64)];
   int lo, hi, k;
   cand_range(a, b, lo, hi, k);
-  if (k <= 0 || a.done[pi]) return;
-  // this workgroup's keys, loaded while the state is derived
-  constexpr int KPT = TPB / ST;
-  const int t0 = blockIdx.x * TPB;
+  if (k <= 0) return;   // (finish writes the -1 padding)
+  coarse_threshold<ST>(a.hist + pi * HW, k, s_res, s_wsum);
+  const uint32_t tb = (uint32_t)s_res[0];
+  const int N = item_count(a.c, a.blocks);
+  const int nwords = (N + 31) / 32;
   const uint64_t* keys = a.keys + pi * a.c.max_tokens;
-  uint64_t kv[KPT];
+  const int base = blockIdx.x * CT;
+  uint64_t kv[R];
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int t = t0 + tid + i * ST;
-    kv[i] = t < a.c.max_tokens ? keys[t] : 0ull;
+  for (int j = 0; j < R; ++j) {
+    const int i = base + j * ST + tid;
+    kv[j] = i < N ? keys[i] : 0ull;
   }
-  sh[tid] = 0u;
-  state_after(a, pi, p, k, s_prefix, s_krem, s_scan);
-  const uint64_t prefix = s_prefix[0];
-  const bool whole = s_krem[1] == s_krem[0];   // every key of the bucket is taken: done
-  if (blockIdx.x == 0 && tid == 0) {   // every workgroup derived the same state
-    a.prefix[pi * PASSES + p - 1] = prefix;
-    a.krem[pi * PASSES + p - 1] = s_krem[0];
-    if (whole) a.done[pi] = 8 * p;
-  }
-  if (whole) return;
-  const int shift = 64 - 8 * p;   // bits above the current byte
+  uint64_t cand[R];
 #pragma unroll
-  for (int i = 0; i < KPT; ++i)
-    if (kv[i] && (kv[i] >> shift) == prefix) atomicAdd(&sh[(kv[i] >> (shift - 8)) & 255u], 1u);
+  for (int j = 0; j < R; ++j) {
+    const uint32_t cb = coarse_of(kv[j]);
+    const uint64_t ab = __ballot(kv[j] != 0 && cb > tb);
+    cand[j] = __ballot(kv[j] != 0 && cb == tb);
+    const int wd = (base + j * ST + wv * 64) / 32;   // the wave's first word
+    uint32_t* aw = a.above + pi * (a.c.max_tokens / 32);
+    if (lane == 0 && wd < nwords) aw[wd] = (uint32_t)ab;
+    if (lane == 32 && wd + 1 < nwords) aw[wd + 1] = (uint32_t)(ab >> 32);
+    if (lane == 0) s_cnt[j * (ST / 64) + wv] = (uint32_t)__popcll(cand[j]);
+  }
   __syncthreads();
-  if (sh[tid]) atomicAdd(&a.hist[pi * HSTRIDE + (p * HREP + blockIdx.x % HREP) * 256 + tid], sh[tid]);
-}
-
-// ------------------------------------------------------------------ mark
-// One thread per key; a wave's ballots are two 32-token words of each bitmap.
-__global__ __launch_bounds__(ST) void mark_kernel(TopkArgs a) {
-  const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, lane = tid & 63;
-  const int64_t pi = pair_index(a, b, g);
-  __shared__ uint64_t s_prefix[1];
-  __shared__ int s_krem[2];
-  __shared__ uint32_t s_scan[256 + 4];
-  int lo, hi, k;
-  cand_range(a, b, lo, hi, k);
-  // keys of this workgroup, loaded while the threshold is derived
-  constexpr int KPT = TPB / ST;
-  const uint64_t* keys = a.keys + pi * a.c.max_tokens;
-  uint64_t kv[KPT];
+  if (tid < 64) {   // exclusive scan over the R * 4 (round, wave) counts, in index order
+    uint32_t x = tid < R * (ST / 64) ? s_cnt[tid] : 0u;
+    const uint32_t own = x;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int t = blockIdx.x * TPB + tid + i * ST;
-    kv[i] = t < a.c.max_tokens ? keys[t] : 0ull;
-  }
-  // selected: key above the k-th largest key T, or equal to it (first ones by
-  // index, in emit); when a pass found its bucket taken whole, every key whose
-  // top `bits` bits reach the stored prefix
-  uint64_t T = ~0ull;     // nothing is above the all-ones key and nothing equals it
-  int bits = 0;
-  uint64_t P = 0;
-  if (k > 0) {
-    bits = a.done[pi];
-    if (bits) {
-      P = a.prefix[pi * PASSES + bits / 8 - 1];   // the prefix of the pass that found it whole
-    } else {
-      state_after(a, pi, PASSES, k, s_prefix, s_krem, s_scan);
-      T = s_prefix[0];
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o);
+      if (lane >= o) x += y;
     }
+    if (tid < R * (ST / 64)) s_off[tid] = x - own;
+    if (tid == R * (ST / 64) - 1) a.ccount[pi * a.nreg + blockIdx.x] = (int32_t)x;
   }
-  const int words = a.c.max_tokens / 32;
+  __syncthreads();
+  const int64_t reg = (pi * a.nreg + blockIdx.x) * (int64_t)CT;
+  const uint64_t below = (1ull << lane) - 1ull;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int t = blockIdx.x * TPB + tid + i * ST;
-    if (t >= a.c.max_tokens) break;   // whole waves (max_tokens and TPB are multiples of 64)
-    const uint64_t key = kv[i];
-    const bool ab_t = bits ? (key >> (64 - bits)) >= P : key > T;
-    const uint64_t ab = __ballot(key != 0 && ab_t && k > 0);
-    const uint64_t eq = __ballot(key != 0 && !bits && key == T && k > 0);
-    const int wd = (t - lane) / 32;   // first of the wave's two words
-    if (lane == 0) {
-      a.above[pi * words + wd] = (uint32_t)ab;
-      a.equal[pi * words + wd] = (uint32_t)eq;
-    } else if (lane == 32) {
-      a.above[pi * words + wd + 1] = (uint32_t)(ab >> 32);
-      a.equal[pi * words + wd + 1] = (uint32_t)(eq >> 32);
+  for (int j = 0; j < R; ++j) {
+    if ((cand[j] >> lane) & 1ull) {
+      const uint32_t pos = s_off[j * (ST / 64) + wv] + (uint32_t)__popcll(cand[j] & below);
+      a.ckey[reg + pos] = kv[j];
+      a.cidx[reg + pos] = base + j * ST + tid;
     }
   }
 }
 
-// ------------------------------------------------------------------ emit
-// Exclusive prefix sum over the ET threads (wave scans, then the wave totals).
-__device__ inline int block_exclusive_scan(int v, int* s, int& total) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) s[wv] = x;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-  for (int k = 0; k < ET / 64; ++k) {
-    const int t = s[k];
-    before += k < wv ? t : 0;
-    total += t;
-  }
-  __syncthreads();
-  return before + x - v;
-}
+// ------------------------------------------------------------------ finish
+// One workgroup (FT threads) per (sequence, KV head).  The k best items are
+// those in coarse bins above tb plus the krem = k - n_gt best of bin tb; the
+// latter are found by an exact radix select among bin tb's keys (8-bit digits
+// from the first bit where those keys differ, LDS histograms; once a digit's
+// bucket is taken whole the rest of it is selected by prefix), lower index
+// first among keys equal to the threshold.  Bin tb's items come from the
+// compaction regions (into LDS, up to CAP of them) or, for short ranges or a
+// bin too large for LDS, straight from the key row (staged in LDS when it has
+// at most DIRECT_MAX items).  Output: the selected items in ascending order,
+// then -1.
+struct FinishLds {
+  uint64_t key[CAP];        // bin-tb keys (region path) or the key row (direct path)
+  int32_t idx[CAP];         // their items (region path)
+  uint32_t bm[EW];          // bitmap chunk (region path)
+  uint8_t sel[CAP];         // selected flags of bin-tb items (region path)
+  int32_t roff[MAXR + 1];   // region offsets (region path)
+  uint32_t bins[256];
+  uint32_t wsum[FT / 64];
+  uint64_t red[2 * (FT / 64)];
+  int res[4];
+  uint64_t pfx;
+};
 
-constexpr int EPR = 8;   // bitmap words a thread loads at once
-__global__ __launch_bounds__(ET) void emit_kernel(TopkArgs a) {
-  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int64_t pi = pair_index(a, b, g);
-  __shared__ int s[ET];
-  int lo, hi, k;
-  cand_range(a, b, lo, hi, k);
-  const int words = a.c.max_tokens / 32;
-  const int per = (words + ET - 1) / ET;
-  const int wa = tid * per, wb = min(wa + per, words);
-  const uint32_t* ab = a.above + pi * words;
-  const uint32_t* eq = a.equal + pi * words;
-  int32_t* out = a.out_idx + pi * a.k_max;
-  // how many equal keys to take: k - #above.  A thread's words are read
-  // EPR at a time with every load issued before any is used; the first EPR
-  // (all of them for caches up to 256K tokens) are read once and kept in
-  // registers for the three passes below.
-  typedef uint32_t Words[EPR];
-  auto load_chunk = [&](int base, Words& x, Words& y) {
-#pragma unroll
-    for (int i = 0; i < EPR; ++i) {
-      x[i] = base + i < wb ? ab[base + i] : 0u;
-      y[i] = base + i < wb ? eq[base + i] : 0u;
-    }
-  };
-  Words ab0, eq0;
-  load_chunk(wa, ab0, eq0);
-  auto for_chunks = [&](auto&& f) {
-    for (int base = wa; base < wb; base += EPR) {
-      if (base == wa) {
-        f(base, ab0, eq0);
-      } else {
-        Words x, y;
-        load_chunk(base, x, y);
-        f(base, x, y);
-      }
-    }
-  };
-  int n_ab = 0, n_eq = 0;
-  for_chunks([&](int, Words& abw, Words& eqw) {
-#pragma unroll
-    for (int i = 0; i < EPR; ++i) {
-      n_ab += __popc(abw[i]);
-      n_eq += __popc(eqw[i]);
-    }
-  });
-  int tot_ab, tot_eq;
-  block_exclusive_scan(n_ab, s, tot_ab);
-  const int eq_before = block_exclusive_scan(n_eq, s, tot_eq);
-  const int take_eq = max(0, k - tot_ab);
-  // selected = above | (first take_eq equal bits by index)
-  int n_sel = 0;
-  int eq_seen = eq_before;
-  for_chunks([&](int, Words& abw, Words& eqw) {
-#pragma unroll
-    for (int i = 0; i < EPR; ++i) {
-      uint32_t e = eqw[i];
-      uint32_t keep = 0u;
-      while (e && eq_seen < take_eq) {
-        const uint32_t bit = e & (0u - e);
-        keep |= bit;
-        e ^= bit;
-        ++eq_seen;
-      }
-      n_sel += __popc(abw[i] | keep);
-    }
-  });
-  int total;
-  int pos = block_exclusive_scan(n_sel, s, total);
-  eq_seen = eq_before;
-  for_chunks([&](int base, Words& abw, Words& eqw) {
-#pragma unroll
-    for (int i = 0; i < EPR; ++i) {
-      uint32_t e = eqw[i];
-      uint32_t keep = 0u;
-      while (e && eq_seen < take_eq) {
-        const uint32_t bit = e & (0u - e);
-        keep |= bit;
-        e ^= bit;
-        ++eq_seen;
-      }
-      uint32_t m = abw[i] | keep;
-      while (m) {
-        const int j = __ffs(m) - 1;
-        m &= m - 1;
-        if (pos < a.k_max) out[pos] = (base + i) * 32 + j;
-        ++pos;
-      }
-    }
-  });
-  for (int e = total + tid; e < a.k_max; e += ET) out[e] = -1;
-}
-
-// ------------------------------------------------------------------ select (one workgroup per pair)
-// After the score kernel, the remaining radix passes, the threshold and the
-// ascending output of one (sequence, KV head) in one 1024-thread workgroup:
-// the pass-0 histogram is summed from its copies into LDS, the candidates'
-// keys are staged in LDS (re-read from L2 each pass if they do not fit), and
-// each pass histograms its byte with LDS atomics.  Same passes and tie rule as
-// radix / mark / emit above, without their launches; used when a pair's
-// candidate range is short.
-constexpr int SELT = 1024;
-constexpr int SEL_LDS_KEYS = 12288;   // 96 KB of keys in LDS
-
-// Byte of the current pass among 256 LDS bins (threads < 256 scan; every
-// thread calls): the bucket holding the krem-th largest key; results through
-// s_prefix / s_krem (bucket size in s_krem[1]).
-__device__ void select_byte_lds(const uint32_t* bins, uint64_t prefix, int krem, uint64_t* s_prefix,
-                                int* s_krem, uint32_t* s_scan) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  uint32_t x = tid < 256 ? bins[255 - tid] : 0u;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
+__device__ inline void select_digit(FinishLds& L, uint64_t prefix, int krem, uint64_t* new_prefix,
+                                    int* new_krem, int* bucket) {
+  // suffix sums over the 256 bins: thread d < 256 holds bin 255 - d
+  const int tid = threadIdx.x;
+  uint32_t x = tid < 256 ? L.bins[255 - tid] : 0u;
+  if (tid == 0) {   // (krem is at most the keys counted, so some thread overwrites these)
+    L.pfx = prefix << 8;
+    L.res[2] = krem;
+    L.res[3] = 0;
   }
-  if (tid < 256 && lane == 63) s_scan[256 + wv] = x;
-  __syncthreads();
+  uint32_t total;
+  const uint32_t incl = block_scan<FT>(x, L.wsum, &total);   // keys in bins >= 255 - tid
   if (tid < 256) {
-    for (int k = 0; k < wv; ++k) x += s_scan[256 + k];
-    s_scan[255 - tid] = x;   // keys in buckets >= d
-  }
-  __syncthreads();
-  if (tid < 256) {
-    const uint32_t ge = s_scan[tid];
-    const uint32_t gt = tid < 255 ? s_scan[tid + 1] : 0u;
+    const uint32_t ge = incl, gt = incl - x;
     if (ge >= (uint32_t)krem && gt < (uint32_t)krem) {
-      s_prefix[0] = (prefix << 8) | (uint64_t)tid;
-      s_krem[0] = krem - (int)gt;
-      s_krem[1] = (int)(ge - gt);
+      L.pfx = (prefix << 8) | (uint64_t)(255 - tid);
+      L.res[2] = krem - (int)gt;
+      L.res[3] = (int)x;
     }
   }
   __syncthreads();
+  *new_prefix = L.pfx;
+  *new_krem = L.res[2];
+  *bucket = L.res[3];
+  __syncthreads();
 }
 
-__global__ __launch_bounds__(SELT) void select_kernel(TopkArgs a) {
+__global__ __launch_bounds__(FT) void finish_kernel(TopkArgs a) {
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t pi = pair_index(a, b, g);
-  __shared__ uint64_t skeys[SEL_LDS_KEYS];
-  __shared__ uint32_t bins[256];
-  __shared__ uint32_t s_scan[256 + 4];
-  __shared__ uint64_t s_prefix[1];
-  __shared__ int s_krem[2];
-  __shared__ int s_tot[SELT / 64];
+  __shared__ FinishLds L;
   int lo, hi, k;
   cand_range(a, b, lo, hi, k);
   int32_t* out = a.out_idx + pi * a.k_max;
-  int written = 0;
-  if (k > 0) {
-    const uint64_t* gkeys = a.keys + pi * a.c.max_tokens;
-    const int nc = hi - lo;
-    const bool in_lds = nc <= SEL_LDS_KEYS;
-    if (in_lds)
-      for (int i = tid; i < nc; i += SELT) skeys[i] = gkeys[lo + i];
-    if (tid < 256) {
-      uint32_t x = 0;
-      const uint32_t* h = a.hist + pi * HSTRIDE;
-#pragma unroll
-      for (int r = 0; r < HREP; ++r) x += h[r * 256 + tid];
-      bins[tid] = x;
-    }
+  if (k <= 0) {
+    for (int e = tid; e < a.k_max; e += FT) out[e] = -1;
+    return;
+  }
+  coarse_threshold<FT>(a.hist + pi * HW, k, L.res, L.wsum);
+  const uint32_t tb = (uint32_t)L.res[0];
+  const int krem0 = k - L.res[1];
+  const int N = item_count(a.c, a.blocks);
+  const uint64_t* gkeys = a.keys + pi * a.c.max_tokens;
+  const uint64_t below = (1ull << lane) - 1ull;
+
+  // ---- where bin tb's items are
+  const bool direct = N <= DIRECT_MAX;
+  int C = 0;            // region path: bin-tb items in LDS
+  bool regions = false;
+  if (direct) {
+    for (int i = tid; i < N; i += FT) L.key[i] = gkeys[i];
     __syncthreads();
-    auto key_at = [&](int i) -> uint64_t { return in_lds ? skeys[i] : gkeys[lo + i]; };
-
-    // ---- passes: pick each byte; stop once a bucket is taken whole
-    uint64_t prefix = 0;
-    int krem = k, bits = 0;
-    for (int p = 0; p < PASSES; ++p) {
-      select_byte_lds(bins, prefix, krem, s_prefix, s_krem, s_scan);
-      prefix = s_prefix[0];
-      krem = s_krem[0];
-      if (s_krem[1] == krem) {
-        bits = 8 * (p + 1);
-        break;
-      }
-      if (p == PASSES - 1) break;
-      if (tid < 256) bins[tid] = 0u;
-      __syncthreads();
-      const int shift = 56 - 8 * p;   // bits above the next byte
-      for (int i = tid; i < nc; i += SELT) {
-        const uint64_t key = key_at(i);
-        if (key && (key >> shift) == prefix) atomicAdd(&bins[(key >> (shift - 8)) & 255u], 1u);
-      }
-      __syncthreads();
+  } else if (a.nreg <= MAXR) {
+    uint32_t run = 0;
+    for (int r0 = 0; r0 < a.nreg; r0 += FT) {
+      const int r = r0 + tid;
+      const uint32_t c = r < a.nreg ? (uint32_t)a.ccount[pi * a.nreg + r] : 0u;
+      uint32_t tot;
+      const uint32_t incl = block_scan<FT>(c, L.wsum, &tot);
+      if (r < a.nreg) L.roff[r] = (int32_t)(run + incl - c);
+      run += tot;
     }
-
-    // ---- selected = above the threshold, plus the first krem keys equal to it
-    // by index (bits > 0: every key whose top `bits` bits reach the prefix)
-    const uint64_t T = prefix;
-    int eq_taken = 0;
-    for (int c0 = 0; c0 < nc; c0 += SELT) {
-      const int i = c0 + tid;
-      const uint64_t key = i < nc ? key_at(i) : 0ull;
-      const bool ab = key != 0 && (bits ? (key >> (64 - bits)) >= T : key > T);
-      const bool eq = key != 0 && !bits && key == T;
-      const uint64_t eb = __ballot(eq);
-      if (lane == 0) s_tot[wv] = __popcll(eb);
-      __syncthreads();
-      int eq_before = eq_taken, eq_chunk = 0;
-      for (int x = 0; x < SELT / 64; ++x) {
-        const int v = s_tot[x];
-        eq_before += x < wv ? v : 0;
-        eq_chunk += v;
+    C = (int)run;
+    if (tid == 0) L.roff[a.nreg] = C;
+    regions = C <= CAP;
+    __syncthreads();
+    if (regions) {
+      for (int e = tid; e < C; e += FT) {   // region of entry e: last r with roff[r] <= e
+        int rl = 0, rh = a.nreg - 1;
+        while (rl < rh) {
+          const int m = (rl + rh + 1) >> 1;
+          if (L.roff[m] <= e) rl = m; else rh = m - 1;
+        }
+        const int64_t src = (pi * a.nreg + rl) * (int64_t)CT + (e - L.roff[rl]);
+        L.key[e] = a.ckey[src];
+        L.idx[e] = a.cidx[src];
       }
-      eq_before += __popcll(eb & ((1ull << lane) - 1ull));
-      const bool take = ab || (eq && eq_before < krem);
-      __syncthreads();
-      const uint64_t tb = __ballot(take);
-      if (lane == 0) s_tot[wv] = __popcll(tb);
-      __syncthreads();
-      int pos = written, chunk = 0;
-      for (int x = 0; x < SELT / 64; ++x) {
-        const int v = s_tot[x];
-        pos += x < wv ? v : 0;
-        chunk += v;
-      }
-      pos += __popcll(tb & ((1ull << lane) - 1ull));
-      if (take && pos < a.k_max) out[pos] = lo + i;
-      written += chunk;
-      eq_taken += eq_chunk;
       __syncthreads();
     }
   }
-  for (int e = written + tid; e < a.k_max; e += SELT) out[e] = -1;
+  // bin-tb keys, in index order: f(key, position) for each
+  auto key_row = [&](int i) -> uint64_t { return direct ? L.key[i] : gkeys[i]; };
+  auto for_cand = [&](auto&& f) {
+    if (regions) {
+      for (int e = tid; e < C; e += FT) f(L.key[e]);
+    } else {
+      for (int i = tid; i < N; i += FT) {
+        const uint64_t key = key_row(i);
+        if (key && coarse_of(key) == tb) f(key);
+      }
+    }
+  };
+
+  // ---- common prefix of bin tb's keys: the digits before the first
+  // differing bit need no pass
+  uint64_t kand = ~0ull, kor = 0ull;
+  for_cand([&](uint64_t key) {
+    kand &= key;
+    kor |= key;
+  });
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kand &= __shfl_xor(kand, o);
+    kor |= __shfl_xor(kor, o);
+  }
+  if (lane == 0) {
+    L.red[wv] = kand;
+    L.red[FT / 64 + wv] = kor;
+  }
+  __syncthreads();
+  kand = ~0ull;
+  kor = 0ull;
+#pragma unroll
+  for (int w2 = 0; w2 < FT / 64; ++w2) {
+    kand &= L.red[w2];
+    kor |= L.red[FT / 64 + w2];
+  }
+  const uint64_t diff = kand ^ kor;   // bits where bin tb's keys differ
+  const int first = diff ? __clzll(diff) / 8 : 8;   // first digit with a difference
+
+  // ---- radix passes
+  uint64_t P = first > 0 ? (kand >> (64 - 8 * first)) : 0ull;   // the chosen top 8p bits
+  int krem = krem0, bits = 0;   // bits > 0: the bucket of those top bits is taken whole
+  for (int p = first; p < 8; ++p) {
+    if (tid < 256) L.bins[tid] = 0u;
+    __syncthreads();
+    const int sh = 56 - 8 * p;
+    for_cand([&](uint64_t key) {
+      if (p == 0 || (key >> (sh + 8)) == P) atomicAdd(&L.bins[(key >> sh) & 255u], 1u);
+    });
+    __syncthreads();
+    int bucket;
+    select_digit(L, P, krem, &P, &krem, &bucket);
+    if (bucket == krem) {
+      bits = 8 * (p + 1);
+      break;
+    }
+  }
+  // selected among bin tb: top `bits` bits >= P (a bucket taken whole), or,
+  // after all digits, key > T = P, or key == T for the first krem by index
+  const uint64_t T = P;
+  auto chosen = [&](uint64_t key, bool eq_ok) {
+    return bits ? (key >> (64 - bits)) >= P : (key > T || (key == T && eq_ok));
+  };
+
+  int written = 0;
+  if (regions) {
+    // ranks of the keys equal to T: thread t owns entries [t per, (t + 1) per)
+    const int per = (C + FT - 1) / FT;
+    const int e0 = min(tid * per, C), e1 = min(e0 + per, C);
+    uint32_t neq = 0;
+    for (int e = e0; e < e1; ++e) neq += (!bits && L.key[e] == T) ? 1u : 0u;
+    uint32_t tot;
+    uint32_t rank = block_scan<FT>(neq, L.wsum, &tot) - neq;
+    for (int e = e0; e < e1; ++e) {
+      const bool eq = !bits && L.key[e] == T;
+      L.sel[e] = chosen(L.key[e], eq && rank < (uint32_t)krem) ? 1 : 0;
+      rank += eq ? 1u : 0u;
+    }
+    __syncthreads();
+    // emission: the above bitmap chunk by chunk with the chosen bin-tb items
+    // OR'ed in, then each thread's EW / FT words in order
+    const int nwords = (N + 31) / 32;
+    const uint32_t* aw = a.above + pi * (a.c.max_tokens / 32);
+    constexpr int WPT = EW / FT;
+    for (int w0 = 0; w0 < nwords; w0 += EW) {
+      const int nw = min(EW, nwords - w0);
+      for (int x = tid; x < EW; x += FT) L.bm[x] = x < nw ? aw[w0 + x] : 0u;
+      __syncthreads();
+      for (int e = tid; e < C; e += FT) {
+        const int it = L.idx[e];
+        if (L.sel[e] && it >= 32 * w0 && it < 32 * (w0 + nw))
+          atomicOr(&L.bm[(it >> 5) - w0], 1u << (it & 31));
+      }
+      __syncthreads();
+      uint32_t wds[WPT];
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int x = 0; x < WPT; ++x) {
+        wds[x] = L.bm[tid * WPT + x];
+        cnt += (uint32_t)__popc(wds[x]);
+      }
+      uint32_t tot2;
+      int pos = written + (int)(block_scan<FT>(cnt, L.wsum, &tot2) - cnt);
+#pragma unroll
+      for (int x = 0; x < WPT; ++x) {
+        uint32_t m = wds[x];
+        while (m) {
+          const int j = __ffs(m) - 1;
+          m &= m - 1u;
+          if (pos < a.k_max) out[pos] = 32 * (w0 + tid * WPT + x) + j;
+          ++pos;
+        }
+      }
+      written += (int)tot2;
+      __syncthreads();
+    }
+  } else {
+    // emission straight from the key row, FT items a round in index order
+    uint32_t eq_taken = 0;
+    for (int c0 = 0; c0 < N; c0 += FT) {
+      const int i = c0 + tid;
+      const uint64_t key = i < N ? key_row(i) : 0ull;
+      const uint32_t cb = coarse_of(key);
+      const bool above = key != 0 && cb > tb;
+      const bool inb = key != 0 && cb == tb;
+      const bool eq = inb && !bits && key == T;
+      uint32_t eq_tot;
+      const uint32_t eq_incl = block_scan<FT>(eq ? 1u : 0u, L.wsum, &eq_tot);
+      const bool take = above || (inb && chosen(key, eq_taken + eq_incl - 1u < (uint32_t)krem));
+      uint32_t take_tot;
+      const uint32_t take_incl = block_scan<FT>(take ? 1u : 0u, L.wsum, &take_tot);
+      const int pos = written + (int)take_incl - 1;
+      if (take && pos < a.k_max) out[pos] = i;
+      written += (int)take_tot;
+      eq_taken += eq_tot;
+    }
+  }
+  for (int e = written + tid; e < a.k_max; e += FT) out[e] = -1;
 }
 
 }  // namespace
@@ -748,12 +782,14 @@ __global__ __launch_bounds__(SELT) void select_kernel(TopkArgs a) {
 size_t topk_workspace_bytes(const kvc_cache& c) {
   const size_t pairs = (size_t)c.batch * c.num_kv_heads;
   const size_t words = c.max_tokens / 32;
+  const size_t nreg = (c.max_tokens + CT - 1) / CT;   // (token items: the most regions)
   size_t bytes = 2 * pairs * c.max_tokens * sizeof(uint64_t);   // keys, block-mode token scores
   bytes += pairs * GMAX * D * sizeof(double);                    // critical-mode q operands
-  bytes += pairs * HSTRIDE * sizeof(uint32_t);
-  bytes += 2 * pairs * words * sizeof(uint32_t);
-  bytes += pairs * D * sizeof(int32_t);
-  bytes += pairs * PASSES * (sizeof(uint64_t) + sizeof(int32_t)) + pairs * sizeof(int32_t);
+  bytes += pairs * HW * sizeof(uint32_t);                        // coarse histogram
+  bytes += pairs * words * sizeof(uint32_t);                     // above bitmap
+  bytes += pairs * nreg * CT * (sizeof(uint64_t) + sizeof(int32_t));   // bin-tb regions
+  bytes += pairs * nreg * sizeof(int32_t);                       // region counts
+  bytes += pairs * D * sizeof(int32_t);                          // channel lists
   return bytes;
 }
 
@@ -780,6 +816,9 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   a.out_channels = out_channels;
   const size_t pairs = (size_t)c.batch * c.num_kv_heads;
   const size_t words = c.max_tokens / 32;
+  const int items = item_count(c, a.blocks);
+  const size_t nreg_ws = (c.max_tokens + CT - 1) / CT;
+  a.nreg = (items + CT - 1) / CT;
   char* p = static_cast<char*>(ws);
   a.keys = reinterpret_cast<uint64_t*>(p);
   p += pairs * c.max_tokens * sizeof(uint64_t);
@@ -788,35 +827,29 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   a.qsel = reinterpret_cast<double*>(p);
   p += pairs * GMAX * D * sizeof(double);
   a.hist = reinterpret_cast<uint32_t*>(p);
-  p += pairs * HSTRIDE * sizeof(uint32_t);
+  p += pairs * HW * sizeof(uint32_t);
   a.above = reinterpret_cast<uint32_t*>(p);
   p += pairs * words * sizeof(uint32_t);
-  a.equal = reinterpret_cast<uint32_t*>(p);
-  p += pairs * words * sizeof(uint32_t);
+  a.ckey = reinterpret_cast<uint64_t*>(p);
+  p += pairs * nreg_ws * CT * sizeof(uint64_t);
+  a.cidx = reinterpret_cast<int32_t*>(p);
+  p += pairs * nreg_ws * CT * sizeof(int32_t);
+  a.ccount = reinterpret_cast<int32_t*>(p);
+  p += pairs * nreg_ws * sizeof(int32_t);
   a.channels = reinterpret_cast<int32_t*>(p);
-  p += pairs * D * sizeof(int32_t);
-  a.prefix = reinterpret_cast<uint64_t*>(p);
-  p += pairs * PASSES * sizeof(uint64_t);
-  a.krem = reinterpret_cast<int32_t*>(p);
-  p += pairs * PASSES * sizeof(int32_t);
-  a.done = reinterpret_cast<int32_t*>(p);
 
   const int Hkv = c.num_kv_heads, B = c.batch;
-  // candidate ranges whose keys fit in LDS: one selection workgroup per pair
-  // after scoring, instead of seven radix launches, mark and emit (measured:
-  // longer ranges re-read from L2 by one workgroup lose to the radix kernels)
-  const bool one_wg = (a.blocks ? c.max_tokens / GS : c.max_tokens) <= SEL_LDS_KEYS;
-  a.hist_words = one_wg ? HREP * 256 : HSTRIDE;
   prep_kernel<<<dim3(Hkv, B), D, 0, s>>>(a);
-  const dim3 sgrid((c.max_tokens + ST - 1) / ST, Hkv, B);
   const bool exact = mode == KVC_SCORE_EXACT;
+  const int snt = exact || (a.G != 1 && a.G != 2 && a.G != 4) ? ST : SCT;
+  const dim3 sgrid((c.max_tokens + snt - 1) / snt, Hkv, B);
   // the scorer's q operands in LDS: G heads x the channels it sums over
   const int nch = mode == KVC_SCORE_CRITICAL ? n_crit : (exact ? D : 0);
   const size_t sq_bytes = (size_t)std::max(1, a.G * nch) * sizeof(double);
 #define KVC_SCORE_E(F, KT, GG)                                                \
   do {                                                                        \
-    if (exact) score_kernel<F, KT, GG, true><<<sgrid, ST, sq_bytes, s>>>(a);  \
-    else score_kernel<F, KT, GG, false><<<sgrid, ST, sq_bytes, s>>>(a);       \
+    if (exact) score_kernel<F, KT, GG, true><<<sgrid, snt, sq_bytes, s>>>(a); \
+    else score_kernel<F, KT, GG, false><<<sgrid, snt, sq_bytes, s>>>(a);      \
   } while (0)
 #define KVC_SCORE_G(F, KT)                                                    \
   do {                                                                        \
@@ -837,14 +870,8 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
 #undef KVC_SCORE_E
   if (a.blocks)
     block_key_kernel<<<dim3((c.max_tokens / GS + BPW - 1) / BPW, Hkv, B), ST, 0, s>>>(a);
-  if (one_wg) {
-    select_kernel<<<dim3(Hkv, B), SELT, 0, s>>>(a);
-    return hipGetLastError();
-  }
-  const dim3 rgrid((c.max_tokens + TPB - 1) / TPB, Hkv, B);
-  for (int pass = 1; pass < PASSES; ++pass) radix_kernel<<<rgrid, ST, 0, s>>>(a, pass);
-  mark_kernel<<<rgrid, ST, 0, s>>>(a);
-  emit_kernel<<<dim3(Hkv, B), ET, 0, s>>>(a);
+  if (items > DIRECT_MAX) compact_kernel<<<dim3(a.nreg, Hkv, B), ST, 0, s>>>(a);
+  finish_kernel<<<dim3(Hkv, B), FT, 0, s>>>(a);
   return hipGetLastError();
 }
 
