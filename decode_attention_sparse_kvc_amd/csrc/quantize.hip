@@ -32,6 +32,9 @@ struct GroupQuant {
     constexpr float levels = float((1 << BITS) - 1);
     const float s32 = __fadd_rn(__fdiv_rn(__fsub_rn(mx, mn), levels), 0.0f);
     s16 = f2h(s32);
+    // a range past the largest finite fp16 scale (1 bit, max - min > 65504)
+    // stores 65504 instead of infinity
+    if (s16 == 0x7C00u) s16 = 0x7BFFu;
     z16 = f2h(__fadd_rn(mn, 0.0f));
     s = h2f(s16);
     z = h2f(z16);

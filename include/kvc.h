@@ -84,7 +84,9 @@ enum { KVC_OP_SCORE_TOPK = 1, KVC_OP_ATTEND = 2 };
  * Quantized store (format INT4 or INT1; [TKV] 2.2, [DEV] 3.1).  K is quantized
  * per channel over each complete 64-token group, V per token over each
  * 64-channel half, both asymmetric min-max with fp16 scale s and zero z:
- *     s = fp16((max - min) / (2^b - 1) + 0)   (fp32 subtract and divide)
+ *     s = fp16((max - min) / (2^b - 1) + 0)   (fp32 subtract and divide; a
+ *         result past the largest finite fp16 stores 65504: only a 1-bit group
+ *         with max - min > 65504 reaches it)
  *     z = fp16(min + 0)
  *     code = s == 0 ? 0 : clamp(rint((x - z) / s), 0, 2^b - 1)   (fp32, half-even)
  * and dequantized as code * s + z.  A group is quantized when its 64th token

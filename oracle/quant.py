@@ -24,6 +24,11 @@ Readings taken where the pages are silent or garbled:
     zero point); the on-device article's "symmetric V" is not built.
   * A group is quantized only once all 64 of its tokens exist; until then its
     tokens stay fp16 (a "tail").  V follows K's group boundary.
+  * The fp16 scale saturates: a range whose fp32 scale rounds past the largest
+    finite fp16 (only possible at 1 bit, a range above 65504) stores 65504
+    rather than infinity, so the codes stay 0/1 and every dequantized value is
+    finite (the pages never meet such ranges; an infinite scale would turn the
+    zero codes' products into NaN).
 """
 from __future__ import annotations
 
@@ -46,9 +51,10 @@ def quantize_groups(x16: np.ndarray, bits: int):
     mn = x.min(axis=-1)
     mx = x.max(axis=-1)
     s32 = (mx - mn) / levels + F32(0.0)           # fp32, round to nearest even; +0 not -0
-    s16 = s32.astype(np.float16)
+    with np.errstate(over="ignore"):
+        s16 = s32.astype(np.float16)
+    s16 = np.where(np.isinf(s16), np.float16(65504.0), s16)   # saturate (s32 >= 0)
     z16 = (mn + F32(0.0)).astype(np.float16)      # exact: mn is an fp16 value
-    assert np.all(np.isfinite(s16)), "group range overflows the fp16 scale"
     s = s16.astype(F32)[..., None]
     z = z16.astype(F32)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):

@@ -124,3 +124,26 @@ def test_full_size_prefill(make):
     cache.append(dev(w.k), dev(w.v))
     torch.cuda.synchronize()
     check_cache_state(cache, w.k, w.v, w.seq_lens)
+
+
+def test_one_bit_scale_saturates():
+    """1-bit groups whose range exceeds 65504 (K per channel and V per token) store the
+    saturated scale 65504 as the oracle does, and attention over them stays finite."""
+    from decode_attention_sparse_kvc_amd import kvc
+    rng = np.random.default_rng(30)
+    k, v = _rows(rng, 1, 128, 1, outliers=False)
+    k[0, :64, 0, 9] = np.linspace(-40000, 40000, 64).astype(np.float16)   # one K channel group
+    v[0, 70, 0, :64] = np.linspace(-33000, 33000, 64).astype(np.float16)  # one V token group
+    cache = KvcCache("int1", 1, 1, 192)
+    cache.append(dev(k), dev(v))
+    torch.cuda.synchronize()
+    check_cache_state(cache, k, v, [128])
+    assert host(cache.k_meta)[0, 0, 0, 0, 9] == np.float16(65504.0)
+    q = dev(rng.standard_normal((1, 1, 128)).astype(np.float16) * np.float16(1e-5))
+    out = torch.empty(1, 1, 128, device="cuda")
+    lse = torch.empty(1, 1, device="cuda")
+    nb = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, cache.desc, 1)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    kvc.kvc_attend_decode(cache.desc, q, 1, 128 ** -0.5, 0, None, 0, 0, 0, out, lse, None, 0, ws, nb)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(host(out))) and np.all(np.isfinite(host(lse)))

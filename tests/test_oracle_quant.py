@@ -169,3 +169,19 @@ def test_signed_zero_groups_store_positive_zeros():
         code, s, z = Q.quantize_groups(x[None], bits)
         assert s[0] == 0 and not np.signbit(s[0]) and not np.signbit(z[0])
         assert np.all(code == 0)
+
+
+def test_one_bit_scale_saturates_at_the_largest_fp16():
+    """A 1-bit group whose range exceeds 65504 stores scale 65504 (not infinity): the
+    codes stay a midpoint threshold against it and every dequantized value is finite.
+    Hand values: z = -40000; (x - z) / 65504 is 0, 1.22, exactly 0.5 (-> 0, half to
+    even), 0.50049 and 0.61 for x = -40000, 40000, -7248, -7216, 0."""
+    x = _group([-40000.0, 40000.0, -7248.0, -7216.0, 0.0], 0.0)
+    code, s, z = Q.quantize_groups(x[None], 1)
+    assert s[0] == np.float16(65504.0) and np.isfinite(s[0])
+    assert float(z[0]) == -40000.0
+    assert code[0, :5].tolist() == [0, 1, 0, 1, 1]
+    assert np.all(np.isfinite(Q.dequantize(code, s[:, None], z[:, None])))
+    # INT4 cannot reach it: the widest fp16 range over 15 levels is below 65504
+    code4, s4, _ = Q.quantize_groups(_group([-65504.0, 65504.0], 0.0)[None], 4)
+    assert float(s4[0]) == float(np.float16(np.float32(131008.0) / np.float32(15.0)))
