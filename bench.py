@@ -10,6 +10,12 @@ with the cache already resident in HBM:
 heads, all sequences).  Cache replicas are rotated so that the working set
 exceeds the 256 MB Infinity Cache and bytes come from HBM.
 
+The default run (the INT4 layer at 128K) also times, in the same process,
+the second gated call -- the 1-bit 128K layer's kvc_attend_decode -- under
+``roofline.gates``, a plain streaming read of the replica buffer
+(kvc_stream_read) under ``roofline.ceiling``, and the CPU oracle's attention
+leg on the host's cores under ``cpu_baseline``.
+
 Prints one JSON line.  ``--gpus N`` with N > 1 is refused: the benchmark runs on
 one GPU.
 """
@@ -39,6 +45,10 @@ def parse():
     ap.add_argument("--replica-bytes", type=float, default=1.5 * 2**30,
                     help="total bytes of rotated cache replicas (defeats the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gates", action="store_true",
+                    help="default workload: skip the second gated call (1-bit 128K attend)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling measurement")
     ap.add_argument("--workgroups", type=int, default=0,
                     help="workgroups the attend call is planned for (0: the library default)")
     ap.add_argument("--no-graph", action="store_true",
@@ -134,31 +144,183 @@ def read_traffic(kernel: str, workload: str, digest: str):
         return None
 
 
-def cpu_baseline(w, seconds: float):
-    """The oracle's decode step on a bounded sample: whole KV heads, timed on host cores."""
+def cpu_baseline(w, seconds: float, runs: int = 3):
+    """The oracle's attention leg on host cores: for each (sequence, KV head)
+    pair, dequantize its cached tokens (oracle.step.token_rows) and attend its
+    query group over them (oracle.attend.attend_group) -- the work one
+    kvc_attend_decode call does.  The pair caches are built before timing (the
+    GPU step does not re-quantize the context either).  Timed on one thread
+    over a bounded subset of pairs, and on every core of the affinity mask
+    (one pair per thread, BLAS single-threaded) over all pairs; median of
+    `runs` runs each, scaled to context tokens per second of the layer."""
+    import concurrent.futures as cf
     from threadpoolctl import threadpool_limits
+    from oracle import attend as A
+    from oracle import select as S
     from oracle import step as ST
-    pairs_all = [(b, g) for b in range(w.batch) for g in range(w.hkv)]
+    cores = len(os.sched_getaffinity(0))
+    pairs = [(b, g) for b in range(w.batch) for g in range(w.hkv)]
+    G = w.group
+    if w.mode not in ("dense",):
+        raise ValueError("cpu_baseline times dense layers")
+    ctx = sum(int(w.seq_lens[b]) for b in range(w.batch))
+
+    def build(p):
+        b, g = p
+        n = int(w.seq_lens[b])
+        oc = None if getattr(w, "outlier_ch", None) is None else w.outlier_ch[g]
+        return ST.build_head_cache(w.k[b, :n, g], w.v[b, :n, g], w.fmt, oc,
+                                   getattr(w, "outlier_v", True))
+
+    def leg(i):
+        b, g = pairs[i]
+        keys, vals = ST.token_rows(hcs[i])
+        toks = S.attended_tokens("dense", hcs[i].n, 0, 0, None)
+        A.attend_group(w.q[b, g * G:(g + 1) * G], keys[toks], vals[toks], w.sm_scale)
+
     with threadpool_limits(limits=1):
+        workers = max(1, min(cores, len(pairs)))
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            hcs = list(ex.map(build, pairs))
+        # one thread: as many pairs as fit about `seconds` / runs (at least one)
         t0 = time.perf_counter()
-        done = []
-        for p in pairs_all:
-            ST.decode_step(w, append=True, pairs=[p])
-            done.append(p)
-            if time.perf_counter() - t0 > seconds:
-                break
-        dt = time.perf_counter() - t0
-    frac = len(done) / len(pairs_all)
-    ctx = sum(int(w.seq_lens[b]) + 1 for b in range(w.batch))
+        leg(0)
+        one = time.perf_counter() - t0
+        m = max(1, min(len(pairs), int(seconds / max(runs, 1) / max(one, 1e-3))))
+        single = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            for i in range(m):
+                leg(i)
+            single.append(time.perf_counter() - t0)
+        # every core: all pairs, one per thread
+        multi = []
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                list(ex.map(leg, range(len(pairs))))
+                multi.append(time.perf_counter() - t0)
+    t1 = sorted(single)[len(single) // 2]
+    tm = sorted(multi)[len(multi) // 2]
+    v1 = ctx * (m / len(pairs)) / t1
+    vm = ctx / tm
     return {
-        "value": ctx * frac / dt,
+        "value": vm,
         "unit": "context-tokens/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{len(done)} of {len(pairs_all)} (sequence, KV head) pairs, each a full "
-                  f"decode step (append + quantize + attend over the whole context) in numpy "
-                  f"on 1 thread, {dt:.1f} s; scaled by the fraction of pairs",
+        "value_1thread": v1,
+        "cores_available": cores,
+        "sample": f"attention leg of kvc_attend_decode (dequantize the cached codes, fp64 softmax "
+                  f"attention of the query group) per (sequence, KV head) pair, caches prebuilt; "
+                  f"all {len(pairs)} pairs on {workers} threads (one pair a thread, "
+                  f"{cores} cores in the affinity mask) and {m} pair(s) on 1 thread scaled by "
+                  f"{m}/{len(pairs)}; median of {runs} runs ({tm:.2f} s and {t1:.2f} s)",
     }
+
+
+def make_caches(w, args, extra: int):
+    """The workload's cache, prefilled on the GPU, and copies of it: enough
+    replicas that rotating over them exceeds args.replica_bytes (defeats the
+    256 MB Infinity Cache).  Capacity leaves room for `extra` appended tokens."""
+    import numpy as np
+    import torch
+    from decode_attention_sparse_kvc_amd import KvcCache
+    dev = torch.device("cuda")
+    cap = ((int(w.seq_lens.max()) + extra + 63) // 64) * 64
+    table, num_pages = None, 0
+    if w.page_size:   # shuffled pages covering the grown capacity of every sequence
+        per = cap // w.page_size
+        num_pages = w.batch * per
+        perm = np.random.default_rng(w.seed).permutation(num_pages).astype(np.int32)
+        table = torch.from_numpy(perm.reshape(w.batch, per))
+    oc = torch.from_numpy(w.outlier_ch) if w.outlier_ch is not None else None
+    base = KvcCache(w.fmt, w.batch, w.hkv, cap, page_size=w.page_size, block_table=table,
+                    num_pages=num_pages, fp16_rows=w.fp16_shadow, kT=w.kT, outlier_ch=oc,
+                    outlier_v=w.outlier_v)
+    base.append(torch.from_numpy(w.k).to(dev), torch.from_numpy(w.v).to(dev),
+                torch.from_numpy(w.seq_lens).to(dev))
+    torch.cuda.synchronize()
+    nrep = max(1, math.ceil(args.replica_bytes / base.nbytes()))
+    reps = [base] + [base.clone() for _ in range(nrep - 1)]
+    return base, reps, cap
+
+
+def replay_us(fns, calls: int) -> float:
+    """Average duration of one call when `fns` (callables taking a stream, one
+    call each) are captured in one HIP graph and replayed until at least
+    `calls` calls have run, bracketed by events on the launch stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = torch.cuda.current_stream()
+        for f in fns:
+            f(st)
+    torch.cuda.synchronize()
+    g.replay()   # (warm)
+    torch.cuda.synchronize()
+    reps = -(-calls // len(fns))
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * len(fns)) * 1e3
+
+
+def attend_gate(name: str, args, calls: int) -> dict:
+    """The kvc_attend_decode call alone on a dense workload (graph replay over
+    rotated cache replicas): its duration and algorithmic HBM rate."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from decode_attention_sparse_kvc_amd import kvc
+    w = W.FULL[name]()
+    base, reps, cap = make_caches(w, args, 64)
+    dev = torch.device("cuda")
+    q = torch.from_numpy(w.q).to(dev)
+    out = torch.empty(w.batch, w.hq, 128, device=dev)
+    lse = torch.empty(w.batch, w.hq, device=dev)
+    nbytes = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, base.desc, w.hq, 0, 0, 0, 0, args.workgroups)
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    per = len(reps) * -(-GRAPH_CALLS // len(reps))
+    fns = [lambda st, r=i % len(reps): kvc.kvc_attend_decode(
+        reps[r].desc, q, w.hq, w.sm_scale, 0, None, 0, 0, 0, out, lse, None, 0, ws, nbytes, st,
+        workgroups=args.workgroups) for i in range(per)]
+    us = replay_us(fns, calls)
+    nb = attend_bytes(w, np.array(w.seq_lens, np.int64), None)
+    achieved = nb / (us * 1e-6) / 1e9
+    del reps, base
+    torch.cuda.empty_cache()
+    return {"workload": name, "launch_us": us, "achieved": achieved, "peak": PEAK_HBM_GBS,
+            "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": nb,
+            "context_tokens_per_s": float(np.sum(w.seq_lens)) / (us * 1e-6)}
+
+
+def stream_ceiling(call_bytes: int, total_bytes: float, calls: int) -> dict:
+    """Plain streaming read (kvc_stream_read) over a buffer of total_bytes:
+    once per call over the whole buffer, and in call_bytes pieces rotating
+    over it (the size of one attend call's reads, launch and ramp included)."""
+    import torch
+    from decode_attention_sparse_kvc_amd import kvc
+    chunk = (int(call_bytes) + 4095) // 4096 * 4096
+    nchunk = max(2, math.ceil(total_bytes / chunk))
+    buf = torch.ones(nchunk * chunk, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4 * 1024, dtype=torch.int32, device="cuda")
+    wg = 1024
+    whole = replay_us([lambda st: kvc.kvc_stream_read(buf, buf.numel(), sink, wg, st)] * 4, 8)
+    pieces = replay_us([lambda st, i=i: kvc.kvc_stream_read(buf[(i % nchunk) * chunk:], chunk, sink, wg, st)
+                        for i in range(nchunk)], calls)
+    res = {"kernel": "kvc_stream_read", "unit": "GB/s",
+           "read_GBs_whole": buf.numel() / (whole * 1e-6) / 1e9, "whole_bytes": buf.numel(),
+           "read_GBs_call_size": chunk / (pieces * 1e-6) / 1e9, "call_bytes": chunk,
+           "call_size_us": pieces}
+    del buf
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -182,22 +344,8 @@ def main():
     w = W.FULL[args.workload]()
     dev = torch.device("cuda")
     extra = args.warmup + 2 * args.steps + 2 * GRAPH_CALLS + 64   # room for the tokens the steps append
-    cap = ((int(w.seq_lens.max()) + extra + 63) // 64) * 64
-    table, num_pages = None, 0
-    if w.page_size:   # shuffled pages covering the grown capacity of every sequence
-        per = cap // w.page_size
-        num_pages = w.batch * per
-        perm = np.random.default_rng(w.seed).permutation(num_pages).astype(np.int32)
-        table = torch.from_numpy(perm.reshape(w.batch, per))
-    oc = torch.from_numpy(w.outlier_ch) if w.outlier_ch is not None else None
-    base = KvcCache(w.fmt, w.batch, w.hkv, cap, page_size=w.page_size, block_table=table,
-                    num_pages=num_pages, fp16_rows=w.fp16_shadow, kT=w.kT, outlier_ch=oc,
-                    outlier_v=w.outlier_v)
-    base.append(torch.from_numpy(w.k).to(dev), torch.from_numpy(w.v).to(dev),
-                torch.from_numpy(w.seq_lens).to(dev))
-    torch.cuda.synchronize()
-    nrep = max(1, math.ceil(args.replica_bytes / base.nbytes()))
-    reps = [base] + [base.clone() for _ in range(nrep - 1)]
+    base, reps, cap = make_caches(w, args, extra)
+    nrep = len(reps)
     lens = [np.array(w.seq_lens, np.int64) for _ in reps]
 
     q = torch.from_numpy(w.q).to(dev)
@@ -389,8 +537,24 @@ def main():
             "src_digest": digest,
         },
     }
+    calls = max(args.steps, 2 * GRAPH_CALLS)
+    if not args.no_ceiling:
+        ceil = stream_ceiling(attend_calls_bytes, args.replica_bytes, calls)
+        result["roofline"]["ceiling"] = ceil
+        result["roofline"]["frac_of_ceiling"] = achieved / ceil["read_GBs_whole"]
+    if args.workload == DEFAULT_WORKLOAD and not args.no_gates:
+        # both gated calls of the layer at 128K: this INT4 layer's (above) and
+        # the 1-bit layer's, measured the same way in the same run
+        result["roofline"]["gates"] = {
+            "int4_128k": {"workload": args.workload, "launch_us": attend_us, "achieved": achieved,
+                          "frac": achieved / PEAK_HBM_GBS},
+            "int1_128k": attend_gate("llama8b_layer_int1_dense_128k", args, calls),
+        }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seconds)
+        if w.mode == "dense":
+            result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seconds)
+        else:
+            result["cpu_baseline"] = None
     print(json.dumps(result))
 
 

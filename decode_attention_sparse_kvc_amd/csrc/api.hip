@@ -219,6 +219,14 @@ kvc_status kvc_topk_mass(const kvc_cache* cache, int32_t num_q_heads, const floa
   return hip_status(launch_topk_mass(*cache, num_q_heads, logits, logits_stride, lse, k, out, stream));
 }
 
+kvc_status kvc_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                           hipStream_t stream) {
+  if (!src || !sink || !aligned(src, 4096) || !aligned(sink, 4) || bytes % 4096) return KVC_ERR_INVALID;
+  if (workgroups < 1 || workgroups > KVC_MAX_WORKGROUPS) return KVC_ERR_INVALID;
+  if (bytes == 0) return KVC_OK;
+  return hip_status(launch_stream_read(src, bytes, sink, workgroups, stream));
+}
+
 size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t mode,
                            int32_t k_max, int32_t n_sink, int32_t n_window, int32_t workgroups) {
   if (check_cache(cache) != KVC_OK) return 0;

@@ -1351,11 +1351,15 @@ __global__ __launch_bounds__(256) void plan_kernel(AttendArgs a) {
 }
 
 // ---------------------------------------------------------------- split merge
-// Log-sum-exp merge of the split partials, one workgroup per (sequence, query
-// head).  Thread (quad cq, replica r) folds splits r, r + 8, ... into a running
-// (max, sum, o[4 cq .. 4 cq + 3]) with online rescaling, so its loads do not
-// wait on one another; the 8 replicas are then combined through LDS.
+// Log-sum-exp merge of the split partials (meeting-LLM article, section 8.1:
+// the online-softmax rescale, applied across splits), one workgroup per
+// (sequence, query head).  Thread (quad cq, replica r) folds splits r, r + 8,
+// ... into a running (max, sum, o[4 cq .. 4 cq + 3]) with online rescaling,
+// MB splits a round with every load of the round issued before the first is
+// used; the 8 replicas are then combined through LDS.
 constexpr int MT = 256;
+constexpr int MR = MT / 32;   // replicas per query head
+constexpr int MB = 8;         // splits a replica loads per round
 __global__ __launch_bounds__(MT) void merge_kernel(const float* __restrict__ part, int s_total,
                                                    float* __restrict__ out, float* __restrict__ lse,
                                                    int pairs, int G) {
@@ -1367,17 +1371,28 @@ __global__ __launch_bounds__(MT) void merge_kernel(const float* __restrict__ par
   const float* pp = part + (int64_t)bh * s_total * PART;
   float mr = -INFINITY, lr = 0.f;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int sp = r; sp < s_total; sp += MT / 32) {
-    const float m = pp[(int64_t)sp * PART];
-    const float l = pp[(int64_t)sp * PART + 1];
-    const f4 o = *reinterpret_cast<const f4*>(pp + (int64_t)sp * PART + PO + 4 * cq);
-    const float mn = fmaxf(mr, m);
-    const float sc = mr == -INFINITY ? 0.f : exp2f(mr - mn);
-    const float wt = m == -INFINITY ? 0.f : exp2f(m - mn);
-    acc = acc * sc + o * wt;
-    lr = fmaf(lr, sc, l * wt);
-    mr = mn;
+  for (int s0 = r; s0 < s_total; s0 += MR * MB) {
+    float2 ml[MB];
+    f4 ov[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const int64_t sp = min(s0 + i * MR, s_total - 1);
+      ml[i] = *reinterpret_cast<const float2*>(pp + sp * PART);
+      ov[i] = *reinterpret_cast<const f4*>(pp + sp * PART + PO + 4 * cq);
+    }
+    // (no early exit: a branch here lets the compiler sink each load into it,
+    // one memory round trip per split; a split past the end repeats the last
+    // one with weight zero instead)
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const float m = s0 + i * MR < s_total ? ml[i].x : -INFINITY, l = ml[i].y;
+      const float mn = fmaxf(mr, m);
+      const float sc = mr == -INFINITY ? 0.f : exp2f(mr - mn);
+      const float wt = m == -INFINITY ? 0.f : exp2f(m - mn);
+      acc = acc * sc + ov[i] * wt;
+      lr = fmaf(lr, sc, l * wt);
+      mr = mn;
+    }
   }
   sacc[tid] = acc;
   sml[2 * tid] = mr;
@@ -1385,7 +1400,7 @@ __global__ __launch_bounds__(MT) void merge_kernel(const float* __restrict__ par
   __syncthreads();
   if (r == 0) {
 #pragma unroll
-    for (int k = 1; k < MT / 32; ++k) {
+    for (int k = 1; k < MR; ++k) {
       const int t = tid + 32 * k;
       const float m = sml[2 * t], l = sml[2 * t + 1];
       const float mn = fmaxf(mr, m);

@@ -151,6 +151,9 @@ hipError_t launch_accum(const kvc_cache& c, int hq, const float* logits, int64_t
                         const float* lse, int mode, const int32_t* sel, int k_max, int n_sink,
                         int n_window, float* acc, hipStream_t s);
 
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups,
+                              hipStream_t s);
+
 hipError_t launch_topk_mass(const kvc_cache& c, int hq, const float* logits, int64_t stride,
                             const float* lse, int k, float* out, hipStream_t s);
 

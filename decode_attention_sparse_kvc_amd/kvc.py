@@ -88,6 +88,8 @@ def _load():
                                      c_int32, c_int32, c_int32, c_void_p, c_void_p]
     lib.kvc_topk_mass.restype = c_int32
     lib.kvc_topk_mass.argtypes = [P, c_int32, c_void_p, c_int64, c_void_p, c_int32, c_void_p, c_void_p]
+    lib.kvc_stream_read.restype = c_int32
+    lib.kvc_stream_read.argtypes = [c_void_p, c_size_t, c_void_p, c_int32, c_void_p]
     lib.kvc_workspace_bytes.restype = c_size_t
     lib.kvc_workspace_bytes.argtypes = [c_int32, P, c_int32, c_int32, c_int32, c_int32, c_int32,
                                         c_int32]
@@ -173,6 +175,11 @@ def kvc_topk_mass(cache, num_q_heads: int, logits, logits_stride: int, lse, k: i
     _check("kvc_topk_mass", lib().kvc_topk_mass(
         ctypes.byref(cache), num_q_heads, _ptr(logits), logits_stride, _ptr(lse), k, _ptr(out),
         _stream(stream)))
+
+
+def kvc_stream_read(src, nbytes: int, sink, workgroups: int, stream=None):
+    _check("kvc_stream_read", lib().kvc_stream_read(_ptr(src), nbytes, _ptr(sink), workgroups,
+                                                    _stream(stream)))
 
 
 def kvc_workspace_bytes(op: int, cache, num_q_heads: int, mode: int = 0, k_max: int = 0,

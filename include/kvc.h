@@ -264,8 +264,10 @@ kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num
  *           [n_sink, n - n_window).  INT4/INT1 read only the groups of kept
  *           blocks, sinks and window.  KVC_ERR_UNSUPPORTED when a quantized
  *           cache is too long for the per-wave block list (over 2^23 tokens).
- *   sel   int32 [B][Hkv][k_max], ascending, -1 padded (kvc_score_topk's
- *         out_idx); entries outside [n_sink, n - n_window) are ignored.
+ *   sel   int32 [B][Hkv][k_max], strictly ascending, then -1 padding
+ *         (kvc_score_topk's out_idx); entries outside [n_sink, n - n_window)
+ *         are ignored.  A row with a repeated or out-of-order entry gives
+ *         undefined results (never an access outside the buffers).
  *   out   float32 [B][Hq][128];  lse  float32 [B][Hq] (natural log; -inf and
  *         out = 0 when nothing is attended).
  *   logits optional float32, row (b, h) at logits + (b*Hq + h)*logits_stride:
@@ -327,6 +329,20 @@ kvc_status kvc_topk_mass(const kvc_cache* cache, int32_t num_q_heads, const floa
  * 0 on invalid arguments.  Host only. */
 size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t mode,
                            int32_t k_max, int32_t n_sink, int32_t n_window, int32_t workgroups);
+
+/*
+ * kvc_stream_read -- a measurement aid, not a step of the method: reads
+ * `bytes` of device memory at src once, in 4 KB chunks spread over
+ * `workgroups` 256-thread workgroups (nontemporal 16-byte loads, two chunks
+ * in flight per wave), so that timing it gives the plain streaming-read rate
+ * the roofline figures are set against next to the nominal HBM peak.
+ *   src        device pointer, 4096-byte aligned; bytes a multiple of 4096.
+ *   sink       device uint32 [4 * workgroups]; written only in the case no
+ *              real data produces (it keeps the loads from being removed).
+ *   workgroups 1..KVC_MAX_WORKGROUPS.
+ */
+kvc_status kvc_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                           hipStream_t stream);
 
 /* Static description of a status code. */
 const char* kvc_status_str(kvc_status status);
