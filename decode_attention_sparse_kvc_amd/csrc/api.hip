@@ -123,6 +123,9 @@ const char* kvc_status_str(kvc_status s) {
     case KVC_ERR_UNSUPPORTED: return "unsupported format, mode or size";
     case KVC_ERR_WORKSPACE: return "workspace missing or too small";
     case KVC_ERR_HIP: return "HIP kernel launch failed";
+    case KVC_ERR_SCRATCH:
+      return "the call needs more than the static scratch of kvc_attend_decode_noalloc "
+             "(KVC_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -189,6 +192,24 @@ kvc_status kvc_attend_decode(const kvc_cache* cache, const uint16_t* q, int32_t 
   return hip_status(launch_attend(*cache, q, num_q_heads, sm_scale, mode, sel, k_max, n_sink,
                                   n_window, out, lse, logits, logits_stride, workgroups, workspace,
                                   stream));
+}
+
+kvc_status kvc_attend_decode_noalloc(const kvc_cache* cache, const uint16_t* q,
+                                     int32_t num_q_heads, float sm_scale, int32_t mode,
+                                     const int32_t* sel, int32_t k_max, int32_t n_sink,
+                                     int32_t n_window, float* out, float* lse, float* logits,
+                                     int64_t logits_stride, hipStream_t stream) {
+  size_t ws = 0;
+  const kvc_status st = check_attend_call(cache, q, num_q_heads, sm_scale, mode, sel, k_max,
+                                          n_sink, n_window, out, lse, logits, logits_stride, 0, &ws);
+  if (st != KVC_OK) return st;
+  // the size check comes before any HIP call: an oversized request is
+  // rejected without touching the device
+  if (ws > (size_t)KVC_NOALLOC_SCRATCH_BYTES) return KVC_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (noalloc_scratch(&scratch) != hipSuccess) return KVC_ERR_HIP;
+  return hip_status(launch_attend(*cache, q, num_q_heads, sm_scale, mode, sel, k_max, n_sink,
+                                  n_window, out, lse, logits, logits_stride, 0, scratch, stream));
 }
 
 kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const float* logits,

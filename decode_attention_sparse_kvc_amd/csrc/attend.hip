@@ -30,6 +30,9 @@
 
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "internal.h"
 
 namespace kvc {
@@ -1624,6 +1627,39 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
   if (e != hipSuccess) return e;
   merge_kernel<<<c.batch * hq, MT, 0, s>>>(a.part, a.s_total, out, lse, a.pairs, a.G);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- static scratch
+// The workspace of kvc_attend_decode_noalloc: a file-scope device array that
+// every GPU the library runs on holds (its own copy, at its own address) until
+// the process ends.  Host code never passes `scratch` itself to a kernel (on the
+// host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+namespace {
+__device__ __align__(256) uint8_t scratch[KVC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> scratch_addr[MAX_DEVICES];
+std::mutex scratch_mutex;
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    p = scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace kvc

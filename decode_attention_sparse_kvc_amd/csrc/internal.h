@@ -142,6 +142,10 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
                          float* lse, float* logits, int64_t logits_stride, int workgroups,
                          void* ws, hipStream_t s);
 
+// Device address of the current device's static scratch (kvc_attend_decode_noalloc);
+// looked up with hipGetSymbolAddress on the device's first call, then cached.
+hipError_t noalloc_scratch(void** ptr);
+
 size_t topk_workspace_bytes(const kvc_cache& c);
 hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int mode, int n_crit,
                              const float* ext, int n_sink, int n_window, const int32_t* k_per_seq,

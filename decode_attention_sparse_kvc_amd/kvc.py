@@ -26,6 +26,7 @@ SCORE = {"exact": 0, "critical": 1, "external": 2}
 SCORE_BLOCKS = 16   # OR'ed into a score mode: rank 64-token blocks
 MODE = {"dense": 0, "drop": 1, "keep": 2, "blocks": 3}
 OP_SCORE_TOPK, OP_ATTEND = 1, 2
+NOALLOC_SCRATCH_BYTES = 32 << 20   # KVC_NOALLOC_SCRATCH_BYTES
 
 
 class KvcError(RuntimeError):
@@ -83,6 +84,10 @@ def _load():
     lib.kvc_attend_decode.argtypes = [P, c_void_p, c_int32, c_float, c_int32, c_void_p, c_int32,
                                       c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_int64,
                                       c_int32, c_void_p, c_size_t, c_void_p]
+    lib.kvc_attend_decode_noalloc.restype = c_int32
+    lib.kvc_attend_decode_noalloc.argtypes = [P, c_void_p, c_int32, c_float, c_int32, c_void_p,
+                                              c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                                              c_void_p, c_int64, c_void_p]
     lib.kvc_accum_scores.restype = c_int32
     lib.kvc_accum_scores.argtypes = [P, c_int32, c_void_p, c_int64, c_void_p, c_int32, c_void_p,
                                      c_int32, c_int32, c_int32, c_void_p, c_void_p]
@@ -161,6 +166,14 @@ def kvc_attend_decode(cache, q, num_q_heads: int, sm_scale: float, mode: int, se
         ctypes.byref(cache), _ptr(q), num_q_heads, sm_scale, mode, _ptr(sel), k_max, n_sink,
         n_window, _ptr(out), _ptr(lse), _ptr(logits), logits_stride, workgroups, _ptr(workspace),
         workspace_bytes, _stream(stream)))
+
+
+def kvc_attend_decode_noalloc(cache, q, num_q_heads: int, sm_scale: float, mode: int, sel,
+                              k_max: int, n_sink: int, n_window: int, out, lse, logits=None,
+                              logits_stride: int = 0, stream=None):
+    _check("kvc_attend_decode_noalloc", lib().kvc_attend_decode_noalloc(
+        ctypes.byref(cache), _ptr(q), num_q_heads, sm_scale, mode, _ptr(sel), k_max, n_sink,
+        n_window, _ptr(out), _ptr(lse), _ptr(logits), logits_stride, _stream(stream)))
 
 
 def kvc_accum_scores(cache, num_q_heads: int, logits, logits_stride: int, lse, mode: int, sel,

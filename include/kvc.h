@@ -53,6 +53,7 @@ extern "C" {
 #define KVC_MAX_GQA 8          /* query heads per KV head supported by attend */
 #define KVC_MAX_OUTLIERS 4     /* fp16 outlier channels per KV head (INT4) */
 #define KVC_MAX_WORKGROUPS 65536  /* largest workgroup count an attend call may be planned for */
+#define KVC_NOALLOC_SCRATCH_BYTES (32u << 20)  /* static scratch of kvc_attend_decode_noalloc */
 
 typedef int32_t kvc_status;
 enum {
@@ -61,7 +62,9 @@ enum {
   KVC_ERR_SHAPE = 2,        /* inconsistent sizes */
   KVC_ERR_UNSUPPORTED = 3,  /* format / mode / size not built */
   KVC_ERR_WORKSPACE = 4,    /* workspace missing or too small */
-  KVC_ERR_HIP = 5           /* a kernel launch failed (hipGetLastError) */
+  KVC_ERR_HIP = 5,          /* a kernel launch failed (hipGetLastError) */
+  KVC_ERR_SCRATCH = 6       /* kvc_attend_decode_noalloc: the call needs more than the
+                               static scratch (KVC_NOALLOC_SCRATCH_BYTES) */
 };
 
 enum { KVC_FMT_FP16 = 0, KVC_FMT_INT4 = 1, KVC_FMT_INT1 = 2, KVC_FMT_FP8 = 3 };
@@ -294,6 +297,27 @@ kvc_status kvc_attend_decode(const kvc_cache* cache, const uint16_t* q, int32_t 
                              int32_t n_sink, int32_t n_window, float* out, float* lse,
                              float* logits, int64_t logits_stride, int32_t workgroups,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kvc_attend_decode_noalloc -- kvc_attend_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, arguments and
+ * results with workgroups = 0, but no workspace argument.  Its split partials,
+ * selection bitmaps and plans live in a static device array of
+ * KVC_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends (one copy per device; its address is looked up once
+ * per device, on the first call with that device current).  A call that would
+ * need more scratch than that returns KVC_ERR_SCRATCH before touching the
+ * device.  The call allocates and frees nothing.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and give undefined results; serialize them.  The stream must
+ * belong to the current device.
+ */
+kvc_status kvc_attend_decode_noalloc(const kvc_cache* cache, const uint16_t* q,
+                                     int32_t num_q_heads, float sm_scale, int32_t mode,
+                                     const int32_t* sel, int32_t k_max, int32_t n_sink,
+                                     int32_t n_window, float* out, float* lse, float* logits,
+                                     int64_t logits_stride, hipStream_t stream);
 
 /*
  * kvc_accum_scores -- H2O cumulative scores ([SRV] 3.2): for every attended

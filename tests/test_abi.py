@@ -167,3 +167,21 @@ def test_library_digest_names_its_sources():
     from decode_attention_sparse_kvc_amd.build import source_digest
     assert kvc.kvc_build_digest() == source_digest()
     assert len(source_digest()) == 16
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    """kvc_attend_decode_noalloc refuses a call whose workspace exceeds the static scratch,
+    before any device work (so this runs without a GPU); its other checks are the
+    workspace call's."""
+    L = kvc.lib()
+    # 64 sequences x 64K tokens, keep mode: the row plan alone exceeds 32 MiB
+    d = _desc(batch=64, num_kv_heads=8, max_tokens=65536, k16=0x100000, v16=0x200000)
+    need = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, d, 32, 2, 20000, 4, 2048)
+    assert need > kvc.NOALLOC_SCRATCH_BYTES
+    st = L.kvc_attend_decode_noalloc(ctypes.byref(d), 0x30000, 32, 0.088, 2, 0x40000, 20000, 4,
+                                     2048, 0x50000, 0x60000, None, 0, None)
+    assert st == 6 and "static scratch" in kvc.kvc_status_str(6)
+    assert L.kvc_attend_decode_noalloc(None, 0x30000, 32, 0.088, 0, None, 0, 0, 0, 0x50000,
+                                       0x60000, None, 0, None) == 1
+    assert L.kvc_attend_decode_noalloc(ctypes.byref(d), 0x30000, 32, 0.0, 0, None, 0, 0, 0,
+                                       0x50000, 0x60000, None, 0, None) == 1
