@@ -152,6 +152,7 @@ kvc_status kvc_score_topk(const kvc_cache* cache, const uint16_t* q, int32_t num
   if (st != KVC_OK) return st;
   if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads) return KVC_ERR_SHAPE;
   if (num_q_heads / cache->num_kv_heads > 16) return KVC_ERR_UNSUPPORTED;
+  if (cache->max_tokens > KVC_TOPK_MAX_ITEMS) return KVC_ERR_UNSUPPORTED;
   const int32_t base_mode = score_mode & ~KVC_SCORE_BLOCKS;
   if (base_mode < KVC_SCORE_EXACT || base_mode > KVC_SCORE_EXTERNAL) return KVC_ERR_INVALID;
   if (n_sink < 0 || n_window < 0 || k_max < 0) return KVC_ERR_INVALID;

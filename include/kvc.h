@@ -53,6 +53,7 @@ extern "C" {
 #define KVC_MAX_GQA 8          /* query heads per KV head supported by attend */
 #define KVC_MAX_OUTLIERS 4     /* fp16 outlier channels per KV head (INT4) */
 #define KVC_MAX_WORKGROUPS 65536  /* largest workgroup count an attend call may be planned for */
+#define KVC_TOPK_MAX_ITEMS (1 << 24)  /* kvc_score_topk: max_tokens at most this */
 #define KVC_NOALLOC_SCRATCH_BYTES (32u << 20)  /* static scratch of kvc_attend_decode_noalloc */
 
 typedef int32_t kvc_status;

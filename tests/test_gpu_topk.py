@@ -136,6 +136,55 @@ def test_sixteen_heads_per_kv_head():
     topk_case(w)
 
 
+def test_region_path_ties_across_regions():
+    """Above 8192 items each 4096-item region emits its own indices: identical scores spread
+    over five regions, the selection boundary among them (lower index wins across regions)."""
+    w = W.sparse_crit8(n_ctx=20000, n_planted=0, top_k=500)
+    k = w.k.copy()
+    for g in range(w.hkv):           # ~610 identical rows per KV head, scoring far above the rest
+        k[0, 100:19000:31, g] = (2 * w.q[0, 4 * g].astype(np.float32)).astype(np.float16)
+    w.k = k
+    w.n_crit = 128                    # every channel: identical rows score identically
+    topk_case(w)
+
+
+def _region_external(values, probs, top_k, seed=0, k_max=None):
+    """External scores drawn from a few values over three sequences of 12000-17000 tokens."""
+    w = W.batched_joint(batch=3, lo=12000, hi=17000, n_window=128)
+    rng = np.random.default_rng(seed)
+    vals = np.asarray(values, np.float32)
+    acc = vals[rng.choice(len(vals), size=w.acc.shape, p=probs)]
+    for b in range(w.batch):
+        acc[b, :, w.seq_lens[b]:] = 0.0
+    w.acc = acc.astype(np.float32)
+    w.top_k = np.asarray(top_k, np.int32)
+    return topk_case(w, k_max=k_max)
+
+
+@pytest.mark.parametrize("top_k", [[3000, 1, 9000], [0, 2500, 20000]])
+def test_region_path_all_scores_equal(top_k):
+    """One value everywhere: the threshold bin holds every candidate (more than fit in LDS),
+    so the first k candidates by index are the answer; k = 0 and k above the candidates too."""
+    _region_external([0.5], [1.0], top_k)
+
+
+def test_region_path_one_bin_many_digits():
+    """Three values inside one coarse bin (same sign, exponent and top mantissa bits): a bin
+    too large for LDS whose keys differ only in later digits."""
+    _region_external([1.0, 1.0000001, 1.0000002], [0.5, 0.3, 0.2], [2000, 7000, 11000], seed=1)
+
+
+def test_region_path_bin_with_ties_in_lds():
+    """Value classes of a few thousand items: the boundary inside a class that fits in LDS."""
+    _region_external([1.0, 2.0, 4.0], [0.6, 0.3, 0.1], [2000, 5000, 100], seed=2)
+
+
+def test_region_path_extreme_exponents():
+    """Scores outside the coarse bins' exponent window (clamped into the end bins), zero and
+    negative values."""
+    _region_external([-1e30, -2.5, 1e-30, 0.0, 7.0, 3e30], [1 / 6] * 6, [4000, 6000, 10], seed=3)
+
+
 @pytest.mark.parametrize("make", [lambda: W.sparse_crit8(), lambda: W.batched_joint()],
                          ids=["crit8_top4096_128k", "batch16_external"])
 def test_full_size(make):
