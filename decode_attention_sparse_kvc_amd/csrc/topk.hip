@@ -1172,7 +1172,9 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
     return dim3((unsigned)std::min<int64_t>(chunks, per_pair), Hkv, B);
   };
   const int vchunks = (c.max_tokens + SCT * TPT - 1) / (SCT * TPT);
-  const bool kt = c.kT && c.page_size == 0;   // (FP8: kT holds the decoded values)
+  // the channel-major copy serves fp16 and FP8 caches (FP8: kT holds the decoded
+  // values); quantized caches score their codes
+  const bool kt = c.kT && c.page_size == 0 && (c.format == KVC_FMT_FP16 || c.format == KVC_FMT_FP8);
   if (mode == KVC_SCORE_EXTERNAL) {
     score_ext_kernel<<<score_grid(vchunks, 2), SCT, 0, s>>>(a);
   } else if (mode == KVC_SCORE_CRITICAL && kt && (a.G == 1 || a.G == 2 || a.G == 4)) {

@@ -23,16 +23,18 @@ def sel_tensor(res, w, k_max):
     return sel
 
 
-def run_attend(cache, w, sel=None, k_max=0, logits=True, workgroups=0):
+def run_attend(cache, w, sel=None, k_max=0, logits=True, workgroups=0, fill=0):
+    """kvc_attend_decode on w (workspace bytes preset to `fill`); host out, lse, logits, stride."""
     mode = kvc.MODE[w.mode]
     B, hq = w.batch, w.hq
     out = torch.full((B, hq, 128), float("nan"), device="cuda")
     lse = torch.full((B, hq), float("nan"), device="cuda")
-    stride = w.n_sink + k_max + w.n_window if w.mode == "drop" else cache.max_tokens
+    stride = (w.n_sink + k_max + w.n_window if w.mode == "drop"
+              else w.n_sink + 64 * k_max + w.n_window if w.mode == "blocks" else cache.max_tokens)
     lg = torch.full((B, hq, stride), float("nan"), device="cuda") if logits else None
     nbytes = kvc.kvc_workspace_bytes(kvc.OP_ATTEND, cache.desc, hq, mode, k_max, w.n_sink, w.n_window,
                                      workgroups)
-    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.full((max(nbytes, 16),), fill, dtype=torch.uint8, device="cuda")
     sel_t = dev(sel) if sel is not None else None
     kvc.kvc_attend_decode(cache.desc, dev(w.q), hq, w.sm_scale, mode, sel_t, k_max, w.n_sink,
                           w.n_window, out, lse, lg, stride, ws, nbytes, workgroups=workgroups)
@@ -250,6 +252,19 @@ def test_keep_paged_int4(append):
     check_against_oracle(w, res, out, lse, lg)
 
 
+@pytest.mark.parametrize("append", [False, True])
+def test_keep_paged_int1(append):
+    """Joint tiers on a 1-bit cache with 64-token pages: keep set in fp16, rest 1-bit codes."""
+    w = W.batched_joint(batch=3, lo=500, hi=900, n_window=128, page=64)
+    w.fmt = "int1"
+    res, cache = oracle_and_cache(w, append=append)
+    if append:
+        cache.append(dev(w.k_new), dev(w.v_new))
+    k_max = int(w.top_k.max())
+    out, lse, lg, _ = run_attend(cache, w, sel_tensor(res, w, k_max), k_max)
+    check_against_oracle(w, res, out, lse, lg)
+
+
 @pytest.mark.parametrize("target", [1, 64, 4096])
 def test_split_count_invariance(target):
     """The result does not depend on how the context is split across workgroups."""
@@ -280,8 +295,8 @@ def test_full_size_dense(make):
 ], ids=["batch16_keep", "crit8_drop_128k"])
 def test_full_size_sparse(make, pairs):
     """The benchmark's keep / drop workloads at full size: the GPU Top-K feeds the GPU
-    attention (as in a step); on sampled pairs the selection must equal the oracle's and
-    o / lse / logits must match it."""
+    attention and the H2O update (as in a step); on sampled pairs the selection must equal
+    the oracle's and o / lse / logits / cumulative scores must match it."""
     from test_gpu_topk import run_topk
     w = make()
     res = ST.decode_step(w, append=False, pairs=pairs)
@@ -304,3 +319,11 @@ def test_full_size_sparse(make, pairs):
                             out, lse, None)
     check_against_oracle(w, sampled, out, lse, lg, k_max, stride)
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    # the H2O update of the step, on the sampled pairs
+    from test_gpu_topk import run_accum
+    acc = run_accum(cache, w, dev(lg), stride, dev(lse), np.ascontiguousarray(idx.astype(np.int32)),
+                    k_max)
+    for (b, g) in pairs:
+        n = res.caches[(b, g)].n
+        assert_close(acc[b, g, :n], res.acc[b, g, :n], f"acc b={b} g={g}")
+        assert np.array_equal(acc[b, g, n:], w.acc[b, g, n:]), "tokens past the end are untouched"

@@ -85,6 +85,30 @@ def test_full_size_layers_decision():
             assert S.quantization_friendly(p_gpu) == S.quantization_friendly(p_ref), name
 
 
+def test_full_size_concentrated_layer_decision():
+    """The other branch of the classifier at full size: the 128K fp16 layer with 300 keys per
+    KV head turned onto their query head's direction at a large norm, so each row's top 3%
+    holds nearly all of its probability (P far below tau: sparsity-friendly); mass, P and
+    the decision match the oracle."""
+    k = 3932
+    w = W.FULL["llama8b_layer_fp16_crit8_top4096_128k"]()
+    w.mode, w.score, w.accumulate = "dense", None, False
+    rng = np.random.default_rng(21)
+    kk = w.k.copy()
+    g = 0
+    for j, t in enumerate(rng.choice(131072, 300, replace=False)):
+        qh = w.q[0, 4 * g + j % 4].astype(np.float64)
+        kk[0, t, g] = (qh / np.linalg.norm(qh) * 40.0).astype(np.float16)
+    w.k = kk
+    res, m = mass_case(w, [k], pairs=[(0, 0)])
+    ref = [S.topk_mass(np.exp(res.logits[(0, 0)][j] - res.lse[0, j]), k) for j in range(w.group)]
+    p_gpu = S.dense_preference(m[k][0, :w.group]) / w.group
+    p_ref = S.dense_preference(ref) / w.group
+    assert p_ref < 0.1, p_ref   # the layer really is on the sparsity-friendly side
+    assert abs(p_gpu - p_ref) <= 1e-3 + 2e-3 * abs(p_ref), (p_gpu, p_ref)
+    assert not S.quantization_friendly(p_gpu) and not S.quantization_friendly(p_ref)
+
+
 def test_bucket_larger_than_lds():
     """40000 equal logits share one top-byte bucket, more than the kernel stages in
     LDS: the row is re-read from memory, and the mass is k / n."""
