@@ -72,6 +72,8 @@ struct AttendArgs {
                               // derives its positions from sel itself (no plan kernel)
   int32_t* glist;             // blocks mode, INT4/INT1: [B][Hkv][max_tokens/64] groups to walk
   int32_t* gcount;            // blocks mode, INT4/INT1: [B][Hkv] their number
+  int32_t* kfill;             // keep mode: [B][Hkv] sel entries before the -1 padding (the
+                              // fp16-rows role skips the padding's positions)
   int s_q, s_total;
   int ppw;                    // rows role: positions per wave (multiple of 16)
   int gpw;                    // quantized role: planned groups per wave
@@ -981,7 +983,16 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
   const int G = a.G;
   const int col = lane & 15, kb = lane >> 4;
   const bool hv = col < G;
-  const int np = DENSE ? n - nq : a.np;
+  // keep mode: the positions of the sel padding (ROW_SKIP entries past the
+  // pair's filled entries) are left out, so a pair uses only the waves its own
+  // selection needs; position p of the walk is plan position p (before the
+  // padding) or p + gap (after it)
+  int kf = a.k_max, gap = 0;
+  if (!DENSE && a.mode == KVC_ATTEND_KEEP) {
+    kf = min(max(*scalar_ptr(a.kfill + (int64_t)b * c.num_kv_heads + g), 0), a.k_max);
+    gap = a.k_max - kf;
+  }
+  const int np = DENSE ? n - nq : a.np - gap;
   const int pa = (rsplit * NW + w) * a.ppw;
   const int pb = min(pa + a.ppw, np);
   const bool drop = compact(a.mode);
@@ -1029,7 +1040,7 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
           const int si = q < 0 ? INT_MAX / 8 : (blocks ? q / GS : q);
           return uint2{bc<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(rplan, (int)(4u * (uint32_t)min(si, INT_MAX / 8)), 0, 0)), 0u};
         }
-        return buf_load8(rplan, 8u * (uint32_t)p);
+        return buf_load8(rplan, 8u * (uint32_t)(p >= a.n_sink + kf ? p + gap : p));
       }
     };
     auto plan_decode = [&](uint2 raw, int i) -> int2 {
@@ -1229,14 +1240,30 @@ void attend_kernel(AttendArgs a) {
   } else if (DENSE) {
     pair = id / a.s_total;
     split = id - pair * a.s_total;
-  } else if (id < a.s_q * a.pairs) {
-    pair = id / a.s_q;
-    split = id - pair * a.s_q;
   } else {
-    id -= a.s_q * a.pairs;
-    const int s_r = a.s_total - a.s_q;
-    pair = id / s_r;
-    split = a.s_q + (id - pair * s_r);
+    // drop / blocks: every quantized-role workgroup before every fp16-rows one
+    // (the longer quantized runs of a ragged batch start first); keep mode,
+    // whose fp16 rows are a large share of the bytes: the two roles spread
+    // evenly over the grid, so both run side by side from the start (ragged
+    // keep batch 247 -> 229 us with eight rows workgroups a CU)
+    const int64_t Q = (int64_t)a.s_q * a.pairs, T = (int64_t)a.s_total * a.pairs;
+    int64_t qi, ri;
+    if (a.mode == KVC_ATTEND_KEEP) {
+      const int64_t qa = (int64_t)id * Q / T, qb = ((int64_t)id + 1) * Q / T;
+      qi = qb > qa ? qa : -1;
+      ri = id - qb;
+    } else {
+      qi = id < Q ? id : -1;
+      ri = id - Q;
+    }
+    if (qi >= 0) {
+      pair = (int)(qi / a.s_q);
+      split = (int)(qi - (int64_t)pair * a.s_q);
+    } else {
+      const int s_r = a.s_total - a.s_q;
+      pair = (int)(ri / s_r);
+      split = a.s_q + (int)(ri - (int64_t)pair * s_r);
+    }
   }
   const int b = pair / a.c.num_kv_heads, g = pair - b * a.c.num_kv_heads;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1348,6 +1375,17 @@ __global__ __launch_bounds__(256) void plan_kernel(AttendArgs a) {
         for (int h = 0; h < G; ++h)
           a.logits[((int64_t)b * a.hq + g * G + h) * a.logits_stride + a.n_sink + q] = -INFINITY;
       }
+    }
+  }
+  if (a.mode == KVC_ATTEND_KEEP) {
+    // the sel entries before the -1 padding: the one thread at the last filled
+    // entry (or at entry 0 of an empty row) writes their number
+    if (a.k_max == 0) {
+      if (e == 0) a.kfill[pi] = 0;
+    } else if (e < a.k_max) {
+      const bool v = sel[e] >= 0, nv = e + 1 < a.k_max && sel[e + 1] >= 0;
+      if (v && !nv) a.kfill[pi] = e + 1;
+      else if (e == 0 && !v) a.kfill[pi] = 0;
     }
   }
   if (e < a.np) a.rplan[pi * a.np + e] = plan_entry<QUANT>(a, b, g, n, e);
@@ -1470,8 +1508,10 @@ Plan plan_attend(const kvc_cache& c, int mode, int k_max, int n_sink, int n_wind
   // fp16-rows workgroups per CU: one for fp16 / FP8 caches (the rows role is
   // the whole call; measured at 128K: FP8 dense 62.6 -> 59.5 us, fp16 Top-4096
   // drop 15.6 -> 13.9 us against four), four beside the quantized role of the
-  // drop / keep modes (the ragged keep batch: 262 against 272 us with one)
-  const int rows_per_cu = quant ? 4 : 1;
+  // drop / blocks modes, eight in keep mode, where the keep set is about half
+  // the bytes (ragged keep batch 262 us with one, 247 with four, 229 with
+  // eight and the roles interleaved)
+  const int rows_per_cu = quant ? (mode == KVC_ATTEND_KEEP ? 8 : 4) : 1;
   const int64_t rwaves = (quant && mode == KVC_ATTEND_DENSE) ? (int64_t)pairs * NW
                                                              : (int64_t)rows_per_cu * target * NW;
   const int64_t tpw = std::max<int64_t>(1, (tiles * pairs + rwaves - 1) / rwaves);
@@ -1544,6 +1584,8 @@ size_t attend_workspace_bytes(const kvc_cache& c, int hq, int mode, int k_max, i
              rows_positions(mode, k_max, n_sink, n_window, grouped(c.format)) * sizeof(int2);
   if (mode == KVC_ATTEND_BLOCKS && grouped(c.format))   // group list + count
     bytes += (size_t)c.batch * c.num_kv_heads * (c.max_tokens / GS + 1) * sizeof(int32_t);
+  if (mode == KVC_ATTEND_KEEP)                                // filled sel entries per pair
+    bytes += (size_t)c.batch * c.num_kv_heads * sizeof(int32_t);
   return bytes;
 }
 
@@ -1586,6 +1628,7 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
                   (mode == KVC_ATTEND_DROP || mode == KVC_ATTEND_BLOCKS);
   a.glist = nullptr;
   a.gcount = nullptr;
+  a.kfill = nullptr;
   const bool quant = grouped(c.format);
   char* wp = static_cast<char*>(ws) + (size_t)c.batch * hq * (p.s_q + p.s_r) * PART * sizeof(float);
   const size_t sel_words = (size_t)c.batch * c.num_kv_heads * (c.max_tokens / 32);
@@ -1602,6 +1645,7 @@ hipError_t launch_attend(const kvc_cache& c, const uint16_t* q, int hq, float sm
     a.glist = reinterpret_cast<int32_t*>(wp);
     a.gcount = a.glist + (size_t)c.batch * c.num_kv_heads * (c.max_tokens / GS);
   }
+  if (mode == KVC_ATTEND_KEEP) a.kfill = reinterpret_cast<int32_t*>(wp);
   a.s_q = p.s_q;
   a.s_total = p.s_q + p.s_r;
   a.ppw = p.ppw;
