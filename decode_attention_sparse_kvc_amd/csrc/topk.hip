@@ -78,6 +78,8 @@ struct TopkArgs {
   int32_t* pmeta;      // [B][Hkv][2] threshold bin tb, items in the bins above it
   int nreg;            // compaction regions per pair (ceil(items / CT))
   bool blocks;         // rank 64-token blocks (items = block ids)
+  bool use_hist;       // long ranges: the coarse histogram is built (short ranges select
+                       // from the key row alone)
   double* tscore;      // block mode: [B][Hkv][max_tokens] token scores
 };
 
@@ -284,6 +286,7 @@ __device__ void critical_channels(const TopkArgs& a, int b, int g, int64_t pi, i
 template <int NT>
 __device__ inline void flush_hist(const TopkArgs& a, int64_t pi, const uint32_t* sh, int tid) {
   static_assert(NT % 64 == 0 && CBINS % NT == 0, "whole super-bins a wave");
+  if (!a.use_hist) return;
   const int rep = blockIdx.x % HREP;
   uint32_t* h = a.hist + pi * HW + rep * CBINS;
   uint32_t* hs = a.hist + pi * HW + HREP * CBINS + rep * SUP;
@@ -334,6 +337,22 @@ __global__ __launch_bounds__((score_threads<EXACT, GT>())) void score_kernel(Top
   const kvc_cache& c = a.c;
   const int nch = a.mode == KVC_SCORE_CRITICAL ? a.n_crit : D;
   for (int e = tid; e < CBINS; e += NT) sh[e] = 0u;
+  // K metadata words of a chunk's groups (quantized caches), channel pairs a
+  // thread; the first chunk's go out with the setup loads, each next chunk's
+  // while the current one is scored
+  const int chunks = (c.max_tokens + NT - 1) / NT;
+  auto meta_load = [&](int ci, uint32_t& s2, uint32_t& z2) {
+    const int groups = c.max_tokens / GS;
+    const int gq = ci * (NT / GS) + tid / 64, j = tid % 64;
+    s2 = z2 = 0u;
+    if (gq < groups) {
+      const uint32_t* km = reinterpret_cast<const uint32_t*>(c.k_meta + (pi * groups + gq) * 2 * D);
+      s2 = km[j];
+      z2 = km[D / 2 + j];
+    }
+  };
+  uint32_t ms2 = 0u, mz2 = 0u;
+  if (grouped(FMT) && (int)blockIdx.x < chunks) meta_load(blockIdx.x, ms2, mz2);
   int lo, hi, kk;
   cand_range(a, b, lo, hi, kk);   // (its loads go out with the channel ranking's)
   if (a.blocks) {   // every token of the candidate blocks
@@ -350,20 +369,12 @@ __global__ __launch_bounds__((score_threads<EXACT, GT>())) void score_kernel(Top
   }
   lds_sync();
 
-  const int chunks = (c.max_tokens + NT - 1) / NT;
   for (int ci = blockIdx.x; ci < chunks; ci += gridDim.x) {
     const int t = ci * NT + tid;
-    if (grouped(FMT)) {   // K metadata of the chunk's groups, channel pairs a thread
-      lds_sync();    // (the previous chunk's is no longer read)
-      const int groups = c.max_tokens / GS;
-      const int gq = ci * (NT / GS) + tid / 64, j = tid % 64;
-      uint32_t s2 = 0u, z2 = 0u;
-      if (gq < groups) {
-        const uint32_t* km = reinterpret_cast<const uint32_t*>(c.k_meta + (pi * groups + gq) * 2 * D);
-        s2 = km[j];
-        z2 = km[D / 2 + j];
-      }
-      uint32_t m0 = (s2 & 0xFFFFu) | (z2 << 16), m1 = (s2 >> 16) | (z2 & 0xFFFF0000u);
+    if (grouped(FMT)) {   // stage the chunk's metadata: (scale | zero << 16) per channel
+      if (ci != (int)blockIdx.x) lds_sync();   // (the previous chunk's is no longer read)
+      const int j = tid % 64;
+      uint32_t m0 = (ms2 & 0xFFFFu) | (mz2 << 16), m1 = (ms2 >> 16) | (mz2 & 0xFFFF0000u);
       // outlier channels (INT4): the word names the outlier store entry instead
       // (a zero-point field of all ones is a NaN no quantized group stores)
       for (int e = 0; e < c.n_outlier; ++e) {
@@ -374,6 +385,7 @@ __global__ __launch_bounds__((score_threads<EXACT, GT>())) void score_kernel(Top
       smeta[(tid / 64) * D + 2 * j] = m0;
       smeta[(tid / 64) * D + 2 * j + 1] = m1;
       lds_sync();
+      if (ci + (int)gridDim.x < chunks) meta_load(ci + gridDim.x, ms2, mz2);
     }
     const bool in = t < c.max_tokens;
     uint64_t key = 0;
@@ -432,7 +444,7 @@ __global__ __launch_bounds__((score_threads<EXACT, GT>())) void score_kernel(Top
     }
     if (key) {   // (key rows hold candidates only; block mode: none)
       __builtin_nontemporal_store(key, a.keys + pi * c.max_tokens + t);
-      atomicAdd(&sh[coarse_of(key)], 1u);
+      if (a.use_hist) atomicAdd(&sh[coarse_of(key)], 1u);
     }
   }
   lds_sync();
@@ -448,7 +460,7 @@ __device__ inline void put_keys(const TopkArgs& a, int64_t pi, int t0, const uin
   __builtin_nontemporal_store(u4v{(uint32_t)kv[2], (uint32_t)(kv[2] >> 32), (uint32_t)kv[3], (uint32_t)(kv[3] >> 32)}, dst + 1);
 #pragma unroll
   for (int u = 0; u < TPT; ++u)
-    if (kv[u]) atomicAdd(&sh[coarse_of(kv[u])], 1u);
+    if (kv[u] && a.use_hist) atomicAdd(&sh[coarse_of(kv[u])], 1u);
 }
 
 // External scores (H2O cumulative scores, or any the caller gives), any
@@ -478,7 +490,7 @@ __global__ __launch_bounds__(SCT) void score_ext_kernel(TopkArgs a) {
     for (int u = 0; u < TPT; ++u) {   // (no key row: later stages derive the keys from ext)
       const int t = t0 + u;
       const uint64_t key = t >= lo && t < hi ? emit_score(a, pi, t, (double)ev[u]) : 0ull;
-      if (key) atomicAdd(&sh[coarse_of(key)], 1u);
+      if (key && a.use_hist) atomicAdd(&sh[coarse_of(key)], 1u);
     }
   }
   lds_sync();
@@ -592,7 +604,7 @@ __global__ __launch_bounds__(ST) void block_key_kernel(TopkArgs a) {
       const uint64_t key = order_key(r);
       a.keys[pi * a.c.max_tokens + j] = key;
       if (a.out_scores) a.out_scores[pi * a.c.max_tokens + j] = r;
-      atomicAdd(&sh[coarse_of(key)], 1u);
+      if (a.use_hist) atomicAdd(&sh[coarse_of(key)], 1u);
     }
   }
   lds_sync();
@@ -894,18 +906,19 @@ __global__ __launch_bounds__(FT) void finish_direct_kernel(TopkArgs a) {
   const uint64_t* gkeys = a.keys + pi * a.c.max_tokens;
   const bool fx = keys_from_ext(a);
   const float* ex = fx ? a.ext + pi * a.c.max_tokens : nullptr;
-  for (int i = tid; i < N; i += FT) {   // (in LDS by coarse_threshold's end; candidates only)
+  for (int i = tid; i < N; i += FT) {   // (candidates only)
     const int ic = min(max(i, lo), hi - 1);
     const uint64_t key = fx ? ext_key(ex[ic]) : gkeys[ic];
     L.key[i] = i >= lo && i < hi ? key : 0ull;
   }
-  coarse_threshold(a.hist + pi * HW, k, L.s.res);
-  const uint32_t tb = (uint32_t)L.s.res[0];
-  const int krem0 = k - L.s.res[1];
+  lds_sync();
+  // the selection runs over every candidate key (no histogram is built for
+  // short ranges)
+  const int krem0 = k;
   auto for_cand = [&](auto&& f) {
     for (int i = tid; i < N; i += FT) {
       const uint64_t key = L.key[i];
-      if (key && coarse_of(key) == tb) f(key);
+      if (key) f(key);
     }
   };
   uint64_t P;
@@ -915,25 +928,39 @@ __global__ __launch_bounds__(FT) void finish_direct_kernel(TopkArgs a) {
   auto chosen = [&](uint64_t key, bool eq_ok) {
     return bits ? (key >> (64 - bits)) >= P : (key > T || (key == T && eq_ok));
   };
-  int written = 0;
-  uint32_t eq_taken = 0;
-  for (int c0 = 0; c0 < N; c0 += FT) {
-    const int i = c0 + tid;
-    const uint64_t key = i < N ? L.key[i] : 0ull;
-    const uint32_t cb = coarse_of(key);
-    const bool above = key != 0 && cb > tb;
-    const bool inb = key != 0 && cb == tb;
-    const bool eq = inb && !bits && key == T;
-    uint32_t eq_tot;
-    const uint32_t eq_incl = block_scan<FT>(eq ? 1u : 0u, L.s.wsum, &eq_tot);
-    const bool take = above || (inb && chosen(key, eq_taken + eq_incl - 1u < (uint32_t)krem));
-    uint32_t take_tot;
-    const uint32_t take_incl = block_scan<FT>(take ? 1u : 0u, L.s.wsum, &take_tot);
-    const int pos = written + (int)take_incl - 1;
-    if (take && pos < a.k_max) out[pos] = i;
-    written += (int)take_tot;
-    eq_taken += eq_tot;
+  // emission: thread t owns items [t per, (t + 1) per) of the row, so one scan
+  // of the keys equal to T gives their ranks in index order and one scan of
+  // the taken counts gives the output positions
+  const int per = (N + FT - 1) / FT;
+  const int i0 = min(tid * per, N), i1 = min(i0 + per, N);
+  uint32_t neq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint64_t key = L.key[i];
+    neq += key != 0 && !bits && key == T ? 1u : 0u;
   }
+  uint32_t eq_tot;
+  uint32_t rank = block_scan<FT>(neq, L.s.wsum, &eq_tot) - neq;
+  const uint32_t rank0 = rank;
+  uint32_t ntake = 0;
+  for (int i = i0; i < i1; ++i) {   // (the same walk, counting what is taken)
+    const uint64_t key = L.key[i];
+    const bool eq = key != 0 && !bits && key == T;
+    ntake += key != 0 && chosen(key, eq && rank < (uint32_t)krem) ? 1u : 0u;
+    rank += eq ? 1u : 0u;
+  }
+  uint32_t take_tot;
+  int pos = (int)(block_scan<FT>(ntake, L.s.wsum, &take_tot) - ntake);
+  rank = rank0;
+  for (int i = i0; i < i1; ++i) {
+    const uint64_t key = L.key[i];
+    const bool eq = key != 0 && !bits && key == T;
+    if (key != 0 && chosen(key, eq && rank < (uint32_t)krem)) {
+      if (pos < a.k_max) out[pos] = i;
+      ++pos;
+    }
+    rank += eq ? 1u : 0u;
+  }
+  const int written = (int)take_tot;
   for (int e = written + tid; e < a.k_max; e += FT) out[e] = -1;
 }
 
@@ -1142,6 +1169,7 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   const int items = item_count(c, a.blocks);
   const size_t nreg_ws = (c.max_tokens + CT - 1) / CT;
   a.nreg = (items + CT - 1) / CT;
+  a.use_hist = items > DIRECT_MAX;
   char* p = static_cast<char*>(ws);
   a.keys = reinterpret_cast<uint64_t*>(p);
   p += pairs * c.max_tokens * sizeof(uint64_t);
@@ -1162,7 +1190,7 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   a.pmeta = reinterpret_cast<int32_t*>(p);
 
   const int Hkv = c.num_kv_heads, B = c.batch;
-  prep_kernel<<<dim3(Hkv, B), ST, 0, s>>>(a);
+  if (a.use_hist) prep_kernel<<<dim3(Hkv, B), ST, 0, s>>>(a);
   // scoring grid: as many workgroups as are resident at once (per_cu a CU,
   // from the kernel's registers and LDS), split evenly over the pairs; each
   // loops over its chunks
