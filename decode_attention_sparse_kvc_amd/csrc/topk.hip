@@ -590,9 +590,19 @@ __global__ __launch_bounds__(ST) void block_key_kernel(TopkArgs a) {
   const int j0 = blockIdx.x * BPW;
   const double* ts = a.tscore + pi * a.c.max_tokens;
   for (int e = tid; e < CBINS; e += ST) sh[e] = 0u;
-  for (int e = tid; e < BPW * GS; e += ST) {
-    const int j = j0 + e / GS;
-    ss[e] = j >= lo && j < hi ? ts[(int64_t)j0 * GS + e] : 0.0;
+  {   // every load is issued before the LDS stores (a load-store loop waits each time)
+    constexpr int R = BPW * GS / ST;
+    double v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int e = r * ST + tid, j = j0 + e / GS;
+      v[r] = ts[(int64_t)j0 * GS + (j >= lo && j < hi ? e : 0)];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int e = r * ST + tid, j = j0 + e / GS;
+      ss[e] = j >= lo && j < hi ? v[r] : 0.0;
+    }
   }
   lds_sync();
   if (tid < BPW) {
@@ -906,10 +916,24 @@ __global__ __launch_bounds__(FT) void finish_direct_kernel(TopkArgs a) {
   const uint64_t* gkeys = a.keys + pi * a.c.max_tokens;
   const bool fx = keys_from_ext(a);
   const float* ex = fx ? a.ext + pi * a.c.max_tokens : nullptr;
-  for (int i = tid; i < N; i += FT) {   // (candidates only)
-    const int ic = min(max(i, lo), hi - 1);
-    const uint64_t key = fx ? ext_key(ex[ic]) : gkeys[ic];
-    L.key[i] = i >= lo && i < hi ? key : 0ull;
+  {   // candidates only; every load of the row is issued before the LDS stores
+    constexpr int R = DIRECT_MAX / FT;
+    uint64_t kv[R];
+    if (fx) {
+      float xv[R];
+#pragma unroll
+      for (int j = 0; j < R; ++j) xv[j] = ex[min(max(j * FT + tid, lo), hi - 1)];
+#pragma unroll
+      for (int j = 0; j < R; ++j) kv[j] = ext_key(xv[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < R; ++j) kv[j] = gkeys[min(max(j * FT + tid, lo), hi - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int i = j * FT + tid;
+      if (i < N) L.key[i] = i >= lo && i < hi ? kv[j] : 0ull;
+    }
   }
   lds_sync();
   // the selection runs over every candidate key (no histogram is built for
