@@ -15,6 +15,12 @@
 // FP8 (E4M3) caches encode every appended row at once (no groups, no tail);
 // the channel-major copy then holds the decoded values.
 // A second, per-sequence kernel then rewrites the fp16 tail and seq_lens.
+// A one-token append (the decode step) runs in a single launch instead: each
+// workgroup takes the length with an atomic add that also counts it in bits
+// 24..30 of seq_lens[b], writes its new row to the tail itself, and the last
+// of the sequence's Hkv workgroups to arrive stores the new length.
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -48,10 +54,15 @@ struct GroupQuant {
   }
 };
 
-template <int FMT>
+// Arrival count of the one-token path: seq_lens values stay below 2^24 there,
+// and at most 127 workgroups per sequence keep the count clear of the sign bit.
+constexpr int ARRIVE = 1 << 24;
+constexpr int LEN_MASK = ARRIVE - 1;
+
+template <int FMT, bool ONE>
 __global__ __launch_bounds__(NT) void append_groups_kernel(
     kvc_cache c, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int32_t* __restrict__ n_new, int n_new_max) {
+    const int32_t* __restrict__ n_new, int n_new_max, int32_t* overflow) {
   constexpr int BITS = FMT == KVC_FMT_INT4 ? 4 : 1;
   __shared__ __align__(16) uint16_t sK[GS][D];
   __shared__ __align__(16) uint16_t sV[GS][D];
@@ -61,9 +72,35 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
 
   const int b = blockIdx.z, g = blockIdx.y, tid = threadIdx.x;
   const int Hkv = c.num_kv_heads;
-  const int L = c.seq_lens[b];
   const int n = n_new ? n_new[b] : n_new_max;
-  if (n <= 0 || n > n_new_max || L < 0 || L + n > c.max_tokens) return;
+  int L;
+  uint4 newK, newV;   // ONE: this thread's 8 channels of the new row (threads 0..15)
+  if constexpr (ONE) {
+    __shared__ int sL;
+    if (n <= 0) return;
+    if (tid < 16) {   // the new row's address does not depend on the length
+      const int64_t off = ((int64_t)b * Hkv + g) * D + tid * 8;
+      newK = *reinterpret_cast<const uint4*>(k_new + off);
+      newV = *reinterpret_cast<const uint4*>(v_new + off);
+    }
+    if (tid == 0) {
+      const int old = atomicAdd(c.seq_lens + b, ARRIVE);
+      const int len = old & LEN_MASK;
+      const bool ok = n == 1 && len + 1 <= c.max_tokens;
+      if ((old >> 24) == Hkv - 1) {   // every workgroup of sequence b holds the length now
+        __hip_atomic_store(c.seq_lens + b, len + (ok ? 1 : 0), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (!ok && overflow) *overflow = 1;
+      }
+      sL = ok ? len : -1;
+    }
+    __syncthreads();
+    L = sL;
+    if (L < 0) return;
+  } else {
+    L = c.seq_lens[b];
+    if (n <= 0 || n > n_new_max || L < 0 || L + n > c.max_tokens) return;
+  }
   const int g0 = (L / GS + (int)blockIdx.x) * GS;
   if (g0 >= L + n) return;
   const int hi = min(g0 + GS, L + n);   // tokens [g0, hi) exist after the append
@@ -74,8 +111,20 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
   const bool complete = grouped(FMT) && hi == g0 + GS;
   const int r0 = complete ? 0 : lo - g0;
 
+  if constexpr (ONE) {
+    if (tid < 16) {
+      *reinterpret_cast<uint4*>(&sK[L - g0][tid * 8]) = newK;
+      *reinterpret_cast<uint4*>(&sV[L - g0][tid * 8]) = newV;
+      if (grouped(FMT) && !complete) {   // the row joins the tail (a completed group empties it)
+        const int64_t off = (((int64_t)b * Hkv + g) * GS + (L - g0)) * D + tid * 8;
+        *reinterpret_cast<uint4*>(c.k_tail + off) = newK;
+        *reinterpret_cast<uint4*>(c.v_tail + off) = newV;
+      }
+    }
+  }
   // ---- stage rows [g0 + r0, hi) in LDS: 16 threads per row, 8 halves each
-  for (int e = tid; e < (hi - g0 - r0) * 16; e += NT) {
+  // (ONE: only the old tail rows of a completed group; the new row is staged above)
+  for (int e = tid; e < ((ONE ? L : hi) - g0 - r0) * 16; e += NT) {
     const int r = r0 + (e >> 4), ch = (e & 15) * 8;
     const int t = g0 + r;
     const uint4* srcK;
@@ -306,23 +355,26 @@ hipError_t launch_append(const kvc_cache& c, const uint16_t* k_new, const uint16
                          const int32_t* n_new, int32_t n_new_max, int32_t* overflow,
                          hipStream_t s) {
   if (n_new_max <= 0) return hipSuccess;
-  const dim3 grid((n_new_max + GS - 1) / GS + 1, c.num_kv_heads, c.batch);
+  // one token: a single launch (the arrival count needs lengths below 2^24
+  // and at most 127 KV heads)
+  const bool one = n_new_max == 1 && c.max_tokens < ARRIVE && c.num_kv_heads <= 127;
+  const dim3 grid(one ? 1 : (n_new_max + GS - 1) / GS + 1, c.num_kv_heads, c.batch);
+  auto run = [&](auto fmt) {
+    constexpr int F = decltype(fmt)::value;
+    if (one)
+      append_groups_kernel<F, true><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, 1, overflow);
+    else
+      append_groups_kernel<F, false><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max,
+                                                         overflow);
+  };
   switch (c.format) {
-    case KVC_FMT_INT4:
-      append_groups_kernel<KVC_FMT_INT4><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max);
-      break;
-    case KVC_FMT_INT1:
-      append_groups_kernel<KVC_FMT_INT1><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max);
-      break;
-    case KVC_FMT_FP8:
-      append_groups_kernel<KVC_FMT_FP8><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max);
-      break;
-    default:
-      append_groups_kernel<KVC_FMT_FP16><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max);
-      break;
+    case KVC_FMT_INT4: run(std::integral_constant<int, KVC_FMT_INT4>{}); break;
+    case KVC_FMT_INT1: run(std::integral_constant<int, KVC_FMT_INT1>{}); break;
+    case KVC_FMT_FP8: run(std::integral_constant<int, KVC_FMT_FP8>{}); break;
+    default: run(std::integral_constant<int, KVC_FMT_FP16>{}); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || one) return e;
   append_finish_kernel<<<c.batch, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max, overflow);
   return hipGetLastError();
 }

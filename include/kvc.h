@@ -141,8 +141,10 @@ enum { KVC_OP_SCORE_TOPK = 1, KVC_OP_ATTEND = 2 };
  *             channels without touching whole rows ([TKV] 2.3).
  *   k_absmax  float32 [B][Hkv][128]: max |K| per channel over all appended
  *             tokens (fp16-exact values); zero-filled by the caller at creation.
- *   seq_lens  int32 [B]: tokens cached per sequence; updated by
- *             kvc_quantize_append.
+ *   seq_lens  int32 [B]: tokens cached per sequence, each in [0, max_tokens];
+ *             updated by kvc_quantize_append (while a one-token append runs,
+ *             bits 24..30 count its workgroups: nothing may read seq_lens
+ *             concurrently with an append).
  *
  * Outlier channels (INT4 only; [MTG] 8.2: the few channels of very large
  * magnitude are found offline by their variance and kept at full precision
@@ -203,7 +205,8 @@ typedef struct kvc_cache {
  *                 exceed max_tokens; that sequence is left unchanged.
  * Writes every 64-token group the append completes (codes, k_meta, v_meta),
  * the new tail rows, k16/v16/kT rows when those pointers are set, k_absmax,
- * and finally seq_lens[b] += n_new[b].
+ * and finally seq_lens[b] += n_new[b].  n_new_max == 1 (a decode step) runs
+ * as one launch when max_tokens < 2^24 and num_kv_heads <= 127, else two.
  */
 kvc_status kvc_quantize_append(const kvc_cache* cache, const uint16_t* k_new,
                                const uint16_t* v_new, const int32_t* n_new,

@@ -116,6 +116,83 @@ def test_overflow_leaves_sequence_unchanged():
     check_cache_state(cache, rows_k, rows_v, [100, 128])
 
 
+def _check_fp8_rows(cache: KvcCache, rows_k, rows_v, lens, table=None):
+    from oracle import quant as Q
+    assert host(cache.seq_lens).tolist() == list(lens)
+    kc = host(cache.k_codes).reshape(-1, 128)
+    vc = host(cache.v_codes).reshape(-1, 128)
+    for b in range(cache.batch):
+        n = int(lens[b])
+        for g in range(cache.hkv):
+            sl = slots(b, g, np.arange(n), cache.hkv, cache.max_tokens, cache.page_size, table)
+            assert np.array_equal(kc[sl], Q.encode_fp8(rows_k[b][:n, g])), (b, g)
+            assert np.array_equal(vc[sl], Q.encode_fp8(rows_v[b][:n, g])), (b, g)
+
+
+@pytest.mark.parametrize("fmt,page", [("int4", 0), ("int1", 0), ("int4", 16), ("int1", 64),
+                                      ("fp16", 0), ("fp8", 16)])
+def test_single_token_steps(fmt, page):
+    """One-token appends (one launch per step) from ragged lengths across group
+    boundaries, with n_new absent and with n_new holding zeros: every buffer
+    equals the oracle's cache after each few steps, for 5 KV heads."""
+    rng = np.random.default_rng(40)
+    B, hkv, cap, steps = 3, 5, 256, 70
+    start = np.array([60, 0, 127], np.int64)
+    k, v = _rows(rng, B, int(start.max()) + steps, hkv)
+    table, kw = None, {}
+    if page:
+        per = cap // page
+        table = rng.permutation(B * per).astype(np.int32).reshape(B, per)
+        kw = dict(page_size=page, block_table=torch.from_numpy(table), num_pages=B * per)
+    cache = KvcCache(fmt, B, hkv, cap, fp16_rows=fmt == "fp16" or (fmt != "fp8" and page == 16),
+                     kT=(fmt == "fp16"), **kw)
+    check = _check_fp8_rows if fmt == "fp8" else check_cache_state
+    cache.append(dev(k[:, :int(start.max())]), dev(v[:, :int(start.max())]),
+                 dev(start.astype(np.int32)))
+    lens = start.copy()
+    for i in range(steps):
+        step = np.ones(B, np.int64) if i % 3 == 0 else rng.integers(0, 2, size=B)
+        kn = np.zeros((B, 1, hkv, 128), np.float16)
+        vn = np.zeros_like(kn)
+        for b in range(B):
+            if step[b]:
+                kn[b, 0], vn[b, 0] = k[b, lens[b]], v[b, lens[b]]
+        cache.append(dev(kn), dev(vn), None if i % 3 == 0 else dev(step.astype(np.int32)))
+        lens += step
+        if i % 10 == 9 or i == steps - 1:
+            torch.cuda.synchronize()
+            check(cache, k, v, lens, table)
+
+
+def test_single_token_overflow():
+    """A one-token append to a full sequence, or with n_new[b] above n_new_max = 1,
+    sets the flag and leaves that sequence as it was; the others grow."""
+    rng = np.random.default_rng(41)
+    B, hkv, cap = 3, 3, 128
+    k, v = _rows(rng, B, cap + 2, hkv)
+    cache = KvcCache("int4", B, hkv, cap)
+    start = np.array([128, 100, 63], np.int32)
+    cache.append(dev(k[:, :128]), dev(v[:, :128]), dev(start))
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kn = np.stack([k[b, start[b] % cap] for b in range(B)])[:, None]
+    vn = np.stack([v[b, start[b] % cap] for b in range(B)])[:, None]
+    cache.append(dev(kn), dev(vn), overflow=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 1
+    rows_k = [k[0, :128], k[1, :101], k[2, :64]]
+    rows_v = [v[0, :128], v[1, :101], v[2, :64]]
+    check_cache_state(cache, rows_k, rows_v, [128, 101, 64])
+    flag.zero_()
+    kn2 = np.stack([k[0, 0], k[1, 101], k[2, 64]])[:, None]
+    vn2 = np.stack([v[0, 0], v[1, 101], v[2, 64]])[:, None]
+    cache.append(dev(kn2), dev(vn2), dev(np.array([0, 2, 1], np.int32)), overflow=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 1
+    rows_k[2] = k[2, :65]
+    rows_v[2] = v[2, :65]
+    check_cache_state(cache, rows_k, rows_v, [128, 101, 65])
+
+
 @pytest.mark.parametrize("make", [lambda: W.int1_dense(131072), lambda: W.int4_dense(32768)],
                          ids=["int1_128k", "int4_32k"])
 def test_full_size_prefill(make):
