@@ -59,10 +59,146 @@ struct GroupQuant {
 constexpr int ARRIVE = 1 << 24;
 constexpr int LEN_MASK = ARRIVE - 1;
 
-template <int FMT, bool ONE>
+// Quantizes the complete group [g0, g0 + 64) of (sequence b, KV head g) from its
+// fp16 rows in sK / sV (all NT threads; the rows are visible to every thread).
+template <int BITS>
+__device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
+                               const uint16_t (&sK)[GS][D], const uint16_t (&sV)[GS][D],
+                               uint8_t (&sKc)[GS][D], uint8_t (&sVc)[GS][D],
+                               float (&sRed)[4][D]) {
+  const int tid = threadIdx.x, Hkv = c.num_kv_heads;
+
+  // ---- K: per channel over 64 tokens.  Thread (channel ck, half hk) scans 32 tokens.
+  const int ck = tid & (D - 1), hk = tid >> 7;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int r = 32 * hk; r < 32 * hk + 32; ++r) {
+    const float x = h2f(sK[r][ck]);
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+  sRed[2 * hk][ck] = mn;
+  sRed[2 * hk + 1][ck] = mx;
+  __syncthreads();
+  mn = fminf(sRed[0][ck], sRed[2][ck]);
+  mx = fmaxf(sRed[1][ck], sRed[3][ck]);
+  // outlier channels (INT4): scale and zero 0, hence codes 0; their values
+  // go to the fp16 outlier store below
+  const int n_out = BITS == 4 ? c.n_outlier : 0;
+  for (int j = 0; j < n_out; ++j)
+    if (c.outlier_ch[g * KVC_MAX_OUTLIERS + j] == ck) mn = mx = 0.0f;
+  float ks, kz;
+  uint16_t ks16, kz16;
+  GroupQuant<BITS>::params(mn, mx, ks, kz, ks16, kz16);
+  const int G = g0 / GS;
+  if (hk == 0) {
+    uint16_t* meta = c.k_meta + ((((int64_t)b * Hkv + g) * (c.max_tokens / GS) + G) * 2) * D;
+    meta[ck] = ks16;
+    meta[D + ck] = kz16;
+  }
+  for (int r = 32 * hk; r < 32 * hk + 32; ++r)
+    sKc[r][ck] = (uint8_t)GroupQuant<BITS>::code(h2f(sK[r][ck]), ks, kz);
+
+  // ---- outlier stores: thread (token r, entry j) writes the token's fp16
+  // values of outlier channel j (0 past the list)
+  if (n_out > 0) {
+    const int r = tid >> 2, j = tid & 3;
+    const int ch = min(max(c.outlier_ch[g * KVC_MAX_OUTLIERS + j], 0), D - 1);
+    const int64_t slot = slot_of(c, b, g, g0 + r);
+    if (slot >= 0) {
+      c.k_outlier[slot * KVC_MAX_OUTLIERS + j] = j < n_out ? sK[r][ch] : (uint16_t)0;
+      if (c.v_outlier) c.v_outlier[slot * KVC_MAX_OUTLIERS + j] = j < n_out ? sV[r][ch] : (uint16_t)0;
+    }
+  }
+
+  // ---- V: per token over each 64-channel half.  Thread (token nv, quarter qv).
+  // Isolated V outlier channels (bits of vout) stay out of the range and get code 0.
+  const int nv = tid >> 2, qv = tid & 3, jv = qv >> 1, c0 = 32 * qv;
+  uint32_t vout = 0u;
+  if (n_out > 0 && c.v_outlier)
+    for (int j = 0; j < n_out; ++j) {
+      const int ch = c.outlier_ch[g * KVC_MAX_OUTLIERS + j] - c0;
+      if (ch >= 0 && ch < 32) vout |= 1u << ch;
+    }
+  float vmn = INFINITY, vmx = -INFINITY;
+  for (int i = 0; i < 32; ++i) {
+    if ((vout >> i) & 1u) continue;
+    const float x = h2f(sV[nv][c0 + i]);
+    vmn = fminf(vmn, x);
+    vmx = fmaxf(vmx, x);
+  }
+  vmn = fminf(vmn, __shfl_xor(vmn, 1));
+  vmx = fmaxf(vmx, __shfl_xor(vmx, 1));
+  float vs, vz;
+  uint16_t vs16, vz16;
+  GroupQuant<BITS>::params(vmn, vmx, vs, vz, vs16, vz16);
+  if ((qv & 1) == 0) {
+    const int64_t slot = slot_of(c, b, g, g0 + nv);
+    if (slot >= 0) {
+      c.v_meta[slot * 4 + jv] = vs16;
+      c.v_meta[slot * 4 + 2 + jv] = vz16;
+    }
+  }
+  for (int i = 0; i < 32; ++i)
+    sVc[nv][c0 + i] = (vout >> i) & 1u ? 0 : (uint8_t)GroupQuant<BITS>::code(h2f(sV[nv][c0 + i]), vs, vz);
+  __syncthreads();
+
+  // ---- pack codes into the lane/dword tile layout
+  const int W = tid, lane = W >> 2, d = W & 3;
+  if constexpr (BITS == 4) {
+    for (int tile = 0; tile < GS / TILE; ++tile) {
+      const int64_t slot = slot_of(c, b, g, g0 + TILE * tile);
+      if (slot < 0) continue;
+      // K: lane = 16*(c/32) + n, dword d = (c%32)/8, nibble j = c%8
+      {
+        const int n = lane & 15, chunk = lane >> 4, tok = TILE * tile + n;
+        const int cb = 32 * chunk + 8 * d;
+        uint32_t u = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u |= (uint32_t)sKc[tok][cb + j] << nib_pos(j);
+        reinterpret_cast<uint32_t*>(c.k_codes + (slot / TILE) * UNIT_BYTES)[W] = u;
+      }
+      // V: lane = 16*(n/4) + c%16, dword d = (c/16)/2, nibble j = 4*((c/16)%2) + n%4
+      {
+        const int kb = lane >> 4, m = lane & 15;
+        uint32_t u = 0;
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            u |= (uint32_t)sVc[TILE * tile + 4 * kb + i][16 * (2 * d + par) + m] << nib_pos(4 * par + i);
+        reinterpret_cast<uint32_t*>(c.v_codes + (slot / TILE) * UNIT_BYTES)[W] = u;
+      }
+    }
+  } else {
+    const int64_t slot = slot_of(c, b, g, g0);
+    if (slot >= 0) {
+      // K: lane = 16*(c/32) + n%16, dword d = n/16, code k = c%32
+      {
+        const int tok = 16 * d + (lane & 15), cb = 32 * (lane >> 4);
+        uint32_t u = 0;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) u |= (uint32_t)sKc[tok][cb + k] << bit_pos(k);
+        reinterpret_cast<uint32_t*>(c.k_codes + (slot / GS) * UNIT_BYTES)[W] = u;
+      }
+      // V: lane = 16*((n%16)/4) + c%16, dword d = n/16, code k = v1_code(c/16, n%4)
+      {
+        const int kb = lane >> 4, m = lane & 15;
+        uint32_t u = 0;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            u |= (uint32_t)sVc[16 * d + 4 * kb + i][16 * ct + m] << bit_pos(v1_code(ct, i));
+        reinterpret_cast<uint32_t*>(c.v_codes + (slot / GS) * UNIT_BYTES)[W] = u;
+      }
+    }
+  }
+}
+
+template <int FMT>
 __global__ __launch_bounds__(NT) void append_groups_kernel(
     kvc_cache c, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int32_t* __restrict__ n_new, int n_new_max, int32_t* overflow) {
+    const int32_t* __restrict__ n_new, int n_new_max) {
   constexpr int BITS = FMT == KVC_FMT_INT4 ? 4 : 1;
   __shared__ __align__(16) uint16_t sK[GS][D];
   __shared__ __align__(16) uint16_t sV[GS][D];
@@ -72,35 +208,9 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
 
   const int b = blockIdx.z, g = blockIdx.y, tid = threadIdx.x;
   const int Hkv = c.num_kv_heads;
+  const int L = c.seq_lens[b];
   const int n = n_new ? n_new[b] : n_new_max;
-  int L;
-  uint4 newK, newV;   // ONE: this thread's 8 channels of the new row (threads 0..15)
-  if constexpr (ONE) {
-    __shared__ int sL;
-    if (n <= 0) return;
-    if (tid < 16) {   // the new row's address does not depend on the length
-      const int64_t off = ((int64_t)b * Hkv + g) * D + tid * 8;
-      newK = *reinterpret_cast<const uint4*>(k_new + off);
-      newV = *reinterpret_cast<const uint4*>(v_new + off);
-    }
-    if (tid == 0) {
-      const int old = atomicAdd(c.seq_lens + b, ARRIVE);
-      const int len = old & LEN_MASK;
-      const bool ok = n == 1 && len + 1 <= c.max_tokens;
-      if ((old >> 24) == Hkv - 1) {   // every workgroup of sequence b holds the length now
-        __hip_atomic_store(c.seq_lens + b, len + (ok ? 1 : 0), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        if (!ok && overflow) *overflow = 1;
-      }
-      sL = ok ? len : -1;
-    }
-    __syncthreads();
-    L = sL;
-    if (L < 0) return;
-  } else {
-    L = c.seq_lens[b];
-    if (n <= 0 || n > n_new_max || L < 0 || L + n > c.max_tokens) return;
-  }
+  if (n <= 0 || n > n_new_max || L < 0 || L + n > c.max_tokens) return;
   const int g0 = (L / GS + (int)blockIdx.x) * GS;
   if (g0 >= L + n) return;
   const int hi = min(g0 + GS, L + n);   // tokens [g0, hi) exist after the append
@@ -111,20 +221,8 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
   const bool complete = grouped(FMT) && hi == g0 + GS;
   const int r0 = complete ? 0 : lo - g0;
 
-  if constexpr (ONE) {
-    if (tid < 16) {
-      *reinterpret_cast<uint4*>(&sK[L - g0][tid * 8]) = newK;
-      *reinterpret_cast<uint4*>(&sV[L - g0][tid * 8]) = newV;
-      if (grouped(FMT) && !complete) {   // the row joins the tail (a completed group empties it)
-        const int64_t off = (((int64_t)b * Hkv + g) * GS + (L - g0)) * D + tid * 8;
-        *reinterpret_cast<uint4*>(c.k_tail + off) = newK;
-        *reinterpret_cast<uint4*>(c.v_tail + off) = newV;
-      }
-    }
-  }
   // ---- stage rows [g0 + r0, hi) in LDS: 16 threads per row, 8 halves each
-  // (ONE: only the old tail rows of a completed group; the new row is staged above)
-  for (int e = tid; e < ((ONE ? L : hi) - g0 - r0) * 16; e += NT) {
+  for (int e = tid; e < (hi - g0 - r0) * 16; e += NT) {
     const int r = r0 + (e >> 4), ch = (e & 15) * 8;
     const int t = g0 + r;
     const uint4* srcK;
@@ -184,136 +282,126 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
               __float_as_uint(m));
   }
 
-  if constexpr (!grouped(FMT)) {
-    return;
-  } else {
-    if (!complete) return;  // group not complete yet: it stays in the tail
+  if constexpr (grouped(FMT)) {
+    if (complete) quantize_group<BITS>(c, b, g, g0, sK, sV, sKc, sVc, sRed);
+  }
+}
 
-    // ---- K: per channel over 64 tokens.  Thread (channel ck, half hk) scans 32 tokens.
-    const int ck = tid & (D - 1), hk = tid >> 7;
-    float mn = INFINITY, mx = -INFINITY;
-    for (int r = 32 * hk; r < 32 * hk + 32; ++r) {
-      const float x = h2f(sK[r][ck]);
-      mn = fminf(mn, x);
-      mx = fmaxf(mx, x);
+// One-token append (a decode step) in a single launch: one workgroup per (KV
+// head g, sequence b).  Thread 0 takes the length L with an atomic add of
+// ARRIVE to seq_lens[b] (bits 24..30 count the sequence's workgroups); the
+// last of the Hkv to arrive stores L + 1 there, or L when n_new[b] is 0, or L
+// with the overflow flag when the token does not fit (or n_new[b] > 1).  Each
+// workgroup alone owns its (b, g) row of k_absmax, so max|K| is a plain
+// read-compare-store.  Every other write of the
+// token comes from registers: threads 0..15 hold 8 channels of the new K and V
+// row each (fp16 copies, E4M3 codes, tail row), threads 0..127 one K channel
+// (max|K|, channel-major copy).  Only a step that completes its group (L % 64
+// == 63) stages the 63 tail rows in LDS and quantizes; the tail is then empty,
+// so no workgroup writes it in that step.
+template <int FMT>
+__global__ __launch_bounds__(NT) void append_token_kernel(
+    kvc_cache c, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ n_new, int32_t* overflow) {
+  constexpr int BITS = FMT == KVC_FMT_INT4 ? 4 : 1;
+  __shared__ __align__(16) uint16_t sK[GS][D];
+  __shared__ __align__(16) uint16_t sV[GS][D];
+  __shared__ uint8_t sKc[GS][D];
+  __shared__ uint8_t sVc[GS][D];
+  __shared__ float sRed[4][D];
+  __shared__ int sL;
+
+  const int b = blockIdx.z, g = blockIdx.y, tid = threadIdx.x;
+  const int Hkv = c.num_kv_heads;
+  const int64_t row = ((int64_t)b * Hkv + g) * D;   // the new row in k_new / v_new
+  // Every load below is independent of the length: all of them are in flight
+  // together with the atomic (n_new[b] too: a sequence with nothing to append
+  // still counts its workgroups and gets its length stored back unchanged).
+  uint4 nk = {}, nv = {};
+  uint16_t kc = 0;
+  uint32_t kabs = 0u;   // max|K| so far of channel tid, as bits (this workgroup alone updates it)
+  if (tid < 16) {
+    nk = *reinterpret_cast<const uint4*>(k_new + row + tid * 8);
+    nv = *reinterpret_cast<const uint4*>(v_new + row + tid * 8);
+  }
+  if (tid < D) {
+    kc = k_new[row + tid];
+    if (c.k_absmax) kabs = reinterpret_cast<const uint32_t*>(c.k_absmax)[row + tid];
+  }
+  if (tid == 0) {
+    const int n = n_new ? n_new[b] : 1;
+    const int old = atomicAdd(c.seq_lens + b, ARRIVE);
+    const int len = old & LEN_MASK;
+    const bool ok = n == 1 && len + 1 <= c.max_tokens;
+    if ((old >> 24) == Hkv - 1) {   // every workgroup of sequence b holds the length now
+      __hip_atomic_store(c.seq_lens + b, len + (ok ? 1 : 0), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      if (n > 0 && !ok && overflow) *overflow = 1;
     }
-    sRed[2 * hk][ck] = mn;
-    sRed[2 * hk + 1][ck] = mx;
+    sL = ok ? len : -1;
+  }
+  __syncthreads();
+  const int L = sL;
+  if (L < 0) return;
+  const int g0 = L & ~(GS - 1), r = L - g0;
+  const bool complete = grouped(FMT) && r == GS - 1;
+
+  if (tid < 16) {
+    const int ch = tid * 8;
+    if (c.k16 || FMT == KVC_FMT_FP8) {
+      const int64_t slot = slot_of(c, b, g, L);
+      if (slot >= 0 && c.k16) {
+        *reinterpret_cast<uint4*>(c.k16 + slot * D + ch) = nk;
+        *reinterpret_cast<uint4*>(c.v16 + slot * D + ch) = nv;
+      }
+      if constexpr (FMT == KVC_FMT_FP8) {
+        if (slot >= 0) {
+          const uint32_t kw[4] = {nk.x, nk.y, nk.z, nk.w}, vw[4] = {nv.x, nv.y, nv.z, nv.w};
+          uint32_t ko[2] = {0u, 0u}, vo[2] = {0u, 0u};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            ko[j >> 2] |= fp8_encode((kw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << (8 * (j & 3));
+            vo[j >> 2] |= fp8_encode((vw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << (8 * (j & 3));
+          }
+          *reinterpret_cast<uint2*>(c.k_codes + slot * D + ch) = uint2{ko[0], ko[1]};
+          *reinterpret_cast<uint2*>(c.v_codes + slot * D + ch) = uint2{vo[0], vo[1]};
+        }
+      }
+    }
+    if constexpr (grouped(FMT)) {
+      if (complete) {
+        *reinterpret_cast<uint4*>(&sK[r][ch]) = nk;
+        *reinterpret_cast<uint4*>(&sV[r][ch]) = nv;
+      } else {   // the row joins the tail
+        const int64_t off = (((int64_t)b * Hkv + g) * GS + r) * D + ch;
+        *reinterpret_cast<uint4*>(c.k_tail + off) = nk;
+        *reinterpret_cast<uint4*>(c.v_tail + off) = nv;
+      }
+    }
+  }
+  if (tid < D) {
+    if (c.kT) {
+      uint16_t x = kc;
+      if constexpr (FMT == KVC_FMT_FP8)   // the decoded value (exact in fp16)
+        x = f2h(h2f((uint16_t)fp8_h16_over256(fp8_encode(x))) * 256.0f);
+      c.kT[(row + tid) * c.max_tokens + L] = x;
+    }
+    // the same order as the unsigned atomic max of the multi-token path
+    const uint32_t a = __float_as_uint(fabsf(h2f(kc)));
+    if (c.k_absmax && a > kabs) reinterpret_cast<uint32_t*>(c.k_absmax)[row + tid] = a;
+  }
+
+  if constexpr (grouped(FMT)) {
+    if (!complete) return;
+    // ---- stage the 63 old rows from the tail: 16 threads per row, 8 halves each
+    for (int e = tid; e < r * 16; e += NT) {
+      const int rr = e >> 4, ch = (e & 15) * 8;
+      const int64_t off = (((int64_t)b * Hkv + g) * GS + rr) * D + ch;
+      *reinterpret_cast<uint4*>(&sK[rr][ch]) = *reinterpret_cast<const uint4*>(c.k_tail + off);
+      *reinterpret_cast<uint4*>(&sV[rr][ch]) = *reinterpret_cast<const uint4*>(c.v_tail + off);
+    }
     __syncthreads();
-    mn = fminf(sRed[0][ck], sRed[2][ck]);
-    mx = fmaxf(sRed[1][ck], sRed[3][ck]);
-    // outlier channels (INT4): scale and zero 0, hence codes 0; their values
-    // go to the fp16 outlier store below
-    const int n_out = BITS == 4 ? c.n_outlier : 0;
-    for (int j = 0; j < n_out; ++j)
-      if (c.outlier_ch[g * KVC_MAX_OUTLIERS + j] == ck) mn = mx = 0.0f;
-    float ks, kz;
-    uint16_t ks16, kz16;
-    GroupQuant<BITS>::params(mn, mx, ks, kz, ks16, kz16);
-    const int G = g0 / GS;
-    if (hk == 0) {
-      uint16_t* meta = c.k_meta + ((((int64_t)b * Hkv + g) * (c.max_tokens / GS) + G) * 2) * D;
-      meta[ck] = ks16;
-      meta[D + ck] = kz16;
-    }
-    for (int r = 32 * hk; r < 32 * hk + 32; ++r)
-      sKc[r][ck] = (uint8_t)GroupQuant<BITS>::code(h2f(sK[r][ck]), ks, kz);
-
-    // ---- outlier stores: thread (token r, entry j) writes the token's fp16
-    // values of outlier channel j (0 past the list)
-    if (n_out > 0) {
-      const int r = tid >> 2, j = tid & 3;
-      const int ch = min(max(c.outlier_ch[g * KVC_MAX_OUTLIERS + j], 0), D - 1);
-      const int64_t slot = slot_of(c, b, g, g0 + r);
-      if (slot >= 0) {
-        c.k_outlier[slot * KVC_MAX_OUTLIERS + j] = j < n_out ? sK[r][ch] : (uint16_t)0;
-        if (c.v_outlier) c.v_outlier[slot * KVC_MAX_OUTLIERS + j] = j < n_out ? sV[r][ch] : (uint16_t)0;
-      }
-    }
-
-    // ---- V: per token over each 64-channel half.  Thread (token nv, quarter qv).
-    // Isolated V outlier channels (bits of vout) stay out of the range and get code 0.
-    const int nv = tid >> 2, qv = tid & 3, jv = qv >> 1, c0 = 32 * qv;
-    uint32_t vout = 0u;
-    if (n_out > 0 && c.v_outlier)
-      for (int j = 0; j < n_out; ++j) {
-        const int ch = c.outlier_ch[g * KVC_MAX_OUTLIERS + j] - c0;
-        if (ch >= 0 && ch < 32) vout |= 1u << ch;
-      }
-    float vmn = INFINITY, vmx = -INFINITY;
-    for (int i = 0; i < 32; ++i) {
-      if ((vout >> i) & 1u) continue;
-      const float x = h2f(sV[nv][c0 + i]);
-      vmn = fminf(vmn, x);
-      vmx = fmaxf(vmx, x);
-    }
-    vmn = fminf(vmn, __shfl_xor(vmn, 1));
-    vmx = fmaxf(vmx, __shfl_xor(vmx, 1));
-    float vs, vz;
-    uint16_t vs16, vz16;
-    GroupQuant<BITS>::params(vmn, vmx, vs, vz, vs16, vz16);
-    if ((qv & 1) == 0) {
-      const int64_t slot = slot_of(c, b, g, g0 + nv);
-      if (slot >= 0) {
-        c.v_meta[slot * 4 + jv] = vs16;
-        c.v_meta[slot * 4 + 2 + jv] = vz16;
-      }
-    }
-    for (int i = 0; i < 32; ++i)
-      sVc[nv][c0 + i] = (vout >> i) & 1u ? 0 : (uint8_t)GroupQuant<BITS>::code(h2f(sV[nv][c0 + i]), vs, vz);
-    __syncthreads();
-
-    // ---- pack codes into the lane/dword tile layout
-    const int W = tid, lane = W >> 2, d = W & 3;
-    if constexpr (BITS == 4) {
-      for (int tile = 0; tile < GS / TILE; ++tile) {
-        const int64_t slot = slot_of(c, b, g, g0 + TILE * tile);
-        if (slot < 0) continue;
-        // K: lane = 16*(c/32) + n, dword d = (c%32)/8, nibble j = c%8
-        {
-          const int n = lane & 15, chunk = lane >> 4, tok = TILE * tile + n;
-          const int cb = 32 * chunk + 8 * d;
-          uint32_t u = 0;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) u |= (uint32_t)sKc[tok][cb + j] << nib_pos(j);
-          reinterpret_cast<uint32_t*>(c.k_codes + (slot / TILE) * UNIT_BYTES)[W] = u;
-        }
-        // V: lane = 16*(n/4) + c%16, dword d = (c/16)/2, nibble j = 4*((c/16)%2) + n%4
-        {
-          const int kb = lane >> 4, m = lane & 15;
-          uint32_t u = 0;
-#pragma unroll
-          for (int par = 0; par < 2; ++par)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              u |= (uint32_t)sVc[TILE * tile + 4 * kb + i][16 * (2 * d + par) + m] << nib_pos(4 * par + i);
-          reinterpret_cast<uint32_t*>(c.v_codes + (slot / TILE) * UNIT_BYTES)[W] = u;
-        }
-      }
-    } else {
-      const int64_t slot = slot_of(c, b, g, g0);
-      if (slot >= 0) {
-        // K: lane = 16*(c/32) + n%16, dword d = n/16, code k = c%32
-        {
-          const int tok = 16 * d + (lane & 15), cb = 32 * (lane >> 4);
-          uint32_t u = 0;
-#pragma unroll
-          for (int k = 0; k < 32; ++k) u |= (uint32_t)sKc[tok][cb + k] << bit_pos(k);
-          reinterpret_cast<uint32_t*>(c.k_codes + (slot / GS) * UNIT_BYTES)[W] = u;
-        }
-        // V: lane = 16*((n%16)/4) + c%16, dword d = n/16, code k = v1_code(c/16, n%4)
-        {
-          const int kb = lane >> 4, m = lane & 15;
-          uint32_t u = 0;
-#pragma unroll
-          for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              u |= (uint32_t)sVc[16 * d + 4 * kb + i][16 * ct + m] << bit_pos(v1_code(ct, i));
-          reinterpret_cast<uint32_t*>(c.v_codes + (slot / GS) * UNIT_BYTES)[W] = u;
-        }
-      }
-    }
+    quantize_group<BITS>(c, b, g, g0, sK, sV, sKc, sVc, sRed);
   }
 }
 
@@ -362,10 +450,9 @@ hipError_t launch_append(const kvc_cache& c, const uint16_t* k_new, const uint16
   auto run = [&](auto fmt) {
     constexpr int F = decltype(fmt)::value;
     if (one)
-      append_groups_kernel<F, true><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, 1, overflow);
+      append_token_kernel<F><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, overflow);
     else
-      append_groups_kernel<F, false><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max,
-                                                         overflow);
+      append_groups_kernel<F><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max);
   };
   switch (c.format) {
     case KVC_FMT_INT4: run(std::integral_constant<int, KVC_FMT_INT4>{}); break;
