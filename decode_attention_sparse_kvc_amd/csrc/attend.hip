@@ -707,12 +707,10 @@ template <int FMT, bool DENSE, bool LOGITS, bool PACK, bool TILED, bool OUTL = f
 __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, int split, int lane, int w,
                            float* sO, float* sML, uint16_t* sKm, uint16_t* sVm, uint16_t* sVo) {
   const kvc_cache& c = a.c;
-  const int n = max(c.seq_lens[b], 0);
   // blocks mode walks the plan's list of groups (sink groups, kept blocks,
   // window groups); the other modes walk every complete group
   const bool listed = !DENSE && a.mode == KVC_ATTEND_BLOCKS;
   const int64_t pair = (int64_t)b * c.num_kv_heads + g;
-  const int ngroups = listed ? *scalar_ptr(a.gcount + pair) : n >> 6;
   const int G = a.G;
   const int col = lane & 15, kb = lane >> 4, head = col & 7;
   const bool hv = head < G;
@@ -720,27 +718,39 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
   // the waves of (b, g) take groups round-robin, so at any moment they read
   // one window of adjacent groups (long runs for the DRAM pages)
   constexpr int NW = waves_per_wg(FMT);
+  const int ga = split * NW + w;
   // dense: all of the pair's waves share its groups; drop / keep (ragged
   // batches): a pair uses only the waves its length needs at the planned
-  // groups per wave, so short sequences free their workgroups at once
-  int W = a.s_q * NW;
-  if (!DENSE) W = min(W, NW * ((ngroups + NW * a.gpw - 1) / (NW * a.gpw)));
-  const int ga = split * NW + w;
-  int nmine = ga < ngroups && ga < W ? (ngroups - 1 - ga) / W + 1 : 0;
-  if (listed) nmine = min(nmine, 64);   // (the planner keeps it there)
+  // groups per wave, so short sequences free their workgroups at once.
+  // Dense walks wait for the length only after issuing their first two
+  // groups (ga and ga + W whatever the length; a group below the capacity
+  // lies in the allocation, and one past the length is never used), so its
+  // latency overlaps theirs; the length load itself goes out first, ahead of
+  // the groups' bytes.
+  int n = c.seq_lens[b], ngroups = 0, W = a.s_q * NW, nmine = 0;
+  int vlist = 0;
+  if constexpr (!DENSE) {
+    n = max(n, 0);
+    ngroups = listed ? *scalar_ptr(a.gcount + pair) : n >> 6;
+    W = min(W, NW * ((ngroups + NW * a.gpw - 1) / (NW * a.gpw)));
+    nmine = ga < ngroups && ga < W ? (ngroups - 1 - ga) / W + 1 : 0;
+    if (listed) nmine = min(nmine, 64);   // (the planner keeps it there)
+    // (blocks mode: the k-th entry comes from lane k of vlist, one load per
+    // wave; the planner keeps nmine <= 64)
+    if (listed && lane < nmine) vlist = a.glist[pair * (c.max_tokens / GS) + ga + lane * W];
+  }
   // k-th group of this wave; past the last one the loads of the last repeat
   // with empty ranges (no memory traffic), so every load is unconditional and
   // the compiler's wait before a group counts exactly (a wave with no group
   // names group 0, whose selection words are in range)
-  // (blocks mode: the k-th entry comes from lane k of vlist, one load per wave;
-  // the planner keeps nmine <= 64)
-  int vlist = 0;
-  if (listed && lane < nmine) vlist = a.glist[pair * (c.max_tokens / GS) + ga + lane * W];
   auto gid = [&](int k) {
     if (nmine <= 0) return 0;
     const int kk = min(k, nmine - 1);
     return listed ? __builtin_amdgcn_readlane(vlist, kk) : ga + kk * W;
   };
+  const int cap = c.max_tokens >> 6;
+  const int gi0 = DENSE ? ga : gid(0), gi1 = DENSE ? ga + W : gid(1);
+  const bool live0 = DENSE ? gi0 < cap : nmine > 0, live1 = DENSE ? gi1 < cap : nmine > 1;
 
   // page-table words of the first groups, then q of this lane's head
   // (channels [32kb, 32kb + 32) as fp16 pairs, zero off-head), then the first
@@ -748,7 +758,7 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
   // issued first so that waiting for them leaves q in flight
   const Buf rtab = make_buf(c.block_table + (int64_t)b * c.max_pages,
                             c.page_size > 0 ? (uint32_t)c.max_pages * 4u : 0u);
-  uint4 t0w = group_table(a, rtab, gid(0)), t1w = group_table(a, rtab, gid(1));
+  uint4 t0w = group_table(a, rtab, gi0), t1w = group_table(a, rtab, gi1);
   uint4 raw[4] = {};
   if (hv) {
     const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + head) * D + 32 * kb);
@@ -768,9 +778,15 @@ __device__ __forceinline__ void quant_role(const AttendArgs& a, int b, int g, in
     }
   }
   GroupData<FMT, TILED, OUTL> d0, d1;
-  load_group<FMT, DENSE, TILED, OUTL>(a, b, g, gid(0), nmine > 0, t0w, lane, d0);
+  load_group<FMT, DENSE, TILED, OUTL>(a, b, g, gi0, live0, t0w, lane, d0);
+  load_group<FMT, DENSE, TILED, OUTL>(a, b, g, gi1, live1, t1w, lane, d1);
+  if constexpr (DENSE) {
+    asm volatile("" : "+v"(n) :: "memory");   // the length is waited for only here
+    n = max(__builtin_amdgcn_readfirstlane(n), 0);
+    ngroups = n >> 6;
+    nmine = ga < ngroups ? (ngroups - 1 - ga) / W + 1 : 0;
+  }
   t0w = group_table(a, rtab, gid(2));
-  load_group<FMT, DENSE, TILED, OUTL>(a, b, g, gid(1), nmine > 1, t1w, lane, d1);
   t1w = group_table(a, rtab, gid(3));
   // q is in registers before the group loop (so no wait inside the loop, where
   // the next group's loads are in flight, is spent on it); the memory clobber
