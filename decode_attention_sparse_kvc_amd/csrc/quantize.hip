@@ -46,11 +46,10 @@ struct GroupQuant {
     z = h2f(z16);
   }
   __device__ static inline uint32_t code(float x, float s, float z) {
-    if (s == 0.0f) return 0u;
     constexpr float top = float((1 << BITS) - 1);
     float t = rintf(__fdiv_rn(__fsub_rn(x, z), s));
-    t = fminf(fmaxf(t, 0.0f), top);
-    return (uint32_t)t;
+    t = fminf(fmaxf(t, 0.0f), top);   // (a NaN quotient, s == 0, becomes 0 below)
+    return s == 0.0f ? 0u : (uint32_t)t;
   }
 };
 
@@ -221,23 +220,31 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
   const bool complete = grouped(FMT) && hi == g0 + GS;
   const int r0 = complete ? 0 : lo - g0;
 
-  // ---- stage rows [g0 + r0, hi) in LDS: 16 threads per row, 8 halves each
-  for (int e = tid; e < (hi - g0 - r0) * 16; e += NT) {
+  // ---- stage rows [g0 + r0, hi) in LDS: 16 threads per row, 8 halves each.
+  // Every thread issues all of its (up to 4 + 4) row loads before its first
+  // LDS store, with no branch between them: an element past the rows repeats
+  // the last one (the same value loaded and stored to the same place again).
+  constexpr int PER = GS * 16 / NT;
+  const int nst = (hi - g0 - r0) * 16;
+  uint4 ks[PER], vs[PER];
+  int es[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = es[i] = min(tid + i * NT, nst - 1);
     const int r = r0 + (e >> 4), ch = (e & 15) * 8;
     const int t = g0 + r;
-    const uint4* srcK;
-    const uint4* srcV;
-    if (t < L) {  // old row, still in the tail
-      const int64_t off = (((int64_t)b * Hkv + g) * GS + r) * D + ch;
-      srcK = reinterpret_cast<const uint4*>(c.k_tail + off);
-      srcV = reinterpret_cast<const uint4*>(c.v_tail + off);
-    } else {
-      const int64_t off = (((int64_t)b * n_new_max + (t - L)) * Hkv + g) * D + ch;
-      srcK = reinterpret_cast<const uint4*>(k_new + off);
-      srcV = reinterpret_cast<const uint4*>(v_new + off);
-    }
-    *reinterpret_cast<uint4*>(&sK[r][ch]) = *srcK;
-    *reinterpret_cast<uint4*>(&sV[r][ch]) = *srcV;
+    const int64_t offT = (((int64_t)b * Hkv + g) * GS + r) * D + ch;   // old row, in the tail
+    const int64_t offN = (((int64_t)b * n_new_max + max(t - L, 0)) * Hkv + g) * D + ch;
+    const uint16_t* srcK = t < L ? c.k_tail + offT : k_new + offN;
+    const uint16_t* srcV = t < L ? c.v_tail + offT : v_new + offN;
+    ks[i] = *reinterpret_cast<const uint4*>(srcK);
+    vs[i] = *reinterpret_cast<const uint4*>(srcV);
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int r = r0 + (es[i] >> 4), ch = (es[i] & 15) * 8;
+    *reinterpret_cast<uint4*>(&sK[r][ch]) = ks[i];
+    *reinterpret_cast<uint4*>(&sV[r][ch]) = vs[i];
   }
   __syncthreads();
 
@@ -277,6 +284,7 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
   }
   if (c.k_absmax && tid < D) {
     float m = 0.0f;
+#pragma unroll 16
     for (int r = lo - g0; r < hi - g0; ++r) m = fmaxf(m, fabsf(h2f(sK[r][tid])));
     atomicMax(reinterpret_cast<unsigned int*>(c.k_absmax) + ((int64_t)b * Hkv + g) * D + tid,
               __float_as_uint(m));
