@@ -45,10 +45,19 @@ struct GroupQuant {
     s = h2f(s16);
     z = h2f(z16);
   }
-  __device__ static inline uint32_t code(float x, float s, float z) {
+  // code = rint(fl((x - z) / s)) clamped, with r = fl(1 / s).  a = fl((x - z) * r)
+  // lies within 2^-17.9 of fl((x - z) / s) while a < 17 (two roundings of
+  // 2^-24 each on a quotient below 17, plus the quotient's own rounding), and
+  // any larger a clamps to the top code either way; so rint(a) is the code
+  // unless a lies within 2^-17 of a half-integer, where the division decides
+  // (rare: the branch is skipped by every wave whose lanes all avoid it).
+  __device__ static inline uint32_t code(float x, float s, float z, float r) {
     constexpr float top = float((1 << BITS) - 1);
-    float t = rintf(__fdiv_rn(__fsub_rn(x, z), s));
-    t = fminf(fmaxf(t, 0.0f), top);   // (a NaN quotient, s == 0, becomes 0 below)
+    const float d = __fsub_rn(x, z);
+    const float a = __fmul_rn(d, r);
+    float t = rintf(a);
+    if (fabsf(__fsub_rn(__fsub_rn(a, floorf(a)), 0.5f)) <= 0x1p-17f) t = rintf(__fdiv_rn(d, s));
+    t = fminf(fmaxf(t, 0.0f), top);   // (s == 0 becomes 0 below)
     return s == 0.0f ? 0u : (uint32_t)t;
   }
 };
@@ -60,29 +69,30 @@ constexpr int LEN_MASK = ARRIVE - 1;
 
 // Quantizes the complete group [g0, g0 + 64) of (sequence b, KV head g) from its
 // fp16 rows in sK / sV (all NT threads; the rows are visible to every thread).
+// Every thread first takes the values it quantizes into registers; after a
+// barrier the one-byte codes overwrite the rows' first 8 KB (sKc / sVc), so
+// the group needs no LDS beyond its 32 KB of rows.
 template <int BITS>
 __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
-                               const uint16_t (&sK)[GS][D], const uint16_t (&sV)[GS][D],
-                               uint8_t (&sKc)[GS][D], uint8_t (&sVc)[GS][D],
-                               float (&sRed)[4][D]) {
+                               uint16_t (&sK)[GS][D], uint16_t (&sV)[GS][D]) {
   const int tid = threadIdx.x, Hkv = c.num_kv_heads;
+  const int n_out = BITS == 4 ? c.n_outlier : 0;
 
-  // ---- K: per channel over 64 tokens.  Thread (channel ck, half hk) scans 32 tokens.
-  const int ck = tid & (D - 1), hk = tid >> 7;
+  // ---- K: per channel over 64 tokens.  Threads 2ck and 2ck + 1 hold rows
+  // [0, 32) and [32, 64) of channel ck and combine their extremes.
+  const int ck = tid >> 1, hk = tid & 1;
+  float kx[32];
   float mn = INFINITY, mx = -INFINITY;
-  for (int r = 32 * hk; r < 32 * hk + 32; ++r) {
-    const float x = h2f(sK[r][ck]);
-    mn = fminf(mn, x);
-    mx = fmaxf(mx, x);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    kx[i] = h2f(sK[32 * hk + i][ck]);
+    mn = fminf(mn, kx[i]);
+    mx = fmaxf(mx, kx[i]);
   }
-  sRed[2 * hk][ck] = mn;
-  sRed[2 * hk + 1][ck] = mx;
-  __syncthreads();
-  mn = fminf(sRed[0][ck], sRed[2][ck]);
-  mx = fmaxf(sRed[1][ck], sRed[3][ck]);
+  mn = fminf(mn, __shfl_xor(mn, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 1));
   // outlier channels (INT4): scale and zero 0, hence codes 0; their values
   // go to the fp16 outlier store below
-  const int n_out = BITS == 4 ? c.n_outlier : 0;
   for (int j = 0; j < n_out; ++j)
     if (c.outlier_ch[g * KVC_MAX_OUTLIERS + j] == ck) mn = mx = 0.0f;
   float ks, kz;
@@ -94,8 +104,10 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
     meta[ck] = ks16;
     meta[D + ck] = kz16;
   }
-  for (int r = 32 * hk; r < 32 * hk + 32; ++r)
-    sKc[r][ck] = (uint8_t)GroupQuant<BITS>::code(h2f(sK[r][ck]), ks, kz);
+  const float kr = __fdiv_rn(1.0f, ks);
+  uint32_t kq[8] = {};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) kq[i >> 2] |= GroupQuant<BITS>::code(kx[i], ks, kz, kr) << (8 * (i & 3));
 
   // ---- outlier stores: thread (token r, entry j) writes the token's fp16
   // values of outlier channel j (0 past the list)
@@ -109,8 +121,9 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
     }
   }
 
-  // ---- V: per token over each 64-channel half.  Thread (token nv, quarter qv).
-  // Isolated V outlier channels (bits of vout) stay out of the range and get code 0.
+  // ---- V: per token over each 64-channel half.  Thread (token nv, quarter qv)
+  // reads its 32 values with four 16-byte LDS reads.  Isolated V outlier
+  // channels (bits of vout) stay out of the range and get code 0.
   const int nv = tid >> 2, qv = tid & 3, jv = qv >> 1, c0 = 32 * qv;
   uint32_t vout = 0u;
   if (n_out > 0 && c.v_outlier)
@@ -118,12 +131,22 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
       const int ch = c.outlier_ch[g * KVC_MAX_OUTLIERS + j] - c0;
       if (ch >= 0 && ch < 32) vout |= 1u << ch;
     }
+  uint32_t vw[16];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint4 u = *reinterpret_cast<const uint4*>(&sV[nv][c0 + 8 * k]);
+    vw[4 * k] = u.x;
+    vw[4 * k + 1] = u.y;
+    vw[4 * k + 2] = u.z;
+    vw[4 * k + 3] = u.w;
+  }
+  auto vval = [&](int i) { return h2f((uint16_t)(vw[i >> 1] >> (16 * (i & 1)))); };
   float vmn = INFINITY, vmx = -INFINITY;
+#pragma unroll
   for (int i = 0; i < 32; ++i) {
-    if ((vout >> i) & 1u) continue;
-    const float x = h2f(sV[nv][c0 + i]);
-    vmn = fminf(vmn, x);
-    vmx = fmaxf(vmx, x);
+    const bool out = (vout >> i) & 1u;
+    vmn = out ? vmn : fminf(vmn, vval(i));
+    vmx = out ? vmx : fmaxf(vmx, vval(i));
   }
   vmn = fminf(vmn, __shfl_xor(vmn, 1));
   vmx = fmaxf(vmx, __shfl_xor(vmx, 1));
@@ -137,8 +160,20 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
       c.v_meta[slot * 4 + 2 + jv] = vz16;
     }
   }
+  const float vr = __fdiv_rn(1.0f, vs);
+  uint32_t vq[8] = {};
+#pragma unroll
   for (int i = 0; i < 32; ++i)
-    sVc[nv][c0 + i] = (vout >> i) & 1u ? 0 : (uint8_t)GroupQuant<BITS>::code(h2f(sV[nv][c0 + i]), vs, vz);
+    vq[i >> 2] |= ((vout >> i) & 1u ? 0u : GroupQuant<BITS>::code(vval(i), vs, vz, vr)) << (8 * (i & 3));
+
+  // ---- codes over the rows: every row value has been read above
+  __syncthreads();
+  uint8_t (&sKc)[GS][D] = *reinterpret_cast<uint8_t (*)[GS][D]>(&sK[0][0]);
+  uint8_t (&sVc)[GS][D] = *reinterpret_cast<uint8_t (*)[GS][D]>(&sV[0][0]);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) sKc[32 * hk + i][ck] = (uint8_t)(kq[i >> 2] >> (8 * (i & 3)));
+  *reinterpret_cast<uint4*>(&sVc[nv][c0]) = uint4{vq[0], vq[1], vq[2], vq[3]};
+  *reinterpret_cast<uint4*>(&sVc[nv][c0 + 16]) = uint4{vq[4], vq[5], vq[6], vq[7]};
   __syncthreads();
 
   // ---- pack codes into the lane/dword tile layout
@@ -201,16 +236,16 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
   constexpr int BITS = FMT == KVC_FMT_INT4 ? 4 : 1;
   __shared__ __align__(16) uint16_t sK[GS][D];
   __shared__ __align__(16) uint16_t sV[GS][D];
-  __shared__ uint8_t sKc[GS][D];
-  __shared__ uint8_t sVc[GS][D];
-  __shared__ float sRed[4][D];
 
-  const int b = blockIdx.z, g = blockIdx.y, tid = threadIdx.x;
+  // x = (group, KV head), the head fastest: the Hkv workgroups of one group
+  // run together and read adjacent 256-byte pieces of the same new rows
   const int Hkv = c.num_kv_heads;
+  const int b = blockIdx.z, gx = (int)blockIdx.x / Hkv, g = (int)blockIdx.x - gx * Hkv;
+  const int tid = threadIdx.x;
   const int L = c.seq_lens[b];
   const int n = n_new ? n_new[b] : n_new_max;
   if (n <= 0 || n > n_new_max || L < 0 || L + n > c.max_tokens) return;
-  const int g0 = (L / GS + (int)blockIdx.x) * GS;
+  const int g0 = (L / GS + gx) * GS;
   if (g0 >= L + n) return;
   const int hi = min(g0 + GS, L + n);   // tokens [g0, hi) exist after the append
   const int lo = max(g0, L);            // tokens [lo, hi) are new
@@ -291,7 +326,7 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
   }
 
   if constexpr (grouped(FMT)) {
-    if (complete) quantize_group<BITS>(c, b, g, g0, sK, sV, sKc, sVc, sRed);
+    if (complete) quantize_group<BITS>(c, b, g, g0, sK, sV);
   }
 }
 
@@ -314,9 +349,6 @@ __global__ __launch_bounds__(NT) void append_token_kernel(
   constexpr int BITS = FMT == KVC_FMT_INT4 ? 4 : 1;
   __shared__ __align__(16) uint16_t sK[GS][D];
   __shared__ __align__(16) uint16_t sV[GS][D];
-  __shared__ uint8_t sKc[GS][D];
-  __shared__ uint8_t sVc[GS][D];
-  __shared__ float sRed[4][D];
   __shared__ int sL;
 
   const int b = blockIdx.z, g = blockIdx.y, tid = threadIdx.x;
@@ -409,7 +441,7 @@ __global__ __launch_bounds__(NT) void append_token_kernel(
       *reinterpret_cast<uint4*>(&sV[rr][ch]) = *reinterpret_cast<const uint4*>(c.v_tail + off);
     }
     __syncthreads();
-    quantize_group<BITS>(c, b, g, g0, sK, sV, sKc, sVc, sRed);
+    quantize_group<BITS>(c, b, g, g0, sK, sV);
   }
 }
 
@@ -454,11 +486,12 @@ hipError_t launch_append(const kvc_cache& c, const uint16_t* k_new, const uint16
   // one token: a single launch (the arrival count needs lengths below 2^24
   // and at most 127 KV heads)
   const bool one = n_new_max == 1 && c.max_tokens < ARRIVE && c.num_kv_heads <= 127;
-  const dim3 grid(one ? 1 : (n_new_max + GS - 1) / GS + 1, c.num_kv_heads, c.batch);
+  const dim3 grid_one(1, c.num_kv_heads, c.batch);
+  const dim3 grid((uint32_t)((n_new_max + GS - 1) / GS + 1) * (uint32_t)c.num_kv_heads, 1, c.batch);
   auto run = [&](auto fmt) {
     constexpr int F = decltype(fmt)::value;
     if (one)
-      append_token_kernel<F><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, overflow);
+      append_token_kernel<F><<<grid_one, NT, 0, s>>>(c, k_new, v_new, n_new, overflow);
     else
       append_groups_kernel<F><<<grid, NT, 0, s>>>(c, k_new, v_new, n_new, n_new_max);
   };

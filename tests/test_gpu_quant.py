@@ -203,6 +203,37 @@ def test_full_size_prefill(make):
     check_cache_state(cache, w.k, w.v, w.seq_lens)
 
 
+@pytest.mark.parametrize("fmt", ["int4", "int1"])
+def test_code_rounding_at_half_integers(fmt):
+    """Values whose quotient (x - z) / s is exactly a half-integer, or one fp16 step
+    off it, for scales with inexact reciprocals (3, 7, 0.75, 5/16, ...): the
+    kernel's codes (a reciprocal product, the division near half-integers) equal
+    the oracle's correctly rounded quotient, ties to even, for K channels and V rows."""
+    top = 15 if fmt == "int4" else 1
+    rng = np.random.default_rng(50)
+    hkv = 2
+    k = rng.standard_normal((1, 128, hkv, 128)).astype(np.float16)
+    v = rng.standard_normal((1, 128, hkv, 128)).astype(np.float16)
+    scales = [1.0, 3.0, 7.0, 0.75, 0.3125, 5.0, 6.0, 0.1875, 11.0, 13.0, 0.0390625]
+    for ci, sc in enumerate(scales):
+        for grp in range(2):
+            z = float(np.float16(-2.0 * (ci + 1) + grp))
+            col = [z, z + top * sc]
+            for kk in range(top):
+                h = np.float16(z + (kk + 0.5) * sc)
+                col += [float(h), float(np.nextafter(h, np.float16(np.inf))),
+                        float(np.nextafter(h, np.float16(-np.inf)))]
+            col = np.resize(np.array(col, np.float32), 64).astype(np.float16)
+            for g in range(hkv):
+                k[0, 64 * grp:64 * grp + 64, g, ci] = col             # a K channel over the group
+                v[0, 64 * grp + ci, g, :64] = col                     # a V row, low half
+                v[0, 64 * grp + ci, g, 64:] = col[::-1]               # and high half
+    cache = KvcCache(fmt, 1, hkv, 192)
+    cache.append(dev(k), dev(v))
+    torch.cuda.synchronize()
+    check_cache_state(cache, k, v, [128])
+
+
 def test_one_bit_scale_saturates():
     """1-bit groups whose range exceeds 65504 (K per channel and V per token) store the
     saturated scale 65504 as the oracle does, and attention over them stays finite."""
