@@ -975,10 +975,25 @@ struct RowTile {
 // with three or four: 72.8 / 75.3 us against 70.8 us at 128K).
 constexpr int ROWS_AHEAD = 2;
 
-// V tile staging in LDS: row t's 16-byte chunk j lives at chunk j ^ (t >> 2)
-// of the row, so the four 16-lane groups of a transposed read (rows 4 apart)
-// hit different banks.
-__device__ inline int vt_off(int t, int chunk) { return t * D + ((chunk ^ (t >> 2)) << 3); }
+// V tile staging in LDS: row t's 16-byte chunk j lives at chunk j ^ 2(t & 7)
+// of the row.  Chunk pairs (2m, 2m + 1) stay adjacent, and the 32-byte block m
+// of rows t and t' (t & 7 != t' & 7) lands on different banks, so a transposed
+// read (one 32-byte block of each of 16 rows) runs in two conflict-free passes.
+__device__ inline int vt_off(int t, int chunk) { return t * D + ((chunk ^ (2 * (t & 7))) << 3); }
+
+// A = V^T operand of a 16x16x16 P.V product from the staged tile with one
+// LDS transpose read (ds_read_b64_tr_b16).  In each 16-lane group kb, lane s
+// addresses row 4kb + s/4, channels 16ct + 4(s%4) .. +3; the read hands lane
+// col element col%4 of the words addressed by lanes col/4 + 4j (j = 0..3):
+// channel 16ct + col of row 4kb + j, in element j.
+typedef short s4v __attribute__((ext_vector_type(4)));
+__device__ inline h4 vt_read_tr(const uint16_t* vt, int ct, int col, int kb) {
+  const int t = 4 * kb + (col >> 2);
+  const uint16_t* p = vt + vt_off(t, 2 * ct + ((col & 3) >> 1)) + 4 * (col & 1);
+  const s4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4v*)(p));
+  return bc<h4>(r);
+}
 
 // fp16-rows role: positions [pa, pb) of (b, g) in 16-row tiles, software
 // pipelined -- the plan entries of tile i + 2 and the rows of tile i + 1 are
@@ -1181,13 +1196,8 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
       wave_sync_lds();
       // O^T += V^T P^T: A = V^T (row = channel 16ct + col, k = rows 4kb..4kb+3)
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const int chunk = 2 * ct + (col >> 3);
-        h4 va;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) va[j] = bc<_Float16>(vt[vt_off(4 * kb + j, chunk) + (col & 7)]);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pt, acc[ct], 0, 0, 0);
-      }
+      for (int ct = 0; ct < 8; ++ct)
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(vt_read_tr(vt, ct, col, kb), pt, acc[ct], 0, 0, 0);
     };
 
     // ROWS_AHEAD tiles in registers: while tile i computes, tiles i + 1 ..
