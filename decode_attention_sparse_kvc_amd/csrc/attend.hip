@@ -962,10 +962,12 @@ __device__ inline void fp8_row_decode(uint4 r0, uint4 r1, uint4* out) {
   }
 }
 
-// One 16-row tile in registers: lane (row, kb) holds channels [32kb, 32kb+32)
-// of its row, of K (the matrix-core A operand of S = K q) and of V (staged
+// One 16-row tile in registers: lane (row, kb) holds 32 channels of its row,
+// word k channels 32k + 8kb .. +7 (so each load reads 64 contiguous bytes of
+// every row), of K (the matrix-core A operand of S = K q) and of V (staged
 // through LDS into the transposed A operand of O^T = V^T P^T).
-// (FP8 rows are half as wide: two 16-byte words of codes each.)
+// (FP8 rows are half as wide: two 16-byte words of codes each, channels
+// [32kb, 32kb + 32) in the decoder's order.)
 template <int FMT>
 struct RowTile {
   uint4 k[FMT == KVC_FMT_FP8 ? 2 : 4];
@@ -1039,9 +1041,13 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
     {
       uint4 raw[4] = {};
       if (hv) {
-        const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)b * a.hq + g * G + col) * D + 32 * kb);
+        // fp16 rows: register k holds channels 32k + 8kb .. +7 (so a row's four
+        // lanes read 64 contiguous bytes per load); FP8 rows: channels
+        // 32kb + 8k .. +7, the decoder's order
+        const uint16_t* qh = a.q + ((int64_t)b * a.hq + g * G + col) * D;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) raw[k] = qp[k];
+        for (int k = 0; k < 4; ++k)
+          raw[k] = *reinterpret_cast<const uint4*>(qh + (FP8 ? 32 * kb + 8 * k : 32 * k + 8 * kb));
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) qb[k] = bc<h8>(raw[k]);
@@ -1123,13 +1129,14 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
         d.v[0] = vq[0];
         d.v[1] = vq[1];
       } else {
-        const int64_t off = (int64_t)e.y * D + 32 * kb;
-        const uint4* kq = reinterpret_cast<const uint4*>(on ? (e.x <= -3 ? c.k_tail : c.k16) + off : ksafe);
-        const uint4* vq = reinterpret_cast<const uint4*>(on ? (e.x <= -3 ? c.v_tail : c.v16) + off : vsafe);
+        // load k: the row's four lanes read 64 contiguous bytes (channels 32k + 8kb)
+        const int64_t off = (int64_t)e.y * D + 8 * kb;
+        const uint16_t* kq = on ? (e.x <= -3 ? c.k_tail : c.k16) + off : ksafe;
+        const uint16_t* vq = on ? (e.x <= -3 ? c.v_tail : c.v16) + off : vsafe;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) d.k[k] = kq[k];
+        for (int k = 0; k < 4; ++k) d.k[k] = *reinterpret_cast<const uint4*>(kq + 32 * k);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) d.v[k] = vq[k];
+        for (int k = 0; k < 4; ++k) d.v[k] = *reinterpret_cast<const uint4*>(vq + 32 * k);
       }
       if (lane < TILE) tok[lane] = e.x;
     };
@@ -1154,8 +1161,9 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
       }
       // stage V (empty rows were read from a valid row; their p is 0)
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<uint4*>(vt + vt_off(row, 4 * kb + k)) = row_on(mine) ? vr[k] : uint4{0u, 0u, 0u, 0u};
+      for (int k = 0; k < 4; ++k)   // vr[k]: channels 32kb + 8k (FP8) or 32k + 8kb (fp16)
+        *reinterpret_cast<uint4*>(vt + vt_off(row, FP8 ? 4 * kb + k : 4 * k + kb)) =
+            row_on(mine) ? vr[k] : uint4{0u, 0u, 0u, 0u};
       f4 sc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < 4; ++k) sc = mfma32(bc<h8>(kr[k]), qb[k], sc);
