@@ -376,6 +376,8 @@ def main():
         stride = cap
         logits = torch.empty(w.batch, w.hq, stride, device=dev)
     mass = torch.empty(w.batch, w.hq, device=dev)
+    tm_bytes = kvc.kvc_workspace_bytes(kvc.OP_TOPK_MASS, base.desc, w.hq) if w.prefer_k else 0
+    tm_ws = torch.empty(max(tm_bytes, 16), dtype=torch.uint8, device=dev)
     want_logits = bool(accs) or w.prefer_k > 0
     names = (["append"] + (["score_topk"] if sparse else []) + ["attend"] + (["accum"] if accs else [])
              + (["topk_mass"] if w.prefer_k else []))
@@ -400,7 +402,8 @@ def main():
                              k_max, w.n_sink, w.n_window, accs[r], st)
 
     def op_topk_mass(r, st):
-        kvc.kvc_topk_mass(reps[r].desc, w.hq, logits, stride, lse, w.prefer_k, mass, st)
+        kvc.kvc_topk_mass(reps[r].desc, w.hq, logits, stride, lse, w.prefer_k, mass, tm_ws, tm_bytes,
+                          st)
 
     ops = {"append": op_append, "score_topk": op_score_topk, "attend": op_attend, "accum": op_accum,
            "topk_mass": op_topk_mass}

@@ -230,7 +230,7 @@ kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const f
 
 kvc_status kvc_topk_mass(const kvc_cache* cache, int32_t num_q_heads, const float* logits,
                          int64_t logits_stride, const float* lse, int32_t k, float* out,
-                         hipStream_t stream) {
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
   kvc_status st = check_cache(cache);
   if (st != KVC_OK) return st;
   if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads) return KVC_ERR_SHAPE;
@@ -238,7 +238,11 @@ kvc_status kvc_topk_mass(const kvc_cache* cache, int32_t num_q_heads, const floa
     return KVC_ERR_INVALID;
   if (k < 0) return KVC_ERR_INVALID;
   if (logits_stride < cache->max_tokens) return KVC_ERR_SHAPE;
-  return hip_status(launch_topk_mass(*cache, num_q_heads, logits, logits_stride, lse, k, out, stream));
+  if (!workspace || !aligned(workspace, 16) ||
+      workspace_bytes < topk_mass_workspace_bytes(*cache, num_q_heads))
+    return KVC_ERR_WORKSPACE;
+  return hip_status(launch_topk_mass(*cache, num_q_heads, logits, logits_stride, lse, k, out,
+                                     workspace, stream));
 }
 
 kvc_status kvc_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
@@ -259,6 +263,10 @@ size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_hea
     return attend_workspace_bytes(*cache, num_q_heads, mode, k_max, n_sink, n_window, workgroups);
   }
   if (op == KVC_OP_SCORE_TOPK) return topk_workspace_bytes(*cache);
+  if (op == KVC_OP_TOPK_MASS) {
+    if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads) return 0;
+    return topk_mass_workspace_bytes(*cache, num_q_heads);
+  }
   return 0;
 }
 

@@ -158,7 +158,9 @@ hipError_t launch_accum(const kvc_cache& c, int hq, const float* logits, int64_t
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups,
                               hipStream_t s);
 
+// Top-k mass: workspace bytes and the three launches.
+size_t topk_mass_workspace_bytes(const kvc_cache& c, int hq);
 hipError_t launch_topk_mass(const kvc_cache& c, int hq, const float* logits, int64_t stride,
-                            const float* lse, int k, float* out, hipStream_t s);
+                            const float* lse, int k, float* out, void* workspace, hipStream_t s);
 
 }  // namespace kvc

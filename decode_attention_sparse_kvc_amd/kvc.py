@@ -17,7 +17,7 @@ from ctypes import POINTER, c_double, c_float, c_int32, c_int64, c_size_t, c_voi
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libkvc.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 HEAD_DIM = 128
 GROUP = 64
 MAX_OUTLIERS = 4
@@ -25,7 +25,7 @@ FMT = {"fp16": 0, "int4": 1, "int1": 2, "fp8": 3}
 SCORE = {"exact": 0, "critical": 1, "external": 2}
 SCORE_BLOCKS = 16   # OR'ed into a score mode: rank 64-token blocks
 MODE = {"dense": 0, "drop": 1, "keep": 2, "blocks": 3}
-OP_SCORE_TOPK, OP_ATTEND = 1, 2
+OP_SCORE_TOPK, OP_ATTEND, OP_TOPK_MASS = 1, 2, 3
 NOALLOC_SCRATCH_BYTES = 32 << 20   # KVC_NOALLOC_SCRATCH_BYTES
 
 
@@ -92,7 +92,8 @@ def _load():
     lib.kvc_accum_scores.argtypes = [P, c_int32, c_void_p, c_int64, c_void_p, c_int32, c_void_p,
                                      c_int32, c_int32, c_int32, c_void_p, c_void_p]
     lib.kvc_topk_mass.restype = c_int32
-    lib.kvc_topk_mass.argtypes = [P, c_int32, c_void_p, c_int64, c_void_p, c_int32, c_void_p, c_void_p]
+    lib.kvc_topk_mass.argtypes = [P, c_int32, c_void_p, c_int64, c_void_p, c_int32, c_void_p,
+                                  c_void_p, c_size_t, c_void_p]
     lib.kvc_stream_read.restype = c_int32
     lib.kvc_stream_read.argtypes = [c_void_p, c_size_t, c_void_p, c_int32, c_void_p]
     lib.kvc_workspace_bytes.restype = c_size_t
@@ -184,10 +185,10 @@ def kvc_accum_scores(cache, num_q_heads: int, logits, logits_stride: int, lse, m
 
 
 def kvc_topk_mass(cache, num_q_heads: int, logits, logits_stride: int, lse, k: int, out,
-                  stream=None):
+                  workspace=None, workspace_bytes: int = 0, stream=None):
     _check("kvc_topk_mass", lib().kvc_topk_mass(
         ctypes.byref(cache), num_q_heads, _ptr(logits), logits_stride, _ptr(lse), k, _ptr(out),
-        _stream(stream)))
+        _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def kvc_stream_read(src, nbytes: int, sink, workgroups: int, stream=None):

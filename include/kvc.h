@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 3
+#define KVC_ABI_VERSION 4
 #define KVC_HEAD_DIM 128
 #define KVC_GROUP 64
 #define KVC_MAX_GQA 8          /* query heads per KV head supported by attend */
@@ -73,7 +73,7 @@ enum { KVC_SCORE_EXACT = 0, KVC_SCORE_CRITICAL = 1, KVC_SCORE_EXTERNAL = 2 };
 /* OR'ed into a score mode: rank 64-token blocks instead of tokens ([MTG] 8.1) */
 enum { KVC_SCORE_BLOCKS = 16 };
 enum { KVC_ATTEND_DENSE = 0, KVC_ATTEND_DROP = 1, KVC_ATTEND_KEEP = 2, KVC_ATTEND_BLOCKS = 3 };
-enum { KVC_OP_SCORE_TOPK = 1, KVC_OP_ATTEND = 2 };
+enum { KVC_OP_SCORE_TOPK = 1, KVC_OP_ATTEND = 2, KVC_OP_TOPK_MASS = 3 };
 
 /*
  * kvc_cache -- description of one layer's KV cache (plain data, caller-owned
@@ -346,15 +346,20 @@ kvc_status kvc_accum_scores(const kvc_cache* cache, int32_t num_q_heads, const f
  *   out          float32 [B][Hq]: sum over the k_b largest logits of
  *                exp(logit - lse) (fp32 sums; 0 when k_b = 0).  The value does
  *                not depend on which of several equal entries are counted.
+ *   workspace    kvc_workspace_bytes(KVC_OP_TOPK_MASS, cache, num_q_heads, ...)
+ *                bytes, 16-byte aligned (each row's per-slice histograms and
+ *                the keys of its k-th largest key's top-byte bucket); contents
+ *                on entry are ignored; KVC_ERR_WORKSPACE when missing or small.
+ * Three launches: each row is split into slices spread over the GPU.
  * The caller sums 1 - out over its n_q recent queries to form P.
  */
 kvc_status kvc_topk_mass(const kvc_cache* cache, int32_t num_q_heads, const float* logits,
                          int64_t logits_stride, const float* lse, int32_t k, float* out,
-                         hipStream_t stream);
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes for op (KVC_OP_*) called with these arguments (mode and
- * workgroups are the attend call's; both are ignored for KVC_OP_SCORE_TOPK);
- * 0 on invalid arguments.  Host only. */
+/* Workspace bytes for op (KVC_OP_*) called with these arguments (mode, k_max,
+ * n_sink, n_window and workgroups are the attend call's; they are ignored for
+ * KVC_OP_SCORE_TOPK and KVC_OP_TOPK_MASS); 0 on invalid arguments.  Host only. */
 size_t kvc_workspace_bytes(int32_t op, const kvc_cache* cache, int32_t num_q_heads, int32_t mode,
                            int32_t k_max, int32_t n_sink, int32_t n_window, int32_t workgroups);
 

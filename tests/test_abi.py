@@ -153,13 +153,18 @@ def test_topk_mass_argument_checks():
     d = _desc(max_tokens=4096, num_kv_heads=2)
     L = kvc.lib()
 
-    def call(hq=8, logits=0x10000, stride=4096, lse=0x20000, k=16, out=0x30000):
-        return L.kvc_topk_mass(ctypes.byref(d), hq, logits, stride, lse, k, out, None)
+    need = kvc.kvc_workspace_bytes(kvc.OP_TOPK_MASS, d, 8)
+    assert need > 0 and kvc.kvc_workspace_bytes(kvc.OP_TOPK_MASS, d, 3) == 0
+
+    def call(hq=8, logits=0x10000, stride=4096, lse=0x20000, k=16, out=0x30000, ws=0x40000, nb=None):
+        return L.kvc_topk_mass(ctypes.byref(d), hq, logits, stride, lse, k, out, ws,
+                               need if nb is None else nb, None)
     assert call(hq=0) == 2 and call(hq=3) == 2
     assert call(logits=None) == 1 and call(lse=None) == 1 and call(out=None) == 1
     assert call(logits=0x10002) == 1
     assert call(k=-1) == 1
     assert call(stride=4095) == 2
+    assert call(ws=None) == 4 and call(ws=0x40008) == 4 and call(nb=need - 1) == 4
 
 
 def test_library_digest_names_its_sources():

@@ -16,6 +16,14 @@ from test_gpu_attend import run_attend
 pytestmark = pytest.mark.gpu
 
 
+def topk_mass(cache, hq, logits, stride, lse, k, out):
+    """kvc_topk_mass with a workspace of the size the library asks for, filled with 0xFF
+    (its contents on entry must not matter)."""
+    nb = kvc.kvc_workspace_bytes(kvc.OP_TOPK_MASS, cache.desc, hq)
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
+    kvc.kvc_topk_mass(cache.desc, hq, logits, stride, lse, k, out, ws, nb)
+
+
 def mass_case(w, ks, pairs=None):
     res = ST.decode_step(w, append=False, pairs=pairs)
     cache = cache_for(w)
@@ -26,7 +34,7 @@ def mass_case(w, ks, pairs=None):
     got = {}
     for k in ks:
         m = torch.full((w.batch, w.hq), float("nan"), device="cuda")
-        kvc.kvc_topk_mass(cache.desc, w.hq, lg_t, stride, lse_t, k, m)
+        topk_mass(cache, w.hq, lg_t, stride, lse_t, k, m)
         torch.cuda.synchronize()
         m = host(m)
         got[k] = m
@@ -61,7 +69,7 @@ def test_empty_rows():
     lg = torch.zeros(1, w.hq, cache.max_tokens, device="cuda")
     lse = torch.zeros(1, w.hq, device="cuda")
     m = torch.full((1, w.hq), float("nan"), device="cuda")
-    kvc.kvc_topk_mass(cache.desc, w.hq, lg, cache.max_tokens, lse, 8, m)
+    topk_mass(cache, w.hq, lg, cache.max_tokens, lse, 8, m)
     torch.cuda.synchronize()
     assert np.all(host(m) == 0)
 
@@ -110,8 +118,9 @@ def test_full_size_concentrated_layer_decision():
 
 
 def test_bucket_larger_than_lds():
-    """40000 equal logits share one top-byte bucket, more than the kernel stages in
-    LDS: the row is re-read from memory, and the mass is k / n."""
+    """40000 equal logits share one first-level bucket, more keys than the finishing
+    kernel stages in LDS: they are re-read from the slices' regions, and the mass is
+    k / n."""
     w = W.int4_dense(40000)
     w.fmt = "fp16"
     w.k[0, :, 1] = w.k[0, 0, 1]
@@ -129,7 +138,7 @@ def test_wider_logits_stride():
     wide = np.full((1, w.hq, stride + 40), -1e30, np.float32)
     wide[:, :, :stride] = lg
     m = torch.full((1, w.hq), float("nan"), device="cuda")
-    kvc.kvc_topk_mass(cache.desc, w.hq, dev(wide), stride + 40, dev(lse), 33, m)
+    topk_mass(cache, w.hq, dev(wide), stride + 40, dev(lse), 33, m)
     torch.cuda.synchronize()
     for j in range(w.group):
         h = 4 * w.group + j
