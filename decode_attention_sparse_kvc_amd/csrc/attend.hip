@@ -966,8 +966,14 @@ __device__ inline void fp8_row_decode(uint4 r0, uint4 r1, uint4* out) {
 // word k channels 32k + 8kb .. +7 (so each load reads 64 contiguous bytes of
 // every row), of K (the matrix-core A operand of S = K q) and of V (staged
 // through LDS into the transposed A operand of O^T = V^T P^T).
-// (FP8 rows are half as wide: two 16-byte words of codes each, channels
-// [32kb, 32kb + 32) in the decoder's order.)
+// (FP8 rows are half as wide: two 16-byte words of codes, channels 16kb and
+// 64 + 16kb onward, which decode to words k of channels rows_ch(k, kb).)
+// First channel of word k of lane group kb in the fp16-rows role (8 channels).
+template <int FMT>
+__device__ inline int rows_ch(int k, int kb) {
+  return FMT == KVC_FMT_FP8 ? 64 * (k >> 1) + 16 * kb + 8 * (k & 1) : 32 * k + 8 * kb;
+}
+
 template <int FMT>
 struct RowTile {
   uint4 k[FMT == KVC_FMT_FP8 ? 2 : 4];
@@ -1041,13 +1047,10 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
     {
       uint4 raw[4] = {};
       if (hv) {
-        // fp16 rows: register k holds channels 32k + 8kb .. +7 (so a row's four
-        // lanes read 64 contiguous bytes per load); FP8 rows: channels
-        // 32kb + 8k .. +7, the decoder's order
+        // register k holds the channels of the rows' word k (rows_ch)
         const uint16_t* qh = a.q + ((int64_t)b * a.hq + g * G + col) * D;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          raw[k] = *reinterpret_cast<const uint4*>(qh + (FP8 ? 32 * kb + 8 * k : 32 * k + 8 * kb));
+        for (int k = 0; k < 4; ++k) raw[k] = *reinterpret_cast<const uint4*>(qh + rows_ch<FMT>(k, kb));
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) qb[k] = bc<h8>(raw[k]);
@@ -1120,14 +1123,13 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
     const uint16_t* vsafe = c.v16 ? c.v16 : c.v_tail;
     auto load_rows = [&](int2 e, RowTile<FMT>& d, int* tok) {
       const bool on = row_on(e.x);
-      if constexpr (FP8) {   // 32 codes of the row: two 16-byte loads each for K and V
-        const int64_t off = (int64_t)e.y * D + 32 * kb;
-        const uint4* kq = reinterpret_cast<const uint4*>(c.k_codes + (on ? off : 0));
-        const uint4* vq = reinterpret_cast<const uint4*>(c.v_codes + (on ? off : 0));
-        d.k[0] = kq[0];
-        d.k[1] = kq[1];
-        d.v[0] = vq[0];
-        d.v[1] = vq[1];
+      if constexpr (FP8) {   // 32 codes of the row: two 16-byte loads each for K and V,
+                             // a row's four lanes reading 64 contiguous bytes per load
+        const int64_t off = (on ? (int64_t)e.y * D : 0) + 16 * kb;
+        d.k[0] = *reinterpret_cast<const uint4*>(c.k_codes + off);
+        d.k[1] = *reinterpret_cast<const uint4*>(c.k_codes + off + 64);
+        d.v[0] = *reinterpret_cast<const uint4*>(c.v_codes + off);
+        d.v[1] = *reinterpret_cast<const uint4*>(c.v_codes + off + 64);
       } else {
         // load k: the row's four lanes read 64 contiguous bytes (channels 32k + 8kb)
         const int64_t off = (int64_t)e.y * D + 8 * kb;
@@ -1161,8 +1163,8 @@ __device__ __forceinline__ void rows_role(const AttendArgs& a, int b, int g, int
       }
       // stage V (empty rows were read from a valid row; their p is 0)
 #pragma unroll
-      for (int k = 0; k < 4; ++k)   // vr[k]: channels 32kb + 8k (FP8) or 32k + 8kb (fp16)
-        *reinterpret_cast<uint4*>(vt + vt_off(row, FP8 ? 4 * kb + k : 4 * k + kb)) =
+      for (int k = 0; k < 4; ++k)   // vr[k]: channels rows_ch(k, kb) .. +7
+        *reinterpret_cast<uint4*>(vt + vt_off(row, rows_ch<FMT>(k, kb) >> 3)) =
             row_on(mine) ? vr[k] : uint4{0u, 0u, 0u, 0u};
       f4 sc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
