@@ -5,13 +5,14 @@
 // cumulative scores).
 //
 // Kernels, all on the caller's stream:
-//   prep     zeroes each (sequence, KV head)'s coarse histogram.
 //   score    the fp64 score of every candidate token, summed channel by channel
 //            in ascending order from +0.0 (the order the interface fixes, so
 //            results are reproducible bit for bit), max over the query group,
 //            turned into an order-preserving 64-bit key (0 = not a candidate);
 //            histogram of the keys' 12-bit coarse bins (sign, clamped exponent,
-//            4 mantissa bits: a monotone function of the key).  Critical mode
+//            4 mantissa bits: a monotone function of the key), each workgroup's
+//            stored whole in its own slot (no atomics, nothing to clear before
+//            the call; the compaction sums the slots).  Critical mode
 //            ranks the channels in every workgroup (importance from q and the
 //            cache's per-channel maximum).  Workgroups loop over chunks of the
 //            pair's tokens; external scores and channel-major fp16 keys take
@@ -44,9 +45,9 @@ constexpr int SCT = 1024;      // threads of a scoring workgroup (one token each
 constexpr int TPT = 4;         // tokens a thread scores a chunk (vector-load kernels)
 constexpr int CUS = 256;       // compute units of an MI355X (scoring grids are sized to fill them once)
 constexpr int CBINS = 4096;    // coarse bins of the keys
-constexpr int HREP = 2;        // copies of the coarse histogram (spread the global atomics)
 constexpr int SUP = CBINS / 64;    // super-bins (64 coarse bins each)
-constexpr int HW = HREP * (CBINS + SUP);   // histogram words per (sequence, KV head)
+constexpr int HWS = CBINS + SUP;   // histogram words of one workgroup's slot
+constexpr int NSLOT = 256;     // histogram slots (counting workgroups) per pair at most
 constexpr int CT = 4096;       // items per compaction region
 constexpr int RW = CT / 32;    // bitmap words per region
 constexpr int FT = 1024;       // threads of the short-range finish workgroup
@@ -69,7 +70,9 @@ struct TopkArgs {
   int32_t* out_channels;
   // workspace
   uint64_t* keys;      // [B][Hkv][max_tokens] item keys (0: not a candidate)
-  uint32_t* hist;      // [B][Hkv]: [HREP][CBINS] coarse histogram, then [HREP][SUP] super-bin sums
+  uint32_t* hist;      // [B][Hkv][nslot]: each counting workgroup's [CBINS] coarse histogram,
+                       // then its [SUP] super-bin sums (written whole: nothing to clear)
+  int nslot;           // counting workgroups per pair (the grid's x size)
   uint32_t* above;     // [B][Hkv][max_tokens / 32] items in bins above the threshold bin
   uint64_t* ckey;      // [B][Hkv][nreg * CT] keys of the threshold bin, per compaction region
   int32_t* cidx;       // [B][Hkv][nreg * CT] their item indices
@@ -146,13 +149,6 @@ __device__ inline bool keys_from_ext(const TopkArgs& a) {
   return a.mode == KVC_SCORE_EXTERNAL && !a.blocks;
 }
 __device__ inline uint64_t ext_key(float x) { return order_key(__dadd_rn((double)x, 0.0)); }
-
-// ------------------------------------------------------------------ prep
-// Zeroes the pair's histogram copies, which the scoring workgroups add into.
-__global__ __launch_bounds__(ST) void prep_kernel(TopkArgs a) {
-  uint4* h = reinterpret_cast<uint4*>(a.hist + pair_index(a, blockIdx.y, blockIdx.x) * HW);
-  for (int e = threadIdx.x; e < HW / 4; e += ST) h[e] = uint4{0u, 0u, 0u, 0u};
-}
 
 // ------------------------------------------------------------------ score
 constexpr int GMAX = 16;       // query heads per KV head supported by scoring
@@ -279,24 +275,23 @@ __device__ void critical_channels(const TopkArgs& a, int b, int g, int64_t pi, i
   }
 }
 
-// Adds the workgroup's LDS histogram into the pair's global copy
-// (blockIdx.x % HREP): one atomic per non-empty bin, and one per non-empty
-// super-bin into the super-bin sums (a wave's 64 consecutive bins are one
-// super-bin, summed across the wave).
-template <int NT>
+// Stores the workgroup's LDS histogram in its slot of the pair (slot
+// blockIdx.x, every bin, zeros too) with the super-bin sums after it (a
+// wave's 64 consecutive bins are one super-bin, summed across the wave).
+// Plain stores: no atomics, and no slot needs clearing before the call.
+// In block mode only the block-key workgroups count (BK).
+template <int NT, bool BK = false>
 __device__ inline void flush_hist(const TopkArgs& a, int64_t pi, const uint32_t* sh, int tid) {
   static_assert(NT % 64 == 0 && CBINS % NT == 0, "whole super-bins a wave");
-  if (!a.use_hist) return;
-  const int rep = blockIdx.x % HREP;
-  uint32_t* h = a.hist + pi * HW + rep * CBINS;
-  uint32_t* hs = a.hist + pi * HW + HREP * CBINS + rep * SUP;
+  if (!a.use_hist || a.blocks != BK) return;
+  uint32_t* h = a.hist + (pi * a.nslot + blockIdx.x) * HWS;
   for (int e = tid; e < CBINS; e += NT) {
     const uint32_t c = sh[e];
-    if (c) atomicAdd(&h[e], c);
+    h[e] = c;
     uint32_t t = c;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
-    if ((tid & 63) == 0 && t) atomicAdd(&hs[e >> 6], t);
+    if ((tid & 63) == 0) h[CBINS + (e >> 6)] = t;
   }
 }
 
@@ -587,38 +582,42 @@ __global__ __launch_bounds__(ST) void block_key_kernel(TopkArgs a) {
   __shared__ uint32_t sh[CBINS];
   int lo, hi, kk;
   cand_range(a, b, lo, hi, kk);
-  const int j0 = blockIdx.x * BPW;
   const double* ts = a.tscore + pi * a.c.max_tokens;
   for (int e = tid; e < CBINS; e += ST) sh[e] = 0u;
-  {   // every load is issued before the LDS stores (a load-store loop waits each time)
-    constexpr int R = BPW * GS / ST;
-    double v[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int e = r * ST + tid, j = j0 + e / GS;
-      v[r] = ts[(int64_t)j0 * GS + (j >= lo && j < hi ? e : 0)];
+  const int nchunk = (a.c.max_tokens / GS + BPW - 1) / BPW;
+  for (int ch = blockIdx.x; ch < nchunk; ch += gridDim.x) {   // BPW blocks a round
+    const int j0 = ch * BPW;
+    lds_sync();   // (the previous round's LDS reads are done)
+    {   // every load is issued before the LDS stores (a load-store loop waits each time)
+      constexpr int R = BPW * GS / ST;
+      double v[R];
+  #pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int e = r * ST + tid, j = j0 + e / GS;
+        v[r] = ts[(int64_t)j0 * GS + (j >= lo && j < hi ? e : 0)];
+      }
+  #pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int e = r * ST + tid, j = j0 + e / GS;
+        ss[e] = j >= lo && j < hi ? v[r] : 0.0;
+      }
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int e = r * ST + tid, j = j0 + e / GS;
-      ss[e] = j >= lo && j < hi ? v[r] : 0.0;
+    lds_sync();
+    if (tid < BPW) {
+      const int j = j0 + tid;
+      if (j >= lo && j < hi) {
+        double sum = 0.0;
+        for (int i = 0; i < GS; ++i) sum = __dadd_rn(sum, ss[tid * GS + i]);
+        const double r = __dadd_rn(__ddiv_rn(sum, (double)GS), 0.0);
+        const uint64_t key = order_key(r);
+        a.keys[pi * a.c.max_tokens + j] = key;
+        if (a.out_scores) a.out_scores[pi * a.c.max_tokens + j] = r;
+        if (a.use_hist) atomicAdd(&sh[coarse_of(key)], 1u);
+      }
     }
   }
   lds_sync();
-  if (tid < BPW) {
-    const int j = j0 + tid;
-    if (j >= lo && j < hi) {
-      double sum = 0.0;
-      for (int i = 0; i < GS; ++i) sum = __dadd_rn(sum, ss[tid * GS + i]);
-      const double r = __dadd_rn(__ddiv_rn(sum, (double)GS), 0.0);
-      const uint64_t key = order_key(r);
-      a.keys[pi * a.c.max_tokens + j] = key;
-      if (a.out_scores) a.out_scores[pi * a.c.max_tokens + j] = r;
-      if (a.use_hist) atomicAdd(&sh[coarse_of(key)], 1u);
-    }
-  }
-  lds_sync();
-  flush_hist<ST>(a, pi, sh, tid);
+  flush_hist<ST, true>(a, pi, sh, tid);
 }
 
 // ------------------------------------------------------------------ selection helpers
@@ -663,7 +662,7 @@ __device__ inline uint32_t wave_incl_scan(uint32_t x) {
 // SUP - 1 - l, highest first), then the bin inside it from that super-bin's
 // 64 bins.  Results in s_res[0] (tb) and s_res[1] (n_gt); every thread calls
 // it.
-__device__ void coarse_threshold(const uint32_t* hist, int k, int* s_res) {
+__device__ void coarse_threshold(const uint32_t* hist, int nslot, int k, int* s_res) {
   static_assert(SUP == 64, "one super-bin a lane");
   const int tid = threadIdx.x;
   if (tid < 64) {
@@ -671,17 +670,17 @@ __device__ void coarse_threshold(const uint32_t* hist, int k, int* s_res) {
       s_res[0] = 0;
       s_res[1] = 0;
     }
-    uint32_t x = 0;
-#pragma unroll
-    for (int r = 0; r < HREP; ++r) x += hist[HREP * CBINS + r * SUP + (SUP - 1 - tid)];
+    uint32_t x = 0;   // super-bin SUP - 1 - tid summed over the slots
+#pragma unroll 8
+    for (int sl = 0; sl < nslot; ++sl) x += hist[sl * HWS + CBINS + (SUP - 1 - tid)];
     const uint32_t incl = wave_incl_scan(x);
     const uint64_t hit = __ballot(incl - x < (uint32_t)k && incl >= (uint32_t)k);
     const int L = hit ? __ffsll((unsigned long long)hit) - 1 : SUP - 1;
     const int S = SUP - 1 - L;
     const uint32_t above = __shfl(incl - x, L);   // keys in the super-bins above S
     uint32_t y = 0;
-#pragma unroll
-    for (int r = 0; r < HREP; ++r) y += hist[r * CBINS + S * 64 + (63 - tid)];
+#pragma unroll 8
+    for (int sl = 0; sl < nslot; ++sl) y += hist[sl * HWS + S * 64 + (63 - tid)];
     const uint32_t incl2 = wave_incl_scan(y) + above;
     if (incl2 - y < (uint32_t)k && incl2 >= (uint32_t)k) {
       s_res[0] = S * 64 + 63 - tid;
@@ -728,7 +727,7 @@ __global__ __launch_bounds__(ST) void compact_kernel(TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < R; ++j) kv[j] = keys[min(max(base + j * ST + tid, lo), hi - 1)];
   }
-  coarse_threshold(a.hist + pi * HW, k, s_res);
+  coarse_threshold(a.hist + pi * a.nslot * HWS, a.nslot, k, s_res);
   const uint32_t tb = (uint32_t)s_res[0];
   if (blockIdx.x == 0 && tid == 0) {
     a.pmeta[2 * pi] = (int32_t)tb;
@@ -1154,12 +1153,19 @@ __global__ __launch_bounds__(FR) void finish_region_kernel(TopkArgs a, int rpw) 
 
 }  // namespace
 
+// Histogram slots a pair has room for: the counting grids give a pair at most
+// this many workgroups (about four resident a CU over all pairs, NSLOT at most).
+int topk_slots(const kvc_cache& c) {
+  const int64_t pairs = (int64_t)c.batch * c.num_kv_heads;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(NSLOT, (4 * (int64_t)CUS + pairs - 1) / pairs));
+}
+
 size_t topk_workspace_bytes(const kvc_cache& c) {
   const size_t pairs = (size_t)c.batch * c.num_kv_heads;
   const size_t words = c.max_tokens / 32;
   const size_t nreg = (c.max_tokens + CT - 1) / CT;   // (token items: the most regions)
   size_t bytes = 2 * pairs * c.max_tokens * sizeof(uint64_t);   // keys, block-mode token scores
-  bytes += pairs * HW * sizeof(uint32_t);                        // coarse histogram
+  bytes += pairs * topk_slots(c) * HWS * sizeof(uint32_t);       // histogram slots
   bytes += pairs * words * sizeof(uint32_t);                     // above bitmap
   bytes += pairs * nreg * CT * (sizeof(uint64_t) + sizeof(int32_t));   // threshold-bin lists
   bytes += 2 * pairs * nreg * sizeof(int32_t);                   // per-region counts
@@ -1200,7 +1206,7 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   a.tscore = reinterpret_cast<double*>(p);
   p += pairs * c.max_tokens * sizeof(double);
   a.hist = reinterpret_cast<uint32_t*>(p);
-  p += pairs * HW * sizeof(uint32_t);
+  p += pairs * topk_slots(c) * HWS * sizeof(uint32_t);
   a.above = reinterpret_cast<uint32_t*>(p);
   p += pairs * words * sizeof(uint32_t);
   a.ckey = reinterpret_cast<uint64_t*>(p);
@@ -1214,21 +1220,25 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
   a.pmeta = reinterpret_cast<int32_t*>(p);
 
   const int Hkv = c.num_kv_heads, B = c.batch;
-  if (a.use_hist) prep_kernel<<<dim3(Hkv, B), ST, 0, s>>>(a);
   // scoring grid: as many workgroups as are resident at once (per_cu a CU,
   // from the kernel's registers and LDS), split evenly over the pairs; each
   // loops over its chunks
+  // (at most topk_slots workgroups a pair: one histogram slot each)
+  const int slots = topk_slots(c);
   auto score_grid = [&](int chunks, int per_cu) {
     const int64_t per_pair =
         std::max<int64_t>(1, ((int64_t)CUS * per_cu + (int64_t)pairs - 1) / (int64_t)pairs);
-    return dim3((unsigned)std::min<int64_t>(chunks, per_pair), Hkv, B);
+    const dim3 gr((unsigned)std::min<int64_t>(std::min<int64_t>(chunks, per_pair), slots), Hkv, B);
+    if (!a.blocks) a.nslot = (int)gr.x;
+    return gr;
   };
   const int vchunks = (c.max_tokens + SCT * TPT - 1) / (SCT * TPT);
   // the channel-major copy serves fp16 and FP8 caches (FP8: kT holds the decoded
   // values); quantized caches score their codes
   const bool kt = c.kT && c.page_size == 0 && (c.format == KVC_FMT_FP16 || c.format == KVC_FMT_FP8);
   if (mode == KVC_SCORE_EXTERNAL) {
-    score_ext_kernel<<<score_grid(vchunks, 2), SCT, 0, s>>>(a);
+    const dim3 grid = score_grid(vchunks, 2);   // (sets a.nslot before a is passed)
+    score_ext_kernel<<<grid, SCT, 0, s>>>(a);
   } else if (mode == KVC_SCORE_CRITICAL && kt && (a.G == 1 || a.G == 2 || a.G == 4)) {
     const size_t sq_bytes = (size_t)a.G * n_crit * sizeof(double);
     const dim3 grid = score_grid(vchunks, a.G == 4 ? 1 : 2);
@@ -1264,8 +1274,12 @@ hipError_t launch_score_topk(const kvc_cache& c, const uint16_t* q, int hq, int 
 #undef KVC_SCORE_G
 #undef KVC_SCORE_E
   }
-  if (a.blocks)
-    block_key_kernel<<<dim3((c.max_tokens / GS + BPW - 1) / BPW, Hkv, B), ST, 0, s>>>(a);
+  if (a.blocks) {
+    const int nchunk = (c.max_tokens / GS + BPW - 1) / BPW;
+    const dim3 bg((unsigned)std::min(nchunk, slots), Hkv, B);
+    a.nslot = (int)bg.x;
+    block_key_kernel<<<bg, ST, 0, s>>>(a);
+  }
   if (items > DIRECT_MAX) {
     compact_kernel<<<dim3(a.nreg, Hkv, B), ST, 0, s>>>(a);
     // finish: regions split over as many workgroups as are resident at once
