@@ -132,6 +132,40 @@ def test_blocks_exact_and_external_scores():
     block_case(w2, pairs=[(0, 4)])
 
 
+def test_blocks_long_range_histogram():
+    """More than 8192 candidate blocks (one pair of 528K tokens, external scores with
+    planted equal block means): the block keys are counted into histogram slots by
+    block-key workgroups that each take several rounds of blocks, and the long-range path
+    selects; block means and ids equal the oracle's bit for bit."""
+    from decode_attention_sparse_kvc_amd import KvcCache
+    n = 8300 * 64 + 37
+    cap = -(-(n + 1) // 64) * 64
+    cache = KvcCache("fp16", 1, 1, cap)
+    cache.seq_lens.fill_(n)
+    rng = np.random.default_rng(61)
+    ext = rng.lognormal(0.0, 1.5, size=(1, 1, cap)).astype(np.float32)
+    ext[..., n:] = 0.0
+    for blk in rng.choice(8000, 40, replace=False):          # 40 blocks with one equal mean
+        ext[0, 0, 64 * (blk + 1): 64 * (blk + 2)] = 5.0
+    n_sink, n_window, k, k_max = 4, 64, 600, 700
+    idx = torch.full((1, 1, k_max), -7, dtype=torch.int32, device="cuda")
+    sc = torch.full((1, 1, cap), float("nan"), dtype=torch.float64, device="cuda")
+    nb = kvc.kvc_workspace_bytes(kvc.OP_SCORE_TOPK, cache.desc, 1)
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device="cuda")
+    q = torch.zeros((1, 1, 128), dtype=torch.float16, device="cuda")
+    kvc.kvc_score_topk(cache.desc, q, 1, kvc.SCORE["external"] | kvc.SCORE_BLOCKS, 8, dev(ext),
+                       n_sink, n_window, dev(np.array([k], np.int32)), k_max, idx, sc, None, ws, nb)
+    torch.cuda.synchronize()
+    r = ext[0, 0].astype(np.float64)
+    lo, hi = S.block_range(n, n_sink, n_window)
+    assert hi - lo > 8192
+    bs = S.block_scores(r, lo, hi)
+    got = host(sc)[0, 0, lo:hi]
+    assert np.array_equal(got.view(np.uint64), bs[lo:hi].view(np.uint64)), "block means"
+    want = S.topk_indices(bs, lo, hi, k, k_max)
+    assert np.array_equal(host(idx)[0, 0], want), (host(idx)[0, 0][:12], want[:12])
+
+
 def test_blocks_more_than_candidates_and_empty():
     w = W.sparse_blocks(n_ctx=1000, fmt="int4", top_blocks=50)   # 15 candidates, k_max 50
     block_case(w, pairs=[(0, 0)])

@@ -85,6 +85,15 @@ def test_exact_int4_single_head(n):
     topk_case(W.single_head_4k(n))
 
 
+def test_exact_int4_single_head_long():
+    """One pair of 200K tokens with exact scores: more counting workgroups than histogram
+    slots would allow, so the scoring grid is capped (256 slots) and each workgroup loops
+    over several chunks; the long-range path (compaction, regions) selects."""
+    w = W.single_head_4k(200_000)
+    w.top_k = np.array([3000], np.int32)
+    topk_case(w)
+
+
 def test_exact_int4_after_append():
     topk_case(W.single_head_4k(700), append=True)
 
