@@ -45,20 +45,23 @@ struct GroupQuant {
     s = h2f(s16);
     z = h2f(z16);
   }
-  // code = rint(fl((x - z) / s)) clamped, with r = fl(1 / s).  a = fl((x - z) * r)
+  // code = rint(fl((x - z) / s)) clamped, from r = recip(s).  a = fl((x - z) * r)
   // lies within 2^-17.9 of fl((x - z) / s) while a < 17 (two roundings of
   // 2^-24 each on a quotient below 17, plus the quotient's own rounding), and
   // any larger a clamps to the top code either way; so rint(a) is the code
-  // unless a lies within 2^-17 of a half-integer, where the division decides
-  // (rare: the branch is skipped by every wave whose lanes all avoid it).
+  // unless a lies within 2^-17 of a half-integer (|a - rint(a)| >= 0.5 - 2^-17),
+  // where the division decides (rare: the branch is skipped by every wave
+  // whose lanes all avoid it).  x >= z (z is the group's minimum; values left
+  // out of the range get their code elsewhere), so a >= 0 and only the top
+  // needs a clamp; s == 0 has r = 0, hence a = 0 and code 0.
+  __device__ static inline float recip(float s) { return s == 0.0f ? 0.0f : __fdiv_rn(1.0f, s); }
   __device__ static inline uint32_t code(float x, float s, float z, float r) {
     constexpr float top = float((1 << BITS) - 1);
     const float d = __fsub_rn(x, z);
     const float a = __fmul_rn(d, r);
     float t = rintf(a);
-    if (fabsf(__fsub_rn(__fsub_rn(a, floorf(a)), 0.5f)) <= 0x1p-17f) t = rintf(__fdiv_rn(d, s));
-    t = fminf(fmaxf(t, 0.0f), top);   // (s == 0 becomes 0 below)
-    return s == 0.0f ? 0u : (uint32_t)t;
+    if (fabsf(__fsub_rn(a, t)) >= 0.5f - 0x1p-17f) t = rintf(__fdiv_rn(d, s));
+    return (uint32_t)fminf(t, top);
   }
 };
 
@@ -104,7 +107,7 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
     meta[ck] = ks16;
     meta[D + ck] = kz16;
   }
-  const float kr = __fdiv_rn(1.0f, ks);
+  const float kr = GroupQuant<BITS>::recip(ks);
   uint32_t kq[8] = {};
 #pragma unroll
   for (int i = 0; i < 32; ++i) kq[i >> 2] |= GroupQuant<BITS>::code(kx[i], ks, kz, kr) << (8 * (i & 3));
@@ -160,7 +163,7 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
       c.v_meta[slot * 4 + 2 + jv] = vz16;
     }
   }
-  const float vr = __fdiv_rn(1.0f, vs);
+  const float vr = GroupQuant<BITS>::recip(vs);
   uint32_t vq[8] = {};
 #pragma unroll
   for (int i = 0; i < 32; ++i)
