@@ -117,6 +117,22 @@ __device__ inline uint32_t fp8_encode(uint32_t h) {
   return s | r;
 }
 
+// fp8_encode of the two fp16 values in w (low half first), as two bytes in the
+// low 16 bits: gfx950's conversion (round to nearest, ties to even; checked
+// against fp8_encode on all 65536 inputs) agrees with it for |x| < 464, where
+// it would return NaN instead of saturating; inputs of magnitude >= 448
+// (0x5F00, also inf and NaN) are set to the saturated code here.
+typedef short kvc_s2v __attribute__((ext_vector_type(2)));
+typedef _Float16 kvc_h2v __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t fp8_encode2(uint32_t w) {
+  const kvc_s2v r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(kvc_s2v{0, 0},
+                                                             __builtin_bit_cast(kvc_h2v, w), 1.0f, false);
+  uint32_t c = __builtin_bit_cast(uint32_t, r) & 0xFFFFu;
+  if ((w & 0x7FFFu) >= 0x5F00u) c = (c & 0xFF00u) | ((w >> 8) & 0x80u) | 0x7Eu;
+  if (((w >> 16) & 0x7FFFu) >= 0x5F00u) c = (c & 0x00FFu) | ((((w >> 24) & 0x80u) | 0x7Eu) << 8);
+  return c;
+}
+
 // E4M3 code c -> fp16 bits of value / 256, exactly: sign to bit 15 and the
 // exponent and mantissa fields shifted into fp16's (bias 15 = 7 + 8, and an
 // E4M3 subnormal lands on the matching fp16 subnormal).

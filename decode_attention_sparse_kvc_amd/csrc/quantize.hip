@@ -301,14 +301,12 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
       const int r = lo - g0 + (e >> 4), ch = (e & 15) * 8;
       const int64_t slot = slot_of(c, b, g, g0 + r);
       if (slot < 0) continue;
-      uint32_t kw[2] = {0u, 0u}, vw[2] = {0u, 0u};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        kw[j >> 2] |= fp8_encode(sK[r][ch + j]) << (8 * (j & 3));
-        vw[j >> 2] |= fp8_encode(sV[r][ch + j]) << (8 * (j & 3));
-      }
-      *reinterpret_cast<uint2*>(c.k_codes + slot * D + ch) = uint2{kw[0], kw[1]};
-      *reinterpret_cast<uint2*>(c.v_codes + slot * D + ch) = uint2{vw[0], vw[1]};
+      const uint4 kx = *reinterpret_cast<const uint4*>(&sK[r][ch]);
+      const uint4 vx = *reinterpret_cast<const uint4*>(&sV[r][ch]);
+      *reinterpret_cast<uint2*>(c.k_codes + slot * D + ch) =
+          uint2{fp8_encode2(kx.x) | (fp8_encode2(kx.y) << 16), fp8_encode2(kx.z) | (fp8_encode2(kx.w) << 16)};
+      *reinterpret_cast<uint2*>(c.v_codes + slot * D + ch) =
+          uint2{fp8_encode2(vx.x) | (fp8_encode2(vx.y) << 16), fp8_encode2(vx.z) | (fp8_encode2(vx.w) << 16)};
     }
   }
   if (c.kT) {  // channel-major: consecutive lanes write consecutive tokens of one channel
@@ -316,7 +314,7 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
       const int ch = e / (hi - lo), r = lo - g0 + e % (hi - lo);
       uint16_t x = sK[r][ch];
       if constexpr (FMT == KVC_FMT_FP8)   // the decoded value (exact in fp16)
-        x = f2h(h2f((uint16_t)fp8_h16_over256(fp8_encode(x))) * 256.0f);
+        x = f2h(h2f((uint16_t)fp8_h16_over256(fp8_encode2(x) & 0xFFu)) * 256.0f);
       c.kT[(((int64_t)b * Hkv + g) * D + ch) * c.max_tokens + g0 + r] = x;
     }
   }
@@ -399,15 +397,10 @@ __global__ __launch_bounds__(NT) void append_token_kernel(
       }
       if constexpr (FMT == KVC_FMT_FP8) {
         if (slot >= 0) {
-          const uint32_t kw[4] = {nk.x, nk.y, nk.z, nk.w}, vw[4] = {nv.x, nv.y, nv.z, nv.w};
-          uint32_t ko[2] = {0u, 0u}, vo[2] = {0u, 0u};
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            ko[j >> 2] |= fp8_encode((kw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << (8 * (j & 3));
-            vo[j >> 2] |= fp8_encode((vw[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) << (8 * (j & 3));
-          }
-          *reinterpret_cast<uint2*>(c.k_codes + slot * D + ch) = uint2{ko[0], ko[1]};
-          *reinterpret_cast<uint2*>(c.v_codes + slot * D + ch) = uint2{vo[0], vo[1]};
+          *reinterpret_cast<uint2*>(c.k_codes + slot * D + ch) =
+              uint2{fp8_encode2(nk.x) | (fp8_encode2(nk.y) << 16), fp8_encode2(nk.z) | (fp8_encode2(nk.w) << 16)};
+          *reinterpret_cast<uint2*>(c.v_codes + slot * D + ch) =
+              uint2{fp8_encode2(nv.x) | (fp8_encode2(nv.y) << 16), fp8_encode2(nv.z) | (fp8_encode2(nv.w) << 16)};
         }
       }
     }
@@ -426,7 +419,7 @@ __global__ __launch_bounds__(NT) void append_token_kernel(
     if (c.kT) {
       uint16_t x = kc;
       if constexpr (FMT == KVC_FMT_FP8)   // the decoded value (exact in fp16)
-        x = f2h(h2f((uint16_t)fp8_h16_over256(fp8_encode(x))) * 256.0f);
+        x = f2h(h2f((uint16_t)fp8_h16_over256(fp8_encode2(x) & 0xFFu)) * 256.0f);
       c.kT[(row + tid) * c.max_tokens + L] = x;
     }
     // the same order as the unsigned atomic max of the multi-token path
