@@ -77,7 +77,7 @@ constexpr int LEN_MASK = ARRIVE - 1;
 // the group needs no LDS beyond its 32 KB of rows.
 template <int BITS>
 __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
-                               uint16_t (&sK)[GS][D], uint16_t (&sV)[GS][D]) {
+                               uint16_t (&sK)[GS][D], uint16_t (&sV)[GS][D], bool kabs) {
   const int tid = threadIdx.x, Hkv = c.num_kv_heads;
   const int n_out = BITS == 4 ? c.n_outlier : 0;
 
@@ -94,6 +94,10 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
   }
   mn = fminf(mn, __shfl_xor(mn, 1));
   mx = fmaxf(mx, __shfl_xor(mx, 1));
+  // max|K| of a group whose rows are all new: the larger magnitude of its extremes
+  if (kabs && hk == 0)
+    atomicMax(reinterpret_cast<unsigned int*>(c.k_absmax) + ((int64_t)b * Hkv + g) * D + ck,
+              __float_as_uint(fmaxf(fabsf(mn), fabsf(mx))));
   // outlier channels (INT4): scale and zero 0, hence codes 0; their values
   // go to the fp16 outlier store below
   for (int j = 0; j < n_out; ++j)
@@ -318,7 +322,9 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
       c.kT[(((int64_t)b * Hkv + g) * D + ch) * c.max_tokens + g0 + r] = x;
     }
   }
-  if (c.k_absmax && tid < D) {
+  // (a complete group of new rows takes max|K| from its extremes instead)
+  const bool abs_from_group = complete && lo == g0;
+  if (c.k_absmax && tid < D && !abs_from_group) {
     float m = 0.0f;
 #pragma unroll 16
     for (int r = lo - g0; r < hi - g0; ++r) m = fmaxf(m, fabsf(h2f(sK[r][tid])));
@@ -327,7 +333,7 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
   }
 
   if constexpr (grouped(FMT)) {
-    if (complete) quantize_group<BITS>(c, b, g, g0, sK, sV);
+    if (complete) quantize_group<BITS>(c, b, g, g0, sK, sV, c.k_absmax && abs_from_group);
   }
 }
 
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(NT) void append_token_kernel(
       *reinterpret_cast<uint4*>(&sV[rr][ch]) = *reinterpret_cast<const uint4*>(c.v_tail + off);
     }
     __syncthreads();
-    quantize_group<BITS>(c, b, g, g0, sK, sV);
+    quantize_group<BITS>(c, b, g, g0, sK, sV, false);
   }
 }
 
