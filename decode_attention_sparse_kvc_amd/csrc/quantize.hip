@@ -70,74 +70,98 @@ struct GroupQuant {
 constexpr int ARRIVE = 1 << 24;
 constexpr int LEN_MASK = ARRIVE - 1;
 
+// Packed-fp16 helpers of the group quantizer.
+__device__ inline uint32_t pk_min(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(kvc_h2v, a),
+                                                                __builtin_bit_cast(kvc_h2v, b)));
+}
+__device__ inline uint32_t pk_max(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(kvc_h2v, a),
+                                                                __builtin_bit_cast(kvc_h2v, b)));
+}
+// Elementwise minimum / maximum of fp16 pairs over lanes l, l ^ 16, l ^ 32, l ^ 48
+// (gfx950 row-swap moves: each swap of a value with itself yields it and the
+// partner lane's value).
+__device__ inline uint32_t rows_min(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = pk_min(r[0], r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return pk_min(t[0], t[1]);
+}
+__device__ inline uint32_t rows_max(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = pk_max(r[0], r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return pk_max(t[0], t[1]);
+}
+// x | the same register of lanes l ^ 1 and l ^ 2 (DPP quad permutations).
+__device__ inline uint32_t quad_or(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);   // [1, 0, 3, 2]
+  x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);   // [2, 3, 0, 1]
+  return x;
+}
+
+// Code of one value as a float in [0, 2^BITS - 1] (see GroupQuant::code).  The
+// fast form rounds a = fl((x - z) * r) and records how close a came to a
+// half-integer in worst; a caller whose wave saw worst >= NEAR_HALF anywhere
+// recomputes its codes with SLOW, which takes the division where a is that close.
+constexpr float NEAR_HALF = 0.5f - 0x1p-17f;
+// fl(h - z) for the fp16 value h in half H of the dword u and nz = -z, as
+// one mixed-precision fma (h * 1 + nz, rounded once): the conversion of h
+// rides in the instruction.
+template <int H>
+__device__ inline float sub_h(uint32_t u, float nz) {
+  float d;
+  if constexpr (H == 0)
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(u), "v"(nz));
+  else
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(u), "v"(nz));
+  return d;
+}
+template <int BITS, bool SLOW>
+__device__ inline float qcode(float d, float s, float r, float& e) {
+  const float a = __fmul_rn(d, r);
+  float t = rintf(a);
+  e = __fsub_rn(a, t);
+  if constexpr (SLOW) {
+    if (fabsf(e) >= NEAR_HALF) t = rintf(__fdiv_rn(d, s));
+  }
+  return fminf(t, float((1 << BITS) - 1));
+}
+// worst of two rounding distances
+__device__ inline float worst2(float w, float e0, float e1) { return fmaxf(w, fmaxf(fabsf(e0), fabsf(e1))); }
+
 // Quantizes the complete group [g0, g0 + 64) of (sequence b, KV head g) from its
 // fp16 rows in sK / sV (all NT threads; the rows are visible to every thread).
-// Every thread first takes the values it quantizes into registers; after a
-// barrier the one-byte codes overwrite the rows' first 8 KB (sKc / sVc), so
-// the group needs no LDS beyond its 32 KB of rows.
+// Every thread first takes the values it quantizes into registers:
+//   K: thread (octet o, row quad rq) = channels [8o, 8o + 8) of rows
+//      [4rq, 4rq + 4), so that its codes of one row form one dword of the
+//      packed tile (INT4: 8 nibbles of one token; INT1: a quarter of the 32
+//      bits of one token, OR-ed over the four lanes of a quad);
+//   V: thread (token nv, quarter qv) = channels [32qv, 32qv + 32) of row nv.
+// The K channel extremes are combined over the row quads through LDS, the V
+// token extremes over two lanes.  After the first barrier the rows' LDS
+// holds the K extremes, the K parameters and the one-byte V codes, so the
+// group needs no LDS beyond its 32 KB of rows.
 template <int BITS>
 __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
                                uint16_t (&sK)[GS][D], uint16_t (&sV)[GS][D], bool kabs) {
-  const int tid = threadIdx.x, Hkv = c.num_kv_heads;
+  using Q = GroupQuant<BITS>;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, Hkv = c.num_kv_heads;
   const int n_out = BITS == 4 ? c.n_outlier : 0;
-
-  // ---- K: per channel over 64 tokens.  Threads 2ck and 2ck + 1 hold rows
-  // [0, 32) and [32, 64) of channel ck and combine their extremes.
-  const int ck = tid >> 1, hk = tid & 1;
-  float kx[32];
-  float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    kx[i] = h2f(sK[32 * hk + i][ck]);
-    mn = fminf(mn, kx[i]);
-    mx = fmaxf(mx, kx[i]);
-  }
-  mn = fminf(mn, __shfl_xor(mn, 1));
-  mx = fmaxf(mx, __shfl_xor(mx, 1));
-  // max|K| of a group whose rows are all new: the larger magnitude of its extremes
-  if (kabs && hk == 0)
-    atomicMax(reinterpret_cast<unsigned int*>(c.k_absmax) + ((int64_t)b * Hkv + g) * D + ck,
-              __float_as_uint(fmaxf(fabsf(mn), fabsf(mx))));
-  // outlier channels (INT4): scale and zero 0, hence codes 0; their values
-  // go to the fp16 outlier store below
-  for (int j = 0; j < n_out; ++j)
-    if (c.outlier_ch[g * KVC_MAX_OUTLIERS + j] == ck) mn = mx = 0.0f;
-  float ks, kz;
-  uint16_t ks16, kz16;
-  GroupQuant<BITS>::params(mn, mx, ks, kz, ks16, kz16);
   const int G = g0 / GS;
-  if (hk == 0) {
-    uint16_t* meta = c.k_meta + ((((int64_t)b * Hkv + g) * (c.max_tokens / GS) + G) * 2) * D;
-    meta[ck] = ks16;
-    meta[D + ck] = kz16;
-  }
-  const float kr = GroupQuant<BITS>::recip(ks);
-  uint32_t kq[8] = {};
+  const int o = tid & 15, rq = tid >> 4;   // K: channel octet, row quad
+  // Slots of the group's four 16-token tiles (a page holds whole tiles, so
+  // token 16j + x has slot tslot[j] + x), from uniform tokens.  Wave w's V
+  // rows (nv), outlier rows and K row quads (rq) all lie in tile w.
+  int64_t tslot[GS / TILE];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) kq[i >> 2] |= GroupQuant<BITS>::code(kx[i], ks, kz, kr) << (8 * (i & 3));
+  for (int j = 0; j < GS / TILE; ++j) tslot[j] = slot_of(c, b, g, g0 + TILE * j);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int64_t wslot = wu == 0 ? tslot[0] : wu == 1 ? tslot[1] : wu == 2 ? tslot[2] : tslot[3];
 
-  // ---- outlier stores: thread (token r, entry j) writes the token's fp16
-  // values of outlier channel j (0 past the list)
-  if (n_out > 0) {
-    const int r = tid >> 2, j = tid & 3;
-    const int ch = min(max(c.outlier_ch[g * KVC_MAX_OUTLIERS + j], 0), D - 1);
-    const int64_t slot = slot_of(c, b, g, g0 + r);
-    if (slot >= 0) {
-      c.k_outlier[slot * KVC_MAX_OUTLIERS + j] = j < n_out ? sK[r][ch] : (uint16_t)0;
-      if (c.v_outlier) c.v_outlier[slot * KVC_MAX_OUTLIERS + j] = j < n_out ? sV[r][ch] : (uint16_t)0;
-    }
-  }
-
-  // ---- V: per token over each 64-channel half.  Thread (token nv, quarter qv)
-  // reads its 32 values with four 16-byte LDS reads.  Isolated V outlier
-  // channels (bits of vout) stay out of the range and get code 0.
+  // ---- V values into registers
   const int nv = tid >> 2, qv = tid & 3, jv = qv >> 1, c0 = 32 * qv;
-  uint32_t vout = 0u;
-  if (n_out > 0 && c.v_outlier)
-    for (int j = 0; j < n_out; ++j) {
-      const int ch = c.outlier_ch[g * KVC_MAX_OUTLIERS + j] - c0;
-      if (ch >= 0 && ch < 32) vout |= 1u << ch;
-    }
   uint32_t vw[16];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -148,96 +172,256 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
     vw[4 * k + 3] = u.w;
   }
   auto vval = [&](int i) { return h2f((uint16_t)(vw[i >> 1] >> (16 * (i & 1)))); };
-  float vmn = INFINITY, vmx = -INFINITY;
+
+  // ---- outlier stores: thread (token r, entry j) writes the token's fp16
+  // values of outlier channel j (0 past the list)
+  if (n_out > 0) {
+    const int r = tid >> 2, j = tid & 3;
+    const int ch = min(max(c.outlier_ch[g * KVC_MAX_OUTLIERS + j], 0), D - 1);
+    if (wslot >= 0) {
+      const int64_t slot = wslot + (r & (TILE - 1));
+      c.k_outlier[slot * KVC_MAX_OUTLIERS + j] = j < n_out ? sK[r][ch] : (uint16_t)0;
+      if (c.v_outlier) c.v_outlier[slot * KVC_MAX_OUTLIERS + j] = j < n_out ? sV[r][ch] : (uint16_t)0;
+    }
+  }
+
+  // ---- V: per token over each 64-channel half (threads 2m, 2m + 1).  Isolated
+  // V outlier channels (bits of vout) stay out of the range and get code 0.
+  const bool viso = n_out > 0 && c.v_outlier;
+  uint32_t vout = 0u;
+  float vmn, vmx;
+  if (viso) {
+    for (int j = 0; j < n_out; ++j) {
+      const int ch = c.outlier_ch[g * KVC_MAX_OUTLIERS + j] - c0;
+      if (ch >= 0 && ch < 32) vout |= 1u << ch;
+    }
+    vmn = INFINITY;
+    vmx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const bool out = (vout >> i) & 1u;
-    vmn = out ? vmn : fminf(vmn, vval(i));
-    vmx = out ? vmx : fmaxf(vmx, vval(i));
+    for (int i = 0; i < 32; ++i) {
+      const bool out = (vout >> i) & 1u;
+      vmn = out ? vmn : fminf(vmn, vval(i));
+      vmx = out ? vmx : fmaxf(vmx, vval(i));
+    }
+  } else {
+    uint32_t a = pk_min(vw[0], vw[1]), m = pk_max(vw[0], vw[1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) {
+      a = pk_min(a, vw[i]);
+      m = pk_max(m, vw[i]);
+    }
+    vmn = fminf(h2f((uint16_t)a), h2f((uint16_t)(a >> 16)));
+    vmx = fmaxf(h2f((uint16_t)m), h2f((uint16_t)(m >> 16)));
   }
   vmn = fminf(vmn, __shfl_xor(vmn, 1));
   vmx = fmaxf(vmx, __shfl_xor(vmx, 1));
   float vs, vz;
   uint16_t vs16, vz16;
-  GroupQuant<BITS>::params(vmn, vmx, vs, vz, vs16, vz16);
-  if ((qv & 1) == 0) {
-    const int64_t slot = slot_of(c, b, g, g0 + nv);
-    if (slot >= 0) {
-      c.v_meta[slot * 4 + jv] = vs16;
-      c.v_meta[slot * 4 + 2 + jv] = vz16;
+  Q::params(vmn, vmx, vs, vz, vs16, vz16);
+  if ((qv & 1) == 0 && wslot >= 0) {
+    const int64_t slot = wslot + (nv & (TILE - 1));
+    c.v_meta[slot * 4 + jv] = vs16;
+    c.v_meta[slot * 4 + 2 + jv] = vz16;
+  }
+  const float vr = Q::recip(vs);
+  // one byte per code, channel order.  The second pass (rare, see qcode)
+  // takes its parameters through an empty asm so that the compiler keeps no
+  // value of the first pass alive for it.
+  uint32_t vq[8];
+  auto vcodes = [&](auto slow) {
+    constexpr bool SLOW = decltype(slow)::value;
+    float s = vs, z = vz, r = vr;
+    if constexpr (SLOW) asm volatile("" : "+v"(s), "+v"(z), "+v"(r));
+    float worst = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+      float e0, e1;
+      const float q0 = qcode<BITS, SLOW>(sub_h<0>(vw[i >> 1], -z), s, r, e0);
+      const float q1 = qcode<BITS, SLOW>(sub_h<1>(vw[i >> 1], -z), s, r, e1);
+      worst = worst2(worst, e0, e1);
+      vq[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(q0, (uint32_t)(i & 3), (i & 3) ? vq[i >> 2] : 0u);
+      vq[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(q1, (uint32_t)((i + 1) & 3), vq[i >> 2]);
+    }
+    return worst;
+  };
+  if (__builtin_amdgcn_ballot_w64(vcodes(std::false_type{}) >= NEAR_HALF) != 0)
+    vcodes(std::true_type{});
+  if (viso) {   // code 0 for the isolated channels: bit i of vout -> byte i of the codes
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const uint32_t bits = ((((vout >> (4 * m)) & 0xFu) * 0x00204081u) & 0x01010101u);
+      vq[m] &= ~((bits << 8) - bits);
     }
   }
-  const float vr = GroupQuant<BITS>::recip(vs);
-  uint32_t vq[8] = {};
-#pragma unroll
-  for (int i = 0; i < 32; ++i)
-    vq[i >> 2] |= ((vout >> i) & 1u ? 0u : GroupQuant<BITS>::code(vval(i), vs, vz, vr)) << (8 * (i & 3));
 
-  // ---- codes over the rows: every row value has been read above
-  __syncthreads();
-  uint8_t (&sKc)[GS][D] = *reinterpret_cast<uint8_t (*)[GS][D]>(&sK[0][0]);
-  uint8_t (&sVc)[GS][D] = *reinterpret_cast<uint8_t (*)[GS][D]>(&sV[0][0]);
+  // ---- K values into registers; kw[k][j] = channels 8o + 2j, 8o + 2j + 1 of row 4rq + k
+  uint32_t kw[4][4];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) sKc[32 * hk + i][ck] = (uint8_t)(kq[i >> 2] >> (8 * (i & 3)));
+  for (int k = 0; k < 4; ++k) {
+    const uint4 u = *reinterpret_cast<const uint4*>(&sK[4 * rq + k][8 * o]);
+    kw[k][0] = u.x;
+    kw[k][1] = u.y;
+    kw[k][2] = u.z;
+    kw[k][3] = u.w;
+  }
+  // ---- K extremes of the thread's 8 channels over its 4 rows, then over the
+  // wave's 4 row quads of the same octet (lanes o, o + 16, o + 32, o + 48)
+  uint32_t kmn[4], kmx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    kmn[j] = rows_min(pk_min(pk_min(kw[0][j], kw[1][j]), pk_min(kw[2][j], kw[3][j])));
+    kmx[j] = rows_max(pk_max(pk_max(kw[0][j], kw[1][j]), pk_max(kw[2][j], kw[3][j])));
+  }
+
+  // ---- every row value is in registers: the rows' LDS takes the K extremes
+  // (per wave and octet: 4 min pairs, 4 max pairs), the K parameters and the V codes
+  __syncthreads();
+  uint32_t* X = reinterpret_cast<uint32_t*>(&sK[0][0]);            // [4 waves][16 octets][8]
+  float* P = reinterpret_cast<float*>(&sK[0][0]) + (NT / 64) * 16 * 8;   // s[D], z[D], 1/s[D]
+  uint8_t (&sVc)[GS][D] = *reinterpret_cast<uint8_t (*)[GS][D]>(&sV[0][0]);
+  if (lane < 16) {
+    *reinterpret_cast<uint4*>(X + (w * 16 + o) * 8) = uint4{kmn[0], kmn[1], kmn[2], kmn[3]};
+    *reinterpret_cast<uint4*>(X + (w * 16 + o) * 8 + 4) = uint4{kmx[0], kmx[1], kmx[2], kmx[3]};
+  }
   *reinterpret_cast<uint4*>(&sVc[nv][c0]) = uint4{vq[0], vq[1], vq[2], vq[3]};
   *reinterpret_cast<uint4*>(&sVc[nv][c0 + 16]) = uint4{vq[4], vq[5], vq[6], vq[7]};
   __syncthreads();
 
-  // ---- pack codes into the lane/dword tile layout
-  const int W = tid, lane = W >> 2, d = W & 3;
-  if constexpr (BITS == 4) {
-    for (int tile = 0; tile < GS / TILE; ++tile) {
-      const int64_t slot = slot_of(c, b, g, g0 + TILE * tile);
-      if (slot < 0) continue;
-      // K: lane = 16*(c/32) + n, dword d = (c%32)/8, nibble j = c%8
-      {
-        const int n = lane & 15, chunk = lane >> 4, tok = TILE * tile + n;
-        const int cb = 32 * chunk + 8 * d;
-        uint32_t u = 0;
+  // ---- K parameters, one thread per channel
+  if (tid < D) {
+    const int ck = tid, oc = ck >> 3, j = (ck & 7) >> 1, sh = 16 * (ck & 1);
+    float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) u |= (uint32_t)sKc[tok][cb + j] << nib_pos(j);
-        reinterpret_cast<uint32_t*>(c.k_codes + (slot / TILE) * UNIT_BYTES)[W] = u;
+    for (int ww = 0; ww < NT / 64; ++ww) {
+      mn = fminf(mn, h2f((uint16_t)(X[(ww * 16 + oc) * 8 + j] >> sh)));
+      mx = fmaxf(mx, h2f((uint16_t)(X[(ww * 16 + oc) * 8 + 4 + j] >> sh)));
+    }
+    // max|K| of a group whose rows are all new: the larger magnitude of its extremes
+    if (kabs)
+      atomicMax(reinterpret_cast<unsigned int*>(c.k_absmax) + ((int64_t)b * Hkv + g) * D + ck,
+                __float_as_uint(fmaxf(fabsf(mn), fabsf(mx))));
+    // outlier channels (INT4): scale and zero 0, hence codes 0; their values
+    // went to the fp16 outlier store above
+    for (int e = 0; e < n_out; ++e)
+      if (c.outlier_ch[g * KVC_MAX_OUTLIERS + e] == ck) mn = mx = 0.0f;
+    float s, z;
+    uint16_t s16, z16;
+    Q::params(mn, mx, s, z, s16, z16);
+    uint16_t* meta = c.k_meta + ((((int64_t)b * Hkv + g) * (c.max_tokens / GS) + G) * 2) * D;
+    meta[ck] = s16;
+    meta[D + ck] = z16;
+    P[ck] = s;
+    P[D + ck] = z;
+    P[2 * D + ck] = Q::recip(s);
+  }
+  __syncthreads();
+
+  // ---- K codes, one packed dword per row
+  float ks[8], kz[8], kr[8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float4 s4 = *reinterpret_cast<const float4*>(P + 8 * o + 4 * h);
+    const float4 z4 = *reinterpret_cast<const float4*>(P + D + 8 * o + 4 * h);
+    const float4 r4 = *reinterpret_cast<const float4*>(P + 2 * D + 8 * o + 4 * h);
+    ks[4 * h] = s4.x; ks[4 * h + 1] = s4.y; ks[4 * h + 2] = s4.z; ks[4 * h + 3] = s4.w;
+    kz[4 * h] = z4.x; kz[4 * h + 1] = z4.y; kz[4 * h + 2] = z4.z; kz[4 * h + 3] = z4.w;
+    kr[4 * h] = r4.x; kr[4 * h + 1] = r4.y; kr[4 * h + 2] = r4.z; kr[4 * h + 3] = r4.w;
+  }
+  uint32_t kd[4];
+  auto kcodes = [&](auto slow) {
+    constexpr bool SLOW = decltype(slow)::value;
+    if constexpr (SLOW) {   // (as for V)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(ks[e]), "+v"(kz[e]), "+v"(kr[e]));
+    }
+    float worst = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float q[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float e0, e1;
+        q[2 * j] = qcode<BITS, SLOW>(sub_h<0>(kw[k][j], -kz[2 * j]), ks[2 * j], kr[2 * j], e0);
+        q[2 * j + 1] = qcode<BITS, SLOW>(sub_h<1>(kw[k][j], -kz[2 * j + 1]), ks[2 * j + 1], kr[2 * j + 1], e1);
+        worst = worst2(worst, e0, e1);
       }
-      // V: lane = 16*(n/4) + c%16, dword d = (c/16)/2, nibble j = 4*((c/16)%2) + n%4
-      {
-        const int kb = lane >> 4, m = lane & 15;
-        uint32_t u = 0;
+      if constexpr (BITS == 4) {
+        // channel e of the octet is nibble slot e (bit 16 (e & 1) + 4 (e >> 1)):
+        // byte 0 = slots 0 | 2 << 4, byte 1 = 4 | 6 << 4, byte 2 = 1 | 3 << 4, byte 3 = 5 | 7 << 4
+        uint32_t u = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[2], 16.0f, q[0]), 0u, 0u);
+        u = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[6], 16.0f, q[4]), 1u, u);
+        u = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[3], 16.0f, q[1]), 2u, u);
+        kd[k] = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[7], 16.0f, q[5]), 3u, u);
+      } else {
+        // octet 0 of a 32-channel block: channel e at bit 6 + (e >> 1) + 16 (e & 1)
+        // (bits 6..25, so the float sum of the set bits is exact)
+        float f = 0.0f;
 #pragma unroll
-        for (int par = 0; par < 2; ++par)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            u |= (uint32_t)sVc[TILE * tile + 4 * kb + i][16 * (2 * d + par) + m] << nib_pos(4 * par + i);
-        reinterpret_cast<uint32_t*>(c.v_codes + (slot / TILE) * UNIT_BYTES)[W] = u;
+        for (int e = 0; e < 8; ++e) f = fmaf(q[e], float(1u << (6 + (e >> 1) + 16 * (e & 1))), f);
+        kd[k] = (uint32_t)f;
       }
     }
+    return worst;
+  };
+  if (__builtin_amdgcn_ballot_w64(kcodes(std::false_type{}) >= NEAR_HALF) != 0)
+    kcodes(std::true_type{});
+
+  if constexpr (BITS == 4) {
+    // K tile of rows [16 tile, 16 tile + 16): lane 16 (c / 32) + n, dword (c % 32) / 8
+    if (wslot >= 0) {
+      uint32_t* unit = reinterpret_cast<uint32_t*>(c.k_codes + (wslot / TILE) * UNIT_BYTES);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) unit[4 * (16 * (o >> 2) + ((4 * rq + k) & 15)) + (o & 3)] = kd[k];
+    }
   } else {
-    const int64_t slot = slot_of(c, b, g, g0);
+    // octet v = o % 4 of its 32-channel block: octet 0's bit pattern rotated
+    // left by 0 / 4 / 28 / 24 bits, then OR-ed over the quad; lane v stores row 4rq + v
+    const int v = o & 3;
+    const uint32_t rr = v == 0 ? 0u : v == 1 ? 28u : v == 2 ? 4u : 8u;   // right rotation
+#pragma unroll
+    for (int k = 0; k < 4; ++k) kd[k] = quad_or(__builtin_amdgcn_alignbit(kd[k], kd[k], rr));
+    const uint32_t mine = v == 0 ? kd[0] : v == 1 ? kd[1] : v == 2 ? kd[2] : kd[3];
+    const int64_t slot = tslot[0];
     if (slot >= 0) {
-      // K: lane = 16*(c/32) + n%16, dword d = n/16, code k = c%32
-      {
-        const int tok = 16 * d + (lane & 15), cb = 32 * (lane >> 4);
-        uint32_t u = 0;
+      const int n = 4 * rq + v;
+      // lane 16 (c / 32) + n % 16, dword n / 16
+      reinterpret_cast<uint32_t*>(c.k_codes + (slot / GS) * UNIT_BYTES)[4 * (16 * (o >> 2) + (n & 15)) + (n >> 4)] = mine;
+    }
+  }
+
+  // ---- V: pack the byte codes into the lane/dword tile layout
+  const int W = tid, vl = W >> 2, d = W & 3;
+  if constexpr (BITS == 4) {
+    for (int tile = 0; tile < GS / TILE; ++tile) {
+      const int64_t slot = tslot[tile];
+      if (slot < 0) continue;
+      // lane = 16*(n/4) + c%16, dword d = (c/16)/2, nibble j = 4*((c/16)%2) + n%4
+      const int kb = vl >> 4, m = vl & 15;
+      uint32_t u = 0;
 #pragma unroll
-        for (int k = 0; k < 32; ++k) u |= (uint32_t)sKc[tok][cb + k] << bit_pos(k);
-        reinterpret_cast<uint32_t*>(c.k_codes + (slot / GS) * UNIT_BYTES)[W] = u;
-      }
-      // V: lane = 16*((n%16)/4) + c%16, dword d = n/16, code k = v1_code(c/16, n%4)
-      {
-        const int kb = lane >> 4, m = lane & 15;
-        uint32_t u = 0;
+      for (int par = 0; par < 2; ++par)
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+        for (int i = 0; i < 4; ++i)
+          u |= (uint32_t)sVc[TILE * tile + 4 * kb + i][16 * (2 * d + par) + m] << nib_pos(4 * par + i);
+      reinterpret_cast<uint32_t*>(c.v_codes + (slot / TILE) * UNIT_BYTES)[W] = u;
+    }
+  } else {
+    const int64_t slot = tslot[0];
+    if (slot >= 0) {
+      // lane = 16*((n%16)/4) + c%16, dword d = n/16, code k = v1_code(c/16, n%4)
+      const int kb = vl >> 4, m = vl & 15;
+      uint32_t u = 0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            u |= (uint32_t)sVc[16 * d + 4 * kb + i][16 * ct + m] << bit_pos(v1_code(ct, i));
-        reinterpret_cast<uint32_t*>(c.v_codes + (slot / GS) * UNIT_BYTES)[W] = u;
-      }
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          u |= (uint32_t)sVc[16 * d + 4 * kb + i][16 * ct + m] << bit_pos(v1_code(ct, i));
+      reinterpret_cast<uint32_t*>(c.v_codes + (slot / GS) * UNIT_BYTES)[W] = u;
     }
   }
 }
-
 template <int FMT>
-__global__ __launch_bounds__(NT) void append_groups_kernel(
+__global__ __launch_bounds__(NT, 5) void append_groups_kernel(
     kvc_cache c, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ n_new, int n_new_max) {
   constexpr int BITS = FMT == KVC_FMT_INT4 ? 4 : 1;
@@ -350,7 +534,7 @@ __global__ __launch_bounds__(NT) void append_groups_kernel(
 // == 63) stages the 63 tail rows in LDS and quantizes; the tail is then empty,
 // so no workgroup writes it in that step.
 template <int FMT>
-__global__ __launch_bounds__(NT) void append_token_kernel(
+__global__ __launch_bounds__(NT, 5) void append_token_kernel(
     kvc_cache c, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ n_new, int32_t* overflow) {
   constexpr int BITS = FMT == KVC_FMT_INT4 ? 4 : 1;
