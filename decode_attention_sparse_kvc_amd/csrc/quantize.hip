@@ -101,10 +101,16 @@ __device__ inline uint32_t quad_or(uint32_t x) {
   return x;
 }
 
-// Code of one value as a float in [0, 2^BITS - 1] (see GroupQuant::code).  The
-// fast form rounds a = fl((x - z) * r) and records how close a came to a
-// half-integer in worst; a caller whose wave saw worst >= NEAR_HALF anywhere
-// recomputes its codes with SLOW, which takes the division where a is that close.
+// Code of one value as a float in [0, 2^BITS - 1] from d = fl(x - z) (see
+// GroupQuant::code).  The fast form rounds a = fl(d * r) and returns a - rint(a)
+// in e; a caller whose wave saw |e| >= NEAR_HALF anywhere recomputes its codes
+// with SLOW, which takes the division where a is that close to a half-integer.
+// The fast form's rounding is written as instructions, since the compiler
+// would first canonicalize the rounded value for fminf (one more instruction
+// per code): 1 bit, rint with the clamp modifier, which is the code
+// min(max(rint(a), 0), 1) for the a < 1.5 of an unsaturated scale, while a
+// larger a (a saturated scale) lands 0.5 or more from the clamped value and
+// takes the second pass; INT4, v_min_f32 with the top code.
 constexpr float NEAR_HALF = 0.5f - 0x1p-17f;
 // fl(h - z) for the fp16 value h in half H of the dword u and nz = -z, as
 // one mixed-precision fma (h * 1 + nz, rounded once): the conversion of h
@@ -120,13 +126,25 @@ __device__ inline float sub_h(uint32_t u, float nz) {
 }
 template <int BITS, bool SLOW>
 __device__ inline float qcode(float d, float s, float r, float& e) {
+  constexpr float TOP = float((1 << BITS) - 1);
   const float a = __fmul_rn(d, r);
-  float t = rintf(a);
-  e = __fsub_rn(a, t);
   if constexpr (SLOW) {
+    float t = rintf(a);
+    e = __fsub_rn(a, t);
     if (fabsf(e) >= NEAR_HALF) t = rintf(__fdiv_rn(d, s));
+    return fminf(t, TOP);
+  } else if constexpr (BITS == 1) {
+    float t;
+    asm("v_rndne_f32_e64 %0, %1 clamp" : "=v"(t) : "v"(a));
+    e = __fsub_rn(a, t);
+    return t;
+  } else {
+    const float t = rintf(a);
+    e = __fsub_rn(a, t);
+    float q;
+    asm("v_min_f32_e32 %0, %1, %2" : "=v"(q) : "s"(TOP), "v"(t));
+    return q;
   }
-  return fminf(t, float((1 << BITS) - 1));
 }
 // worst of two rounding distances
 __device__ inline float worst2(float w, float e0, float e1) { return fmaxf(w, fmaxf(fabsf(e0), fabsf(e1))); }
@@ -143,9 +161,14 @@ __device__ inline float worst2(float w, float e0, float e1) { return fmaxf(w, fm
 // token extremes over two lanes.  After the first barrier the rows' LDS
 // holds the K extremes, the K parameters and the one-byte V codes, so the
 // group needs no LDS beyond its 32 KB of rows.
-template <int BITS>
+// DIRECT: the rows are read from global memory instead (row r at krow + r *
+// rstride, vrow + r * rstride; no outlier channels), each thread loading
+// exactly the values it quantizes, and the LDS only carries the exchanges.
+template <int BITS, bool DIRECT = false>
 __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
-                               uint16_t (&sK)[GS][D], uint16_t (&sV)[GS][D], bool kabs) {
+                               uint16_t (&sK)[GS][D], uint16_t (&sV)[GS][D], bool kabs,
+                               const uint16_t* krow = nullptr, const uint16_t* vrow = nullptr,
+                               int64_t rstride = 0) {
   using Q = GroupQuant<BITS>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, Hkv = c.num_kv_heads;
   const int n_out = BITS == 4 ? c.n_outlier : 0;
@@ -165,7 +188,8 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
   uint32_t vw[16];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint4 u = *reinterpret_cast<const uint4*>(&sV[nv][c0 + 8 * k]);
+    const uint4 u = DIRECT ? *reinterpret_cast<const uint4*>(vrow + nv * rstride + c0 + 8 * k)
+                           : *reinterpret_cast<const uint4*>(&sV[nv][c0 + 8 * k]);
     vw[4 * k] = u.x;
     vw[4 * k + 1] = u.y;
     vw[4 * k + 2] = u.z;
@@ -175,7 +199,7 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
 
   // ---- outlier stores: thread (token r, entry j) writes the token's fp16
   // values of outlier channel j (0 past the list)
-  if (n_out > 0) {
+  if (!DIRECT && n_out > 0) {
     const int r = tid >> 2, j = tid & 3;
     const int ch = min(max(c.outlier_ch[g * KVC_MAX_OUTLIERS + j], 0), D - 1);
     if (wslot >= 0) {
@@ -256,13 +280,16 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
 
   // ---- K values into registers; kw[k][j] = channels 8o + 2j, 8o + 2j + 1 of row 4rq + k
   uint32_t kw[4][4];
+  {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint4 u = *reinterpret_cast<const uint4*>(&sK[4 * rq + k][8 * o]);
-    kw[k][0] = u.x;
-    kw[k][1] = u.y;
-    kw[k][2] = u.z;
-    kw[k][3] = u.w;
+    for (int k = 0; k < 4; ++k) {
+      const uint4 u = DIRECT ? *reinterpret_cast<const uint4*>(krow + (4 * rq + k) * rstride + 8 * o)
+                             : *reinterpret_cast<const uint4*>(&sK[4 * rq + k][8 * o]);
+      kw[k][0] = u.x;
+      kw[k][1] = u.y;
+      kw[k][2] = u.z;
+      kw[k][3] = u.w;
+    }
   }
   // ---- K extremes of the thread's 8 channels over its 4 rows, then over the
   // wave's 4 row quads of the same octet (lanes o, o + 16, o + 32, o + 48)
@@ -274,8 +301,9 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
   }
 
   // ---- every row value is in registers: the rows' LDS takes the K extremes
-  // (per wave and octet: 4 min pairs, 4 max pairs), the K parameters and the V codes
-  __syncthreads();
+  // (per wave and octet: 4 min pairs, 4 max pairs), the K parameters and the V
+  // codes (DIRECT: no row was staged there)
+  if constexpr (!DIRECT) __syncthreads();
   uint32_t* X = reinterpret_cast<uint32_t*>(&sK[0][0]);            // [4 waves][16 octets][8]
   float* P = reinterpret_cast<float*>(&sK[0][0]) + (NT / 64) * 16 * 8;   // s[D], z[D], 1/s[D]
   uint8_t (&sVc)[GS][D] = *reinterpret_cast<uint8_t (*)[GS][D]>(&sV[0][0]);
@@ -445,6 +473,18 @@ __global__ __launch_bounds__(NT, 5) void append_groups_kernel(
   // the group of a quantized cache (nothing else needs them; an fp16 cache has no tail).
   const bool complete = grouped(FMT) && hi == g0 + GS;
   const int r0 = complete ? 0 : lo - g0;
+
+  // A complete group of new rows on a cache without fp16 copies or outlier
+  // channels (the bulk of a prefill) goes straight from the new rows to the
+  // quantizer's registers.
+  if constexpr (grouped(FMT)) {
+    if (complete && lo == g0 && !c.k16 && !c.kT && (BITS == 1 || c.n_outlier == 0)) {
+      const int64_t base = (((int64_t)b * n_new_max + (g0 - L)) * Hkv + g) * D;
+      quantize_group<BITS, true>(c, b, g, g0, sK, sV, c.k_absmax != nullptr, k_new + base,
+                                 v_new + base, (int64_t)Hkv * D);
+      return;
+    }
+  }
 
   // ---- stage rows [g0 + r0, hi) in LDS: 16 threads per row, 8 halves each.
   // Every thread issues all of its (up to 4 + 4) row loads before its first
