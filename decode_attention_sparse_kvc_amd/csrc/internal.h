@@ -26,6 +26,7 @@ __host__ __device__ inline int page_tokens(const kvc_cache& c) {
 // Returns -1 when the block table names a page outside the pools, so callers
 // skip the token instead of touching memory they do not own.
 __device__ inline int64_t slot_of(const kvc_cache& c, int b, int g, int t) {
+  if (c.page_size == 0) return ((int64_t)b * c.num_kv_heads + g) * (int64_t)c.max_tokens + t;
   const int P = page_tokens(c);
   const int page = t / P;
   const int off = t - page * P;

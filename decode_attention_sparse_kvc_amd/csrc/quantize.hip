@@ -70,14 +70,19 @@ struct GroupQuant {
 constexpr int ARRIVE = 1 << 24;
 constexpr int LEN_MASK = ARRIVE - 1;
 
-// Packed-fp16 helpers of the group quantizer.
+// Packed-fp16 minimum / maximum of the group quantizer's extremes, written as
+// the instructions: the compiler would first canonicalize both operands (two
+// more instructions each time).  The inputs are fp16 K / V values; a quiet NaN
+// among them is passed over as by fminf / fmaxf.
 __device__ inline uint32_t pk_min(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(kvc_h2v, a),
-                                                                __builtin_bit_cast(kvc_h2v, b)));
+  uint32_t r;
+  asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 __device__ inline uint32_t pk_max(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(kvc_h2v, a),
-                                                                __builtin_bit_cast(kvc_h2v, b)));
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 // Elementwise minimum / maximum of fp16 pairs over lanes l, l ^ 16, l ^ 32, l ^ 48
 // (gfx950 row-swap moves: each swap of a value with itself yields it and the
@@ -94,6 +99,9 @@ __device__ inline uint32_t rows_max(uint32_t x) {
   const auto t = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return pk_max(t[0], t[1]);
 }
+// LDS accesses of one wave execute in issue order, so values exchanged through
+// LDS inside a wave only need the compiler to keep program order.
+__device__ inline void wave_lds_order() { asm volatile("" ::: "memory"); }
 // x | the same register of lanes l ^ 1 and l ^ 2 (DPP quad permutations).
 __device__ inline uint32_t quad_or(uint32_t x) {
   x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);   // [1, 0, 3, 2]
@@ -149,39 +157,44 @@ __device__ inline float qcode(float d, float s, float r, float& e) {
 // worst of two rounding distances
 __device__ inline float worst2(float w, float e0, float e1) { return fmaxf(w, fmaxf(fabsf(e0), fabsf(e1))); }
 
-// Quantizes the complete group [g0, g0 + 64) of (sequence b, KV head g) from its
-// fp16 rows in sK / sV (all NT threads; the rows are visible to every thread).
-// Every thread first takes the values it quantizes into registers:
+// Quantizes the complete group [g0, g0 + 64) of (sequence b, KV head g) (all
+// NT threads).  Every thread first takes the values it quantizes into registers:
 //   K: thread (octet o, row quad rq) = channels [8o, 8o + 8) of rows
 //      [4rq, 4rq + 4), so that its codes of one row form one dword of the
 //      packed tile (INT4: 8 nibbles of one token; INT1: a quarter of the 32
 //      bits of one token, OR-ed over the four lanes of a quad);
-//   V: thread (token nv, quarter qv) = channels [32qv, 32qv + 32) of row nv.
-// The K channel extremes are combined over the row quads through LDS, the V
-// token extremes over two lanes.  After the first barrier the rows' LDS
-// holds the K extremes, the K parameters and the one-byte V codes, so the
-// group needs no LDS beyond its 32 KB of rows.
-// DIRECT: the rows are read from global memory instead (row r at krow + r *
-// rstride, vrow + r * rstride; no outlier channels), each thread loading
-// exactly the values it quantizes, and the LDS only carries the exchanges.
+//   V: thread (token nv, quarter qv) = channels [32qv, 32qv + 32) of row nv
+//      (wave w: rows [16w, 16w + 16), one 16-token tile).
+// The V token extremes are combined over two lanes, the K channel extremes
+// over the threads of an octet.
+// Staged mode (DIRECT false): the rows are in sK / sV (visible to every
+// thread); octet o = tid % 16, row quad rq = tid / 16, so an octet's row quads
+// span the four waves and the K extremes and parameters go through LDS with
+// workgroup barriers; the rows' LDS then holds those and the one-byte V codes.
+// DIRECT: row r is read from krow + r * rstride / vrow + r * rstride (a
+// complete group of new rows, no outlier channels); wave w takes octets
+// [4w, 4w + 4) (o = 4w + lane % 4, rq = lane / 4), so every exchange stays
+// inside the wave (its own LDS area, no barrier) and the workgroup never
+// synchronizes.
 template <int BITS, bool DIRECT = false>
 __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
                                uint16_t (&sK)[GS][D], uint16_t (&sV)[GS][D], bool kabs,
                                const uint16_t* krow = nullptr, const uint16_t* vrow = nullptr,
                                int64_t rstride = 0) {
   using Q = GroupQuant<BITS>;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, Hkv = c.num_kv_heads;
-  const int n_out = BITS == 4 ? c.n_outlier : 0;
+  const int tid = threadIdx.x, lane = tid & 63, Hkv = c.num_kv_heads;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_out = (BITS == 4 && !DIRECT) ? c.n_outlier : 0;
   const int G = g0 / GS;
-  const int o = tid & 15, rq = tid >> 4;   // K: channel octet, row quad
+  const int o = DIRECT ? 4 * w + (lane & 3) : (tid & 15);   // K: channel octet
+  const int rq = DIRECT ? (lane >> 2) : (tid >> 4);         // K: row quad
   // Slots of the group's four 16-token tiles (a page holds whole tiles, so
   // token 16j + x has slot tslot[j] + x), from uniform tokens.  Wave w's V
-  // rows (nv), outlier rows and K row quads (rq) all lie in tile w.
+  // rows (nv) and outlier rows lie in tile w.
   int64_t tslot[GS / TILE];
 #pragma unroll
   for (int j = 0; j < GS / TILE; ++j) tslot[j] = slot_of(c, b, g, g0 + TILE * j);
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int64_t wslot = wu == 0 ? tslot[0] : wu == 1 ? tslot[1] : wu == 2 ? tslot[2] : tslot[3];
+  const int64_t wslot = w == 0 ? tslot[0] : w == 1 ? tslot[1] : w == 2 ? tslot[2] : tslot[3];
 
   // ---- V values into registers
   const int nv = tid >> 2, qv = tid & 3, jv = qv >> 1, c0 = 32 * qv;
@@ -199,7 +212,7 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
 
   // ---- outlier stores: thread (token r, entry j) writes the token's fp16
   // values of outlier channel j (0 past the list)
-  if (!DIRECT && n_out > 0) {
+  if (n_out > 0) {
     const int r = tid >> 2, j = tid & 3;
     const int ch = min(max(c.outlier_ch[g * KVC_MAX_OUTLIERS + j], 0), D - 1);
     if (wslot >= 0) {
@@ -280,52 +293,76 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
 
   // ---- K values into registers; kw[k][j] = channels 8o + 2j, 8o + 2j + 1 of row 4rq + k
   uint32_t kw[4][4];
-  {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint4 u = DIRECT ? *reinterpret_cast<const uint4*>(krow + (4 * rq + k) * rstride + 8 * o)
-                             : *reinterpret_cast<const uint4*>(&sK[4 * rq + k][8 * o]);
-      kw[k][0] = u.x;
-      kw[k][1] = u.y;
-      kw[k][2] = u.z;
-      kw[k][3] = u.w;
-    }
+  for (int k = 0; k < 4; ++k) {
+    const uint4 u = DIRECT ? *reinterpret_cast<const uint4*>(krow + (4 * rq + k) * rstride + 8 * o)
+                           : *reinterpret_cast<const uint4*>(&sK[4 * rq + k][8 * o]);
+    kw[k][0] = u.x;
+    kw[k][1] = u.y;
+    kw[k][2] = u.z;
+    kw[k][3] = u.w;
   }
   // ---- K extremes of the thread's 8 channels over its 4 rows, then over the
-  // wave's 4 row quads of the same octet (lanes o, o + 16, o + 32, o + 48)
+  // octet's other row quads in the wave: lanes o + 16i (staged), lanes
+  // 4rq + o % 4 (DIRECT: rotations by 4 and 8 inside each 16-lane row first)
   uint32_t kmn[4], kmx[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    kmn[j] = rows_min(pk_min(pk_min(kw[0][j], kw[1][j]), pk_min(kw[2][j], kw[3][j])));
-    kmx[j] = rows_max(pk_max(pk_max(kw[0][j], kw[1][j]), pk_max(kw[2][j], kw[3][j])));
+    uint32_t mn = pk_min(pk_min(kw[0][j], kw[1][j]), pk_min(kw[2][j], kw[3][j]));
+    uint32_t mx = pk_max(pk_max(kw[0][j], kw[1][j]), pk_max(kw[2][j], kw[3][j]));
+    if constexpr (DIRECT) {
+      mn = pk_min(mn, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mn, 0x124, 0xF, 0xF, false));
+      mx = pk_max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x124, 0xF, 0xF, false));
+      mn = pk_min(mn, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mn, 0x128, 0xF, 0xF, false));
+      mx = pk_max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, 0x128, 0xF, 0xF, false));
+    }
+    kmn[j] = rows_min(mn);
+    kmx[j] = rows_max(mx);
   }
 
-  // ---- every row value is in registers: the rows' LDS takes the K extremes
-  // (per wave and octet: 4 min pairs, 4 max pairs), the K parameters and the V
-  // codes (DIRECT: no row was staged there)
-  if constexpr (!DIRECT) __syncthreads();
-  uint32_t* X = reinterpret_cast<uint32_t*>(&sK[0][0]);            // [4 waves][16 octets][8]
-  float* P = reinterpret_cast<float*>(&sK[0][0]) + (NT / 64) * 16 * 8;   // s[D], z[D], 1/s[D]
+  // ---- K parameters, one channel per thread (staged: threads 0..127 after
+  // a barrier; DIRECT: channel 32w + lane / 2 in lanes 2m, 2m + 1 of wave w),
+  // from the extremes in X; they go to P
   uint8_t (&sVc)[GS][D] = *reinterpret_cast<uint8_t (*)[GS][D]>(&sV[0][0]);
-  if (lane < 16) {
-    *reinterpret_cast<uint4*>(X + (w * 16 + o) * 8) = uint4{kmn[0], kmn[1], kmn[2], kmn[3]};
-    *reinterpret_cast<uint4*>(X + (w * 16 + o) * 8 + 4) = uint4{kmx[0], kmx[1], kmx[2], kmx[3]};
+  uint32_t* X;
+  float* P;
+  if constexpr (DIRECT) {
+    X = reinterpret_cast<uint32_t*>(&sK[0][0]) + w * 32;                 // [4 octets][8]
+    P = reinterpret_cast<float*>(&sK[0][0]) + (NT / 64) * 32 + w * 96;    // s[32], z[32], 1/s[32]
+    if (lane < 4) {
+      *reinterpret_cast<uint4*>(X + lane * 8) = uint4{kmn[0], kmn[1], kmn[2], kmn[3]};
+      *reinterpret_cast<uint4*>(X + lane * 8 + 4) = uint4{kmx[0], kmx[1], kmx[2], kmx[3]};
+    }
+    *reinterpret_cast<uint4*>(&sVc[nv][c0]) = uint4{vq[0], vq[1], vq[2], vq[3]};
+    *reinterpret_cast<uint4*>(&sVc[nv][c0 + 16]) = uint4{vq[4], vq[5], vq[6], vq[7]};
+    wave_lds_order();
+  } else {
+    // every row value is in registers: the rows' LDS takes the K extremes
+    // (per wave and octet: 4 min pairs, 4 max pairs), the K parameters and the V codes
+    __syncthreads();
+    X = reinterpret_cast<uint32_t*>(&sK[0][0]);                          // [4 waves][16 octets][8]
+    P = reinterpret_cast<float*>(&sK[0][0]) + (NT / 64) * 16 * 8;         // s[D], z[D], 1/s[D]
+    if (lane < 16) {
+      *reinterpret_cast<uint4*>(X + (w * 16 + o) * 8) = uint4{kmn[0], kmn[1], kmn[2], kmn[3]};
+      *reinterpret_cast<uint4*>(X + (w * 16 + o) * 8 + 4) = uint4{kmx[0], kmx[1], kmx[2], kmx[3]};
+    }
+    *reinterpret_cast<uint4*>(&sVc[nv][c0]) = uint4{vq[0], vq[1], vq[2], vq[3]};
+    *reinterpret_cast<uint4*>(&sVc[nv][c0 + 16]) = uint4{vq[4], vq[5], vq[6], vq[7]};
+    __syncthreads();
   }
-  *reinterpret_cast<uint4*>(&sVc[nv][c0]) = uint4{vq[0], vq[1], vq[2], vq[3]};
-  *reinterpret_cast<uint4*>(&sVc[nv][c0 + 16]) = uint4{vq[4], vq[5], vq[6], vq[7]};
-  __syncthreads();
-
-  // ---- K parameters, one thread per channel
-  if (tid < D) {
-    const int ck = tid, oc = ck >> 3, j = (ck & 7) >> 1, sh = 16 * (ck & 1);
+  if (DIRECT || tid < D) {
+    const int cl = DIRECT ? (lane >> 1) : tid;         // channel inside P
+    const int ck = DIRECT ? 32 * w + cl : tid;         // channel of the head
+    const int oc = cl >> 3, j = (cl & 7) >> 1, sh = 16 * (cl & 1);
     float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < NT / 64; ++ww) {
+    for (int ww = 0; ww < (DIRECT ? 1 : NT / 64); ++ww) {
       mn = fminf(mn, h2f((uint16_t)(X[(ww * 16 + oc) * 8 + j] >> sh)));
       mx = fmaxf(mx, h2f((uint16_t)(X[(ww * 16 + oc) * 8 + 4 + j] >> sh)));
     }
+    const bool writer = !DIRECT || (lane & 1) == 0;
     // max|K| of a group whose rows are all new: the larger magnitude of its extremes
-    if (kabs)
+    if (kabs && writer)
       atomicMax(reinterpret_cast<unsigned int*>(c.k_absmax) + ((int64_t)b * Hkv + g) * D + ck,
                 __float_as_uint(fmaxf(fabsf(mn), fabsf(mx))));
     // outlier channels (INT4): scale and zero 0, hence codes 0; their values
@@ -335,25 +372,32 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
     float s, z;
     uint16_t s16, z16;
     Q::params(mn, mx, s, z, s16, z16);
-    uint16_t* meta = c.k_meta + ((((int64_t)b * Hkv + g) * (c.max_tokens / GS) + G) * 2) * D;
-    meta[ck] = s16;
-    meta[D + ck] = z16;
-    P[ck] = s;
-    P[D + ck] = z;
-    P[2 * D + ck] = Q::recip(s);
+    if (writer) {
+      uint16_t* meta = c.k_meta + ((((int64_t)b * Hkv + g) * (c.max_tokens / GS) + G) * 2) * D;
+      meta[ck] = s16;
+      meta[D + ck] = z16;
+      const int np = DIRECT ? 32 : D;
+      P[cl] = s;
+      P[np + cl] = z;
+      P[2 * np + cl] = Q::recip(s);
+    }
   }
-  __syncthreads();
+  if constexpr (DIRECT) wave_lds_order();
+  else __syncthreads();
 
   // ---- K codes, one packed dword per row
   float ks[8], kz[8], kr[8];
+  {
+    const int np = DIRECT ? 32 : D, pc = DIRECT ? 8 * (lane & 3) : 8 * o;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float4 s4 = *reinterpret_cast<const float4*>(P + 8 * o + 4 * h);
-    const float4 z4 = *reinterpret_cast<const float4*>(P + D + 8 * o + 4 * h);
-    const float4 r4 = *reinterpret_cast<const float4*>(P + 2 * D + 8 * o + 4 * h);
-    ks[4 * h] = s4.x; ks[4 * h + 1] = s4.y; ks[4 * h + 2] = s4.z; ks[4 * h + 3] = s4.w;
-    kz[4 * h] = z4.x; kz[4 * h + 1] = z4.y; kz[4 * h + 2] = z4.z; kz[4 * h + 3] = z4.w;
-    kr[4 * h] = r4.x; kr[4 * h + 1] = r4.y; kr[4 * h + 2] = r4.z; kr[4 * h + 3] = r4.w;
+    for (int h = 0; h < 2; ++h) {
+      const float4 s4 = *reinterpret_cast<const float4*>(P + pc + 4 * h);
+      const float4 z4 = *reinterpret_cast<const float4*>(P + np + pc + 4 * h);
+      const float4 r4 = *reinterpret_cast<const float4*>(P + 2 * np + pc + 4 * h);
+      ks[4 * h] = s4.x; ks[4 * h + 1] = s4.y; ks[4 * h + 2] = s4.z; ks[4 * h + 3] = s4.w;
+      kz[4 * h] = z4.x; kz[4 * h + 1] = z4.y; kz[4 * h + 2] = z4.z; kz[4 * h + 3] = z4.w;
+      kr[4 * h] = r4.x; kr[4 * h + 1] = r4.y; kr[4 * h + 2] = r4.z; kr[4 * h + 3] = r4.w;
+    }
   }
   uint32_t kd[4];
   auto kcodes = [&](auto slow) {
@@ -396,8 +440,10 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
 
   if constexpr (BITS == 4) {
     // K tile of rows [16 tile, 16 tile + 16): lane 16 (c / 32) + n, dword (c % 32) / 8
-    if (wslot >= 0) {
-      uint32_t* unit = reinterpret_cast<uint32_t*>(c.k_codes + (wslot / TILE) * UNIT_BYTES);
+    const int tq = rq >> 2;
+    const int64_t slot = tq == 0 ? tslot[0] : tq == 1 ? tslot[1] : tq == 2 ? tslot[2] : tslot[3];
+    if (slot >= 0) {
+      uint32_t* unit = reinterpret_cast<uint32_t*>(c.k_codes + (slot / TILE) * UNIT_BYTES);
 #pragma unroll
       for (int k = 0; k < 4; ++k) unit[4 * (16 * (o >> 2) + ((4 * rq + k) & 15)) + (o & 3)] = kd[k];
     }
@@ -417,14 +463,17 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
     }
   }
 
-  // ---- V: pack the byte codes into the lane/dword tile layout
-  const int W = tid, vl = W >> 2, d = W & 3;
+  // ---- V: pack the byte codes into the lane/dword tile layout.  Staged: thread
+  // W writes dword W of every tile; DIRECT: wave w packs its own rows (tile w;
+  // 1 bit: dword w of every lane), 4 dwords a lane (INT4) or 1 (1 bit).
   if constexpr (BITS == 4) {
-    for (int tile = 0; tile < GS / TILE; ++tile) {
-      const int64_t slot = tslot[tile];
+#pragma unroll
+    for (int it = 0; it < (DIRECT ? 4 : GS / TILE); ++it) {
+      const int tile = DIRECT ? w : it, W = DIRECT ? lane + 64 * it : tid;
+      const int64_t slot = DIRECT ? wslot : tslot[it];
       if (slot < 0) continue;
       // lane = 16*(n/4) + c%16, dword d = (c/16)/2, nibble j = 4*((c/16)%2) + n%4
-      const int kb = vl >> 4, m = vl & 15;
+      const int vl = W >> 2, d = W & 3, kb = vl >> 4, m = vl & 15;
       uint32_t u = 0;
 #pragma unroll
       for (int par = 0; par < 2; ++par)
@@ -437,17 +486,18 @@ __device__ void quantize_group(const kvc_cache& c, int b, int g, int g0,
     const int64_t slot = tslot[0];
     if (slot >= 0) {
       // lane = 16*((n%16)/4) + c%16, dword d = n/16, code k = v1_code(c/16, n%4)
-      const int kb = vl >> 4, m = vl & 15;
+      const int vl = DIRECT ? lane : (tid >> 2), d = DIRECT ? w : (tid & 3), kb = vl >> 4, m = vl & 15;
       uint32_t u = 0;
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           u |= (uint32_t)sVc[16 * d + 4 * kb + i][16 * ct + m] << bit_pos(v1_code(ct, i));
-      reinterpret_cast<uint32_t*>(c.v_codes + (slot / GS) * UNIT_BYTES)[W] = u;
+      reinterpret_cast<uint32_t*>(c.v_codes + (slot / GS) * UNIT_BYTES)[4 * vl + d] = u;
     }
   }
 }
+
 template <int FMT>
 __global__ __launch_bounds__(NT, 5) void append_groups_kernel(
     kvc_cache c, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
