@@ -70,9 +70,13 @@ def _rows(rng, B, n, hkv, outliers=True):
 STEPS = [[100, 64, 3], [1, 1, 1], [63, 0, 130], [70, 5, 61], [1, 64, 0]]
 
 
+# (complete groups of new rows on a cache without fp16 rows or outliers take
+# the quantizer's direct-load mode, the others the staged one: both run here)
 @pytest.mark.parametrize("fmt,page", [("int4", 0), ("int1", 0), ("int4", 16), ("int1", 64),
-                                      ("fp16", 0), ("fp16", 16)])
+                                      ("int4", 32), ("int4", -16), ("fp16", 0), ("fp16", 16)])
 def test_incremental_ragged_appends(fmt, page):
+    rows16 = page == 16        # page -16: 16-token pages without the fp16 rows
+    page = abs(page)
     rng = np.random.default_rng(7)
     B, hkv, cap = 3, 2, 384
     total = np.sum(STEPS, axis=0)
@@ -83,7 +87,7 @@ def test_incremental_ragged_appends(fmt, page):
         per = cap // page
         table = rng.permutation(B * per).astype(np.int32).reshape(B, per)
         kw = dict(page_size=page, block_table=torch.from_numpy(table), num_pages=B * per)
-    cache = KvcCache(fmt, B, hkv, cap, fp16_rows=(fmt != "fp16" and page == 16) or fmt == "fp16",
+    cache = KvcCache(fmt, B, hkv, cap, fp16_rows=(fmt != "fp16" and rows16) or fmt == "fp16",
                      kT=(fmt == "fp16" and page == 0), **kw)
     lens = np.zeros(B, np.int64)
     for step in STEPS:
@@ -203,12 +207,14 @@ def test_full_size_prefill(make):
     check_cache_state(cache, w.k, w.v, w.seq_lens)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int1"])
-def test_code_rounding_at_half_integers(fmt):
+@pytest.mark.parametrize("fmt,rows", [("int4", False), ("int1", False), ("int4", True), ("int1", True)])
+def test_code_rounding_at_half_integers(fmt, rows):
     """Values whose quotient (x - z) / s is exactly a half-integer, or one fp16 step
     off it, for scales with inexact reciprocals (3, 7, 0.75, 5/16, ...): the
     kernel's codes (a reciprocal product, the division near half-integers) equal
-    the oracle's correctly rounded quotient, ties to even, for K channels and V rows."""
+    the oracle's correctly rounded quotient, ties to even, for K channels and V rows
+    (without fp16 rows the groups take the direct-load quantizer, with them the
+    staged one)."""
     top = 15 if fmt == "int4" else 1
     rng = np.random.default_rng(50)
     hkv = 2
@@ -228,7 +234,7 @@ def test_code_rounding_at_half_integers(fmt):
                 k[0, 64 * grp:64 * grp + 64, g, ci] = col             # a K channel over the group
                 v[0, 64 * grp + ci, g, :64] = col                     # a V row, low half
                 v[0, 64 * grp + ci, g, 64:] = col[::-1]               # and high half
-    cache = KvcCache(fmt, 1, hkv, 192)
+    cache = KvcCache(fmt, 1, hkv, 192, fp16_rows=rows)
     cache.append(dev(k), dev(v))
     torch.cuda.synchronize()
     check_cache_state(cache, k, v, [128])
