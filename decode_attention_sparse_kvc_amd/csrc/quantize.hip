@@ -1,9 +1,12 @@
 // Append + quantize (TailorKV article section 2.2; on-device KV article section 3.1).
 //
 // One workgroup per (64-token group touched by the append, KV head, sequence).
-// It stages the group's fp16 K/V rows in LDS (old tail rows + new rows), writes
-// the fp16 copies (k16/v16 rows, channel-major kT), folds |K| into k_absmax
-// and, when the append completes the group, quantizes it:
+// A complete group of new rows on a cache without fp16 copies or outlier
+// channels (the bulk of a prefill) is quantized straight from the new rows,
+// each wave on its own share (see quantize_group).  Any other group is staged
+// in LDS (old tail rows + new rows); the workgroup writes the fp16 copies
+// (k16/v16 rows, channel-major kT), folds |K| into k_absmax and, when the
+// append completes the group, quantizes it:
 //   K: per channel over the 64 tokens;  V: per token over each 64-channel half;
 //   s = fp16((max - min) / (2^b - 1) + 0), z = fp16(min + 0),
 //   code = s == 0 ? 0 : clamp(rint((x - z) / s), 0, 2^b - 1) in fp32.
