@@ -657,33 +657,51 @@ __device__ inline uint32_t wave_incl_scan(uint32_t x) {
 }
 
 // The coarse bin tb holding the k-th largest key of the pair (1 <= k <= keys
-// counted) and n_gt, the keys in the bins above it.  Wave 0 finds the
-// super-bin holding the k-th key from the super-bin sums (lane l: super-bin
-// SUP - 1 - l, highest first), then the bin inside it from that super-bin's
-// 64 bins.  Results in s_res[0] (tb) and s_res[1] (n_gt); every thread calls
-// it.
-__device__ void coarse_threshold(const uint32_t* hist, int nslot, int k, int* s_res) {
-  static_assert(SUP == 64, "one super-bin a lane");
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    if (tid == 0) {   // (k is at most the keys counted, so a lane overwrites these)
+// counted) and n_gt, the keys in the bins above it.  The NT / 64 waves sum the
+// slots in shares (lane l: super-bin SUP - 1 - l, highest first; every load of
+// a share in flight at once), wave 0 adds the shares and finds the super-bin
+// holding the k-th key, then the same for that super-bin's 64 bins.  Results in
+// s_res[0] (tb) and s_res[1] (n_gt); s_res[2..3] and s_part[NT] are scratch;
+// every thread calls it.
+template <int NT>
+__device__ void coarse_threshold(const uint32_t* hist, int nslot, int k, int* s_res, uint32_t* s_part) {
+  static_assert(SUP == 64 && NT % 64 == 0, "one super-bin a lane");
+  constexpr int NWV = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t x = 0;   // super-bin SUP - 1 - lane over the wave's share of the slots
+#pragma unroll 8
+  for (int sl = wv; sl < nslot; sl += NWV) x += hist[sl * HWS + CBINS + (SUP - 1 - lane)];
+  s_part[tid] = x;
+  lds_sync();
+  if (wv == 0) {
+    if (lane == 0) {   // (k is at most the keys counted, so a lane overwrites these)
       s_res[0] = 0;
       s_res[1] = 0;
     }
-    uint32_t x = 0;   // super-bin SUP - 1 - tid summed over the slots
-#pragma unroll 8
-    for (int sl = 0; sl < nslot; ++sl) x += hist[sl * HWS + CBINS + (SUP - 1 - tid)];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) x += s_part[w * 64 + lane];
     const uint32_t incl = wave_incl_scan(x);
     const uint64_t hit = __ballot(incl - x < (uint32_t)k && incl >= (uint32_t)k);
     const int L = hit ? __ffsll((unsigned long long)hit) - 1 : SUP - 1;
-    const int S = SUP - 1 - L;
     const uint32_t above = __shfl(incl - x, L);   // keys in the super-bins above S
-    uint32_t y = 0;
+    if (lane == 0) {
+      s_res[2] = SUP - 1 - L;                     // the super-bin S
+      s_res[3] = (int)above;
+    }
+  }
+  lds_sync();
+  const int S = s_res[2];
+  uint32_t y = 0;   // bin 64 S + 63 - lane over the wave's share of the slots
 #pragma unroll 8
-    for (int sl = 0; sl < nslot; ++sl) y += hist[sl * HWS + S * 64 + (63 - tid)];
-    const uint32_t incl2 = wave_incl_scan(y) + above;
+  for (int sl = wv; sl < nslot; sl += NWV) y += hist[sl * HWS + S * 64 + (63 - lane)];
+  s_part[tid] = y;
+  lds_sync();
+  if (wv == 0) {
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) y += s_part[w * 64 + lane];
+    const uint32_t incl2 = wave_incl_scan(y) + (uint32_t)s_res[3];
     if (incl2 - y < (uint32_t)k && incl2 >= (uint32_t)k) {
-      s_res[0] = S * 64 + 63 - tid;
+      s_res[0] = S * 64 + 63 - lane;
       s_res[1] = (int)(incl2 - y);
     }
   }
@@ -701,7 +719,8 @@ __global__ __launch_bounds__(ST) void compact_kernel(TopkArgs a) {
   const int g = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t pi = pair_index(a, b, g);
   constexpr int R = CT / ST;   // rounds
-  __shared__ int s_res[2];
+  __shared__ int s_res[4];
+  __shared__ uint32_t s_part[ST];
   __shared__ uint32_t s_cnt[R * (ST / 64)];
   __shared__ uint32_t s_acnt[R * (ST / 64)];
   __shared__ uint32_t s_off[R * (ST / 64)];
@@ -727,7 +746,7 @@ __global__ __launch_bounds__(ST) void compact_kernel(TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < R; ++j) kv[j] = keys[min(max(base + j * ST + tid, lo), hi - 1)];
   }
-  coarse_threshold(a.hist + pi * a.nslot * HWS, a.nslot, k, s_res);
+  coarse_threshold<ST>(a.hist + pi * a.nslot * HWS, a.nslot, k, s_res, s_part);
   const uint32_t tb = (uint32_t)s_res[0];
   if (blockIdx.x == 0 && tid == 0) {
     a.pmeta[2 * pi] = (int32_t)tb;
