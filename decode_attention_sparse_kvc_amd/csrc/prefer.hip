@@ -182,7 +182,23 @@ __global__ __launch_bounds__(ST) void mass_pick_kernel(MassArgs a) {
   {
     constexpr int PER = NB1 / ST;
     uint32_t tot[PER] = {};
-    for (int s2 = 0; s2 < a.S; ++s2) {
+    // eight slices a trip: 8 * PER loads in flight a thread, a round trip per
+    // eight slices instead of one per slice
+    constexpr int SB = 8;
+    int s2 = 0;
+    for (; s2 + SB <= a.S; s2 += SB) {
+      const uint32_t* hs = a.hist + ((int64_t)r * a.S + s2) * NB1 + tid;
+      uint32_t v[SB][PER];
+#pragma unroll
+      for (int q = 0; q < SB; ++q)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) v[q][j] = hs[q * NB1 + j * ST];
+#pragma unroll
+      for (int q = 0; q < SB; ++q)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) tot[j] += v[q][j];
+    }
+    for (; s2 < a.S; ++s2) {
       const uint32_t* hs = a.hist + ((int64_t)r * a.S + s2) * NB1;
 #pragma unroll
       for (int j = 0; j < PER; ++j) tot[j] += hs[tid + j * ST];
