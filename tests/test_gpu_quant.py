@@ -72,11 +72,10 @@ STEPS = [[100, 64, 3], [1, 1, 1], [63, 0, 130], [70, 5, 61], [1, 64, 0]]
 
 # (complete groups of new rows on a cache without fp16 rows or outliers take
 # the quantizer's direct-load mode, the others the staged one: both run here)
-@pytest.mark.parametrize("fmt,page", [("int4", 0), ("int1", 0), ("int4", 16), ("int1", 64),
-                                      ("int4", 32), ("int4", -16), ("fp16", 0), ("fp16", 16)])
-def test_incremental_ragged_appends(fmt, page):
-    rows16 = page == 16        # page -16: 16-token pages without the fp16 rows
-    page = abs(page)
+@pytest.mark.parametrize("fmt,page,rows", [("int4", 0, False), ("int1", 0, False), ("int4", 16, True),
+                                           ("int1", 64, False), ("int4", 32, False), ("int4", 16, False),
+                                           ("fp16", 0, True), ("fp16", 16, True)])
+def test_incremental_ragged_appends(fmt, page, rows):
     rng = np.random.default_rng(7)
     B, hkv, cap = 3, 2, 384
     total = np.sum(STEPS, axis=0)
@@ -87,8 +86,7 @@ def test_incremental_ragged_appends(fmt, page):
         per = cap // page
         table = rng.permutation(B * per).astype(np.int32).reshape(B, per)
         kw = dict(page_size=page, block_table=torch.from_numpy(table), num_pages=B * per)
-    cache = KvcCache(fmt, B, hkv, cap, fp16_rows=(fmt != "fp16" and rows16) or fmt == "fp16",
-                     kT=(fmt == "fp16" and page == 0), **kw)
+    cache = KvcCache(fmt, B, hkv, cap, fp16_rows=rows, kT=(fmt == "fp16" and page == 0), **kw)
     lens = np.zeros(B, np.int64)
     for step in STEPS:
         nmax = max(step)
