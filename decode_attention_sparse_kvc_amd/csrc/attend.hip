@@ -902,9 +902,9 @@ __device__ inline bool in_sel(const int32_t* sel, int k, int t) {
 // Plan entry of drop/keep position p of (b, g): the sinks, the selected
 // tokens and the recent window (TailorKV article section 2.3, StreamingLLM /
 // H2O survey section 3), then, in keep mode, the fp16 tail tokens outside the
-// keep set.
+// keep set (tail_in_sel: whether the tail token of position p is in sel).
 template <bool QUANT>
-__device__ inline int2 plan_entry(const AttendArgs& a, int b, int g, int n, int p) {
+__device__ inline int2 plan_entry(const AttendArgs& a, int b, int g, int n, int p, bool tail_in_sel) {
   const kvc_cache& c = a.c;
   // blocks mode on codes: the kept blocks are the quantized role's, so this
   // role's positions are the sinks and the window only (position p past the
@@ -942,7 +942,7 @@ __device__ inline int2 plan_entry(const AttendArgs& a, int b, int g, int n, int 
   }
   // keep mode: tail tokens outside the keep set
   const int t = nq + (p - nset);
-  const bool ok = t < n && t >= a.n_sink && t < w0 && !in_sel(sel, a.k_max, t);
+  const bool ok = t < n && t >= a.n_sink && t < w0 && !tail_in_sel;
   return ok ? int2{tail_code(t), tail_row + (t - nq)} : int2{ROW_SKIP, 0};
 }
 
@@ -1351,6 +1351,43 @@ void attend_kernel(AttendArgs a) {
 }
 
 // ---------------------------------------------------------------- selection plan
+// Wave-cooperative lower bounds in sel[0, k) (ascending keys, -1 padding
+// last): the first index whose key is >= T0 (r0) and >= T1 (r1), in every
+// lane.  Each step probes 64 evenly spaced entries at once and keeps the gap
+// where the keys cross the target, so the search takes about log64(k) + 1
+// round trips instead of log2(k).
+__device__ inline void wave_lower_bounds(const int32_t* sel, int k, int T0, int T1, int lane,
+                                         int& r0, int& r1) {
+  int lo0 = 0, hi0 = k, lo1 = 0, hi1 = k;
+  while (hi0 - lo0 > 64 || hi1 - lo1 > 64) {   // (uniform)
+    const int s0 = (hi0 - lo0 + 63) / 64, s1 = (hi1 - lo1 + 63) / 64;
+    const int i0 = lo0 + lane * s0, i1 = lo1 + lane * s1;
+    const bool in0 = i0 < hi0, in1 = i1 < hi1;
+    int v0 = INT_MAX, v1 = INT_MAX;
+    if (in0) v0 = sel_key(sel[i0]);
+    if (in1) v1 = sel_key(sel[i1]);
+    // the probes below the target are a prefix (c of them): the bound lies in
+    // (lo + (c - 1) s, lo + c s], or is lo when c = 0
+    const int c0 = __popcll(__ballot(in0 && v0 < T0)), c1 = __popcll(__ballot(in1 && v1 < T1));
+    if (hi0 - lo0 > 64) {
+      const int nlo = c0 > 0 ? lo0 + (c0 - 1) * s0 + 1 : lo0;
+      hi0 = min(hi0, lo0 + c0 * s0);
+      lo0 = nlo;
+    }
+    if (hi1 - lo1 > 64) {
+      const int nlo = c1 > 0 ? lo1 + (c1 - 1) * s1 + 1 : lo1;
+      hi1 = min(hi1, lo1 + c1 * s1);
+      lo1 = nlo;
+    }
+  }
+  const int i0 = lo0 + lane, i1 = lo1 + lane;
+  int v0 = INT_MAX, v1 = INT_MAX;
+  if (i0 < hi0) v0 = sel_key(sel[i0]);
+  if (i1 < hi1) v1 = sel_key(sel[i1]);
+  r0 = lo0 + __popcll(__ballot(i0 < hi0 && v0 < T0));
+  r1 = lo1 + __popcll(__ballot(i1 < hi1 && v1 < T1));
+}
+
 // Drop / keep modes, one thread per (32-token word, position) of (sequence,
 // KV head): for quantized caches, which valid sel entries fall in the word
 // (bits) and the sel index of the first entry at or after the word's first
@@ -1358,8 +1395,13 @@ void attend_kernel(AttendArgs a) {
 // position.  Every word and entry is written, so no clearing is needed.
 template <bool QUANT>
 __global__ __launch_bounds__(256) void plan_kernel(AttendArgs a) {
+  __shared__ uint32_t s_wc[4][64];   // per wave: sel entries per word
+  __shared__ uint32_t s_wb[4][64];   // per wave: valid-entry bits per word
+  __shared__ uint32_t s_tm[4][2];    // per wave: keep-mode tail tokens in sel (64 bits)
   const int g = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int e = blockIdx.x * 256 + threadIdx.x;
+  const int e0 = blockIdx.x * 256 + 64 * wv;   // the wave's first thread index (uniform)
   const int words = a.c.max_tokens / 32;
   const int64_t pi = (int64_t)b * a.c.num_kv_heads + g;
   const int n = max(a.c.seq_lens[b], 0);
@@ -1372,16 +1414,43 @@ __global__ __launch_bounds__(256) void plan_kernel(AttendArgs a) {
     const bool kept = i < a.k_max && sel[i] == j && j >= blo && j < bhi;
     a.sbits[pi * words + e] = kept ? ~0u : 0u;
     a.spre[pi * words + e] = GS * i + 32 * (e & 1);
-  } else if (QUANT && e < words) {
-    const int lo = lower_bound_sel(sel, a.k_max, 32 * e);
-    const int hi = lower_bound_sel(sel, a.k_max, 32 * e + 32);
-    uint32_t bits = 0u;
-    for (int i = lo; i < hi; ++i) {
-      const int t = sel[i];
-      if (t >= a.n_sink && t < n - a.n_window) bits |= 1u << (t & 31);
+  } else if (QUANT && e0 < words && a.mode != KVC_ATTEND_BLOCKS) {
+    // the wave's 64 words together: the sel range [L0, L1) of their tokens,
+    // then its entries binned by word in the wave's LDS (the prefix of a word
+    // is L0 plus the entries of the words before it)
+    int L0, L1;
+    wave_lower_bounds(sel, a.k_max, 32 * e0, 32 * (e0 + 64), lane, L0, L1);
+    s_wc[wv][lane] = 0u;
+    s_wb[wv][lane] = 0u;
+    wave_sync_lds();
+    for (int i0 = L0; i0 < L1; i0 += 4 * 64) {   // (uniform) four loads in flight a lane
+      int tv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + 64 * u + lane;
+        tv[u] = i < L1 ? sel[i] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = tv[u], w = (t >> 5) - e0;
+        if (i0 + 64 * u + lane < L1 && (unsigned)w < 64u) {
+          atomicAdd(&s_wc[wv][w], 1u);
+          if (t >= a.n_sink && t < n - a.n_window) atomicOr(&s_wb[wv][w], 1u << (t & 31));
+        }
+      }
     }
-    a.sbits[pi * words + e] = bits;
-    a.spre[pi * words + e] = lo;
+    wave_sync_lds();
+    const uint32_t cnt = s_wc[wv][lane];
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t x = __shfl_up(incl, o);
+      if (lane >= o) incl += x;
+    }
+    if (e < words) {
+      a.sbits[pi * words + e] = s_wb[wv][lane];
+      a.spre[pi * words + e] = L0 + (int)(incl - cnt);
+    }
   }
   if (QUANT && a.mode == KVC_ATTEND_BLOCKS) {
     // groups the quantized role walks, ascending and disjoint: those holding
@@ -1424,7 +1493,25 @@ __global__ __launch_bounds__(256) void plan_kernel(AttendArgs a) {
       else if (e == 0 && !v) a.kfill[pi] = 0;
     }
   }
-  if (e < a.np) a.rplan[pi * a.np + e] = plan_entry<QUANT>(a, b, g, n, e);
+  // keep mode, tail positions [nset, nset + 64): whether each tail token is in
+  // sel, from the 64 entries at the lower bound of the tail's first token
+  // (waves that hold such positions, uniform)
+  bool tail_in = false;
+  const int nset = a.n_sink + a.nsel + a.n_window;
+  if (a.mode == KVC_ATTEND_KEEP && e0 < a.np && e0 + 64 > nset && e0 < nset + GS) {
+    const int nq = QUANT ? (n & ~(GS - 1)) : 0;
+    int lb, unused;
+    wave_lower_bounds(sel, a.k_max, nq, nq, lane, lb, unused);
+    if (lane < 2) s_tm[wv][lane] = 0u;
+    wave_sync_lds();
+    const int i = lb + lane;
+    const int t = i < a.k_max ? sel[i] : -1, d = t - nq;
+    if ((unsigned)d < 64u) atomicOr(&s_tm[wv][d >> 5], 1u << (d & 31));
+    wave_sync_lds();
+    const int dp = e - nset;   // this position's tail token is nq + dp
+    if ((unsigned)dp < 64u) tail_in = (s_tm[wv][dp >> 5] >> (dp & 31)) & 1u;
+  }
+  if (e < a.np) a.rplan[pi * a.np + e] = plan_entry<QUANT>(a, b, g, n, e, tail_in);
 }
 
 // ---------------------------------------------------------------- split merge
