@@ -172,14 +172,8 @@ __device__ inline double token_score(int G, int nch_, const int* sch, const doub
   for (int hh = 0; hh < GN; ++hh) acc[hh] = 0.0;
   // (batches stay a loop: unrolling the 128-channel exact sum over G heads
   // leaves more live values than the registers hold)
-#pragma unroll 1
-  for (int k0 = 0; k0 < (ALL ? D : nch); k0 += CB) {
-    int ch[CB];
-    uint32_t raw[CB], mx[CB];
-#pragma unroll
-    for (int u = 0; u < CB; ++u) ch[u] = ALL ? k0 + u : sch[min(k0 + u, nch - 1)];
-#pragma unroll
-    for (int u = 0; u < CB; ++u) raw[u] = load(ch[u]);   // global loads, all in flight
+  const auto add_batch = [&](int k0, const int* ch, const uint32_t* raw) {
+    uint32_t mx[CB];
 #pragma unroll
     for (int u = 0; u < CB; ++u) mx[u] = aux(ch[u]);     // LDS reads, all in flight
 #pragma unroll
@@ -194,6 +188,45 @@ __device__ inline double token_score(int G, int nch_, const int* sch, const doub
           acc[hh] = on ? nx : acc[hh];
         }
       }
+    }
+  };
+  if constexpr (ALL && GT > 0 && GT <= 4) {
+    // Every channel, up to 4 heads: each batch's global loads go out before
+    // the previous batch's arithmetic, so the token's batches share one round
+    // trip (larger groups have no registers to spare for it).
+    int ch[CB];
+    uint32_t raw[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) ch[u] = u;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) raw[u] = load(ch[u]);
+#pragma unroll 1
+    for (int k0 = 0; k0 < D; k0 += CB) {
+      int chn[CB];
+      uint32_t rawn[CB] = {};
+#pragma unroll
+      for (int u = 0; u < CB; ++u) chn[u] = k0 + CB + u;
+      if (k0 + CB < D) {
+#pragma unroll
+        for (int u = 0; u < CB; ++u) rawn[u] = load(chn[u]);
+      }
+      add_batch(k0, ch, raw);
+#pragma unroll
+      for (int u = 0; u < CB; ++u) {
+        ch[u] = chn[u];
+        raw[u] = rawn[u];
+      }
+    }
+  } else {
+#pragma unroll 1
+    for (int k0 = 0; k0 < nch; k0 += CB) {
+      int ch[CB];
+      uint32_t raw[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) ch[u] = ALL ? k0 + u : sch[min(k0 + u, nch - 1)];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) raw[u] = load(ch[u]);   // global loads, all in flight
+      add_batch(k0, ch, raw);
     }
   }
   double r = acc[0];
