@@ -967,9 +967,12 @@ __global__ __launch_bounds__(FT) void finish_direct_kernel(TopkArgs a) {
   const uint64_t* gkeys = a.keys + pi * a.c.max_tokens;
   const bool fx = keys_from_ext(a);
   const float* ex = fx ? a.ext + pi * a.c.max_tokens : nullptr;
-  {   // candidates only; every load of the row is issued before the LDS stores
-    constexpr int R = DIRECT_MAX / FT;
-    uint64_t kv[R];
+  // candidates only; every load of the row is issued before the LDS stores.
+  // Each thread keeps its items (j FT + tid) in registers for the selection
+  // passes; the emission reads the row back from LDS in index order.
+  constexpr int R = DIRECT_MAX / FT;
+  uint64_t kv[R];
+  {
     if (fx) {
       float xv[R];
 #pragma unroll
@@ -983,7 +986,8 @@ __global__ __launch_bounds__(FT) void finish_direct_kernel(TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const int i = j * FT + tid;
-      if (i < N) L.key[i] = i >= lo && i < hi ? kv[j] : 0ull;
+      kv[j] = i >= lo && i < hi && i < N ? kv[j] : 0ull;
+      if (i < N) L.key[i] = kv[j];
     }
   }
   lds_sync();
@@ -991,10 +995,9 @@ __global__ __launch_bounds__(FT) void finish_direct_kernel(TopkArgs a) {
   // short ranges)
   const int krem0 = k;
   auto for_cand = [&](auto&& f) {
-    for (int i = tid; i < N; i += FT) {
-      const uint64_t key = L.key[i];
-      if (key) f(key);
-    }
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (kv[j]) f(kv[j]);
   };
   uint64_t P;
   int krem, bits;
